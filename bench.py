@@ -1,0 +1,256 @@
+"""Decode-step throughput of the tiered KV-cache hot path on one MI355X.
+
+A step is one pass of the whole device path over one batch of synthetic input:
+append the new token's K/V, attention over T0 u T1 with the normalised weights
+written out, the fused importance-score update, and every Delta steps the tier
+ranking, the compaction of the T0 pool / T1 window and the int8 rows of new T2
+tokens.  Inputs are resident in HBM before the timed region starts; the T1
+rows are in their device window (the host-link transfer is measured on its own
+and reported under "pcie", never in `value`).
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--workload", default="chain8k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-pcie", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="bound on the oracle's timed CPU work")
+    return p.parse_args()
+
+
+def step_bytes(wl, n_att: int, n: int) -> dict:
+    """Algorithmic HBM bytes of one decode step (per sequence, all layers)."""
+    L, Hq, Hkv, D = wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim
+    e = 2 if wl.dtype == "bf16" else 4
+    kv = 2 * L * Hkv * n_att * D * e          # K and V rows of the attended set
+    q = L * Hq * D * e
+    o = L * Hq * D * 4
+    alpha = L * Hq * n_att * 4                 # normalised weights, written once
+    s = 8 * n_att                              # score read-modify-write
+    append = 2 * 2 * L * Hkv * D * e           # new row read + pool write
+    return {"kv": kv, "q": q, "o": o, "alpha": alpha, "scores": s, "append": append,
+            "total": kv + q + o + alpha + s + append}
+
+
+def attn_partial_bytes(wl, n_att: int) -> int:
+    """Algorithmic bytes of one attn_partial launch: K/V of the attended set, the
+    queries, and the raw logits it writes (read back once to normalise)."""
+    L, Hq, Hkv, D = wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim
+    e = 2 if wl.dtype == "bf16" else 4
+    return 2 * L * Hkv * n_att * D * e + L * Hq * D * e + L * Hq * n_att * 4
+
+
+def reassign_bytes(wl, n: int, n0: int, n1: int, r2: int) -> int:
+    """Algorithmic bytes of one reassignment (amortised over Delta steps)."""
+    L, Hkv, D = wl.layers, wl.kv_heads, wl.head_dim
+    e = 2 if wl.dtype == "bf16" else 4
+    tiers = n * (4 + 1 + 1)                    # scores + previous map read, new map write
+    compact = (n0 + n1) * 2 * L * Hkv * D * e * 2 + n * 2
+    quant = r2 * L * Hkv * 2 * (D * e + D + 4)
+    return tiers + compact + quant
+
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import Policy, TieredSequence
+    from tiered_kv_cache_amd.synth import SequenceStream
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    st = SequenceStream(wl, 0)
+    K, V = st.context()
+    pol = Policy(wl.prompt, wl.sinks, wl.recent, wl.frac_t1, wl.frac_t2, wl.frac_t3, wl.delta)
+    seq = TieredSequence(K, V, pol, cap=wl.max_ctx)
+    times = []
+    t_start = time.perf_counter()
+    k = 0
+    while k < wl.delta and (time.perf_counter() - t_start) < seconds:
+        k += 1
+        q = st.query(k)
+        kn, vn = st.new_kv(k)
+        t0 = time.perf_counter()
+        seq.step(q, kn, vn, reassign=False)
+        times.append(time.perf_counter() - t0)
+    t0 = time.perf_counter()
+    seq.reassign()
+    t_re = time.perf_counter() - t0
+    step_s = float(np.mean(times)) + t_re / wl.delta
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"first {len(times)} decode steps of {wl.name} (full cache, "
+                       f"{seq.n - len(times)}+ attended tokens, float64 NumPy) plus one "
+                       f"reassignment amortised over delta={wl.delta}"),
+            "ms_per_step": step_s * 1e3, "reassign_ms": t_re * 1e3, "cpu": model,
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def pcie_leg(wl, cache, positions) -> dict:
+    """Host-link path of T1: host pack into pinned staging + H2D on a side stream."""
+    import numpy as np
+    import torch
+    from tiered_kv_cache_amd import tkv
+
+    L, Hkv, D = wl.layers, wl.kv_heads, wl.head_dim
+    cap1, max_ctx = cache.cap1, cache.max_ctx
+    dt = cache.shape.torch_dtype
+    r = np.random.default_rng(0)
+    host_k = torch.from_numpy(r.integers(0, 1 << 15, size=(L, Hkv, max_ctx, D), dtype=np.int16)).view(dt)
+    host_v = host_k.clone()
+    stg_k = torch.empty((L, Hkv, cap1, D), dtype=dt).pin_memory()
+    stg_v = torch.empty((L, Hkv, cap1, D), dtype=dt).pin_memory()
+    dev_k = torch.empty((L, Hkv, cap1, D), dtype=dt, device="cuda")
+    dev_v = torch.empty((L, Hkv, cap1, D), dtype=dt, device="cuda")
+    side = torch.cuda.Stream()
+    n1 = len(positions)
+    bytes_t1 = 2 * L * Hkv * n1 * D * dev_k.element_size()
+    t0 = time.perf_counter()
+    tkv.tkv_gather_t1(cache.model, host_k, host_v, max_ctx, positions, n1, stg_k, stg_v, cap1,
+                      None, None, side, None)
+    t_pack = time.perf_counter() - t0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    ev0.record(side)
+    for _ in range(reps):
+        tkv.tkv_gather_t1(cache.model, None, None, max_ctx, None, n1, stg_k, stg_v, cap1,
+                          dev_k, dev_v, side, None)
+    ev1.record(side)
+    ev1.synchronize()
+    t_h2d = ev0.elapsed_time(ev1) / 1e3 / reps
+    return {"t1_rows": n1, "t1_bytes": bytes_t1, "pack_ms": t_pack * 1e3,
+            "pack_gbps": bytes_t1 / t_pack / 1e9, "h2d_ms": t_h2d * 1e3,
+            "h2d_gbps": bytes_t1 / t_h2d / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the tiered "
+              "path shards by sequence or KV head and needs no collective per step, but no "
+              "multi-GPU run is part of this build", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from tiered_kv_cache_amd import tkv
+    from tiered_kv_cache_amd.synth import WORKLOADS
+    from tiered_kv_cache_amd.workload import DeviceWorkload
+
+    tkv.lib()
+    wl = WORKLOADS[args.workload].scaled(steps=args.steps, warmup=args.warmup)
+    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    dw = DeviceWorkload(wl)
+    cache = dw.make_cache()
+    inputs = dw.preload(1, wl.total_steps)
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up {args.warmup} steps", file=sys.stderr, flush=True)
+    for k in range(1, args.warmup + 1):
+        cache.step(*inputs[k - 1])
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, kernel timers live on the compute stream
+    n_att_steps, n_steps = [], []
+    re_info = []
+    tkv.tkv_timing_reset()
+    tkv.tkv_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.warmup + 1, args.warmup + args.steps + 1):
+        n_att_steps.append(sum(cache.t0_len) + sum(cache.t1_len) + wl.batch)
+        n_steps.append(sum(cache.n) + wl.batch)
+        if cache.step(*inputs[k - 1]):
+            re_info.append((sum(cache.n), sum(cache.t0_len), sum(cache.t1_len), sum(cache.t2_new)))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tkv.tkv_timing_enable(False)
+    kernels = {}
+    for name in ("append", "attn_partial", "attn_combine", "alpha_score", "assign_tiers",
+                 "compact_scan", "compact_copy", "quantize_t2"):
+        ms, cnt = tkv.tkv_timing_read(name)
+        if cnt:
+            kernels[name] = {"launches": cnt, "avg_us": ms * 1e3 / cnt, "total_ms": ms}
+
+    steps_per_s = args.steps / elapsed
+    step_b = [step_bytes(wl, n_att, n)["total"] for n_att, n in zip(n_att_steps, n_steps)]
+    re_b = sum(reassign_bytes(wl, *r) for r in re_info)
+    alg_bytes = (sum(step_b) + re_b) / args.steps
+    attn = kernels.get("attn_partial", {"launches": 1, "avg_us": float("nan"), "total_ms": float("nan")})
+    attn_bytes = float(np.mean([attn_partial_bytes(wl, n) for n in n_att_steps]))
+    achieved = attn_bytes / (attn["avg_us"] * 1e-6) / 1e9
+
+    out = {
+        "metric": "decode steps/sec (attn+score+tier) at 8K ctx; achieved HBM GB/s vs peak",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded generator: sinks, planted resurfacing keys, N(0,1) K/V)",
+        "config": {"workload": f"{wl.name}: {wl.description}", "batch": wl.batch,
+                   "context": list(wl.ctx) if wl.batch > 1 else wl.ctx[0],
+                   "layers": wl.layers, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
+                   "head_dim": wl.head_dim,
+                   "tiers_t0_t1_t2_t3": [round(1 - wl.frac_t1 - wl.frac_t2 - wl.frac_t3, 4),
+                                         wl.frac_t1, wl.frac_t2, wl.frac_t3],
+                   "delta": wl.delta, "reassignments_timed": len(re_info)},
+        "roofline": {"bound": "hbm", "kernel": "attn_partial", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_per_launch": attn_bytes,
+                     "avg_launch_us": attn["avg_us"]},
+        "step_hbm": {"algorithmic_bytes_per_step": alg_bytes,
+                     "achieved_gbps": alg_bytes * steps_per_s / 1e9,
+                     "frac": alg_bytes * steps_per_s / 1e9 / PEAK_HBM_GBS,
+                     "mean_attended_tokens": float(np.mean(n_att_steps))},
+        "kernels": kernels,
+    }
+    if not args.no_pcie:
+        try:
+            t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()
+            out["pcie"] = pcie_leg(wl, cache, t1)
+            out["pcie"]["note"] = ("host-link path of T1, not part of value: host pack into "
+                                   "pinned staging, then hipMemcpy2DAsync on a side stream")
+        except Exception as e:  # reported, never fatal for the device number
+            out["pcie"] = {"error": repr(e)}
+    if not args.no_cpu_baseline:
+        print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

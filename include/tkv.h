@@ -1,0 +1,293 @@
+/*
+ * tkv.h -- C ABI of the tiered KV-cache decode hot path (libtkv.so, gfx950).
+ *
+ * The method: the technical summary pages of "Not All Thoughts Need HBM"
+ * (gist.science, paper 2605.09490; the French page's section names are used
+ * below).  A reasoning model's KV cache is split into four tiers by a cumulative
+ * attention-importance score: T0 in HBM (protected prompt, sink and recent
+ * tokens plus the most important ones), T1 in host DDR at full precision and
+ * brought to the GPU before each attention step, T2 on the host at 8 bits, and
+ * T3 dropped (Methodologie section 1).  The score adds, every decode step, the
+ * attention weight each position receives averaged over heads and layers
+ * (Methodologie section 2).  Tiers are recomputed every Delta = 64 steps
+ * (Methodologie section 4).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns tkv_status: TKV_OK (0) or a negative code.  On a
+ *   negative code nothing has been enqueued, except TKV_ERR_HIP from a failed
+ *   launch or copy; tkv_last_error() then holds a message (thread-local).
+ * - Arguments are validated before any HIP call.  Device-resident contents
+ *   (tier maps, slot maps) cannot be validated from the host; where a kernel
+ *   detects a bad state it reports it through its count outputs (documented
+ *   per call) and leaves its other outputs unspecified.
+ * - The caller owns every buffer.  The library allocates no caller-visible
+ *   memory and keeps no pointer after it returns.  Device buffers must stay
+ *   alive until the stream has passed the call.
+ * - All device work is asynchronous on the caller's stream.  Per-sequence
+ *   lengths arrive as HOST int32 arrays so that grids are sized without a sync.
+ * - Key/value/query elements are bf16 bit patterns (uint16) when
+ *   kv_dtype == TKV_BF16, or float32 when kv_dtype == TKV_F32.
+ * - Layouts are row-major; "[B][L][Hkv][cap][D]" means D is contiguous.
+ *   Per sequence, the T0 pool holds the T0 positions in ascending order in
+ *   slots [0, t0_len) and the T1 window holds the T1 positions in ascending
+ *   order in slots [0, t1_len).  The "attended index" j of a sequence runs over
+ *   T0 slots then T1 slots: j < t0_len is T0 slot j, otherwise T1 slot
+ *   j - t0_len.
+ * - Query head h reads KV head h / (Hq / Hkv) (contiguous grouping).
+ * - Supported shapes: head_dim 64 or 128; 1 <= Hq / Hkv <= 16.
+ * - Calls on one stream are ordered; calls that write the same buffers on
+ *   different streams race.  The library itself holds no mutable global state
+ *   apart from the optional kernel timers (tkv_timing_*), which are meant for
+ *   benchmarks and are not thread-safe.
+ */
+#ifndef TKV_H
+#define TKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tkv_status;
+#define TKV_OK 0
+#define TKV_ERR_ARG (-1)      /* null pointer, bad shape, bad fraction, bad order */
+#define TKV_ERR_CAPACITY (-2) /* a length above its capacity, workspace too small */
+#define TKV_ERR_STATE (-3)    /* inconsistent lengths / maps detected on the host */
+#define TKV_ERR_HIP (-4)      /* a HIP runtime call failed; see tkv_last_error() */
+
+#define TKV_BF16 0
+#define TKV_F32 1
+
+#define TKV_ABI_VERSION 1
+
+/* Model shape.  softmax_scale <= 0 selects 1/sqrt(head_dim). */
+typedef struct {
+  int32_t num_layers;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype; /* TKV_BF16 or TKV_F32 */
+  float softmax_scale;
+} tkv_model;
+
+/* Tier policy (Methodologie sections 1 and 4).  The fractions are of the
+ * current length n: N_k = floor((double)frac_tk * n) for k = 1, 2, 3 and T0
+ * takes the rest.  Protected positions: [0, max(prompt_len, num_sinks)) and
+ * the last recent_window positions. */
+typedef struct {
+  int32_t prompt_len;
+  int32_t num_sinks;
+  int32_t recent_window;
+  float frac_t1;
+  float frac_t2;
+  float frac_t3;
+  int32_t delta;
+} tkv_policy;
+
+int32_t tkv_abi_version(void);
+/* Message of the last failure on this thread ("" if none). */
+const char* tkv_last_error(void);
+
+/*
+ * tkv_append -- every generated token adds one key/value pair, which enters T0
+ * (Enonce du probleme; Methodologie section 1: the recent window is in T0).
+ *
+ * k_new, v_new : device [B][L][Hkv][D]
+ * k_t0, v_t0   : device T0 pools [B][L][Hkv][cap0][D]; row slot t0_len[b] of
+ *                sequence b is written
+ * t0_len       : host [B], current T0 length (the slot written); < cap0
+ * t0_pos       : device [B][cap0] slot -> position map; t0_pos[b][t0_len[b]]
+ *                is set to position[b]
+ * position     : host [B], position of the new token (its current length n)
+ * scores, tier : optional device [B][max_ctx]; if non-null, scores[b][pos] = 0
+ *                and tier[b][pos] = 0 (T0).  position[b] < max_ctx.
+ */
+tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new,
+                      const void* v_new, void* k_t0, void* v_t0, int32_t cap0,
+                      const int32_t* t0_len, int32_t* t0_pos, const int32_t* position,
+                      float* scores, uint8_t* tier, int32_t max_ctx, hipStream_t stream);
+
+/* Bytes of device workspace tkv_decode_step needs for these capacities. */
+size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t n_layers,
+                                  int32_t cap0, int32_t cap1);
+
+/*
+ * tkv_decode_step -- decode attention over the attended set A = T0 u T1 of
+ * layers [layer_begin, layer_end), with the T1 rows already in their device
+ * window (Methodologie section 1, T1 is brought to the GPU before attention;
+ * section 3, it then contributes exactly as if it had stayed in HBM).  Writes
+ * the output and the normalised attention weights alpha, which the importance
+ * score sums (Methodologie section 2).
+ *
+ * q          : device [B][Lr][Hq][D], Lr = layer_end - layer_begin
+ * k_t0, v_t0 : device [B][L][Hkv][cap0][D];  t0_len host [B] (<= cap0)
+ * k_t1, v_t1 : device [B][L][Hkv][cap1][D];  t1_len host [B] (<= cap1); may be
+ *              null when every t1_len is 0
+ * out        : device [B][Lr][Hq][D] float32
+ * alpha      : device [B][Lr][Hq][alpha_stride] float32; entry j is the weight
+ *              of attended index j (alpha_stride >= t0_len + t1_len)
+ * Fused score update (optional: pass scores = null to skip): with t0_pos
+ *   [B][cap0], t1_pos [B][cap1] (device slot -> position maps) and scores
+ *   device [B][max_ctx] float32, adds to scores[b][pos(j)] the sum over the
+ *   call's layers and heads of alpha / (num_layers * Hq), exactly what
+ *   tkv_update_scores would add.
+ * workspace  : device, at least tkv_decode_workspace_bytes(model, batch, Lr,
+ *              cap0, cap1) bytes
+ * A sequence with t0_len + t1_len == 0 gets out = 0 and no weights.
+ */
+tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                           int32_t layer_end, const void* q, const void* k_t0,
+                           const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                           const void* k_t1, const void* v_t1, const int32_t* t1_len,
+                           int32_t cap1, float* out, float* alpha, int32_t alpha_stride,
+                           const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
+                           int32_t max_ctx, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * tkv_update_scores -- the importance-score recurrence (Methodologie section 2):
+ * scores[b][pos(j)] += (1/(num_layers*Hq)) * sum over layers in
+ * [layer_begin, layer_end) and heads of alpha[b][l][h][j], for every attended
+ * index j.  Calling it once for all layers or once per layer adds the same
+ * mass (up to float32 summation order).
+ *
+ * alpha  : device [B][Lr][Hq][alpha_stride] float32 (normalised weights)
+ * t0_pos, t1_pos : device slot -> position maps [B][cap0], [B][cap1]
+ * t0_len, t1_len : host [B]
+ * scores : device [B][max_ctx] float32, read-modify-write
+ */
+tkv_status tkv_update_scores(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                             int32_t layer_end, const float* alpha, int32_t alpha_stride,
+                             const int32_t* t0_pos, const int32_t* t0_len, int32_t cap0,
+                             const int32_t* t1_pos, const int32_t* t1_len, int32_t cap1,
+                             float* scores, int32_t max_ctx, hipStream_t stream);
+
+/*
+ * tkv_assign_tiers -- rank positions [0, ctx_len[b]) of every sequence into
+ * T0..T3 (Methodologie sections 1 and 4).  Keep order: higher score first,
+ * equal scores keep the lower position first.  Always taking the least
+ * important candidates:
+ *   1. T3 is absorbing; evict clamp(N3 - |T3|, 0, |pool|) more from the
+ *      non-protected positions in T0/T1/T2;
+ *   2. surviving T2 positions stay T2; move clamp(N2 - |survivors|, 0, |live|)
+ *      more from the remaining non-protected T0/T1 positions into T2;
+ *   3. move min(N1, |live left|) of the rest into T1;
+ *   4. everything else (with protected T0/T1 positions) becomes T0.
+ *
+ * ctx_len   : host [B], current length n of each sequence (<= max_ctx)
+ * scores    : device [B][max_ctx] float32 (finite values)
+ * tier_prev : device [B][max_ctx] uint8 previous tiers (0..3)
+ * tier_next : device [B][max_ctx] uint8 new tiers; may equal tier_prev
+ * counts    : device [B][4] int32 counts of T0..T3.  If tier_prev holds a
+ *             value above 3, counts[b] is {-1,-1,-1,-1} and tier_next of that
+ *             sequence is left untouched.
+ * Bit-exact and deterministic: ties are broken by position only.
+ */
+tkv_status tkv_assign_tiers(int32_t batch, const int32_t* ctx_len, int32_t max_ctx,
+                            const float* scores, const tkv_policy* policy,
+                            const uint8_t* tier_prev, uint8_t* tier_next, int32_t* counts,
+                            hipStream_t stream);
+
+/* Bytes of device workspace tkv_compact needs. */
+size_t tkv_compact_workspace_bytes(int32_t batch, int32_t cap0, int32_t cap1);
+
+/*
+ * tkv_compact -- after a reassignment, rebuild the resident T0 pool and the
+ * T1 window in ascending position order from the previous pool and window,
+ * and list the positions that newly entered T2 (Methodologie section 4:
+ * tiers change every Delta steps; only tokens that change tier move).
+ * Positions newly in T3 are simply not copied.  Every new T0/T1 row is found
+ * on the device, because T2 and T3 never return to T0/T1.
+ *
+ * Preconditions: the *_src pools/windows hold exactly the tier_prev T0 / T1
+ * positions in ascending order (t0_len_src[b] / t1_len_src[b] of them), and
+ * the *_dst buffers do not overlap the *_src ones.
+ * ctx_len           : host [B]
+ * tier_prev/next    : device [B][max_ctx]
+ * k/v_t0_src, t0_len_src (host [B]), cap0 : previous T0 pool [B][L][Hkv][cap0][D]
+ * k/v_t1_src, t1_len_src (host [B]), cap1 : previous T1 window [B][L][Hkv][cap1][D]
+ * k/v_t0_dst, t0_pos_dst : new T0 pool and its slot -> position map [B][cap0]
+ * k/v_t1_dst, t1_pos_dst : new T1 window and its map [B][cap1]
+ * t2_src    : device [B][t2_cap]: source of each newly-T2 row, in ascending
+ *             position order: s >= 0 is previous T0 slot s, s < 0 is previous
+ *             T1 slot -s-1 (the encoding tkv_quantize_t2 reads)
+ * t2_pos    : device [B][t2_cap]: their positions
+ * new_lens  : device [B][3] int32: new T0 length, new T1 length, newly-T2 count.
+ *             If a capacity would be exceeded or the tier maps disagree with
+ *             the source lengths (a T2/T3 position marked T0/T1 again, or
+ *             counts not matching t0_len_src/t1_len_src), new_lens[b] is
+ *             {-1,-1,-1} and the destination contents are unspecified.
+ */
+tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
+                       int32_t max_ctx, const uint8_t* tier_prev, const uint8_t* tier_next,
+                       const void* k_t0_src, const void* v_t0_src, const int32_t* t0_len_src,
+                       int32_t cap0, const void* k_t1_src, const void* v_t1_src,
+                       const int32_t* t1_len_src, int32_t cap1, void* k_t0_dst,
+                       void* v_t0_dst, int32_t* t0_pos_dst, void* k_t1_dst, void* v_t1_dst,
+                       int32_t* t1_pos_dst, int32_t* t2_src, int32_t* t2_pos, int32_t t2_cap,
+                       int32_t* new_lens, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * tkv_quantize_t2 -- 8-bit rows of the tokens that enter T2 (Methodologie
+ * section 1, T2 holds low-importance tokens at reduced precision, 8-bit
+ * quantisation being the example).  Per (row, layer, KV head, K or V) row of D
+ * values x: scale = absmax(x) / 127 and code = round-half-even(x / scale),
+ * both IEEE float32 divisions, clamped to [-127, 127]; an all-zero row gets
+ * scale 0 and codes 0.  Dequantised value: code * scale.
+ *
+ * k/v_t0, cap0, k/v_t1, cap1 : the pool and window the rows are read from
+ * src     : device [B][max_rows]: s >= 0 is T0 slot s, s < 0 is T1 slot -s-1
+ * n_rows  : device int32, element b * n_rows_stride is the row count of
+ *           sequence b (tkv_compact's new_lens with stride 3, offset 2, fits)
+ * max_rows: host bound on every row count (rows at or beyond it are ignored)
+ * codes   : device [B][max_rows][L][Hkv][2][D] int8 (index 0 = K, 1 = V)
+ * scales  : device [B][max_rows][L][Hkv][2] float32
+ */
+tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_t0,
+                           const void* v_t0, int32_t cap0, const void* k_t1, const void* v_t1,
+                           int32_t cap1, const int32_t* src, const int32_t* n_rows,
+                           int32_t n_rows_stride, int32_t max_rows, int8_t* codes,
+                           float* scales, hipStream_t stream);
+
+/*
+ * tkv_gather_t1 -- bring one sequence's T1 rows to the GPU (Methodologie
+ * section 1: T1 stays in host DDR at full precision and is brought to the GPU
+ * before each attention step).  Packs the rows of the host store at the given
+ * positions, in the given (ascending) order, into contiguous pinned staging
+ * with host threads, then queues the host-to-device copy of the staging on
+ * side_stream and records `ready` there.  The attention stream must wait on
+ * `ready` before reading the window.
+ *
+ * host_k, host_v   : host [L][Hkv][max_ctx][D] full-precision store
+ * positions        : host [n_t1], strictly ascending, each < max_ctx; null
+ *                    re-sends the staging as it is (no pack)
+ * staging_k/v      : pinned host [L][Hkv][cap1][D] (n_t1 <= cap1)
+ * dev_k_t1/dev_v_t1: device window [L][Hkv][cap1][D]; null packs only
+ * ready            : event recorded on side_stream after the copies; may be null
+ * The pack is synchronous on the calling thread; only the copies are queued.
+ */
+tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k, const void* host_v,
+                         int32_t max_ctx, const int32_t* positions, int32_t n_t1,
+                         void* staging_k, void* staging_v, int32_t cap1, void* dev_k_t1,
+                         void* dev_v_t1, hipStream_t side_stream, hipEvent_t ready);
+
+/*
+ * Kernel timers for benchmarks.  While enabled, every kernel the library
+ * launches is bracketed by HIP events on its own stream; tkv_timing_read
+ * synchronises those events and returns the summed milliseconds and launch
+ * count of one kernel (by name, e.g. "attn_partial") since the last reset.
+ * Not thread-safe.
+ */
+tkv_status tkv_timing_enable(int32_t enable);
+tkv_status tkv_timing_reset(void);
+tkv_status tkv_timing_read(const char* kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TKV_H */

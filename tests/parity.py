@@ -1,0 +1,246 @@
+"""Helpers of the GPU parity tests: run the HIP path and the CPU oracle side by side.
+
+Tolerances (written here once, used by every parity test):
+* attention output O: per (sequence, layer, head), max|O_gpu - O_ref| / max|O_ref| <= 2e-3;
+* attention weights alpha: the same per-row bar, plus elementwise |d alpha| <= 1e-3 alpha + 1e-9;
+* importance scores: elementwise |s_gpu - s_ref| <= 1e-5 s_ref + 1e-12;
+* tiers, counts, slot maps, T1 window bytes, int8 codes and scales: bit-exact, given the
+  same float32 scores (the oracle ranks the GPU's scores at each reassignment).
+"""
+from __future__ import annotations
+
+import sys
+from collections import defaultdict
+
+import numpy as np
+import torch
+
+from oracle import Policy, TieredSequence, attention, assign_tiers, quantize_rows, widen
+from tiered_kv_cache_amd.driver import to_device, to_host_bits
+from tiered_kv_cache_amd.synth import SequenceStream, Workload
+from tiered_kv_cache_amd.workload import DeviceWorkload
+
+O_TOL = 2e-3
+S_RTOL = 1e-5
+S_ATOL = 1e-12
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_policy(wl: Workload) -> Policy:
+    return Policy(wl.prompt, wl.sinks, wl.recent, wl.frac_t1, wl.frac_t2, wl.frac_t3, wl.delta)
+
+
+def rel_rows(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows (last axis = row content) of max|got-ref| / max|ref|."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return float((np.abs(got - ref).max(axis=-1) / den).max()) if ref.size else 0.0
+
+
+def check_output(got, ref, stats, what="O"):
+    r = rel_rows(got, ref)
+    stats[what] = max(stats[what], r)
+    assert r <= O_TOL, f"{what}: relative error {r:.3e} > {O_TOL}"
+
+
+def check_alpha(got, ref, stats):
+    check_output(got, ref, stats, "alpha_row")
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    bad = err > 1e-3 * np.abs(ref) + 1e-9
+    stats["alpha_el"] = max(stats["alpha_el"], float((err / np.maximum(ref, 1e-30)).max()))
+    assert not bad.any(), f"alpha elementwise: {int(bad.sum())} entries off, max {err.max():.3e}"
+
+
+def check_scores(got, ref, stats):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    lim = S_RTOL * np.abs(ref) + S_ATOL
+    rel = float((err / np.maximum(np.abs(ref), 1e-30)).max()) if ref.size else 0.0
+    stats["score_rel"] = max(stats["score_rel"], rel)
+    assert (err <= lim).all(), f"scores: {int((err > lim).sum())} positions off, max rel {rel:.3e}"
+
+
+def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, stats):
+    """After both sides reassigned from the same float32 scores: bit-exact state."""
+    n = seq.n
+    t_gpu = cache.tiers[b, :n].cpu().numpy()
+    assert np.array_equal(t_gpu, seq.tier[:n]), \
+        f"tiers differ at {np.nonzero(t_gpu != seq.tier[:n])[0][:10]}"
+    counts = cache.counts[b].cpu().numpy()
+    assert counts.tolist() == [int((seq.tier[:n] == t).sum()) for t in range(4)]
+    t0 = np.nonzero(seq.tier[:n] == 0)[0]
+    assert cache.t0_len[b] == len(t0) and cache.t1_len[b] == len(seq.t1_positions)
+    assert np.array_equal(cache.t0_pos[b, :len(t0)].cpu().numpy(), t0)
+    assert np.array_equal(cache.t1_pos[b, :cache.t1_len[b]].cpu().numpy(), seq.t1_positions)
+    m1 = cache.t1_len[b]
+    k1 = to_host_bits(cache.k_t1[b, :, :, :m1])
+    v1 = to_host_bits(cache.v_t1[b, :, :, :m1])
+    assert k1.tobytes() == np.ascontiguousarray(seq.t1_K).tobytes(), "T1 window keys differ"
+    assert v1.tobytes() == np.ascontiguousarray(seq.t1_V).tobytes(), "T1 window values differ"
+    new_t2 = np.nonzero((seq.tier[:n] == 2) & (prev_tiers[:n] <= 1))[0]
+    pos, codes, scales = cache.last_t2(b)
+    assert np.array_equal(pos, new_t2), "newly-T2 positions differ"
+    for i, p in enumerate(pos.tolist()):
+        rc, rs = seq.t2_codes[p]
+        assert np.array_equal(codes[i], rc), f"int8 codes differ at position {p}"
+        assert np.array_equal(scales[i].view(np.uint32), rs.view(np.uint32)), \
+            f"scales differ at position {p}"
+    stats["t2_rows"] += len(pos)
+    stats["reassignments"] += 1
+
+
+def run_lockstep(wl: Workload, n_steps: int = None, label: str = "") -> dict:
+    """Every step compared; re-sync of the ranking at each reassignment."""
+    n_steps = n_steps or wl.total_steps
+    dw = DeviceWorkload(wl)
+    cache = dw.make_cache()
+    pol = oracle_policy(wl)
+    seqs = []
+    for b in range(wl.batch):
+        K, V = dw.streams[b].context()
+        seqs.append(TieredSequence(K, V, pol, cap=cache.max_ctx))
+    stats = defaultdict(float)
+    for k in range(1, n_steps + 1):
+        q, kn, vn = dw.host_step(k)
+        cache.append(to_device(kn, dw.dtype, dw.device), to_device(vn, dw.dtype, dw.device))
+        cache.attend(to_device(q, dw.dtype, dw.device))
+        cache.steps += 1
+        torch.cuda.synchronize()
+        out = cache.out.cpu().numpy()
+        for b, seq in enumerate(seqs):
+            O, alpha, pos = seq.step(q[b], kn[b], vn[b], reassign=False)
+            assert np.array_equal(cache.attended_positions(b), pos), f"attended set, step {k}"
+            check_output(out[b], O, stats)
+            check_alpha(cache.alpha_of(b), alpha, stats)
+            check_scores(cache.scores[b, :seq.n].cpu().numpy(), seq.s[:seq.n], stats)
+        if k % wl.delta == 0:
+            gpu_scores = cache.scores.cpu().numpy()
+            prevs = [s.tier.copy() for s in seqs]
+            cache.reassign()
+            torch.cuda.synchronize()
+            for b, seq in enumerate(seqs):
+                seq.reassign(scores=gpu_scores[b])
+                check_reassignment(cache, b, seq, prevs[b], gpu_scores[b], stats)
+    stats["steps"] = n_steps
+    say(f"[{label or wl.name}] lockstep ok: " +
+        ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))
+    return stats
+
+
+class HostStore:
+    """Full-precision copy of every sequence's K/V rows ([L][Hkv][cap][D] per sequence),
+    filled from the shared generator: the inputs the sampled full-size checks read."""
+
+    def __init__(self, dw: DeviceWorkload, cap: int):
+        self.K, self.V = [], []
+        for st in dw.streams:
+            K0, V0 = st.context()
+            L, H, n0, D = K0.shape
+            K = np.zeros((L, H, cap, D), K0.dtype)
+            V = np.zeros((L, H, cap, D), V0.dtype)
+            K[:, :, :n0] = K0
+            V[:, :, :n0] = V0
+            self.K.append(K)
+            self.V.append(V)
+
+    def put(self, b, pos, k, v):
+        self.K[b][:, :, pos] = k
+        self.V[b][:, :, pos] = v
+
+
+def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=(),
+                label: str = "") -> dict:
+    """Full-size run, checked on samples the oracle computes one at a time:
+    * O and alpha of the sampled (layer, head) pairs over the GPU's attended set;
+    * the whole score increment at `full_inc_steps` (all layers and heads);
+    * total score mass == steps (any size);
+    * at every reassignment: tiers from the oracle ranking of the GPU's scores, the
+      counts, slot maps, T1 window bytes and the int8 rows of new T2 positions.
+    """
+    dw = DeviceWorkload(wl)
+    cache = dw.make_cache()
+    store = HostStore(dw, cache.max_ctx)
+    pol = oracle_policy(wl)
+    scale = 1.0 / np.sqrt(wl.head_dim)
+    stats = defaultdict(float)
+    group = wl.q_heads // wl.kv_heads
+    for k in range(1, n_steps + 1):
+        q, kn, vn = dw.host_step(k)
+        for b in range(wl.batch):
+            store.put(b, cache.n[b], kn[b], vn[b])
+        s_before = cache.scores.cpu().numpy() if k in full_inc_steps else None
+        cache.append(to_device(kn, dw.dtype, dw.device), to_device(vn, dw.dtype, dw.device))
+        cache.attend(to_device(q, dw.dtype, dw.device))
+        cache.steps += 1
+        if k in sample_steps or k in full_inc_steps:
+            torch.cuda.synchronize()
+            out = cache.out.cpu().numpy()
+            for b in range(wl.batch):
+                pos = cache.attended_positions(b)
+                alpha_gpu = cache.alpha_of(b)
+                layers = range(wl.layers) if k in full_inc_steps else sorted({l for l, _ in heads})
+                inc = np.zeros(cache.n[b])
+                for l in layers:
+                    Kl = store.K[b][l][:, pos]
+                    Vl = store.V[b][l][:, pos]
+                    hs = range(wl.q_heads) if k in full_inc_steps else [h for ll, h in heads if ll == l]
+                    for h in hs:
+                        g = h // group
+                        O, a = attention(q[b][l][h:h + 1], Kl[g:g + 1], Vl[g:g + 1], scale)
+                        check_output(out[b, l, h][None], O, stats)
+                        check_alpha(alpha_gpu[l, h][None], a, stats)
+                        inc[pos] += a[0]
+                if k in full_inc_steps:
+                    inc /= (wl.layers * wl.q_heads)
+                    got = cache.scores[b, :cache.n[b]].cpu().numpy().astype(np.float64) - s_before[b, :cache.n[b]]
+                    err = np.abs(got - inc)
+                    # the difference of two float32 sums carries their rounding (~1 ulp of s)
+                    lim = 1e-5 * inc + 2.0 ** -23 * np.abs(s_before[b, :cache.n[b]]) * 2 + 1e-12
+                    assert (err <= lim).all(), f"score increment, step {k}, seq {b}: max {err.max():.3e}"
+                    stats["inc_checked"] += 1
+        if k % wl.delta == 0:
+            torch.cuda.synchronize()
+            gpu_scores = cache.scores.cpu().numpy()
+            prev = cache.tiers.cpu().numpy()
+            for b in range(wl.batch):
+                mass = float(gpu_scores[b, :cache.n[b]].astype(np.float64).sum())
+                assert abs(mass - k) <= 1e-4 * k, f"score mass {mass} after {k} steps"
+            cache.reassign()
+            torch.cuda.synchronize()
+            for b in range(wl.batch):
+                n = cache.n[b]
+                t_ref, counts = assign_tiers(gpu_scores[b, :n].astype(np.float64), prev[b, :n], n, pol)
+                t_gpu = cache.tiers[b, :n].cpu().numpy()
+                assert np.array_equal(t_gpu, t_ref), f"tiers differ (step {k}, seq {b})"
+                assert cache.counts[b].cpu().numpy().tolist() == counts.tolist()
+                t0 = np.nonzero(t_ref == 0)[0]
+                t1 = np.nonzero(t_ref == 1)[0]
+                assert np.array_equal(cache.t0_pos[b, :cache.t0_len[b]].cpu().numpy(), t0)
+                assert np.array_equal(cache.t1_pos[b, :cache.t1_len[b]].cpu().numpy(), t1)
+                m1 = len(t1)
+                assert to_host_bits(cache.k_t1[b, :, :, :m1]).tobytes() == \
+                    np.ascontiguousarray(store.K[b][:, :, t1]).tobytes()
+                assert to_host_bits(cache.v_t1[b, :, :, :m1]).tobytes() == \
+                    np.ascontiguousarray(store.V[b][:, :, t1]).tobytes()
+                new_t2 = np.nonzero((t_ref == 2) & (prev[b, :n] <= 1))[0]
+                pos, codes, scales = cache.last_t2(b)
+                assert np.array_equal(pos, new_t2)
+                if len(pos):
+                    ck, sk = quantize_rows(widen(store.K[b][:, :, pos]).astype(np.float32))
+                    cv, sv = quantize_rows(widen(store.V[b][:, :, pos]).astype(np.float32))
+                    # oracle layout [L][Hkv][rows][D] -> [rows][L][Hkv][2][D]
+                    ref_codes = np.stack([ck, cv], axis=3).transpose(2, 0, 1, 3, 4)
+                    ref_scales = np.stack([sk, sv], axis=3).transpose(2, 0, 1, 3)
+                    assert np.array_equal(codes, ref_codes), "int8 codes differ"
+                    assert np.array_equal(scales.view(np.uint32), ref_scales.view(np.uint32))
+                stats["t2_rows"] += len(pos)
+                stats["reassignments"] += 1
+    stats["steps"] = n_steps
+    say(f"[{label or wl.name}] sampled ok: " +
+        ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))
+    return stats

@@ -1,0 +1,160 @@
+"""The C ABI (include/tkv.h) on the host: the library loads, exports every declared
+entry point, and rejects bad arguments with the documented status before any HIP call
+(so these run without a GPU; no compute call is made)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tiered_kv_cache_amd import tkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+NULL = None
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tkv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return tkv.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tkv.EXPORTED)
+    assert tkv.tkv_abi_version() == 1
+
+
+def model(**kw):
+    d = dict(layers=2, q_heads=8, kv_heads=2, head_dim=128, kv_dtype=tkv.TKV_BF16)
+    d.update(kw)
+    return tkv.make_model(**d)
+
+
+def policy(**kw):
+    d = dict(prompt=4, sinks=2, recent=4, f1=0.3, f2=0.2, f3=0.1, delta=4)
+    d.update(kw)
+    return tkv.make_policy(**d)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def decode(m, **kw):
+    args = dict(batch=1, layer_begin=0, layer_end=m.num_layers, q=FAKE, k_t0=FAKE, v_t0=FAKE,
+                t0_len=[10], cap0=16, k_t1=FAKE, v_t1=FAKE, t1_len=[2], cap1=8, out=FAKE,
+                alpha=FAKE, alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE, scores=FAKE, max_ctx=64,
+                workspace=FAKE, workspace_bytes=1 << 30, stream=0)
+    args.update(kw)
+    return tkv.tkv_decode_step(m, **args)
+
+
+def status_of(fn, *a, **kw):
+    with pytest.raises(tkv.TkvError) as e:
+        fn(*a, **kw)
+    return e.value.status
+
+
+def test_model_validation():
+    assert status_of(decode, model(q_heads=7, kv_heads=2)) == tkv.TKV_ERR_ARG
+    assert status_of(decode, model(head_dim=96)) == tkv.TKV_ERR_ARG
+    assert status_of(decode, model(kv_dtype=7)) == tkv.TKV_ERR_ARG
+    assert status_of(decode, model(q_heads=24, kv_heads=2)) == tkv.TKV_ERR_ARG  # group 12
+    assert status_of(decode, model(layers=0)) == tkv.TKV_ERR_ARG
+
+
+def test_decode_step_validation():
+    m = model()
+    assert status_of(decode, m, layer_begin=1, layer_end=1) == tkv.TKV_ERR_ARG
+    assert status_of(decode, m, layer_end=3) == tkv.TKV_ERR_ARG
+    assert status_of(decode, m, q=NULL) == tkv.TKV_ERR_ARG
+    assert status_of(decode, m, t0_len=[17]) == tkv.TKV_ERR_CAPACITY
+    assert status_of(decode, m, t1_len=[9]) == tkv.TKV_ERR_CAPACITY
+    assert status_of(decode, m, alpha_stride=11) == tkv.TKV_ERR_CAPACITY
+    assert status_of(decode, m, workspace_bytes=16) == tkv.TKV_ERR_CAPACITY
+    assert status_of(decode, m, k_t1=NULL) == tkv.TKV_ERR_ARG
+    assert status_of(decode, m, t1_pos=NULL) == tkv.TKV_ERR_ARG
+    assert status_of(decode, m, t0_len=[-1]) == tkv.TKV_ERR_ARG
+    msg = tkv.lib().tkv_last_error().decode()
+    assert "negative" in msg
+
+
+def test_workspace_size_formula():
+    m = model()
+    a = tkv.tkv_decode_workspace_bytes(m, 1, 2, 256, 256)
+    b = tkv.tkv_decode_workspace_bytes(m, 2, 2, 256, 256)
+    assert b > a > 0
+    assert tkv.tkv_decode_workspace_bytes(m, -1, 2, 256, 256) == 0
+
+
+def test_assign_tiers_validation():
+    args = dict(batch=1, ctx_len=[10], max_ctx=16, scores=FAKE, tier_prev=FAKE,
+                tier_next=FAKE, counts=FAKE, stream=0)
+    for bad in (policy(f1=-0.1), policy(f1=0.5, f2=0.4, f3=0.2), policy(delta=0),
+                policy(recent=-1)):
+        assert status_of(tkv.tkv_assign_tiers, policy=bad, **args) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_assign_tiers, policy=policy(),
+                     **{**args, "ctx_len": [17]}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_assign_tiers, policy=policy(),
+                     **{**args, "scores": NULL}) == tkv.TKV_ERR_ARG
+
+
+def test_compact_and_quant_validation():
+    m = model()
+    args = dict(model=m, batch=1, ctx_len=[10], max_ctx=16, tier_prev=FAKE, tier_next=FAKE,
+                k_t0_src=FAKE, v_t0_src=FAKE, t0_len_src=[6], cap0=16, k_t1_src=FAKE,
+                v_t1_src=FAKE, t1_len_src=[3], cap1=8, k_t0_dst=FAKE + 64, v_t0_dst=FAKE + 64,
+                t0_pos_dst=FAKE, k_t1_dst=FAKE + 64, v_t1_dst=FAKE + 64, t1_pos_dst=FAKE,
+                t2_src=FAKE, t2_pos=FAKE, t2_cap=8, new_lens=FAKE, workspace=FAKE,
+                workspace_bytes=1 << 20, stream=0)
+    assert status_of(tkv.tkv_compact, **{**args, "t0_len_src": [8]}) == tkv.TKV_ERR_STATE
+    assert status_of(tkv.tkv_compact, **{**args, "t1_len_src": [9]}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_compact, **{**args, "k_t0_dst": FAKE}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_compact, **{**args, "workspace_bytes": 8}) == tkv.TKV_ERR_CAPACITY
+    qargs = dict(model=m, batch=1, k_t0=FAKE, v_t0=FAKE, cap0=16, k_t1=FAKE, v_t1=FAKE, cap1=8,
+                 src=FAKE, n_rows=FAKE, n_rows_stride=3, max_rows=4, codes=FAKE, scales=FAKE,
+                 stream=0)
+    assert status_of(tkv.tkv_quantize_t2, **{**qargs, "src": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_quantize_t2, **{**qargs, "n_rows_stride": 0}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_quantize_t2, **{**qargs, "max_rows": 70000}) == tkv.TKV_ERR_CAPACITY
+
+
+def test_append_validation():
+    m = model()
+    args = dict(model=m, batch=1, k_new=FAKE, v_new=FAKE, k_t0=FAKE, v_t0=FAKE, cap0=16,
+                t0_len=[16], t0_pos=FAKE, position=[20], scores=FAKE, tier=FAKE, max_ctx=64,
+                stream=0)
+    assert status_of(tkv.tkv_append, **args) == tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_append, **{**args, "t0_len": [3], "position": [64]}) == \
+        tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_append, **{**args, "k_new": NULL}) == tkv.TKV_ERR_ARG
+
+
+def test_gather_host_pack_without_device():
+    # positions ascending check, then a pack-only call (no device pointers -> no HIP call)
+    m = model(layers=2, kv_heads=2, q_heads=2, head_dim=64)
+    r = np.random.default_rng(0)
+    max_ctx, cap1 = 40, 8
+    hk = r.integers(0, 65535, size=(2, 2, max_ctx, 64)).astype(np.uint16)
+    hv = r.integers(0, 65535, size=(2, 2, max_ctx, 64)).astype(np.uint16)
+    sk = np.zeros((2, 2, cap1, 64), np.uint16)
+    sv = np.zeros((2, 2, cap1, 64), np.uint16)
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 2], 2, sk, sv, cap1) == \
+        tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 40], 2, sk, sv, cap1) == \
+        tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, list(range(9)), 9, sk, sv, cap1) == \
+        tkv.TKV_ERR_CAPACITY
+    pos = [1, 5, 6, 17, 39]
+    tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), sk, sv, cap1)
+    assert sk[:, :, :5].tobytes() == hk[:, :, pos].tobytes()
+    assert sv[:, :, :5].tobytes() == hv[:, :, pos].tobytes()

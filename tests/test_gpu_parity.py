@@ -1,0 +1,51 @@
+"""GPU parity of the whole decode path against the CPU oracle, through the C ABI.
+
+Small workloads are compared at every step; full-size workloads on sampled outputs
+the oracle computes one at a time and on size-independent properties.  Tolerances are
+in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.parity import run_lockstep, run_sampled, say
+from tiered_kv_cache_amd.synth import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fp32_lockstep():
+    wl = WORKLOADS["tiny"]
+    st = run_lockstep(wl)
+    assert st["reassignments"] == 4 and st["t2_rows"] > 0
+
+
+def test_tiny_prop1_no_eviction_equals_full_attention():
+    # T2 = T3 = 0 (40/60/0/0): the tiered output equals full attention at every step
+    wl = WORKLOADS["tiny"].with_fractions(0.6, 0.0, 0.0, "_40-60-0-0")
+    st = run_lockstep(wl)
+    assert st["reassignments"] == 4 and st["t2_rows"] == 0
+
+
+def test_small_gqa4_lockstep():
+    wl = WORKLOADS["small"]
+    st = run_lockstep(wl)
+    assert st["reassignments"] == 3
+
+
+def test_ragged_batch_d64_lockstep():
+    base = WORKLOADS["small"]
+    wl = base.scaled(name="ragged5_L2_h8kv2_d64", layers=2, head_dim=64, batch=5,
+                     ctx=(130, 700, 257, 1100, 64), warmup=8, steps=16, delta=8, prompt=16,
+                     recent=16, sinks=4, planted=(2, 8, 4, 10, 0), frac_t1=0.4, frac_t2=0.15,
+                     frac_t3=0.05)
+    st = run_lockstep(wl)
+    assert st["reassignments"] == 3
+
+
+def test_chain8k_full_size_sampled():
+    wl = WORKLOADS["chain8k"]
+    heads = [(0, 0), (0, 6), (13, 20), (27, 27)]
+    st = run_sampled(wl, n_steps=130, sample_steps={1, 63, 64, 65, 100, 128, 129},
+                     heads=heads, full_inc_steps={2, 66})
+    assert st["reassignments"] == 2

@@ -1,0 +1,543 @@
+// C ABI of libtkv: argument validation, batch splitting, kernel dispatch.
+// Every check runs before the first HIP call of an entry point.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace tkv {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+tkv_status fail(tkv_status code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+tkv_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TKV_OK;
+  return fail(TKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// kernel timers (benchmark aid)
+// ---------------------------------------------------------------------------
+namespace {
+struct TimerRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+struct TimerState {
+  bool enabled = false;
+  std::vector<TimerRec> pending;
+  std::vector<hipEvent_t> free_events;
+  std::map<std::string, std::pair<double, long long>> totals;
+};
+TimerState& timers() {
+  static TimerState t;
+  return t;
+}
+hipEvent_t take_event() {
+  auto& t = timers();
+  if (!t.free_events.empty()) {
+    hipEvent_t e = t.free_events.back();
+    t.free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+void drain_timers() {
+  auto& t = timers();
+  for (auto& r : t.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess &&
+        hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      auto& tot = t.totals[r.name];
+      tot.first += ms;
+      tot.second += 1;
+    }
+    t.free_events.push_back(r.start);
+    t.free_events.push_back(r.stop);
+  }
+  t.pending.clear();
+}
+}  // namespace
+
+KernelTimer::KernelTimer(const char* name, hipStream_t s) : name_(name), stream_(s), ev_(nullptr) {
+  if (!timers().enabled) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, s) == hipSuccess) ev_ = e;
+}
+
+KernelTimer::~KernelTimer() {
+  if (!ev_) return;
+  hipEvent_t stop = take_event();
+  if (!stop || hipEventRecord(stop, stream_) != hipSuccess) return;
+  timers().pending.push_back({name_, (hipEvent_t)ev_, stop});
+  if (timers().pending.size() > 4096) drain_timers();
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+static tkv_status check_model(const tkv_model* m) {
+  if (!m) return fail(TKV_ERR_ARG, "model is null");
+  if (m->num_layers < 1 || m->num_q_heads < 1 || m->num_kv_heads < 1)
+    return fail(TKV_ERR_ARG, "layers and heads must be positive");
+  if (m->num_q_heads % m->num_kv_heads != 0)
+    return fail(TKV_ERR_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (!attn_group_supported(m->num_q_heads / m->num_kv_heads))
+    return fail(TKV_ERR_ARG, "query heads per KV head must be 1..8 or 16");
+  if (m->head_dim != 64 && m->head_dim != 128) return fail(TKV_ERR_ARG, "head_dim must be 64 or 128");
+  if (m->kv_dtype != TKV_BF16 && m->kv_dtype != TKV_F32) return fail(TKV_ERR_ARG, "bad kv_dtype");
+  if (!(m->softmax_scale == m->softmax_scale) || isinf(m->softmax_scale))
+    return fail(TKV_ERR_ARG, "softmax_scale must be finite");
+  return TKV_OK;
+}
+
+static float scale_of(const tkv_model* m) {
+  return m->softmax_scale > 0.f ? m->softmax_scale : 1.0f / sqrtf((float)m->head_dim);
+}
+
+static size_t elem_size(const tkv_model* m) { return m->kv_dtype == TKV_BF16 ? 2 : 4; }
+
+static int max_splits_for(int cap0, int cap1) { return ceil_div((long)cap0 + cap1, kAttnChunk); }
+
+}  // namespace tkv
+
+using namespace tkv;
+
+extern "C" {
+
+int32_t tkv_abi_version(void) { return TKV_ABI_VERSION; }
+
+const char* tkv_last_error(void) { return g_last_error.c_str(); }
+
+tkv_status tkv_timing_enable(int32_t enable) {
+  timers().enabled = enable != 0;
+  return TKV_OK;
+}
+
+tkv_status tkv_timing_reset(void) {
+  drain_timers();
+  timers().totals.clear();
+  return TKV_OK;
+}
+
+tkv_status tkv_timing_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(TKV_ERR_ARG, "null argument");
+  drain_timers();
+  auto it = timers().totals.find(kernel);
+  *total_ms = it == timers().totals.end() ? 0.0 : it->second.first;
+  *launches = it == timers().totals.end() ? 0 : it->second.second;
+  return TKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new, const void* v_new,
+                      void* k_t0, void* v_t0, int32_t cap0, const int32_t* t0_len,
+                      int32_t* t0_pos, const int32_t* position, float* scores, uint8_t* tier,
+                      int32_t max_ctx, hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (batch == 0) return TKV_OK;
+  if (!k_new || !v_new || !k_t0 || !v_t0 || !t0_len || !t0_pos || !position)
+    return fail(TKV_ERR_ARG, "null pointer");
+  if (cap0 < 1) return fail(TKV_ERR_ARG, "cap0 < 1");
+  for (int b = 0; b < batch; ++b) {
+    if (t0_len[b] < 0 || position[b] < 0) return fail(TKV_ERR_ARG, "negative length or position");
+    if (t0_len[b] >= cap0) return fail(TKV_ERR_CAPACITY, "T0 pool full (t0_len >= cap0)");
+    if ((scores || tier) && position[b] >= max_ctx)
+      return fail(TKV_ERR_CAPACITY, "position >= max_ctx");
+  }
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    AppendArgs a{};
+    a.kn = k_new;
+    a.vn = v_new;
+    a.k0 = k_t0;
+    a.v0 = v_t0;
+    a.t0_pos = t0_pos;
+    a.scores = scores;
+    a.tier = tier;
+    a.cap0 = cap0;
+    a.max_ctx = max_ctx;
+    a.L = model->num_layers;
+    a.hkv = model->num_kv_heads;
+    a.b_offset = b0;
+    for (int i = 0; i < nb; ++i) {
+      a.slot[i] = t0_len[b0 + i];
+      a.pos[i] = position[b0 + i];
+    }
+    launch_append(a, model->kv_dtype, model->head_dim, nb, stream);
+    if ((st = hip_check(hipGetLastError(), "append launch"))) return st;
+  }
+  return TKV_OK;
+}
+
+size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t n_layers,
+                                  int32_t cap0, int32_t cap1) {
+  if (!model || batch < 0 || n_layers < 0 || cap0 < 0 || cap1 < 0) return 0;
+  const size_t rows = (size_t)batch * n_layers * model->num_q_heads;
+  const size_t ms = (size_t)max_splits_for(cap0, cap1);
+  const size_t D = (size_t)model->head_dim;
+  return rows * ms * (D + 2) * sizeof(float) + rows * 2 * sizeof(float) + 256;
+}
+
+tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                           int32_t layer_end, const void* q, const void* k_t0, const void* v_t0,
+                           const int32_t* t0_len, int32_t cap0, const void* k_t1,
+                           const void* v_t1, const int32_t* t1_len, int32_t cap1, float* out,
+                           float* alpha, int32_t alpha_stride, const int32_t* t0_pos,
+                           const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (layer_begin < 0 || layer_end > model->num_layers || layer_begin >= layer_end)
+    return fail(TKV_ERR_ARG, "need 0 <= layer_begin < layer_end <= num_layers");
+  if (batch == 0) return TKV_OK;
+  if (!q || !k_t0 || !v_t0 || !t0_len || !t1_len || !out || !alpha || !workspace)
+    return fail(TKV_ERR_ARG, "null pointer");
+  if (cap0 < 0 || cap1 < 0 || alpha_stride < 1) return fail(TKV_ERR_ARG, "bad capacity or stride");
+  bool any_t1 = false;
+  for (int b = 0; b < batch; ++b) {
+    if (t0_len[b] < 0 || t1_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
+    if (t0_len[b] > cap0 || t1_len[b] > cap1) return fail(TKV_ERR_CAPACITY, "length > capacity");
+    if ((long)t0_len[b] + t1_len[b] > alpha_stride)
+      return fail(TKV_ERR_CAPACITY, "alpha_stride < t0_len + t1_len");
+    any_t1 |= t1_len[b] > 0;
+  }
+  if (any_t1 && (!k_t1 || !v_t1)) return fail(TKV_ERR_ARG, "T1 window is null but t1_len > 0");
+  if (scores && (!t0_pos || (any_t1 && !t1_pos) || max_ctx < 1))
+    return fail(TKV_ERR_ARG, "fused score update needs t0_pos, t1_pos and max_ctx");
+  const int Lr = layer_end - layer_begin;
+  if (workspace_bytes < tkv_decode_workspace_bytes(model, batch, Lr, cap0, cap1))
+    return fail(TKV_ERR_CAPACITY, "workspace too small");
+
+  const int hq = model->num_q_heads;
+  const int D = model->head_dim;
+  const int max_splits = max_splits_for(cap0, cap1);
+  float* part = (float*)workspace;
+  float* ml = part + (size_t)batch * Lr * hq * max_splits * D;
+  float* stat = ml + (size_t)batch * Lr * hq * max_splits * 2;
+
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    AttnArgs a{};
+    a.q = q;
+    a.k0 = k_t0;
+    a.v0 = v_t0;
+    a.k1 = k_t1;
+    a.v1 = v_t1;
+    a.out = out;
+    a.alpha = alpha;
+    a.part = part;
+    a.ml = ml;
+    a.stat = stat;
+    a.alpha_stride = alpha_stride;
+    a.cap0 = cap0;
+    a.cap1 = cap1;
+    a.L = model->num_layers;
+    a.Lr = Lr;
+    a.layer_begin = layer_begin;
+    a.hq = hq;
+    a.hkv = model->num_kv_heads;
+    a.max_splits = max_splits;
+    a.scale = scale_of(model);
+    a.seq.nb = nb;
+    a.seq.b_offset = b0;
+    int chunks = 0, sblocks = 0;
+    ScoreArgs sa{};
+    for (int i = 0; i < nb; ++i) {
+      a.seq.t0_len[i] = t0_len[b0 + i];
+      a.seq.t1_len[i] = t1_len[b0 + i];
+      a.seq.base[i] = chunks;
+      sa.seq.base[i] = sblocks;
+      const int natt = t0_len[b0 + i] + t1_len[b0 + i];
+      chunks += ceil_div(natt, kAttnChunk);
+      sblocks += ceil_div(natt, 64);
+    }
+    a.seq.base[nb] = chunks;
+    if (chunks > 0) {
+      launch_attn_partial(a, model->kv_dtype, D, hq / model->num_kv_heads, chunks, stream);
+      if ((st = hip_check(hipGetLastError(), "attn_partial launch"))) return st;
+    }
+    launch_attn_combine(a, D, nb, stream);
+    if ((st = hip_check(hipGetLastError(), "attn_combine launch"))) return st;
+
+    sa.alpha = alpha;
+    sa.stat = stat;
+    sa.t0_pos = t0_pos;
+    sa.t1_pos = t1_pos;
+    sa.scores = scores;
+    sa.alpha_stride = alpha_stride;
+    sa.rows = Lr * hq;
+    sa.normalise = 1;
+    sa.cap0 = cap0;
+    sa.cap1 = cap1;
+    sa.max_ctx = max_ctx;
+    sa.weight = 1.0 / ((double)model->num_layers * hq);
+    sa.seq.nb = nb;
+    sa.seq.b_offset = b0;
+    for (int i = 0; i < nb; ++i) {
+      sa.seq.t0_len[i] = t0_len[b0 + i];
+      sa.seq.t1_len[i] = t1_len[b0 + i];
+    }
+    sa.seq.base[nb] = sblocks;
+    if (!scores) {
+      // normalise only: the score kernel without a score buffer
+      sa.scores = nullptr;
+    }
+    if (sblocks > 0) {
+      launch_alpha_score(sa, sblocks, stream);
+      if ((st = hip_check(hipGetLastError(), "alpha_score launch"))) return st;
+    }
+  }
+  return TKV_OK;
+}
+
+tkv_status tkv_update_scores(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                             int32_t layer_end, const float* alpha, int32_t alpha_stride,
+                             const int32_t* t0_pos, const int32_t* t0_len, int32_t cap0,
+                             const int32_t* t1_pos, const int32_t* t1_len, int32_t cap1,
+                             float* scores, int32_t max_ctx, hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (layer_begin < 0 || layer_end > model->num_layers || layer_begin >= layer_end)
+    return fail(TKV_ERR_ARG, "need 0 <= layer_begin < layer_end <= num_layers");
+  if (batch == 0) return TKV_OK;
+  if (!alpha || !t0_pos || !t0_len || !t1_len || !scores) return fail(TKV_ERR_ARG, "null pointer");
+  if (alpha_stride < 1 || max_ctx < 1 || cap0 < 0 || cap1 < 0)
+    return fail(TKV_ERR_ARG, "bad capacity or stride");
+  bool any_t1 = false;
+  for (int b = 0; b < batch; ++b) {
+    if (t0_len[b] < 0 || t1_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
+    if (t0_len[b] > cap0 || t1_len[b] > cap1) return fail(TKV_ERR_CAPACITY, "length > capacity");
+    if ((long)t0_len[b] + t1_len[b] > alpha_stride)
+      return fail(TKV_ERR_CAPACITY, "alpha_stride < t0_len + t1_len");
+    any_t1 |= t1_len[b] > 0;
+  }
+  if (any_t1 && !t1_pos) return fail(TKV_ERR_ARG, "t1_pos is null but t1_len > 0");
+  const int Lr = layer_end - layer_begin;
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    ScoreArgs sa{};
+    sa.alpha = const_cast<float*>(alpha);  // read only when normalise == 0
+    sa.stat = nullptr;
+    sa.t0_pos = t0_pos;
+    sa.t1_pos = t1_pos;
+    sa.scores = scores;
+    sa.alpha_stride = alpha_stride;
+    sa.rows = Lr * model->num_q_heads;
+    sa.normalise = 0;
+    sa.cap0 = cap0;
+    sa.cap1 = cap1;
+    sa.max_ctx = max_ctx;
+    sa.weight = 1.0 / ((double)model->num_layers * model->num_q_heads);
+    sa.seq.nb = nb;
+    sa.seq.b_offset = b0;
+    int sblocks = 0;
+    for (int i = 0; i < nb; ++i) {
+      sa.seq.t0_len[i] = t0_len[b0 + i];
+      sa.seq.t1_len[i] = t1_len[b0 + i];
+      sa.seq.base[i] = sblocks;
+      sblocks += ceil_div(t0_len[b0 + i] + t1_len[b0 + i], 64);
+    }
+    sa.seq.base[nb] = sblocks;
+    if (sblocks > 0) {
+      launch_alpha_score(sa, sblocks, stream);
+      if ((st = hip_check(hipGetLastError(), "update_scores launch"))) return st;
+    }
+  }
+  return TKV_OK;
+}
+
+tkv_status tkv_assign_tiers(int32_t batch, const int32_t* ctx_len, int32_t max_ctx,
+                            const float* scores, const tkv_policy* policy,
+                            const uint8_t* tier_prev, uint8_t* tier_next, int32_t* counts,
+                            hipStream_t stream) {
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (!policy) return fail(TKV_ERR_ARG, "policy is null");
+  const float f1 = policy->frac_t1, f2 = policy->frac_t2, f3 = policy->frac_t3;
+  if (!(f1 >= 0.f && f2 >= 0.f && f3 >= 0.f) || (double)f1 + f2 + f3 > 1.0)
+    return fail(TKV_ERR_ARG, "tier fractions must be >= 0 and sum to <= 1");
+  if (policy->prompt_len < 0 || policy->num_sinks < 0 || policy->recent_window < 0)
+    return fail(TKV_ERR_ARG, "negative protected size");
+  if (policy->delta < 1) return fail(TKV_ERR_ARG, "delta < 1");
+  if (batch == 0) return TKV_OK;
+  if (!ctx_len || !scores || !tier_prev || !tier_next || !counts)
+    return fail(TKV_ERR_ARG, "null pointer");
+  if (max_ctx < 1) return fail(TKV_ERR_ARG, "max_ctx < 1");
+  for (int b = 0; b < batch; ++b) {
+    if (ctx_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
+    if (ctx_len[b] > max_ctx) return fail(TKV_ERR_CAPACITY, "ctx_len > max_ctx");
+  }
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    TierArgs a{};
+    a.scores = scores;
+    a.tprev = tier_prev;
+    a.tnext = tier_next;
+    a.counts = counts;
+    a.max_ctx = max_ctx;
+    a.prot_lo = std::max(policy->prompt_len, policy->num_sinks);
+    a.recent = policy->recent_window;
+    a.b_offset = b0;
+    for (int i = 0; i < nb; ++i) {
+      const int n = ctx_len[b0 + i];
+      a.n[i] = n;
+      a.n1[i] = (int)floor((double)f1 * (double)n);
+      a.n2[i] = (int)floor((double)f2 * (double)n);
+      a.n3[i] = (int)floor((double)f3 * (double)n);
+    }
+    launch_assign_tiers(a, nb, stream);
+    tkv_status st = hip_check(hipGetLastError(), "assign_tiers launch");
+    if (st) return st;
+  }
+  return TKV_OK;
+}
+
+size_t tkv_compact_workspace_bytes(int32_t batch, int32_t cap0, int32_t cap1) {
+  if (batch < 0 || cap0 < 0 || cap1 < 0) return 0;
+  return (size_t)batch * ((size_t)cap0 + cap1) * sizeof(int32_t) + 256;
+}
+
+tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
+                       int32_t max_ctx, const uint8_t* tier_prev, const uint8_t* tier_next,
+                       const void* k_t0_src, const void* v_t0_src, const int32_t* t0_len_src,
+                       int32_t cap0, const void* k_t1_src, const void* v_t1_src,
+                       const int32_t* t1_len_src, int32_t cap1, void* k_t0_dst, void* v_t0_dst,
+                       int32_t* t0_pos_dst, void* k_t1_dst, void* v_t1_dst, int32_t* t1_pos_dst,
+                       int32_t* t2_src, int32_t* t2_pos, int32_t t2_cap, int32_t* new_lens,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (batch == 0) return TKV_OK;
+  if (!ctx_len || !tier_prev || !tier_next || !k_t0_src || !v_t0_src || !t0_len_src ||
+      !t1_len_src || !k_t0_dst || !v_t0_dst || !t0_pos_dst || !t2_src || !t2_pos ||
+      !new_lens || !workspace)
+    return fail(TKV_ERR_ARG, "null pointer");
+  if (cap1 > 0 && (!k_t1_src || !v_t1_src || !k_t1_dst || !v_t1_dst || !t1_pos_dst))
+    return fail(TKV_ERR_ARG, "null T1 pointer with cap1 > 0");
+  if (cap0 < 1 || cap1 < 0 || t2_cap < 0 || max_ctx < 1)
+    return fail(TKV_ERR_ARG, "bad capacity");
+  if (k_t0_src == k_t0_dst || v_t0_src == v_t0_dst || (cap1 > 0 && (k_t1_src == k_t1_dst ||
+                                                                    v_t1_src == v_t1_dst)))
+    return fail(TKV_ERR_ARG, "source and destination buffers must differ");
+  int max_n = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (ctx_len[b] < 0 || t0_len_src[b] < 0 || t1_len_src[b] < 0)
+      return fail(TKV_ERR_ARG, "negative length");
+    if (ctx_len[b] > max_ctx) return fail(TKV_ERR_CAPACITY, "ctx_len > max_ctx");
+    if (t0_len_src[b] > cap0 || t1_len_src[b] > cap1)
+      return fail(TKV_ERR_CAPACITY, "source length > capacity");
+    if ((long)t0_len_src[b] + t1_len_src[b] > ctx_len[b])
+      return fail(TKV_ERR_STATE, "t0_len + t1_len > ctx_len");
+    max_n = std::max(max_n, ctx_len[b]);
+  }
+  if (workspace_bytes < tkv_compact_workspace_bytes(batch, cap0, cap1))
+    return fail(TKV_ERR_CAPACITY, "workspace too small");
+  int* src0 = (int*)workspace;
+  int* src1 = src0 + (size_t)batch * cap0;
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    CompactArgs a{};
+    a.tprev = tier_prev;
+    a.tnext = tier_next;
+    a.t0_pos_dst = t0_pos_dst;
+    a.t1_pos_dst = t1_pos_dst;
+    a.src0 = src0;
+    a.src1 = src1;
+    a.t2_src = t2_src;
+    a.t2_pos = t2_pos;
+    a.new_lens = new_lens;
+    a.max_ctx = max_ctx;
+    a.cap0 = cap0;
+    a.cap1 = cap1;
+    a.t2_cap = t2_cap;
+    a.b_offset = b0;
+    int mx = 0;
+    for (int i = 0; i < nb; ++i) {
+      a.n[i] = ctx_len[b0 + i];
+      a.len0[i] = t0_len_src[b0 + i];
+      a.len1[i] = t1_len_src[b0 + i];
+      mx = std::max(mx, ctx_len[b0 + i]);
+    }
+    CopyArgs c{};
+    c.k0s = k_t0_src;
+    c.v0s = v_t0_src;
+    c.k1s = k_t1_src;
+    c.v1s = v_t1_src;
+    c.k0d = k_t0_dst;
+    c.v0d = v_t0_dst;
+    c.k1d = k_t1_dst;
+    c.v1d = v_t1_dst;
+    c.src0 = src0;
+    c.src1 = src1;
+    c.new_lens = new_lens;
+    c.cap0 = cap0;
+    c.cap1 = cap1;
+    c.L = model->num_layers;
+    c.hkv = model->num_kv_heads;
+    c.b_offset = b0;
+    c.nb = nb;
+    launch_compact(a, c, model->kv_dtype, model->head_dim, nb, mx, stream);
+    if ((st = hip_check(hipGetLastError(), "compact launch"))) return st;
+  }
+  (void)max_n;
+  return TKV_OK;
+}
+
+tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_t0,
+                           const void* v_t0, int32_t cap0, const void* k_t1, const void* v_t1,
+                           int32_t cap1, const int32_t* src, const int32_t* n_rows,
+                           int32_t n_rows_stride, int32_t max_rows, int8_t* codes,
+                           float* scales, hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0 || max_rows < 0) return fail(TKV_ERR_ARG, "negative batch or max_rows");
+  if (batch == 0 || max_rows == 0) return TKV_OK;
+  if (!k_t0 || !v_t0 || !src || !n_rows || !codes || !scales)
+    return fail(TKV_ERR_ARG, "null pointer");
+  if (cap1 > 0 && (!k_t1 || !v_t1)) return fail(TKV_ERR_ARG, "null T1 window with cap1 > 0");
+  if (n_rows_stride < 1 || cap0 < 0 || cap1 < 0) return fail(TKV_ERR_ARG, "bad stride or capacity");
+  if (max_rows > 65535) return fail(TKV_ERR_CAPACITY, "max_rows above 65535");
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    QuantArgs a{};
+    a.k0 = k_t0;
+    a.v0 = v_t0;
+    a.k1 = k_t1;
+    a.v1 = v_t1;
+    a.src = src;
+    a.n_rows = n_rows;
+    a.codes = codes;
+    a.scales = scales;
+    a.n_rows_stride = n_rows_stride;
+    a.max_rows = max_rows;
+    a.cap0 = cap0;
+    a.cap1 = cap1;
+    a.L = model->num_layers;
+    a.hkv = model->num_kv_heads;
+    a.b_offset = b0;
+    launch_quantize(a, model->kv_dtype, model->head_dim, nb, stream);
+    if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
+  }
+  return TKV_OK;
+}
+
+}  // extern "C"

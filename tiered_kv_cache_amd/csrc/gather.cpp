@@ -1,0 +1,99 @@
+// T1 gather: host pack of a sequence's T1 rows into pinned staging, then the
+// host-to-device copy of the staging on a side stream.
+//
+// Method: "Not All Thoughts Need HBM" summary pages (gist.science, paper
+// 2605.09490), Methodologie section 1: T1 tokens live in host DDR at full
+// precision and are brought to the GPU before each attention step.  The pack
+// makes the rows contiguous per (layer, KV head) so the copy is one strided 2D
+// transfer per tensor, served by the DMA engines from pinned memory.
+#include <sched.h>
+#include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+int pack_threads() {
+  cpu_set_t set;
+  int n = 0;
+  if (sched_getaffinity(0, sizeof(set), &set) == 0) n = CPU_COUNT(&set);
+  if (n <= 0) n = (int)std::thread::hardware_concurrency();
+  return std::max(1, std::min(n, 16));
+}
+
+}  // namespace
+
+using namespace tkv;
+
+extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
+                                    const void* host_v, int32_t max_ctx,
+                                    const int32_t* positions, int32_t n_t1, void* staging_k,
+                                    void* staging_v, int32_t cap1, void* dev_k_t1,
+                                    void* dev_v_t1, hipStream_t side_stream, hipEvent_t ready) {
+  if (!model) return fail(TKV_ERR_ARG, "model is null");
+  if (model->num_layers < 1 || model->num_kv_heads < 1 ||
+      (model->head_dim != 64 && model->head_dim != 128) ||
+      (model->kv_dtype != TKV_BF16 && model->kv_dtype != TKV_F32))
+    return fail(TKV_ERR_ARG, "bad model shape");
+  if (n_t1 < 0 || cap1 < 0 || max_ctx < 0) return fail(TKV_ERR_ARG, "negative size");
+  if (n_t1 > cap1) return fail(TKV_ERR_CAPACITY, "n_t1 > cap1");
+  if (!staging_k || !staging_v) return fail(TKV_ERR_ARG, "staging is null");
+  if ((dev_k_t1 == nullptr) != (dev_v_t1 == nullptr))
+    return fail(TKV_ERR_ARG, "both or neither device windows must be given");
+  if (positions) {
+    if (!host_k || !host_v) return fail(TKV_ERR_ARG, "host store is null");
+    for (int i = 0; i < n_t1; ++i) {
+      if (positions[i] < 0 || positions[i] >= max_ctx)
+        return fail(TKV_ERR_ARG, "position outside [0, max_ctx)");
+      if (i > 0 && positions[i] <= positions[i - 1])
+        return fail(TKV_ERR_ARG, "positions must be strictly ascending");
+    }
+  }
+  const size_t esz = model->kv_dtype == TKV_BF16 ? 2 : 4;
+  const size_t row = esz * model->head_dim;
+  const long lgs = (long)model->num_layers * model->num_kv_heads;
+
+  if (positions && n_t1 > 0) {
+    const long total = lgs * n_t1;
+    const int nt = (int)std::min<long>(pack_threads(), std::max<long>(1, total / 2048));
+    auto work = [&](int t) {
+      const long lo = total * t / nt, hi = total * (t + 1) / nt;
+      for (long i = lo; i < hi; ++i) {
+        const long lg = i / n_t1;
+        const long r = i - lg * n_t1;
+        const size_t so = ((size_t)lg * max_ctx + positions[r]) * row;
+        const size_t dof = ((size_t)lg * cap1 + r) * row;
+        memcpy((char*)staging_k + dof, (const char*)host_k + so, row);
+        memcpy((char*)staging_v + dof, (const char*)host_v + so, row);
+      }
+    };
+    if (nt == 1) {
+      work(0);
+    } else {
+      std::vector<std::thread> pool;
+      pool.reserve(nt - 1);
+      for (int t = 1; t < nt; ++t) pool.emplace_back(work, t);
+      work(0);
+      for (auto& th : pool) th.join();
+    }
+  }
+  if (dev_k_t1 && n_t1 > 0) {
+    const size_t pitch = (size_t)cap1 * row;
+    const size_t width = (size_t)n_t1 * row;
+    KernelTimer timer("gather_t1_h2d", side_stream);
+    tkv_status st = hip_check(hipMemcpy2DAsync(dev_k_t1, pitch, staging_k, pitch, width, lgs,
+                                               hipMemcpyHostToDevice, side_stream),
+                              "T1 key copy");
+    if (st) return st;
+    st = hip_check(hipMemcpy2DAsync(dev_v_t1, pitch, staging_v, pitch, width, lgs,
+                                    hipMemcpyHostToDevice, side_stream),
+                   "T1 value copy");
+    if (st) return st;
+  }
+  if (ready) return hip_check(hipEventRecord(ready, side_stream), "event record");
+  return TKV_OK;
+}

@@ -1,0 +1,132 @@
+// Kernel argument blocks and launchers of libtkv (internal).
+#pragma once
+
+#include "common.h"
+
+namespace tkv {
+
+constexpr int kAttnThreads = 256;  // threads of an attention workgroup
+constexpr int kAttnChunk = 256;    // attended tokens per split
+
+// Per-launch sequence table: lengths and the prefix of work blocks per sequence.
+struct SeqTable {
+  int nb;        // sequences in this launch
+  int b_offset;  // index of the first one in the caller's batch
+  int t0_len[kMaxSeqPerLaunch];
+  int t1_len[kMaxSeqPerLaunch];
+  int base[kMaxSeqPerLaunch + 1];  // first work block of each sequence
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k0;
+  const void* v0;
+  const void* k1;
+  const void* v1;
+  float* out;
+  float* alpha;   // raw scaled logits on exit of attn_partial
+  float* part;    // [B][Lr][Hq][max_splits][D]
+  float* ml;      // [B][Lr][Hq][max_splits][2]
+  float* stat;    // [B][Lr][Hq][2]: M, 1/Lambda
+  long alpha_stride;
+  int cap0, cap1;
+  int L, Lr, layer_begin, hq, hkv;
+  int max_splits;
+  float scale;
+  SeqTable seq;
+};
+
+struct ScoreArgs {
+  float* alpha;
+  const float* stat;
+  const int* t0_pos;
+  const int* t1_pos;
+  float* scores;
+  long alpha_stride;
+  int rows;  // Lr * Hq
+  int normalise;
+  int cap0, cap1, max_ctx;
+  double weight;  // 1 / (num_layers * Hq)
+  SeqTable seq;   // base[] counts 64-slot blocks
+};
+
+struct AppendArgs {
+  const void* kn;
+  const void* vn;
+  void* k0;
+  void* v0;
+  int* t0_pos;
+  float* scores;
+  uint8_t* tier;
+  int cap0, max_ctx, L, hkv, b_offset;
+  int slot[kMaxSeqPerLaunch];
+  int pos[kMaxSeqPerLaunch];
+};
+
+struct TierArgs {
+  const float* scores;
+  const uint8_t* tprev;
+  uint8_t* tnext;
+  int* counts;
+  int max_ctx, prot_lo, recent, b_offset;
+  int n[kMaxSeqPerLaunch];
+  int n1[kMaxSeqPerLaunch];
+  int n2[kMaxSeqPerLaunch];
+  int n3[kMaxSeqPerLaunch];
+};
+
+struct CompactArgs {
+  const uint8_t* tprev;
+  const uint8_t* tnext;
+  int* t0_pos_dst;
+  int* t1_pos_dst;
+  int* src0;  // workspace [B][cap0]
+  int* src1;  // workspace [B][cap1]
+  int* t2_src;
+  int* t2_pos;
+  int* new_lens;
+  int max_ctx, cap0, cap1, t2_cap, b_offset;
+  int n[kMaxSeqPerLaunch];
+  int len0[kMaxSeqPerLaunch];
+  int len1[kMaxSeqPerLaunch];
+};
+
+struct CopyArgs {
+  const void* k0s;
+  const void* v0s;
+  const void* k1s;
+  const void* v1s;
+  void* k0d;
+  void* v0d;
+  void* k1d;
+  void* v1d;
+  const int* src0;
+  const int* src1;
+  const int* new_lens;
+  int cap0, cap1, L, hkv, b_offset, nb;
+};
+
+struct QuantArgs {
+  const void* k0;
+  const void* v0;
+  const void* k1;
+  const void* v1;
+  const int* src;
+  const int* n_rows;
+  int8_t* codes;
+  float* scales;
+  int n_rows_stride, max_rows, cap0, cap1, L, hkv, b_offset;
+};
+
+bool attn_group_supported(int group);
+void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, int nchunks,
+                         hipStream_t s);
+void launch_attn_combine(const AttnArgs& a, int head_dim, int nb, hipStream_t s);
+void launch_alpha_score(const ScoreArgs& a, int nblocks, hipStream_t s);
+void launch_append(const AppendArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
+void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s);
+void launch_compact(const CompactArgs& a, const CopyArgs& c, int kv_dtype, int head_dim, int nb,
+                    int max_n, hipStream_t s);
+void launch_quantize(const QuantArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
+
+}  // namespace tkv

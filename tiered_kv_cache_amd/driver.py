@@ -1,0 +1,260 @@
+"""Decode state machine of the tiered KV cache on one GPU.
+
+Holds the device state of a batch of sequences and runs the hot path through
+libtkv (every arithmetic step is a HIP kernel; torch only allocates device
+memory and supplies the stream):
+
+    step:      tkv_append  -> tkv_decode_step (attention over T0 u T1, alpha,
+               fused importance-score update)
+    every Delta steps (Methodologie section 4 of the "Not All Thoughts Need
+    HBM" summary pages, gist.science paper 2605.09490):
+               tkv_assign_tiers -> tkv_compact (new T0 pool / T1 window, list of
+               new T2 rows) -> tkv_quantize_t2 -> one host sync for the new
+               lengths.
+
+The T0 pool and the T1 window are double-buffered: compaction reads one copy
+and writes the other.  The tier map is double-buffered the same way.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import tkv
+
+
+def _round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+@dataclass
+class Shape:
+    layers: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    dtype: str  # "bf16" | "f32"
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def kv_code(self):
+        return tkv.TKV_BF16 if self.dtype == "bf16" else tkv.TKV_F32
+
+
+@dataclass
+class PolicyCfg:
+    prompt: int
+    sinks: int
+    recent: int
+    frac_t1: float
+    frac_t2: float
+    frac_t3: float
+    delta: int
+
+
+def to_device(x: np.ndarray, dtype, device) -> torch.Tensor:
+    """Host bf16 bit patterns (uint16) or float32 -> device tensor of `dtype`."""
+    if x.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device=device, dtype=dtype, non_blocking=False)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> host uint16 bit patterns (bf16) or float32."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class TieredKVCache:
+    """Device state of `batch` sequences that decode in lock step."""
+
+    def __init__(self, shape: Shape, policy: PolicyCfg, batch: int, max_ctx: int,
+                 device: str = "cuda", cap0: Optional[int] = None, cap1: Optional[int] = None,
+                 t2_cap: Optional[int] = None):
+        self.shape = shape
+        self.policy = policy
+        self.batch = batch
+        self.device = torch.device(device)
+        self.max_ctx = _round_up(max_ctx, 64)
+        self.cap0 = _round_up(cap0 or self.max_ctx, 64)
+        self.cap1 = _round_up(cap1 if cap1 is not None
+                              else int(math.floor(float(np.float32(policy.frac_t1)) * self.max_ctx)) + 64, 64)
+        self.t2_cap = _round_up(t2_cap if t2_cap is not None
+                                else int(math.floor(float(np.float32(policy.frac_t2)) * self.max_ctx)) + 64, 64)
+        self.alpha_stride = _round_up(self.cap0 + self.cap1, 64)
+        self.model = tkv.make_model(shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim,
+                                    shape.kv_code)
+        self.tpolicy = tkv.make_policy(policy.prompt, policy.sinks, policy.recent,
+                                       policy.frac_t1, policy.frac_t2, policy.frac_t3,
+                                       policy.delta)
+        L, Hq, Hkv, D = shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim
+        dt, dev, B = shape.torch_dtype, self.device, batch
+        pool0 = (B, L, Hkv, self.cap0, D)
+        pool1 = (B, L, Hkv, self.cap1, D)
+        self.k0 = [torch.zeros(pool0, dtype=dt, device=dev) for _ in range(2)]
+        self.v0 = [torch.zeros(pool0, dtype=dt, device=dev) for _ in range(2)]
+        self.k1 = [torch.zeros(pool1, dtype=dt, device=dev) for _ in range(2)]
+        self.v1 = [torch.zeros(pool1, dtype=dt, device=dev) for _ in range(2)]
+        self.pos0 = [torch.zeros((B, self.cap0), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.pos1 = [torch.zeros((B, self.cap1), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.tier = [torch.zeros((B, self.max_ctx), dtype=torch.uint8, device=dev) for _ in range(2)]
+        self.scores = torch.zeros((B, self.max_ctx), dtype=torch.float32, device=dev)
+        self.alpha = torch.zeros((B, L, Hq, self.alpha_stride), dtype=torch.float32, device=dev)
+        self.out = torch.zeros((B, L, Hq, D), dtype=torch.float32, device=dev)
+        self.counts = torch.zeros((B, 4), dtype=torch.int32, device=dev)
+        self.new_lens = torch.zeros((B, 3), dtype=torch.int32, device=dev)
+        self.t2_src = torch.zeros((B, self.t2_cap), dtype=torch.int32, device=dev)
+        self.t2_pos = torch.zeros((B, self.t2_cap), dtype=torch.int32, device=dev)
+        self.t2_codes = torch.zeros((B, self.t2_cap, L, Hkv, 2, D), dtype=torch.int8, device=dev)
+        self.t2_scales = torch.zeros((B, self.t2_cap, L, Hkv, 2), dtype=torch.float32, device=dev)
+        self.ws_bytes = tkv.tkv_decode_workspace_bytes(self.model, B, L, self.cap0, self.cap1)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.cws_bytes = tkv.tkv_compact_workspace_bytes(B, self.cap0, self.cap1)
+        self.cws = torch.zeros(self.cws_bytes, dtype=torch.uint8, device=dev)
+        self.cur = 0       # which pool/window copy is live
+        self.tcur = 0      # which tier map is live
+        self.n = [0] * B
+        self.t0_len = [0] * B
+        self.t1_len = [0] * B
+        self.t2_new = [0] * B   # rows quantised at the last reassignment
+        self.steps = 0
+        self.fused_scores = True
+
+    # ---- views -------------------------------------------------------------
+    @property
+    def k_t0(self):
+        return self.k0[self.cur]
+
+    @property
+    def v_t0(self):
+        return self.v0[self.cur]
+
+    @property
+    def k_t1(self):
+        return self.k1[self.cur]
+
+    @property
+    def v_t1(self):
+        return self.v1[self.cur]
+
+    @property
+    def t0_pos(self):
+        return self.pos0[self.cur]
+
+    @property
+    def t1_pos(self):
+        return self.pos1[self.cur]
+
+    @property
+    def tiers(self):
+        return self.tier[self.tcur]
+
+    # ---- set-up ------------------------------------------------------------
+    def load_context(self, b: int, K: np.ndarray, V: np.ndarray) -> None:
+        """Initial context of sequence b (all in T0, scores 0): K, V [L][Hkv][n0][D]."""
+        n0 = K.shape[2]
+        if n0 > self.cap0:
+            raise ValueError("context longer than the T0 pool")
+        self.k0[self.cur][b, :, :, :n0] = to_device(K, self.shape.torch_dtype, self.device)
+        self.v0[self.cur][b, :, :, :n0] = to_device(V, self.shape.torch_dtype, self.device)
+        self.pos0[self.cur][b, :n0] = torch.arange(n0, dtype=torch.int32, device=self.device)
+        self.tier[self.tcur][b].zero_()
+        self.scores[b].zero_()
+        self.n[b] = n0
+        self.t0_len[b] = n0
+        self.t1_len[b] = 0
+
+    # ---- the step ------------------------------------------------------------
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        tkv.tkv_append(self.model, self.batch, k_new, v_new, self.k_t0, self.v_t0, self.cap0,
+                       self.t0_len, self.t0_pos, self.n, self.scores, self.tiers, self.max_ctx,
+                       stream)
+        self.n = [x + 1 for x in self.n]
+        self.t0_len = [x + 1 for x in self.t0_len]
+
+    def attend(self, q: torch.Tensor, stream=None, layer_begin: int = 0,
+               layer_end: Optional[int] = None, fused_scores: Optional[bool] = None,
+               out: Optional[torch.Tensor] = None, alpha: Optional[torch.Tensor] = None) -> None:
+        """Attention of layers [layer_begin, layer_end) (default all) over T0 u T1.
+
+        A layer subset needs contiguous `out` [B][Lr][Hq][D] and `alpha`
+        [B][Lr][Hq][alpha_stride] buffers from the caller.
+        """
+        le = self.shape.layers if layer_end is None else layer_end
+        fused = self.fused_scores if fused_scores is None else fused_scores
+        full = layer_begin == 0 and le == self.shape.layers
+        if out is None or alpha is None:
+            if not full:
+                raise ValueError("a layer subset needs caller-supplied out and alpha buffers")
+            out, alpha = self.out, self.alpha
+        tkv.tkv_decode_step(self.model, self.batch, layer_begin, le, q, self.k_t0, self.v_t0,
+                            self.t0_len, self.cap0, self.k_t1, self.v_t1, self.t1_len, self.cap1,
+                            out, alpha, self.alpha_stride, self.t0_pos, self.t1_pos,
+                            self.scores if fused else None, self.max_ctx, self.ws, self.ws_bytes,
+                            stream)
+        if not fused:
+            tkv.tkv_update_scores(self.model, self.batch, layer_begin, le, alpha,
+                                  self.alpha_stride, self.t0_pos, self.t0_len, self.cap0,
+                                  self.t1_pos, self.t1_len, self.cap1, self.scores,
+                                  self.max_ctx, stream)
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None,
+             reassign: bool = True) -> bool:
+        """One decode step; returns True when it ended with a reassignment."""
+        self.append(k_new, v_new, stream)
+        self.attend(q, stream)
+        self.steps += 1
+        if reassign and self.steps % self.policy.delta == 0:
+            self.reassign(stream)
+            return True
+        return False
+
+    def reassign(self, stream=None) -> None:
+        """Rank, compact, quantise new T2 rows; one host sync for the new lengths."""
+        nxt, tnx = 1 - self.cur, 1 - self.tcur
+        B = self.batch
+        tkv.tkv_assign_tiers(B, self.n, self.max_ctx, self.scores, self.tpolicy,
+                             self.tier[self.tcur], self.tier[tnx], self.counts, stream)
+        tkv.tkv_compact(self.model, B, self.n, self.max_ctx, self.tier[self.tcur], self.tier[tnx],
+                        self.k0[self.cur], self.v0[self.cur], self.t0_len, self.cap0,
+                        self.k1[self.cur], self.v1[self.cur], self.t1_len, self.cap1,
+                        self.k0[nxt], self.v0[nxt], self.pos0[nxt], self.k1[nxt], self.v1[nxt],
+                        self.pos1[nxt], self.t2_src, self.t2_pos, self.t2_cap, self.new_lens,
+                        self.cws, self.cws_bytes, stream)
+        tkv.tkv_quantize_t2(self.model, B, self.k0[self.cur], self.v0[self.cur], self.cap0,
+                            self.k1[self.cur], self.v1[self.cur], self.cap1, self.t2_src,
+                            self.new_lens[:, 2:], 3, self.t2_cap, self.t2_codes, self.t2_scales,
+                            stream)
+        lens = self.new_lens.cpu().numpy()          # the one sync per reassignment
+        if (lens < 0).any():
+            raise RuntimeError(f"tier state error reported by the device: {lens.tolist()}")
+        self.t0_len = lens[:, 0].tolist()
+        self.t1_len = lens[:, 1].tolist()
+        self.t2_new = lens[:, 2].tolist()
+        self.cur, self.tcur = nxt, tnx
+
+    # ---- read-back helpers (tests, tools) ---------------------------------------
+    def attended_positions(self, b: int) -> np.ndarray:
+        p0 = self.t0_pos[b, :self.t0_len[b]].cpu().numpy()
+        p1 = self.t1_pos[b, :self.t1_len[b]].cpu().numpy()
+        return np.concatenate([p0, p1]).astype(np.int64)
+
+    def alpha_of(self, b: int) -> np.ndarray:
+        m = self.t0_len[b] + self.t1_len[b]
+        return self.alpha[b, :, :, :m].cpu().numpy()
+
+    def last_t2(self, b: int):
+        r = self.t2_new[b]
+        return (self.t2_pos[b, :r].cpu().numpy(), self.t2_codes[b, :r].cpu().numpy(),
+                self.t2_scales[b, :r].cpu().numpy())

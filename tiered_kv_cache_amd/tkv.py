@@ -1,0 +1,266 @@
+"""Python binding of libtkv.so: the C ABI of include/tkv.h, same names.
+
+Argument marshalling only.  Tensors (torch) are passed by ``data_ptr()``; host
+per-sequence lengths are plain Python/NumPy integer sequences; streams are
+torch streams or raw handles.  Every call raises :class:`TkvError` on a
+negative status.  The library must exist: there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkv.so")
+
+TKV_OK = 0
+TKV_ERR_ARG = -1
+TKV_ERR_CAPACITY = -2
+TKV_ERR_STATE = -3
+TKV_ERR_HIP = -4
+TKV_BF16 = 0
+TKV_F32 = 1
+
+EXPORTED = (
+    "tkv_abi_version", "tkv_last_error", "tkv_append", "tkv_decode_workspace_bytes",
+    "tkv_decode_step", "tkv_update_scores", "tkv_assign_tiers", "tkv_compact_workspace_bytes",
+    "tkv_compact", "tkv_quantize_t2", "tkv_gather_t1", "tkv_timing_enable", "tkv_timing_reset",
+    "tkv_timing_read",
+)
+
+
+class TkvError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where} failed with status {status}: {msg}")
+        self.status = status
+
+
+class tkv_model(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class tkv_policy(ctypes.Structure):
+    _fields_ = [("prompt_len", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
+                ("recent_window", ctypes.c_int32), ("frac_t1", ctypes.c_float),
+                ("frac_t2", ctypes.c_float), ("frac_t3", ctypes.c_float),
+                ("delta", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Open libtkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m tiered_kv_cache_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "tkv_abi_version": (_I, []),
+        "tkv_last_error": (ctypes.c_char_p, []),
+        "tkv_append": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _P, _P, _I, _P, _P, _P,
+                            _P, _P, _I, _P]),
+        "tkv_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(tkv_model), _I, _I,
+                                                         _I, _I]),
+        "tkv_decode_step": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _P, _P, _P, _I,
+                                 _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _I, _P,
+                                 ctypes.c_size_t, _P]),
+        "tkv_update_scores": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _I, _P, _P, _I,
+                                   _P, _P, _I, _P, _I, _P]),
+        "tkv_assign_tiers": (_I, [_I, _P, _I, _P, ctypes.POINTER(tkv_policy), _P, _P, _P, _P]),
+        "tkv_compact_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+        "tkv_compact": (_I, [ctypes.POINTER(tkv_model), _I, _P, _I, _P, _P, _P, _P, _P, _I,
+                             _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                             ctypes.c_size_t, _P]),
+        "tkv_quantize_t2": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _I, _P, _P, _I, _P,
+                                 _P, _I, _I, _P, _P, _P]),
+        "tkv_gather_t1": (_I, [ctypes.POINTER(tkv_model), _P, _P, _I, _P, _I, _P, _P, _I, _P,
+                               _P, _P, _P]),
+        "tkv_timing_enable": (_I, [_I]),
+        "tkv_timing_reset": (_I, []),
+        "tkv_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_int64)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot pass {type(x)} as a pointer")
+
+
+class _HostInts:
+    """Keeps a contiguous int32 copy alive for the duration of a call."""
+
+    def __init__(self, seq):
+        self.arr = None if seq is None else np.ascontiguousarray(np.asarray(seq, dtype=np.int32))
+
+    @property
+    def ptr(self):
+        return None if self.arr is None else self.arr.ctypes.data
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        try:
+            import torch
+            return torch.cuda.current_stream().cuda_stream
+        except Exception:
+            return None
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    raise TypeError("stream must be a torch stream or a raw handle")
+
+
+def _event(e) -> Optional[int]:
+    if e is None or isinstance(e, int):
+        return e
+    if hasattr(e, "cuda_event"):
+        return e.cuda_event
+    raise TypeError("event must be a torch event or a raw handle")
+
+
+def _check(status: int, where: str) -> None:
+    if status != TKV_OK:
+        msg = lib().tkv_last_error()
+        raise TkvError(status, where, msg.decode() if msg else "")
+
+
+def make_model(layers: int, q_heads: int, kv_heads: int, head_dim: int, kv_dtype: int,
+               softmax_scale: float = 0.0) -> tkv_model:
+    return tkv_model(layers, q_heads, kv_heads, head_dim, kv_dtype, softmax_scale)
+
+
+def make_policy(prompt: int, sinks: int, recent: int, f1: float, f2: float, f3: float,
+                delta: int) -> tkv_policy:
+    return tkv_policy(prompt, sinks, recent, f1, f2, f3, delta)
+
+
+# --------------------------------------------------------------------------
+# the ABI, one function per entry point
+# --------------------------------------------------------------------------
+def tkv_abi_version() -> int:
+    return lib().tkv_abi_version()
+
+
+def tkv_append(model, batch, k_new, v_new, k_t0, v_t0, cap0, t0_len, t0_pos, position,
+               scores=None, tier=None, max_ctx=0, stream=None) -> None:
+    a, b = _HostInts(t0_len), _HostInts(position)
+    _check(lib().tkv_append(ctypes.byref(model), batch, _ptr(k_new), _ptr(v_new), _ptr(k_t0),
+                            _ptr(v_t0), cap0, a.ptr, _ptr(t0_pos), b.ptr, _ptr(scores),
+                            _ptr(tier), max_ctx, _stream(stream)), "tkv_append")
+
+
+def tkv_decode_workspace_bytes(model, batch, n_layers, cap0, cap1) -> int:
+    return lib().tkv_decode_workspace_bytes(ctypes.byref(model), batch, n_layers, cap0, cap1)
+
+
+def tkv_decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1,
+                    v_t1, t1_len, cap1, out, alpha, alpha_stride, t0_pos=None, t1_pos=None,
+                    scores=None, max_ctx=0, workspace=None, workspace_bytes=0,
+                    stream=None) -> None:
+    a, b = _HostInts(t0_len), _HostInts(t1_len)
+    _check(lib().tkv_decode_step(ctypes.byref(model), batch, layer_begin, layer_end, _ptr(q),
+                                 _ptr(k_t0), _ptr(v_t0), a.ptr, cap0, _ptr(k_t1), _ptr(v_t1),
+                                 b.ptr, cap1, _ptr(out), _ptr(alpha), alpha_stride,
+                                 _ptr(t0_pos), _ptr(t1_pos), _ptr(scores), max_ctx,
+                                 _ptr(workspace), workspace_bytes, _stream(stream)),
+           "tkv_decode_step")
+
+
+def tkv_update_scores(model, batch, layer_begin, layer_end, alpha, alpha_stride, t0_pos,
+                      t0_len, cap0, t1_pos, t1_len, cap1, scores, max_ctx, stream=None) -> None:
+    a, b = _HostInts(t0_len), _HostInts(t1_len)
+    _check(lib().tkv_update_scores(ctypes.byref(model), batch, layer_begin, layer_end,
+                                   _ptr(alpha), alpha_stride, _ptr(t0_pos), a.ptr, cap0,
+                                   _ptr(t1_pos), b.ptr, cap1, _ptr(scores), max_ctx,
+                                   _stream(stream)), "tkv_update_scores")
+
+
+def tkv_assign_tiers(batch, ctx_len, max_ctx, scores, policy, tier_prev, tier_next, counts,
+                     stream=None) -> None:
+    a = _HostInts(ctx_len)
+    _check(lib().tkv_assign_tiers(batch, a.ptr, max_ctx, _ptr(scores), ctypes.byref(policy),
+                                  _ptr(tier_prev), _ptr(tier_next), _ptr(counts),
+                                  _stream(stream)), "tkv_assign_tiers")
+
+
+def tkv_compact_workspace_bytes(batch, cap0, cap1) -> int:
+    return lib().tkv_compact_workspace_bytes(batch, cap0, cap1)
+
+
+def tkv_compact(model, batch, ctx_len, max_ctx, tier_prev, tier_next, k_t0_src, v_t0_src,
+                t0_len_src, cap0, k_t1_src, v_t1_src, t1_len_src, cap1, k_t0_dst, v_t0_dst,
+                t0_pos_dst, k_t1_dst, v_t1_dst, t1_pos_dst, t2_src, t2_pos, t2_cap, new_lens,
+                workspace, workspace_bytes, stream=None) -> None:
+    a, b, c = _HostInts(ctx_len), _HostInts(t0_len_src), _HostInts(t1_len_src)
+    _check(lib().tkv_compact(ctypes.byref(model), batch, a.ptr, max_ctx, _ptr(tier_prev),
+                             _ptr(tier_next), _ptr(k_t0_src), _ptr(v_t0_src), b.ptr, cap0,
+                             _ptr(k_t1_src), _ptr(v_t1_src), c.ptr, cap1, _ptr(k_t0_dst),
+                             _ptr(v_t0_dst), _ptr(t0_pos_dst), _ptr(k_t1_dst), _ptr(v_t1_dst),
+                             _ptr(t1_pos_dst), _ptr(t2_src), _ptr(t2_pos), t2_cap,
+                             _ptr(new_lens), _ptr(workspace), workspace_bytes,
+                             _stream(stream)), "tkv_compact")
+
+
+def tkv_quantize_t2(model, batch, k_t0, v_t0, cap0, k_t1, v_t1, cap1, src, n_rows,
+                    n_rows_stride, max_rows, codes, scales, stream=None) -> None:
+    _check(lib().tkv_quantize_t2(ctypes.byref(model), batch, _ptr(k_t0), _ptr(v_t0), cap0,
+                                 _ptr(k_t1), _ptr(v_t1), cap1, _ptr(src), _ptr(n_rows),
+                                 n_rows_stride, max_rows, _ptr(codes), _ptr(scales),
+                                 _stream(stream)), "tkv_quantize_t2")
+
+
+def tkv_gather_t1(model, host_k, host_v, max_ctx, positions, n_t1, staging_k, staging_v,
+                  cap1, dev_k_t1=None, dev_v_t1=None, side_stream=None, ready=None) -> None:
+    p = _HostInts(positions)
+    _check(lib().tkv_gather_t1(ctypes.byref(model), _ptr(host_k), _ptr(host_v), max_ctx, p.ptr,
+                               n_t1, _ptr(staging_k), _ptr(staging_v), cap1, _ptr(dev_k_t1),
+                               _ptr(dev_v_t1), _stream(side_stream), _event(ready)),
+           "tkv_gather_t1")
+
+
+def tkv_timing_enable(enable: bool) -> None:
+    _check(lib().tkv_timing_enable(1 if enable else 0), "tkv_timing_enable")
+
+
+def tkv_timing_reset() -> None:
+    _check(lib().tkv_timing_reset(), "tkv_timing_reset")
+
+
+def tkv_timing_read(kernel: str):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().tkv_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)),
+           "tkv_timing_read")
+    return ms.value, n.value
