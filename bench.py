@@ -35,6 +35,9 @@ def parse():
     p.add_argument("--no-pcie", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's timed CPU work")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run one plain 256 MiB read + 256 MiB write elementwise kernel first "
+                        "(scale reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -167,6 +170,13 @@ def main():
     from tiered_kv_cache_amd.workload import DeviceWorkload
 
     tkv.lib()
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)       # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
     wl = WORKLOADS[args.workload].scaled(steps=args.steps, warmup=args.warmup)
     print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
     dw = DeviceWorkload(wl)
