@@ -77,9 +77,7 @@ def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, st
     assert cache.t0_len[b] == len(t0) and cache.t1_len[b] == len(seq.t1_positions)
     assert np.array_equal(cache.t0_pos[b, :len(t0)].cpu().numpy(), t0)
     assert np.array_equal(cache.t1_pos[b, :cache.t1_len[b]].cpu().numpy(), seq.t1_positions)
-    m1 = cache.t1_len[b]
-    k1 = to_host_bits(cache.k_t1[b, :, :, :m1])
-    v1 = to_host_bits(cache.v_t1[b, :, :, :m1])
+    k1, v1 = cache.t1_rows(b)
     assert k1.tobytes() == np.ascontiguousarray(seq.t1_K).tobytes(), "T1 window keys differ"
     assert v1.tobytes() == np.ascontiguousarray(seq.t1_V).tobytes(), "T1 window values differ"
     new_t2 = np.nonzero((seq.tier[:n] == 2) & (prev_tiers[:n] <= 1))[0]
@@ -222,11 +220,12 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                 t1 = np.nonzero(t_ref == 1)[0]
                 assert np.array_equal(cache.t0_pos[b, :cache.t0_len[b]].cpu().numpy(), t0)
                 assert np.array_equal(cache.t1_pos[b, :cache.t1_len[b]].cpu().numpy(), t1)
-                m1 = len(t1)
-                assert to_host_bits(cache.k_t1[b, :, :, :m1]).tobytes() == \
-                    np.ascontiguousarray(store.K[b][:, :, t1]).tobytes()
-                assert to_host_bits(cache.v_t1[b, :, :, :m1]).tobytes() == \
-                    np.ascontiguousarray(store.V[b][:, :, t1]).tobytes()
+                k1, v1 = cache.t1_rows(b)
+                assert k1.tobytes() == np.ascontiguousarray(store.K[b][:, :, t1]).tobytes()
+                assert v1.tobytes() == np.ascontiguousarray(store.V[b][:, :, t1]).tobytes()
+                k0, v0 = cache.t0_rows(b)
+                assert k0.tobytes() == np.ascontiguousarray(store.K[b][:, :, t0]).tobytes()
+                assert v0.tobytes() == np.ascontiguousarray(store.V[b][:, :, t0]).tobytes()
                 new_t2 = np.nonzero((t_ref == 2) & (prev[b, :n] <= 1))[0]
                 pos, codes, scales = cache.last_t2(b)
                 assert np.array_equal(pos, new_t2)

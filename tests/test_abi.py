@@ -157,4 +157,8 @@ def test_gather_host_pack_without_device():
     pos = [1, 5, 6, 17, 39]
     tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), sk, sv, cap1)
     assert sk[:, :, :5].tobytes() == hk[:, :, pos].tobytes()
-    assert sv[:, :, :5].tobytes() == hv[:, :, pos].tobytes()
+    # values go to 8-slot panels: slot r, dimension d at [r // 8][d][r % 8]
+    panels = sv.reshape(2, 2, cap1 // 8, 64, 8)
+    rows = panels.transpose(0, 1, 2, 4, 3).reshape(2, 2, cap1, 64)
+    assert rows[:, :, :5].tobytes() == hv[:, :, pos].tobytes()
+    assert not rows[:, :, 5:8].any()            # the tail of the last panel is cleared

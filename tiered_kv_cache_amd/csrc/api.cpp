@@ -1,6 +1,7 @@
 // C ABI of libtkv: argument validation, batch splitting, kernel dispatch.
 // Every check runs before the first HIP call of an entry point.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -109,9 +110,27 @@ static float scale_of(const tkv_model* m) {
   return m->softmax_scale > 0.f ? m->softmax_scale : 1.0f / sqrtf((float)m->head_dim);
 }
 
-static size_t elem_size(const tkv_model* m) { return m->kv_dtype == TKV_BF16 ? 2 : 4; }
+// Splits per (sequence, layer, query head) for any chunk >= kAttnChunkMin (+1: the
+// empty task of an empty sequence).
+static int max_splits_for(int cap0, int cap1) {
+  return ceil_div(cap0, kAttnChunkMin) + ceil_div(cap1, kAttnChunkMin) + 1;
+}
 
-static int max_splits_for(int cap0, int cap1) { return ceil_div((long)cap0 + cap1, kAttnChunk); }
+// Tokens per split of the bf16 path: a multiple of kAttnChunkMin (TKV_ATTN_CHUNK
+// overrides the default for tuning sweeps).
+static int mfma_chunk() {
+  static int c = [] {
+    const char* e = getenv("TKV_ATTN_CHUNK");
+    int v = e ? atoi(e) : 256;
+    if (v < kAttnChunkMin) v = kAttnChunkMin;
+    return v / kAttnChunkMin * kAttnChunkMin;
+  }();
+  return c;
+}
+
+static size_t counters_bytes(int batch, int n_layers, int hkv) {
+  return ((size_t)batch * n_layers * hkv * sizeof(int32_t) + 255) / 256 * 256;
+}
 
 }  // namespace tkv
 
@@ -154,7 +173,7 @@ tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new, 
   if (batch == 0) return TKV_OK;
   if (!k_new || !v_new || !k_t0 || !v_t0 || !t0_len || !t0_pos || !position)
     return fail(TKV_ERR_ARG, "null pointer");
-  if (cap0 < 1) return fail(TKV_ERR_ARG, "cap0 < 1");
+  if (cap0 < 1 || cap0 % 8) return fail(TKV_ERR_ARG, "cap0 must be a positive multiple of 8");
   for (int b = 0; b < batch; ++b) {
     if (t0_len[b] < 0 || position[b] < 0) return fail(TKV_ERR_ARG, "negative length or position");
     if (t0_len[b] >= cap0) return fail(TKV_ERR_CAPACITY, "T0 pool full (t0_len >= cap0)");
@@ -189,10 +208,12 @@ tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new, 
 size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t n_layers,
                                   int32_t cap0, int32_t cap1) {
   if (!model || batch < 0 || n_layers < 0 || cap0 < 0 || cap1 < 0) return 0;
+  if (model->num_kv_heads < 1) return 0;
   const size_t rows = (size_t)batch * n_layers * model->num_q_heads;
   const size_t ms = (size_t)max_splits_for(cap0, cap1);
   const size_t D = (size_t)model->head_dim;
-  return rows * ms * (D + 2) * sizeof(float) + rows * 2 * sizeof(float) + 256;
+  return counters_bytes(batch, n_layers, model->num_kv_heads) +
+         rows * ms * (D + 2) * sizeof(float) + rows * 2 * sizeof(float);
 }
 
 tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
@@ -211,6 +232,7 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   if (!q || !k_t0 || !v_t0 || !t0_len || !t1_len || !out || !alpha || !workspace)
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap0 < 0 || cap1 < 0 || alpha_stride < 1) return fail(TKV_ERR_ARG, "bad capacity or stride");
+  if (cap0 % 8 || cap1 % 8) return fail(TKV_ERR_ARG, "cap0 and cap1 must be multiples of 8");
   bool any_t1 = false;
   for (int b = 0; b < batch; ++b) {
     if (t0_len[b] < 0 || t1_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
@@ -227,9 +249,12 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     return fail(TKV_ERR_CAPACITY, "workspace too small");
 
   const int hq = model->num_q_heads;
+  const int hkv = model->num_kv_heads;
   const int D = model->head_dim;
   const int max_splits = max_splits_for(cap0, cap1);
-  float* part = (float*)workspace;
+  const int chunk = model->kv_dtype == TKV_BF16 ? mfma_chunk() : kAttnChunkValu;
+  int* counters = (int*)workspace;
+  float* part = (float*)((char*)workspace + counters_bytes(batch, Lr, hkv));
   float* ml = part + (size_t)batch * Lr * hq * max_splits * D;
   float* stat = ml + (size_t)batch * Lr * hq * max_splits * 2;
 
@@ -246,36 +271,34 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     a.part = part;
     a.ml = ml;
     a.stat = stat;
+    a.counters = counters;
     a.alpha_stride = alpha_stride;
+    a.chunk = chunk;
     a.cap0 = cap0;
     a.cap1 = cap1;
     a.L = model->num_layers;
     a.Lr = Lr;
     a.layer_begin = layer_begin;
     a.hq = hq;
-    a.hkv = model->num_kv_heads;
+    a.hkv = hkv;
     a.max_splits = max_splits;
     a.scale = scale_of(model);
     a.seq.nb = nb;
     a.seq.b_offset = b0;
-    int chunks = 0, sblocks = 0;
+    int tasks = 0, sblocks = 0;
     ScoreArgs sa{};
     for (int i = 0; i < nb; ++i) {
-      a.seq.t0_len[i] = t0_len[b0 + i];
-      a.seq.t1_len[i] = t1_len[b0 + i];
-      a.seq.base[i] = chunks;
+      const int n0 = t0_len[b0 + i], n1 = t1_len[b0 + i];
+      a.seq.t0_len[i] = n0;
+      a.seq.t1_len[i] = n1;
+      a.seq.base[i] = tasks;
       sa.seq.base[i] = sblocks;
-      const int natt = t0_len[b0 + i] + t1_len[b0 + i];
-      chunks += ceil_div(natt, kAttnChunk);
-      sblocks += ceil_div(natt, 64);
+      tasks += std::max(1, ceil_div(n0, chunk) + ceil_div(n1, chunk));
+      sblocks += ceil_div(n0 + n1, kScoreSlots);
     }
-    a.seq.base[nb] = chunks;
-    if (chunks > 0) {
-      launch_attn_partial(a, model->kv_dtype, D, hq / model->num_kv_heads, chunks, stream);
-      if ((st = hip_check(hipGetLastError(), "attn_partial launch"))) return st;
-    }
-    launch_attn_combine(a, D, nb, stream);
-    if ((st = hip_check(hipGetLastError(), "attn_combine launch"))) return st;
+    a.seq.base[nb] = tasks;
+    launch_attn_partial(a, model->kv_dtype, D, hq / hkv, tasks, stream);
+    if ((st = hip_check(hipGetLastError(), "attn_partial launch"))) return st;
 
     sa.alpha = alpha;
     sa.stat = stat;
@@ -296,10 +319,6 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
       sa.seq.t1_len[i] = t1_len[b0 + i];
     }
     sa.seq.base[nb] = sblocks;
-    if (!scores) {
-      // normalise only: the score kernel without a score buffer
-      sa.scores = nullptr;
-    }
     if (sblocks > 0) {
       launch_alpha_score(sa, sblocks, stream);
       if ((st = hip_check(hipGetLastError(), "alpha_score launch"))) return st;
@@ -354,7 +373,7 @@ tkv_status tkv_update_scores(const tkv_model* model, int32_t batch, int32_t laye
       sa.seq.t0_len[i] = t0_len[b0 + i];
       sa.seq.t1_len[i] = t1_len[b0 + i];
       sa.seq.base[i] = sblocks;
-      sblocks += ceil_div(t0_len[b0 + i] + t1_len[b0 + i], 64);
+      sblocks += ceil_div(t0_len[b0 + i] + t1_len[b0 + i], kScoreSlots);
     }
     sa.seq.base[nb] = sblocks;
     if (sblocks > 0) {
@@ -433,8 +452,8 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap1 > 0 && (!k_t1_src || !v_t1_src || !k_t1_dst || !v_t1_dst || !t1_pos_dst))
     return fail(TKV_ERR_ARG, "null T1 pointer with cap1 > 0");
-  if (cap0 < 1 || cap1 < 0 || t2_cap < 0 || max_ctx < 1)
-    return fail(TKV_ERR_ARG, "bad capacity");
+  if (cap0 < 1 || cap1 < 0 || t2_cap < 0 || max_ctx < 1 || cap0 % 8 || cap1 % 8)
+    return fail(TKV_ERR_ARG, "bad capacity (cap0, cap1 multiples of 8)");
   if (k_t0_src == k_t0_dst || v_t0_src == v_t0_dst || (cap1 > 0 && (k_t1_src == k_t1_dst ||
                                                                     v_t1_src == v_t1_dst)))
     return fail(TKV_ERR_ARG, "source and destination buffers must differ");
@@ -514,7 +533,8 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
   if (!k_t0 || !v_t0 || !src || !n_rows || !codes || !scales)
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap1 > 0 && (!k_t1 || !v_t1)) return fail(TKV_ERR_ARG, "null T1 window with cap1 > 0");
-  if (n_rows_stride < 1 || cap0 < 0 || cap1 < 0) return fail(TKV_ERR_ARG, "bad stride or capacity");
+  if (n_rows_stride < 1 || cap0 < 0 || cap1 < 0 || cap0 % 8 || cap1 % 8)
+    return fail(TKV_ERR_ARG, "bad stride or capacity (cap0, cap1 multiples of 8)");
   if (max_rows > 65535) return fail(TKV_ERR_CAPACITY, "max_rows above 65535");
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, batch - b0);

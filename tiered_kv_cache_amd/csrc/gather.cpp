@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "common.h"
@@ -41,6 +42,7 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
     return fail(TKV_ERR_ARG, "bad model shape");
   if (n_t1 < 0 || cap1 < 0 || max_ctx < 0) return fail(TKV_ERR_ARG, "negative size");
   if (n_t1 > cap1) return fail(TKV_ERR_CAPACITY, "n_t1 > cap1");
+  if (cap1 % 8) return fail(TKV_ERR_ARG, "cap1 must be a multiple of 8");
   if (!staging_k || !staging_v) return fail(TKV_ERR_ARG, "staging is null");
   if ((dev_k_t1 == nullptr) != (dev_v_t1 == nullptr))
     return fail(TKV_ERR_ARG, "both or neither device windows must be given");
@@ -57,18 +59,48 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
   const size_t row = esz * model->head_dim;
   const long lgs = (long)model->num_layers * model->num_kv_heads;
 
+  const int D = model->head_dim;
+  const long npanels = (n_t1 + 7) / 8;
   if (positions && n_t1 > 0) {
-    const long total = lgs * n_t1;
+    const long krows = lgs * n_t1;
+    const long vpanels = lgs * npanels;
+    const long total = krows + vpanels * 8;  // work units: K rows, then V panels (8 rows each)
     const int nt = (int)std::min<long>(pack_threads(), std::max<long>(1, total / 2048));
+    auto pack_v = [&](auto* sv_base, const auto* hv_base, long lo, long hi) {
+      using E = std::remove_const_t<std::remove_pointer_t<decltype(hv_base)>>;
+      for (long i = lo; i < hi; ++i) {
+        const long lg = i / npanels;
+        const long p = i - lg * npanels;
+        E* dst = sv_base + ((size_t)lg * (cap1 / 8) + p) * D * 8;
+        for (int e = 0; e < 8; ++e) {
+          const long r = 8 * p + e;
+          if (r < n_t1) {
+            const E* src = hv_base + ((size_t)lg * max_ctx + positions[r]) * D;
+            for (int d = 0; d < D; ++d) dst[d * 8 + e] = src[d];
+          } else {
+            for (int d = 0; d < D; ++d) dst[d * 8 + e] = E(0);
+          }
+        }
+      }
+    };
     auto work = [&](int t) {
       const long lo = total * t / nt, hi = total * (t + 1) / nt;
-      for (long i = lo; i < hi; ++i) {
+      // K rows in [0, krows)
+      for (long i = lo; i < std::min(hi, krows); ++i) {
         const long lg = i / n_t1;
         const long r = i - lg * n_t1;
         const size_t so = ((size_t)lg * max_ctx + positions[r]) * row;
         const size_t dof = ((size_t)lg * cap1 + r) * row;
         memcpy((char*)staging_k + dof, (const char*)host_k + so, row);
-        memcpy((char*)staging_v + dof, (const char*)host_v + so, row);
+      }
+      // V panels: units [krows, total) in steps of 8
+      const long vlo = std::max(lo, krows), vhi = hi;
+      if (vhi > vlo) {
+        const long plo = (vlo - krows + 7) / 8, phi = (vhi - krows + 7) / 8;
+        if (esz == 2)
+          pack_v((uint16_t*)staging_v, (const uint16_t*)host_v, plo, phi);
+        else
+          pack_v((uint32_t*)staging_v, (const uint32_t*)host_v, plo, phi);
       }
     };
     if (nt == 1) {
@@ -83,14 +115,14 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
   }
   if (dev_k_t1 && n_t1 > 0) {
     const size_t pitch = (size_t)cap1 * row;
-    const size_t width = (size_t)n_t1 * row;
     KernelTimer timer("gather_t1_h2d", side_stream);
-    tkv_status st = hip_check(hipMemcpy2DAsync(dev_k_t1, pitch, staging_k, pitch, width, lgs,
-                                               hipMemcpyHostToDevice, side_stream),
+    tkv_status st = hip_check(hipMemcpy2DAsync(dev_k_t1, pitch, staging_k, pitch,
+                                               (size_t)n_t1 * row, lgs, hipMemcpyHostToDevice,
+                                               side_stream),
                               "T1 key copy");
     if (st) return st;
-    st = hip_check(hipMemcpy2DAsync(dev_v_t1, pitch, staging_v, pitch, width, lgs,
-                                    hipMemcpyHostToDevice, side_stream),
+    st = hip_check(hipMemcpy2DAsync(dev_v_t1, pitch, staging_v, pitch, (size_t)npanels * 8 * row,
+                                    lgs, hipMemcpyHostToDevice, side_stream),
                    "T1 value copy");
     if (st) return st;
   }

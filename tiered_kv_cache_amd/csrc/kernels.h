@@ -5,8 +5,9 @@
 
 namespace tkv {
 
-constexpr int kAttnThreads = 256;  // threads of an attention workgroup
-constexpr int kAttnChunk = 256;    // attended tokens per split
+constexpr int kAttnChunkMin = 128;   // smallest split (bf16 path: 4 waves x 32 tokens)
+constexpr int kAttnChunkValu = 256;  // float32 path: one token per thread
+constexpr int kScoreSlots = 16;      // attended slots per alpha_score workgroup
 
 // Per-launch sequence table: lengths and the prefix of work blocks per sequence.
 struct SeqTable {
@@ -28,7 +29,9 @@ struct AttnArgs {
   float* part;    // [B][Lr][Hq][max_splits][D]
   float* ml;      // [B][Lr][Hq][max_splits][2]
   float* stat;    // [B][Lr][Hq][2]: M, 1/Lambda
+  int* counters;  // [B][Lr][Hkv] arrival counters (zero between calls)
   long alpha_stride;
+  int chunk;      // tokens per split (multiple of kAttnChunkMin)
   int cap0, cap1;
   int L, Lr, layer_begin, hq, hkv;
   int max_splits;
@@ -47,7 +50,7 @@ struct ScoreArgs {
   int normalise;
   int cap0, cap1, max_ctx;
   double weight;  // 1 / (num_layers * Hq)
-  SeqTable seq;   // base[] counts 64-slot blocks
+  SeqTable seq;   // base[] counts kScoreSlots-slot blocks
 };
 
 struct AppendArgs {
@@ -119,9 +122,8 @@ struct QuantArgs {
 };
 
 bool attn_group_supported(int group);
-void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, int nchunks,
+void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, int ntasks,
                          hipStream_t s);
-void launch_attn_combine(const AttnArgs& a, int head_dim, int nb, hipStream_t s);
 void launch_alpha_score(const ScoreArgs& a, int nblocks, hipStream_t s);
 void launch_append(const AppendArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
 void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s);

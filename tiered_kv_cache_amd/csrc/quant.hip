@@ -29,21 +29,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int kv = combo & 1;
   const long lg = combo >> 1;
   const int s = a.src[b * a.max_rows + r];
-  const T* base;
-  long row;
-  if (s >= 0) {
-    base = (const T*)(kv ? a.v0 : a.k0);
-    row = (b * lgs + lg) * a.cap0 + s;
-  } else {
-    base = (const T*)(kv ? a.v1 : a.k1);
-    row = (b * lgs + lg) * a.cap1 + (-s - 1);
-  }
-  const T* x = base + row * D;
+  const int cap = s >= 0 ? a.cap0 : a.cap1;
+  const long slot = s >= 0 ? s : -s - 1;
+  const T* blk = (const T*)(kv ? (s >= 0 ? a.v0 : a.v1) : (s >= 0 ? a.k0 : a.k1)) +
+                 (b * lgs + lg) * cap * D;
   float v[PER];
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    v[i] = to_f32(x[lane * PER + i]);
+    const int d = lane * PER + i;
+    // K rows are contiguous; V sits in 8-slot panels (head_dim-major inside a panel)
+    const long off = kv ? ((slot >> 3) * D + d) * 8 + (slot & 7) : slot * D + d;
+    v[i] = to_f32(blk[off]);
     am = fmaxf(am, fabsf(v[i]));
   }
   am = wave_max(am);

@@ -275,8 +275,8 @@ __global__ __launch_bounds__(kTierThreads) void compact_scan_kernel(CompactArgs 
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compact_copy_kernel(CopyArgs c) {
-  constexpr int ROWS = 64;
-  constexpr int VPR = D * (int)sizeof(T) / 16;  // 16-byte vectors per row
+  constexpr int ROWS = 64;                       // destination slots per workgroup (8 V panels)
+  constexpr int VPR = D * (int)sizeof(T) / 16;  // 16-byte vectors per K row
   const int z = blockIdx.z;                      // 0: T0 destination, 1: T1 destination
   const int lgs = c.L * c.hkv;
   const int bl = blockIdx.y / lgs;
@@ -287,27 +287,50 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(CopyArgs c) {
   if (len <= r0) return;
   const int cap_d = z ? c.cap1 : c.cap0;
   const int* src = z ? c.src1 + b * c.cap1 : c.src0 + b * c.cap0;
-  const long row_s0 = (b * lgs + lg) * c.cap0;
-  const long row_s1 = (b * lgs + lg) * c.cap1;
-  const long row_d = (b * lgs + lg) * cap_d;
-  const uint4* ks0 = (const uint4*)c.k0s;
-  const uint4* vs0 = (const uint4*)c.v0s;
-  const uint4* ks1 = (const uint4*)c.k1s;
-  const uint4* vs1 = (const uint4*)c.v1s;
-  uint4* kd = (uint4*)(z ? c.k1d : c.k0d);
-  uint4* vd = (uint4*)(z ? c.v1d : c.v0d);
-  for (int i = threadIdx.x; i < ROWS * VPR; i += 256) {
-    const int rr = i / VPR;
-    const int v = i - rr * VPR;
-    const int r = r0 + rr;
-    if (r >= len) break;
-    const int s = src[r];
-    const long so = s >= 0 ? (row_s0 + s) * VPR + v : (row_s1 + (-s - 1)) * VPR + v;
-    const long dof = (row_d + r) * VPR + v;
-    const uint4 kv = s >= 0 ? ks0[so] : ks1[so];
-    const uint4 vv = s >= 0 ? vs0[so] : vs1[so];
-    kd[dof] = kv;
-    vd[dof] = vv;
+  const long blk0 = (b * lgs + lg) * c.cap0 * D;  // element offset of this (b, l, g) block
+  const long blk1 = (b * lgs + lg) * c.cap1 * D;
+  const long blkd = (b * lgs + lg) * (long)cap_d * D;
+  // K: row-major, one 16-byte vector per lane
+  {
+    const uint4* ks0 = (const uint4*)((const T*)c.k0s + blk0);
+    const uint4* ks1 = (const uint4*)((const T*)c.k1s + blk1);
+    uint4* kd = (uint4*)((T*)(z ? c.k1d : c.k0d) + blkd);
+    for (int i = threadIdx.x; i < ROWS * VPR; i += 256) {
+      const int rr = i / VPR;
+      const int v = i - rr * VPR;
+      const int r = r0 + rr;
+      if (r >= len) break;
+      const int s = src[r];
+      kd[(long)r * VPR + v] = s >= 0 ? ks0[(long)s * VPR + v] : ks1[(long)(-s - 1) * VPR + v];
+    }
+  }
+  // V: 8-slot panels, element (slot, d) at ((slot/8)*D + d)*8 + slot%8
+  {
+    const T* vs0 = (const T*)c.v0s + blk0;
+    const T* vs1 = (const T*)c.v1s + blk1;
+    T* vd = (T*)(z ? c.v1d : c.v0d) + blkd;
+    const int p0 = r0 >> 3;
+    for (int i = threadIdx.x; i < (ROWS / 8) * D; i += 256) {
+      const int pl = i / D;
+      const int d = i - pl * D;
+      const int p = p0 + pl;
+      if (8 * p >= len) break;
+      T vals[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * p + e;
+        vals[e] = T(0);
+        if (r < len) {
+          const int s = src[r];
+          const long slot = s >= 0 ? s : -s - 1;
+          const T* base = s >= 0 ? vs0 : vs1;
+          vals[e] = base[((slot >> 3) * D + d) * 8 + (slot & 7)];
+        }
+      }
+      T* out = vd + ((long)p * D + d) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = vals[e];
+    }
   }
 }
 
@@ -347,10 +370,10 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const T* ks = (const T*)a.kn + (b * lgs + lg) * D;
   const T* vs = (const T*)a.vn + (b * lgs + lg) * D;
   T* kd = (T*)a.k0 + ((b * lgs + lg) * a.cap0 + slot) * D;
-  T* vd = (T*)a.v0 + ((b * lgs + lg) * a.cap0 + slot) * D;
+  T* vd = (T*)a.v0 + (b * lgs + lg) * a.cap0 * D + (long)(slot >> 3) * D * 8 + (slot & 7);
   for (int d = threadIdx.x; d < D; d += 64) {
     kd[d] = ks[d];
-    vd[d] = vs[d];
+    vd[d * 8] = vs[d];  // V is stored in 8-slot panels, head_dim-major inside a panel
   }
   if (lg == 0 && threadIdx.x == 0) {
     a.t0_pos[b * a.cap0 + slot] = pos;

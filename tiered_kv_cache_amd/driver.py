@@ -68,6 +68,22 @@ def to_device(x: np.ndarray, dtype, device) -> torch.Tensor:
     return t.to(device=device, dtype=dtype, non_blocking=False)
 
 
+def v_rows_to_panels(v: torch.Tensor) -> torch.Tensor:
+    """Rows [..., n, D] (n a multiple of 8) -> the 8-slot panel storage order.
+
+    V pools and windows keep each group of 8 consecutive slots as a [D][8] panel
+    (head_dim-major), so one 16-byte load gives 8 slots of one dimension; the
+    tensor keeps its [..., n, D] shape as a container."""
+    *lead, n, d = v.shape
+    return v.reshape(*lead, n // 8, 8, d).transpose(-1, -2).contiguous().reshape(*lead, n, d)
+
+
+def v_panels_to_rows(v: torch.Tensor, n: int) -> torch.Tensor:
+    """Panel storage [..., cap, D] -> rows [..., n, D] (inverse of v_rows_to_panels)."""
+    *lead, cap, d = v.shape
+    return v.reshape(*lead, cap // 8, d, 8).transpose(-1, -2).reshape(*lead, cap, d)[..., :n, :]
+
+
 def to_host_bits(t: torch.Tensor) -> np.ndarray:
     """Device tensor -> host uint16 bit patterns (bf16) or float32."""
     t = t.detach().contiguous().cpu()
@@ -166,8 +182,14 @@ class TieredKVCache:
         n0 = K.shape[2]
         if n0 > self.cap0:
             raise ValueError("context longer than the T0 pool")
+        n0p = (n0 + 7) // 8 * 8
+        if n0p > self.cap0:
+            raise ValueError("context longer than the T0 pool")
         self.k0[self.cur][b, :, :, :n0] = to_device(K, self.shape.torch_dtype, self.device)
-        self.v0[self.cur][b, :, :, :n0] = to_device(V, self.shape.torch_dtype, self.device)
+        vpad = torch.zeros(K.shape[0], K.shape[1], n0p, K.shape[3], dtype=self.shape.torch_dtype,
+                           device=self.device)
+        vpad[:, :, :n0] = to_device(V, self.shape.torch_dtype, self.device)
+        self.v0[self.cur][b, :, :, :n0p] = v_rows_to_panels(vpad)
         self.pos0[self.cur][b, :n0] = torch.arange(n0, dtype=torch.int32, device=self.device)
         self.tier[self.tcur][b].zero_()
         self.scores[b].zero_()
@@ -249,6 +271,18 @@ class TieredKVCache:
         p0 = self.t0_pos[b, :self.t0_len[b]].cpu().numpy()
         p1 = self.t1_pos[b, :self.t1_len[b]].cpu().numpy()
         return np.concatenate([p0, p1]).astype(np.int64)
+
+    def t0_rows(self, b: int):
+        """Host copies (bf16 bits or float32) of the T0 pool rows of sequence b: K, V [L][Hkv][n][D]."""
+        n = self.t0_len[b]
+        return (to_host_bits(self.k_t0[b, :, :, :n]),
+                to_host_bits(v_panels_to_rows(self.v_t0[b], n)))
+
+    def t1_rows(self, b: int):
+        """Host copies of the T1 window rows of sequence b: K, V [L][Hkv][n][D]."""
+        n = self.t1_len[b]
+        return (to_host_bits(self.k_t1[b, :, :, :n]),
+                to_host_bits(v_panels_to_rows(self.v_t1[b], n)))
 
     def alpha_of(self, b: int) -> np.ndarray:
         m = self.t0_len[b] + self.t1_len[b]
