@@ -28,13 +28,16 @@
  *   lengths arrive as HOST int32 arrays so that grids are sized without a sync.
  * - Key/value/query elements are bf16 bit patterns (uint16) when
  *   kv_dtype == TKV_BF16, or float32 when kv_dtype == TKV_F32.
- * - Layouts are row-major; "[B][L][Hkv][cap][D]" means D is contiguous.
- *   Exception, marked "V-panels" below: value pools and windows keep each
- *   group of 8 consecutive slots as one [D][8] panel, i.e. element (slot, d)
- *   of a (sequence, layer, KV head) block sits at ((slot/8)*D + d)*8 + slot%8.
- *   One 16-byte load then yields 8 slots of one dimension, which is the
- *   operand the P.V matrix-core product consumes.  Capacities of pools and
- *   windows (cap0, cap1) must be multiples of 8.
+ * - Layouts are row-major; "[B][L][Hkv][D]" means D is contiguous.
+ *   Key and value pools, windows and staging ("[B][L][Hkv][cap][D] tiles") hold
+ *   the same elements in the order the matrix-core products consume them:
+ *   each (sequence, layer, KV head) block of cap slots is cut into 32-slot
+ *   blocks of 32*D elements, and element (slot, d) of a block sits at
+ *     keys   (K-tiles): (slot/32)*32*D + u*16*D + ((d/8)*16 + row)*8 + d%8,
+ *            with r = slot%32, u = (r/4)%2, row = 4*(r/8) + r%4;
+ *     values (V-tiles): (slot/32)*32*D + ((d/16)*4 + r/8)*128 + (d%16)*8 + r%8.
+ *   With it every operand load of the attention kernel is one contiguous
+ *   1 KB wave access.  Capacities (cap0, cap1) must be multiples of 32.
  *   Per sequence, the T0 pool holds the T0 positions in ascending order in
  *   slots [0, t0_len) and the T1 window holds the T1 positions in ascending
  *   order in slots [0, t1_len).  The "attended index" j of a sequence runs over
@@ -103,8 +106,8 @@ const char* tkv_last_error(void);
  * (Enonce du probleme; Methodologie section 1: the recent window is in T0).
  *
  * k_new, v_new : device [B][L][Hkv][D]
- * k_t0, v_t0   : device T0 pools [B][L][Hkv][cap0][D] (v_t0: V-panels); slot
- *                t0_len[b] of sequence b is written
+ * k_t0, v_t0   : device T0 pools [B][L][Hkv][cap0][D] tiles; slot t0_len[b]
+ *                of sequence b is written
  * t0_len       : host [B], current T0 length (the slot written); < cap0
  * t0_pos       : device [B][cap0] slot -> position map; t0_pos[b][t0_len[b]]
  *                is set to position[b]
@@ -117,10 +120,8 @@ tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new,
                       const int32_t* t0_len, int32_t* t0_pos, const int32_t* position,
                       float* scores, uint8_t* tier, int32_t max_ctx, hipStream_t stream);
 
-/* Bytes of device workspace tkv_decode_step needs for these capacities.  The
- * workspace must be zero-filled before its first use (it starts with arrival
- * counters); every completed call leaves that region zero again, so one
- * zero-fill at allocation is enough. */
+/* Bytes of device workspace tkv_decode_step needs for these capacities (split
+ * records of the split-K attention and the per-row softmax statistics). */
 size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t n_layers,
                                   int32_t cap0, int32_t cap1);
 
@@ -133,8 +134,8 @@ size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t
  * score sums (Methodologie section 2).
  *
  * q          : device [B][Lr][Hq][D], Lr = layer_end - layer_begin
- * k_t0, v_t0 : device [B][L][Hkv][cap0][D] (v_t0: V-panels); t0_len host [B]
- * k_t1, v_t1 : device [B][L][Hkv][cap1][D] (v_t1: V-panels); t1_len host [B];
+ * k_t0, v_t0 : device [B][L][Hkv][cap0][D] tiles; t0_len host [B] (<= cap0)
+ * k_t1, v_t1 : device [B][L][Hkv][cap1][D] tiles; t1_len host [B] (<= cap1);
  *              may be null when every t1_len is 0
  * out        : device [B][Lr][Hq][D] float32
  * alpha      : device [B][Lr][Hq][alpha_stride] float32; entry j is the weight
@@ -145,7 +146,7 @@ size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t
  *   call's layers and heads of alpha / (num_layers * Hq), exactly what
  *   tkv_update_scores would add.
  * workspace  : device, at least tkv_decode_workspace_bytes(model, batch, Lr,
- *              cap0, cap1) bytes, zero-filled before its first use
+ *              cap0, cap1) bytes (scratch; no initial contents needed)
  * Numerics: bf16 data use the matrix cores with float32 accumulation (the
  * softmax weights enter P.V as a bf16 pair hi + lo, ~2^-17 relative);
  * float32 data use plain float32 FMAs.
@@ -222,7 +223,7 @@ size_t tkv_compact_workspace_bytes(int32_t batch, int32_t cap0, int32_t cap1);
  * tier_prev/next    : device [B][max_ctx]
  * k/v_t0_src, t0_len_src (host [B]), cap0 : previous T0 pool [B][L][Hkv][cap0][D]
  * k/v_t1_src, t1_len_src (host [B]), cap1 : previous T1 window [B][L][Hkv][cap1][D]
- *                                           (values in V-panels, here and below)
+ *                                           (tiles, here and below)
  * k/v_t0_dst, t0_pos_dst : new T0 pool and its slot -> position map [B][cap0]
  * k/v_t1_dst, t1_pos_dst : new T1 window and its map [B][cap1]
  * t2_src    : device [B][t2_cap]: source of each newly-T2 row, in ascending
@@ -279,10 +280,11 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
  * host_k, host_v   : host [L][Hkv][max_ctx][D] full-precision store
  * positions        : host [n_t1], strictly ascending, each < max_ctx; null
  *                    re-sends the staging as it is (no pack)
- * staging_k/v      : pinned host [L][Hkv][cap1][D] (n_t1 <= cap1); staging_v is
- *                    written in V-panels (slots past n_t1 in the last panel are
- *                    zeroed), so the copy is a plain strided transfer
- * dev_k_t1/dev_v_t1: device window [L][Hkv][cap1][D] (V-panels); null packs only
+ * staging_k/v      : pinned host [L][Hkv][cap1][D] tiles (n_t1 <= cap1), written in
+ *                    the device window's storage order (value slots past n_t1
+ *                    in the last panel are zeroed), so the copy is a plain
+ *                    strided transfer of whole 32-slot blocks
+ * dev_k_t1/dev_v_t1: device window [L][Hkv][cap1][D] tiles; null packs only
  * ready            : event recorded on side_stream after the copies; may be null
  * The pack is synchronous on the calling thread; only the copies are queued.
  */

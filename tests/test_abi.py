@@ -51,7 +51,7 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 def decode(m, **kw):
     args = dict(batch=1, layer_begin=0, layer_end=m.num_layers, q=FAKE, k_t0=FAKE, v_t0=FAKE,
-                t0_len=[10], cap0=16, k_t1=FAKE, v_t1=FAKE, t1_len=[2], cap1=8, out=FAKE,
+                t0_len=[10], cap0=32, k_t1=FAKE, v_t1=FAKE, t1_len=[2], cap1=32, out=FAKE,
                 alpha=FAKE, alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE, scores=FAKE, max_ctx=64,
                 workspace=FAKE, workspace_bytes=1 << 30, stream=0)
     args.update(kw)
@@ -77,8 +77,9 @@ def test_decode_step_validation():
     assert status_of(decode, m, layer_begin=1, layer_end=1) == tkv.TKV_ERR_ARG
     assert status_of(decode, m, layer_end=3) == tkv.TKV_ERR_ARG
     assert status_of(decode, m, q=NULL) == tkv.TKV_ERR_ARG
-    assert status_of(decode, m, t0_len=[17]) == tkv.TKV_ERR_CAPACITY
-    assert status_of(decode, m, t1_len=[9]) == tkv.TKV_ERR_CAPACITY
+    assert status_of(decode, m, t0_len=[33]) == tkv.TKV_ERR_CAPACITY
+    assert status_of(decode, m, t1_len=[33]) == tkv.TKV_ERR_CAPACITY
+    assert status_of(decode, m, cap0=48) == tkv.TKV_ERR_ARG      # tile blocks of 32 slots
     assert status_of(decode, m, alpha_stride=11) == tkv.TKV_ERR_CAPACITY
     assert status_of(decode, m, workspace_bytes=16) == tkv.TKV_ERR_CAPACITY
     assert status_of(decode, m, k_t1=NULL) == tkv.TKV_ERR_ARG
@@ -111,16 +112,17 @@ def test_assign_tiers_validation():
 def test_compact_and_quant_validation():
     m = model()
     args = dict(model=m, batch=1, ctx_len=[10], max_ctx=16, tier_prev=FAKE, tier_next=FAKE,
-                k_t0_src=FAKE, v_t0_src=FAKE, t0_len_src=[6], cap0=16, k_t1_src=FAKE,
-                v_t1_src=FAKE, t1_len_src=[3], cap1=8, k_t0_dst=FAKE + 64, v_t0_dst=FAKE + 64,
+                k_t0_src=FAKE, v_t0_src=FAKE, t0_len_src=[6], cap0=32, k_t1_src=FAKE,
+                v_t1_src=FAKE, t1_len_src=[3], cap1=32, k_t0_dst=FAKE + 64, v_t0_dst=FAKE + 64,
                 t0_pos_dst=FAKE, k_t1_dst=FAKE + 64, v_t1_dst=FAKE + 64, t1_pos_dst=FAKE,
                 t2_src=FAKE, t2_pos=FAKE, t2_cap=8, new_lens=FAKE, workspace=FAKE,
                 workspace_bytes=1 << 20, stream=0)
     assert status_of(tkv.tkv_compact, **{**args, "t0_len_src": [8]}) == tkv.TKV_ERR_STATE
-    assert status_of(tkv.tkv_compact, **{**args, "t1_len_src": [9]}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_compact, **{**args, "t1_len_src": [33], "ctx_len": [40],
+                                          "max_ctx": 64}) == tkv.TKV_ERR_CAPACITY
     assert status_of(tkv.tkv_compact, **{**args, "k_t0_dst": FAKE}) == tkv.TKV_ERR_ARG
     assert status_of(tkv.tkv_compact, **{**args, "workspace_bytes": 8}) == tkv.TKV_ERR_CAPACITY
-    qargs = dict(model=m, batch=1, k_t0=FAKE, v_t0=FAKE, cap0=16, k_t1=FAKE, v_t1=FAKE, cap1=8,
+    qargs = dict(model=m, batch=1, k_t0=FAKE, v_t0=FAKE, cap0=32, k_t1=FAKE, v_t1=FAKE, cap1=32,
                  src=FAKE, n_rows=FAKE, n_rows_stride=3, max_rows=4, codes=FAKE, scales=FAKE,
                  stream=0)
     assert status_of(tkv.tkv_quantize_t2, **{**qargs, "src": NULL}) == tkv.TKV_ERR_ARG
@@ -130,8 +132,8 @@ def test_compact_and_quant_validation():
 
 def test_append_validation():
     m = model()
-    args = dict(model=m, batch=1, k_new=FAKE, v_new=FAKE, k_t0=FAKE, v_t0=FAKE, cap0=16,
-                t0_len=[16], t0_pos=FAKE, position=[20], scores=FAKE, tier=FAKE, max_ctx=64,
+    args = dict(model=m, batch=1, k_new=FAKE, v_new=FAKE, k_t0=FAKE, v_t0=FAKE, cap0=32,
+                t0_len=[32], t0_pos=FAKE, position=[40], scores=FAKE, tier=FAKE, max_ctx=64,
                 stream=0)
     assert status_of(tkv.tkv_append, **args) == tkv.TKV_ERR_CAPACITY
     assert status_of(tkv.tkv_append, **{**args, "t0_len": [3], "position": [64]}) == \
@@ -143,7 +145,7 @@ def test_gather_host_pack_without_device():
     # positions ascending check, then a pack-only call (no device pointers -> no HIP call)
     m = model(layers=2, kv_heads=2, q_heads=2, head_dim=64)
     r = np.random.default_rng(0)
-    max_ctx, cap1 = 40, 8
+    max_ctx, cap1 = 40, 32
     hk = r.integers(0, 65535, size=(2, 2, max_ctx, 64)).astype(np.uint16)
     hv = r.integers(0, 65535, size=(2, 2, max_ctx, 64)).astype(np.uint16)
     sk = np.zeros((2, 2, cap1, 64), np.uint16)
@@ -152,13 +154,18 @@ def test_gather_host_pack_without_device():
         tkv.TKV_ERR_ARG
     assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 40], 2, sk, sv, cap1) == \
         tkv.TKV_ERR_ARG
-    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, list(range(9)), 9, sk, sv, cap1) == \
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, list(range(33)), 33, sk, sv, cap1) == \
         tkv.TKV_ERR_CAPACITY
     pos = [1, 5, 6, 17, 39]
     tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), sk, sv, cap1)
-    assert sk[:, :, :5].tobytes() == hk[:, :, pos].tobytes()
-    # values go to 8-slot panels: slot r, dimension d at [r // 8][d][r % 8]
-    panels = sv.reshape(2, 2, cap1 // 8, 64, 8)
-    rows = panels.transpose(0, 1, 2, 4, 3).reshape(2, 2, cap1, 64)
-    assert rows[:, :, :5].tobytes() == hv[:, :, pos].tobytes()
-    assert not rows[:, :, 5:8].any()            # the tail of the last panel is cleared
+    # storage order of 32-slot blocks: K-tiles and V-tiles (element-wise definition)
+    for r in range(len(pos)):
+        for d in range(64):
+            jj, u, i = (r % 32) // 8, (r % 32) // 4 % 2, r % 4
+            ko = (r // 32) * 32 * 64 + u * 16 * 64 + ((d // 8) * 16 + 4 * jj + i) * 8 + d % 8
+            vo = (r // 32) * 32 * 64 + ((d // 16) * 4 + (r % 32) // 8) * 128 + (d % 16) * 8 + r % 8
+            assert sk.reshape(2, 2, -1)[:, :, ko].tolist() == hk[:, :, pos[r], d].tolist()
+            assert sv.reshape(2, 2, -1)[:, :, vo].tolist() == hv[:, :, pos[r], d].tolist()
+    for r in range(len(pos), 8):                 # the rest of the last value panel is cleared
+        vo = [((d // 16) * 4 + r // 8) * 128 + (d % 16) * 8 + r % 8 for d in range(64)]
+        assert not sv.reshape(2, 2, -1)[:, :, vo].any()

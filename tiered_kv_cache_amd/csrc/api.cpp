@@ -110,26 +110,10 @@ static float scale_of(const tkv_model* m) {
   return m->softmax_scale > 0.f ? m->softmax_scale : 1.0f / sqrtf((float)m->head_dim);
 }
 
-// Splits per (sequence, layer, query head) for any chunk >= kAttnChunkMin (+1: the
-// empty task of an empty sequence).
-static int max_splits_for(int cap0, int cap1) {
-  return ceil_div(cap0, kAttnChunkMin) + ceil_div(cap1, kAttnChunkMin) + 1;
-}
-
-// Tokens per split of the bf16 path: a multiple of kAttnChunkMin (TKV_ATTN_CHUNK
-// overrides the default for tuning sweeps).
-static int mfma_chunk() {
-  static int c = [] {
-    const char* e = getenv("TKV_ATTN_CHUNK");
-    int v = e ? atoi(e) : 256;
-    if (v < kAttnChunkMin) v = kAttnChunkMin;
-    return v / kAttnChunkMin * kAttnChunkMin;
-  }();
-  return c;
-}
-
-static size_t counters_bytes(int batch, int n_layers, int hkv) {
-  return ((size_t)batch * n_layers * hkv * sizeof(int32_t) + 255) / 256 * 256;
+// Split records of one launch: at most workers + groups (see attention.hip).
+static size_t max_records(int batch, int n_layers, int hkv) {
+  const int nb = batch < kMaxSeqPerLaunch ? batch : kMaxSeqPerLaunch;
+  return (size_t)kMaxWorkers + (size_t)nb * n_layers * hkv;
 }
 
 }  // namespace tkv
@@ -173,7 +157,7 @@ tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new, 
   if (batch == 0) return TKV_OK;
   if (!k_new || !v_new || !k_t0 || !v_t0 || !t0_len || !t0_pos || !position)
     return fail(TKV_ERR_ARG, "null pointer");
-  if (cap0 < 1 || cap0 % 8) return fail(TKV_ERR_ARG, "cap0 must be a positive multiple of 8");
+  if (cap0 < 1 || cap0 % 32) return fail(TKV_ERR_ARG, "cap0 must be a positive multiple of 32");
   for (int b = 0; b < batch; ++b) {
     if (t0_len[b] < 0 || position[b] < 0) return fail(TKV_ERR_ARG, "negative length or position");
     if (t0_len[b] >= cap0) return fail(TKV_ERR_CAPACITY, "T0 pool full (t0_len >= cap0)");
@@ -208,12 +192,12 @@ tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new, 
 size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t n_layers,
                                   int32_t cap0, int32_t cap1) {
   if (!model || batch < 0 || n_layers < 0 || cap0 < 0 || cap1 < 0) return 0;
-  if (model->num_kv_heads < 1) return 0;
-  const size_t rows = (size_t)batch * n_layers * model->num_q_heads;
-  const size_t ms = (size_t)max_splits_for(cap0, cap1);
+  if (model->num_kv_heads < 1 || model->num_q_heads < 1) return 0;
+  const size_t G = (size_t)(model->num_q_heads / model->num_kv_heads);
   const size_t D = (size_t)model->head_dim;
-  return counters_bytes(batch, n_layers, model->num_kv_heads) +
-         rows * ms * (D + 2) * sizeof(float) + rows * 2 * sizeof(float);
+  const size_t recs = max_records(batch, n_layers, model->num_kv_heads);
+  const size_t rows = (size_t)batch * n_layers * model->num_q_heads;
+  return recs * G * (D + 2) * sizeof(float) + rows * 2 * sizeof(float) + 256;
 }
 
 tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
@@ -232,7 +216,7 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   if (!q || !k_t0 || !v_t0 || !t0_len || !t1_len || !out || !alpha || !workspace)
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap0 < 0 || cap1 < 0 || alpha_stride < 1) return fail(TKV_ERR_ARG, "bad capacity or stride");
-  if (cap0 % 8 || cap1 % 8) return fail(TKV_ERR_ARG, "cap0 and cap1 must be multiples of 8");
+  if (cap0 % 32 || cap1 % 32) return fail(TKV_ERR_ARG, "cap0 and cap1 must be multiples of 32");
   bool any_t1 = false;
   for (int b = 0; b < batch; ++b) {
     if (t0_len[b] < 0 || t1_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
@@ -251,12 +235,18 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   const int hq = model->num_q_heads;
   const int hkv = model->num_kv_heads;
   const int D = model->head_dim;
-  const int max_splits = max_splits_for(cap0, cap1);
-  const int chunk = model->kv_dtype == TKV_BF16 ? mfma_chunk() : kAttnChunkValu;
-  int* counters = (int*)workspace;
-  float* part = (float*)((char*)workspace + counters_bytes(batch, Lr, hkv));
-  float* ml = part + (size_t)batch * Lr * hq * max_splits * D;
-  float* stat = ml + (size_t)batch * Lr * hq * max_splits * 2;
+  const int G = hq / hkv;
+  const bool mfma = model->kv_dtype == TKV_BF16;
+  const int unit = mfma ? kUnitMfma : kUnitValu;
+  const size_t recs = max_records(batch, Lr, hkv);
+  float* part = (float*)workspace;
+  float* ml = part + recs * G * D;
+  float* stat = ml + recs * G * 2;
+  int resident = 0;
+  if (mfma) {
+    resident = mfma_resident_waves(D);
+    if (resident < 1) return fail(TKV_ERR_HIP, "cannot query the device for its occupancy");
+  }
 
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
@@ -271,9 +261,8 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     a.part = part;
     a.ml = ml;
     a.stat = stat;
-    a.counters = counters;
     a.alpha_stride = alpha_stride;
-    a.chunk = chunk;
+    a.unit = unit;
     a.cap0 = cap0;
     a.cap1 = cap1;
     a.L = model->num_layers;
@@ -281,24 +270,33 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     a.layer_begin = layer_begin;
     a.hq = hq;
     a.hkv = hkv;
-    a.max_splits = max_splits;
-    a.scale = scale_of(model);
+    // logits are kept in base 2: q.k * softmax_scale * log2(e)
+    a.scale = (float)((double)scale_of(model) * 1.4426950408889634074);
     a.seq.nb = nb;
     a.seq.b_offset = b0;
-    int tasks = 0, sblocks = 0;
+    long units = 0;
+    int sblocks = 0;
     ScoreArgs sa{};
     for (int i = 0; i < nb; ++i) {
       const int n0 = t0_len[b0 + i], n1 = t1_len[b0 + i];
       a.seq.t0_len[i] = n0;
       a.seq.t1_len[i] = n1;
-      a.seq.base[i] = tasks;
+      a.seq.base[i] = (int)units;
+      a.seq.units[i] = ceil_div(n0, unit) + ceil_div(n1, unit);
+      units += (long)Lr * hkv * a.seq.units[i];
       sa.seq.base[i] = sblocks;
-      tasks += std::max(1, ceil_div(n0, chunk) + ceil_div(n1, chunk));
       sblocks += ceil_div(n0 + n1, kScoreSlots);
     }
-    a.seq.base[nb] = tasks;
-    launch_attn_partial(a, model->kv_dtype, D, hq / hkv, tasks, stream);
-    if ((st = hip_check(hipGetLastError(), "attn_partial launch"))) return st;
+    if (units > (1L << 30)) return fail(TKV_ERR_CAPACITY, "too many attention work units");
+    a.seq.base[nb] = (int)units;
+    a.total_units = units;
+    a.workers = mfma ? resident : std::min<long>(units, kMaxWorkers);
+    if (units > 0) {
+      launch_attn_partial(a, model->kv_dtype, D, G, stream);
+      if ((st = hip_check(hipGetLastError(), "attn_partial launch"))) return st;
+    }
+    launch_attn_combine(a, D, nb, stream);
+    if ((st = hip_check(hipGetLastError(), "attn_combine launch"))) return st;
 
     sa.alpha = alpha;
     sa.stat = stat;
@@ -452,8 +450,8 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap1 > 0 && (!k_t1_src || !v_t1_src || !k_t1_dst || !v_t1_dst || !t1_pos_dst))
     return fail(TKV_ERR_ARG, "null T1 pointer with cap1 > 0");
-  if (cap0 < 1 || cap1 < 0 || t2_cap < 0 || max_ctx < 1 || cap0 % 8 || cap1 % 8)
-    return fail(TKV_ERR_ARG, "bad capacity (cap0, cap1 multiples of 8)");
+  if (cap0 < 1 || cap1 < 0 || t2_cap < 0 || max_ctx < 1 || cap0 % 32 || cap1 % 32)
+    return fail(TKV_ERR_ARG, "bad capacity (cap0, cap1 multiples of 32)");
   if (k_t0_src == k_t0_dst || v_t0_src == v_t0_dst || (cap1 > 0 && (k_t1_src == k_t1_dst ||
                                                                     v_t1_src == v_t1_dst)))
     return fail(TKV_ERR_ARG, "source and destination buffers must differ");
@@ -533,8 +531,8 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
   if (!k_t0 || !v_t0 || !src || !n_rows || !codes || !scales)
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap1 > 0 && (!k_t1 || !v_t1)) return fail(TKV_ERR_ARG, "null T1 window with cap1 > 0");
-  if (n_rows_stride < 1 || cap0 < 0 || cap1 < 0 || cap0 % 8 || cap1 % 8)
-    return fail(TKV_ERR_ARG, "bad stride or capacity (cap0, cap1 multiples of 8)");
+  if (n_rows_stride < 1 || cap0 < 0 || cap1 < 0 || cap0 % 32 || cap1 % 32)
+    return fail(TKV_ERR_ARG, "bad stride or capacity (cap0, cap1 multiples of 32)");
   if (max_rows > 65535) return fail(TKV_ERR_CAPACITY, "max_rows above 65535");
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, batch - b0);

@@ -7,28 +7,42 @@
 // set.  Section 2: the score of a position grows by its attention weight
 // averaged over heads and layers.
 //
-// Kernels (one decode step; every requested layer in one launch each):
-//   attn_partial_mfma -- bf16 path.  A workgroup (4 waves) owns a chunk of one
-//       segment (T0 pool or T1 window) of one (sequence, layer, KV head).  Each
-//       wave walks 32-token pairs: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the
-//       group's query heads padded to 16 columns), an online softmax with lazy
-//       rescaling, and O += P V on the same MFMA with P split into a bf16 high
-//       part and a bf16 remainder (P V is then exact to ~2^-17 relative).  The
-//       token order inside a pair is permuted so that the S^T accumulator is
-//       already the A operand of P V, and V is stored in 8-slot panels
-//       (head_dim-major inside a panel) so its B operand is one 16-byte load:
-//       no LDS transpose, no shuffles.  The raw scaled logits go to `alpha`.
-//   attn_partial_valu -- float32 path (plain FMAs), same work decomposition.
-//   Both end with a split record (m, l, acc) and the last workgroup of each
-//   (sequence, layer, KV head) -- found with a device-scope counter -- merges
-//   the splits: M = max m, Lambda = sum l e^(m-M), O = sum acc e^(m-M) / Lambda,
-//   and stores (M, 1/Lambda).
-//   alpha_score -- per 16 attended slots (8 waves, 32 row groups): alpha = e^(S-M)/Lambda written in
+// Work decomposition (stream-K): each (sequence, layer, KV head) "group" has a
+// T0 segment and a T1 segment, cut into work units of U tokens (U = 32 on the
+// matrix-core path, 256 on the float32 path); units are numbered group after
+// group.  Worker w of W owns units [w*P/W, (w+1)*P/W) -- an equal share, so the
+// launch has no tail -- runs one online softmax per group it touches and writes
+// one split record per group, at record index w + group (unique, and at most
+// W + groups records).
+//
+// Kernels:
+//   attn_partial_mfma -- bf16 path; a worker is one wave, the grid holds as
+//       many waves as fit on the GPU at once.  Per 32-token unit:
+//       S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the group's query heads padded
+//       to 16 columns), an online softmax with lazy rescaling, and O += P V on
+//       the same MFMA with P split into a bf16 high part and a bf16 remainder
+//       (P V is then exact to ~2^-17 relative).  The token order inside a unit
+//       is permuted so that the S^T accumulator is already the A operand of
+//       P V, and keys and values are stored in the operand order (K-tiles,
+//       V-tiles: layout.h), so every operand load is one contiguous 1 KB wave
+//       access: no LDS, no barriers.  The next
+//       unit's loads are issued before the current unit is computed.  The
+//       logits are kept in base 2 (q.k * softmax_scale * log2 e), so every
+//       weight is one v_exp_f32; they go to `alpha` and are normalised there
+//       by alpha_score.
+//   attn_partial_valu -- float32 path (plain FMAs); a worker is a workgroup.
+//   attn_combine -- one wave per (sequence, layer, query head) merges the split
+//       records: M = max m, Lambda = sum l e^(m-M), O = sum acc e^(m-M)/Lambda;
+//       stores (M, 1/Lambda).  (A separate launch: merging in the
+//       last-arriving workgroup would need an agent-scope fence per workgroup,
+//       which on this GPU writes back the per-XCD L2.)
+//   alpha_score -- per 16 attended slots: alpha = e^(S-M)/Lambda written in
 //       place, summed in float64 over every (layer, head) and added, weighted
 //       1/(num_layers*Hq), to the score of the slot's position.  Also the
 //       standalone score update (alpha already normalised).
 #include "common.h"
 #include "kernels.h"
+#include "layout.h"
 
 namespace tkv {
 
@@ -38,266 +52,339 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // ---------------------------------------------------------------------------
-// work decomposition: per sequence, ceil(t0_len/chunk) T0 tasks then
-// ceil(t1_len/chunk) T1 tasks (one empty task for an empty sequence)
+// work units
 // ---------------------------------------------------------------------------
-struct Task {
-  int bl;
-  long b;
-  int seg;    // 0: T0 pool, 1: T1 window
-  int c0, c1; // slot range inside the segment
-  int split;  // index among the sequence's tasks
-  int nsplit;
+struct Unit {
+  long b;      // sequence in the caller's batch
+  long group;  // group index within the launch
+  int lr, g;   // layer (relative) and KV head
+  int seg;     // 0: T0 pool, 1: T1 window
+  int c0, c1;  // slot range inside the segment
+  int n0;      // T0 length (attended index of T1 slot 0)
+};
+
+__device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long p) {
+  int bl = 0;
+  while (bl + 1 < a.seq.nb && a.seq.base[bl + 1] <= p) ++bl;
+  Unit u;
+  u.b = a.seq.b_offset + bl;
+  const int n0 = a.seq.t0_len[bl], n1 = a.seq.t1_len[bl];
+  u.n0 = n0;
+  const long local = p - a.seq.base[bl];
+  const int per = a.seq.units[bl];
+  const int lgl = (int)(local / per);
+  const int q = (int)(local - (long)lgl * per);
+  u.lr = lgl / a.hkv;
+  u.g = lgl - u.lr * a.hkv;
+  u.group = (long)bl * a.Lr * a.hkv + lgl;
+  const int nu0 = (n0 + a.unit - 1) / a.unit;
+  if (q < nu0) {
+    u.seg = 0;
+    u.c0 = q * a.unit;
+    u.c1 = min(n0, u.c0 + a.unit);
+  } else {
+    u.seg = 1;
+    u.c0 = (q - nu0) * a.unit;
+    u.c1 = min(n1, u.c0 + a.unit);
+  }
+  return u;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path: MFMA partial attention, one worker per wave
+// ---------------------------------------------------------------------------
+// Walks the units of a worker's range in order.  Everything here is uniform
+// across the wave (scalar registers); only the first position needs a division.
+struct Cursor {
+  int bl;      // sequence within the launch
+  int lgl;     // group within the sequence: layer * Hkv + KV head
+  int lr, g;
+  int seg;     // 0: T0 pool, 1: T1 window
+  int c0;      // first slot of the unit inside the segment
   int n0, n1;
 };
 
-__device__ __forceinline__ Task decode_task(const AttnArgs& a, int t) {
+__device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
+  Cursor c;
   int bl = 0;
-  while (bl + 1 < a.seq.nb && a.seq.base[bl + 1] <= t) ++bl;
-  Task k;
-  k.bl = bl;
-  k.b = a.seq.b_offset + bl;
-  k.n0 = a.seq.t0_len[bl];
-  k.n1 = a.seq.t1_len[bl];
-  k.split = t - a.seq.base[bl];
-  k.nsplit = a.seq.base[bl + 1] - a.seq.base[bl];
-  const int nt0 = (k.n0 + a.chunk - 1) / a.chunk;
-  if (k.split < nt0) {
-    k.seg = 0;
-    k.c0 = k.split * a.chunk;
-    k.c1 = min(k.n0, k.c0 + a.chunk);
-  } else if (k.n1 > 0) {
-    k.seg = 1;
-    k.c0 = (k.split - nt0) * a.chunk;
-    k.c1 = min(k.n1, k.c0 + a.chunk);
-  } else {
-    k.seg = 0;
-    k.c0 = 0;
-    k.c1 = 0;
-  }
-  return k;
+  while (bl + 1 < a.seq.nb && a.seq.base[bl + 1] <= p) ++bl;
+  c.bl = bl;
+  c.n0 = a.seq.t0_len[bl];
+  c.n1 = a.seq.t1_len[bl];
+  const long local = p - a.seq.base[bl];
+  const int per = a.seq.units[bl];
+  c.lgl = (int)(local / per);
+  const int q = (int)(local - (long)c.lgl * per);
+  c.lr = c.lgl / a.hkv;
+  c.g = c.lgl - c.lr * a.hkv;
+  const int nu0 = (c.n0 + kUnitMfma - 1) / kUnitMfma;
+  c.seg = q < nu0 ? 0 : 1;
+  c.c0 = (q < nu0 ? q : q - nu0) * kUnitMfma;
+  return c;
 }
 
-// Every workgroup calls this after writing its split record (all threads, with
-// `flag` in LDS).  The last one to arrive for its (sequence, layer, KV head)
-// merges the splits into the output and the softmax statistics, and resets the
-// counter for the next call.
-__device__ void merge_if_last(const AttnArgs& a, const Task& k, int lr, int g, int D, int* flag) {
-  const int G = a.hq / a.hkv;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* ctr = a.counters + (k.b * a.Lr + lr) * a.hkv + g;
-    const int prev = atomicAdd(ctr, 1);
-    const int last = prev == k.nsplit - 1;
-    if (last) atomicExch(ctr, 0);
-    *flag = last;
+// Next unit in the global order (T0 units, then T1 units, group after group).
+__device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
+  c.c0 += kUnitMfma;
+  if (c.c0 < (c.seg ? c.n1 : c.n0)) return;
+  c.c0 = 0;
+  if (c.seg == 0 && c.n1 > 0) {
+    c.seg = 1;
+    return;
   }
-  __syncthreads();
-  if (!*flag) return;
-  __threadfence();
-  const long row0 = (k.b * a.Lr + lr) * a.hq + (long)g * G;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D;
-    const int d = i - h * D;
-    const long row = row0 + h;
-    const float* mlp = a.ml + row * a.max_splits * 2;
-    const float* pp = a.part + row * a.max_splits * D + d;
-    float M = -INFINITY;
-    for (int s = 0; s < k.nsplit; ++s) M = fmaxf(M, mlp[2 * s]);
-    float lam = 0.f, o = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < k.nsplit; ++s) {
-        const float ms = mlp[2 * s];
-        if (ms == -INFINITY) continue;
-        const float w = exp_acc(ms - M);
-        lam = fmaf(mlp[2 * s + 1], w, lam);
-        o = fmaf(pp[(long)s * D], w, o);
-      }
-    }
-    a.out[row * D + d] = lam > 0.f ? o / lam : 0.f;
-    if (d == 0) {
-      a.stat[row * 2] = M;
-      a.stat[row * 2 + 1] = lam > 0.f ? 1.0f / lam : 0.f;
+  if (++c.g == a.hkv) {
+    c.g = 0;
+    ++c.lr;
+  }
+  ++c.lgl;
+  if (c.lgl == a.Lr * a.hkv) {  // next sequence with work
+    c.lgl = c.lr = c.g = 0;
+    do {
+      ++c.bl;
+    } while (c.bl < a.seq.nb && a.seq.units[c.bl] == 0);
+    if (c.bl < a.seq.nb) {
+      c.n0 = a.seq.t0_len[c.bl];
+      c.n1 = a.seq.t1_len[c.bl];
     }
   }
+  c.seg = c.n0 > 0 ? 0 : 1;
 }
 
-// ---------------------------------------------------------------------------
-// bf16 path: MFMA partial attention
-// ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void attn_partial_mfma_kernel(AttnArgs a) {
-  constexpr int KB = D / 32;  // k-blocks of S^T = K Q^T
-  constexpr int NB = D / 16;  // n-blocks of O = P V
-  constexpr float kLazy = 8.0f;  // rescale only when a new max exceeds the old by this
-  __shared__ float o_lds[4][16][D + 4];
-  __shared__ float m_lds[4][16], l_lds[4][16];
-  __shared__ int flag;
+struct UnitLoads {
+  uint4 k[2][D / 32];
+  uint4 v[D / 16];
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int h = lane & 15;    // head column of S^T / P row; token row of the K operand
-  const int grp = lane >> 4;  // k-slice of the operands; 8-token block of the pair
-  const int lr = blockIdx.y / a.hkv;
-  const int g = blockIdx.y - lr * a.hkv;
-  const Task k = decode_task(a, blockIdx.x);
-  const int G = a.hq / a.hkv;
-  const long layer = a.layer_begin + lr;
-  const int cap = k.seg ? a.cap1 : a.cap0;
-  const long lg = (k.b * a.L + layer) * a.hkv + g;
-  const uint16_t* Kb = (const uint16_t*)(k.seg ? a.k1 : a.k0) + lg * cap * D;
-  const uint4* Vb = (const uint4*)((const uint16_t*)(k.seg ? a.v1 : a.v0) + lg * cap * D);
-  const long jofs = k.seg ? k.n0 : 0;
+template <int D>
+struct WaveState {
+  f32x4_t acc[D / 16];
+  bf16x8_t qop[D / 32];
+  float m, lsum;  // running max (base-2 logits) and partial sum of this lane's 8 columns
+  long group;     // group index within the launch of the current softmax
+  float* lg_row;  // logits row of this lane's head (null for padding heads)
+};
 
-  // B operand of S^T: lane holds Q[h][kb*32 + grp*8 + e]; heads >= G are zero
-  bf16x8_t qop[KB];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((k.b * a.Lr + lr) * a.hq + (long)g * G + h) * D;
+template <int D>
+__device__ __forceinline__ void begin_group(const AttnArgs& a, const Cursor& c, int h, int grp,
+                                            int G, WaveState<D>& st) {
+  constexpr int KB = D / 32, NB = D / 16;
+  const long b = a.seq.b_offset + c.bl;
+  st.group = (long)c.bl * a.Lr * a.hkv + c.lgl;
+  const long row = (b * a.Lr + c.lr) * a.hq + (long)c.g * G + h;
+  const uint16_t* qrow = (const uint16_t*)a.q + row * D;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (h < G) v = *(const uint4*)(qrow + kb * 32 + grp * 8);
-      qop[kb] = as_bf16x8(v);
+  for (int kb = 0; kb < KB; ++kb) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h < G) v = *(const uint4*)(qrow + kb * 32 + grp * 8);
+    st.qop[kb] = as_bf16x8(v);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) st.acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.lsum = 0.f;
+  st.lg_row = h < G ? a.alpha + row * a.alpha_stride : nullptr;
+}
+
+// Split record of (worker, group): per head of the group, (m, l) and the partial P.V.
+template <int D>
+__device__ __forceinline__ void flush_record(const AttnArgs& a, long worker, int h, int grp, int G,
+                                             WaveState<D>& st) {
+  constexpr int NB = D / 16;
+  float l = st.lsum;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  const long rec = (worker + st.group) * G;
+  if (grp == 0 && h < G) {
+    a.ml[(rec + h) * 2] = st.m;
+    a.ml[(rec + h) * 2 + 1] = l;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int head = grp * 4 + r;
+    if (head < G) {
+      float* dst = a.part + (rec + head) * D + h;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dst[nb * 16] = st.acc[nb][r];
     }
   }
-  f32x4_t acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
-  float* lg_out = a.alpha + ((k.b * a.Lr + lr) * a.hq + (long)g * G + h) * a.alpha_stride + jofs;
-  const bool write_logits = h < G;
+}
 
-  for (int pb = k.c0 + 32 * w; pb < k.c1; pb += 128) {
-    // --- loads: K rows of the permuted tiles, V panels ---------------------
-    uint4 kr[2][KB];
+// Loads of one unit: with K-tiles and V-tiles every operand is one contiguous
+// 1 KB wave access at lane offset kb*64 + lane (K) or nb*64 + lane (V).  The
+// 32-slot block is always inside the allocation (capacities are multiples of
+// 32); slots past the segment end are masked when consumed.
+template <int D>
+__device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, int lane,
+                                            UnitLoads<D>& L) {
+  constexpr int KB = D / 32, NB = D / 16;
+  const long b = a.seq.b_offset + c.bl;
+  const int cap = c.seg ? a.cap1 : a.cap0;
+  const long blk = ((b * a.L + a.layer_begin + c.lr) * a.hkv + c.g) * (long)cap * D + (long)c.c0 * D;
+  const uint4* Ku = (const uint4*)((const uint16_t*)(c.seg ? a.k1 : a.k0) + blk);
+  const uint4* Vu = (const uint4*)((const uint16_t*)(c.seg ? a.v1 : a.v0) + blk);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = pb + 8 * (h >> 2) + 4 * u + (h & 3);
-      if (t < k.c1) {
-        const uint4* src = (const uint4*)(Kb + (long)t * D + grp * 8);
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kr[u][kb] = src[kb * 4];
-      } else {
+    for (int kb = 0; kb < KB; ++kb) L.k[u][kb] = Ku[u * 2 * D + kb * 64 + lane];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kr[u][kb] = make_uint4(0, 0, 0, 0);
+  for (int nb = 0; nb < NB; ++nb) L.v[nb] = Vu[nb * 64 + lane];
+}
+
+template <int D, bool FULL>
+__device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
+                                        int h, int grp, WaveState<D>& st) {
+  constexpr int KB = D / 32, NB = D / 16;
+  constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
+  const int c1 = c.seg ? c.n1 : c.n0;
+  const int tb = c.c0 + 8 * grp;  // first of this lane's 8 tokens
+  if (!FULL) {  // tail panel: zero the value slots past the end of the segment
+    const int valid = c1 - tb;
+    if (valid > 0 && valid < 8) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t* wds = (uint32_t*)&L.v[nb];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= valid) wds[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
       }
     }
-    const int p = (pb >> 3) + grp;  // this lane's V panel (slots 8p .. 8p+7)
-    uint4 vr[NB];
-    if (8 * p < k.c1) {
-      const uint4* vsrc = Vb + (long)p * D + h;
+  }
+  // S^T = K Q^T: this lane gets tokens tb + e (e = 0..7) of head h
+  f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vr[nb] = vsrc[nb * 16];
-      const int valid = k.c1 - 8 * p;
-      if (valid < 8) {  // tail panel: zero the slots past the end
+  for (int kb = 0; kb < KB; ++kb) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.k[0][kb]), st.qop[kb], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.k[1][kb]), st.qop[kb], s1, 0, 0, 0);
+  }
+  float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  float pm = -INFINITY;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          uint32_t* wds = (uint32_t*)&vr[nb];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= valid) wds[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        }
-      }
+  for (int e = 0; e < 8; ++e) {
+    sv[e] *= a.scale;  // base-2 logit: q.k * softmax_scale * log2(e)
+    if (!FULL && tb + e >= c1) sv[e] = -INFINITY;
+    pm = fmaxf(pm, sv[e]);
+  }
+  if (st.lg_row) {
+    float* dst = st.lg_row + (c.seg ? c.n0 : 0) + tb;
+    if (FULL && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
     } else {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vr[nb] = make_uint4(0, 0, 0, 0);
-    }
-
-    // --- S^T = K Q^T: lane gets tokens pb+8grp+e (e = 0..7) of head h -----
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[0][kb]), qop[kb], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[1][kb]), qop[kb], s1, 0, 0, 0);
-    }
-    const int tb = pb + 8 * grp;
-    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    float pm = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sv[e] = (tb + e < k.c1) ? sv[e] * a.scale : -INFINITY;
-      pm = fmaxf(pm, sv[e]);
-    }
-    if (write_logits) {
-#pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (tb + e < k.c1) lg_out[tb + e] = sv[e];
+        if (FULL || tb + e < c1) dst[e] = sv[e];
     }
-    pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-    pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+  }
+  pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+  pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+  if (__ballot(pm > st.m + kLazy) != 0ull) {
+    const float mn = fmaxf(st.m, pm);
+    const float corr = __builtin_amdgcn_exp2f(st.m - mn);  // 0 on the first unit (m = -inf)
+    st.lsum *= corr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float cr = __shfl(corr, grp * 4 + r, 64);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) st.acc[nb][r] *= cr;
+    }
+    st.m = mn;
+  }
+  bf16x8_t phi, plo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float pe = __builtin_amdgcn_exp2f(sv[e] - st.m);  // masked slots: exp2(-inf) = 0
+    st.lsum += pe;
+    const __bf16 hb = (__bf16)pe;
+    phi[e] = hb;
+    plo[e] = (__bf16)(pe - (float)hb);
+  }
+  // O += P V (high part, then the remainder)
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, as_bf16x8(L.v[nb]), st.acc[nb], 0, 0, 0);
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, as_bf16x8(L.v[nb]), st.acc[nb], 0, 0, 0);
+  }
+}
 
-    // --- online softmax, rescaling only when the max moves by > kLazy ------
-    if (__ballot(pm > m + kLazy) != 0ull) {
-      const float mn = fmaxf(m, pm);
-      const float corr = (m == -INFINITY) ? 0.f : exp_acc(m - mn);
-      lsum *= corr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float cr = __shfl(corr, grp * 4 + r, 64);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb][r] *= cr;
-      }
-      m = mn;
-    }
-    bf16x8_t phi, plo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = (sv[e] == -INFINITY) ? 0.f : exp_acc(sv[e] - m);
-      lsum += pe;
-      const __bf16 hb = (__bf16)pe;
-      phi[e] = hb;
-      plo[e] = (__bf16)(pe - (float)hb);
-    }
-    // --- O += P V (high part, then the remainder) --------------------------
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, as_bf16x8(vr[nb]), acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, as_bf16x8(vr[nb]), acc[nb], 0, 0, 0);
-    }
-  }
+// Prefetch depth of the matrix-core kernel: 1 issues the next unit's loads before
+// computing the current one (two register buffers, fewer waves per SIMD); 0 loads
+// and computes one unit at a time (one buffer, more waves per SIMD).
+#ifndef TKV_MFMA_PIPELINE
+#define TKV_MFMA_PIPELINE 0
+#endif
+// Minimum workgroups per CU the compiler must fit (register budget).
+#ifndef TKV_MFMA_MIN_BLOCKS
+#define TKV_MFMA_MIN_BLOCKS 2
+#endif
 
-  // --- merge the 4 waves into this workgroup's split record --------------
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (lane < 16) {
-    m_lds[w][lane] = m;
-    l_lds[w][lane] = lsum;
+template <int D>
+__device__ __forceinline__ bool unit_full(const Cursor& c) {
+  return c.c0 + kUnitMfma <= (c.seg ? c.n1 : c.n0);
+}
+
+template <int D>
+__device__ __forceinline__ void load_unit(const AttnArgs& a, const Cursor& c, int h, int grp,
+                                          UnitLoads<D>& L) {
+  issue_loads<D>(a, c, grp * 16 + h, L);
+}
+
+template <int D>
+__device__ __forceinline__ void step_unit(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
+                                          long w, int h, int grp, int G, WaveState<D>& st) {
+  const long group = (long)c.bl * a.Lr * a.hkv + c.lgl;
+  if (group != st.group) {
+    flush_record<D>(a, w, h, grp, G, st);
+    begin_group<D>(a, c, h, grp, G, st);
   }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o_lds[w][grp * 4 + r][nb * 16 + h] = acc[nb][r];
-  __syncthreads();
-  const long row0 = (k.b * a.Lr + lr) * a.hq + (long)g * G;
-  for (int i = tid; i < G * D; i += 256) {
-    const int hh = i / D;
-    const int d = i - hh * D;
-    float M = fmaxf(fmaxf(m_lds[0][hh], m_lds[1][hh]), fmaxf(m_lds[2][hh], m_lds[3][hh]));
-    float o = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float mw = m_lds[ww][hh];
-        if (mw == -INFINITY) continue;
-        const float c = exp_acc(mw - M);
-        o = fmaf(o_lds[ww][hh][d], c, o);
-        l = fmaf(l_lds[ww][hh], c, l);
-      }
-    }
-    const long row = row0 + hh;
-    a.part[(row * a.max_splits + k.split) * D + d] = o;
-    if (d == 0) {
-      a.ml[(row * a.max_splits + k.split) * 2] = M;
-      a.ml[(row * a.max_splits + k.split) * 2 + 1] = l;
-    }
+  if (unit_full<D>(c)) consume<D, true>(a, c, L, h, grp, st);
+  else consume<D, false>(a, c, L, h, grp, st);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane & 15;    // head column of S^T / P row; token row of the K operand
+  const int grp = lane >> 4;  // k-slice of the operands; 8-token block of the unit
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long P = a.total_units, W = a.workers;
+  const long p0 = w * P / W, p1 = (w + 1) * P / W;
+  if (p0 >= p1) return;  // this wave has no work (small launches)
+  const int G = a.hq / a.hkv;
+  WaveState<D> st;
+  Cursor c = cursor_at(a, p0);
+  begin_group<D>(a, c, h, grp, G, st);
+#if TKV_MFMA_PIPELINE
+  UnitLoads<D> A, B;
+  load_unit<D>(a, c, h, grp, A);
+  for (long p = p0; p < p1; p += 2) {
+    Cursor cb = c;
+    cursor_next(a, cb);
+    const bool more_b = p + 1 < p1;
+    if (more_b) load_unit<D>(a, cb, h, grp, B);
+    step_unit<D>(a, c, A, w, h, grp, G, st);
+    if (!more_b) break;
+    c = cb;
+    cursor_next(a, c);
+    const bool more_a = p + 2 < p1;
+    if (more_a) load_unit<D>(a, c, h, grp, A);
+    step_unit<D>(a, cb, B, w, h, grp, G, st);
+    if (!more_a) break;
   }
-  merge_if_last(a, k, lr, g, D, &flag);
+#else
+  UnitLoads<D> A;
+  for (long p = p0; p < p1; ++p) {
+    load_unit<D>(a, c, h, grp, A);
+    step_unit<D>(a, c, A, w, h, grp, G, st);
+    cursor_next(a, c);
+  }
+#endif
+  flush_record<D>(a, w, h, grp, G, st);
 }
 
 // ---------------------------------------------------------------------------
-// float32 path: VALU partial attention, one token per thread for Q.K
+// float32 path: VALU partial attention, one worker per workgroup, one token per
+// thread for Q.K, units of 256 tokens
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
@@ -310,117 +397,207 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
   __shared__ float red[G][NT / kWave];
   __shared__ float mfin[G], lfin[G];
   __shared__ float pv[NG][G][D];
-  __shared__ int flag;
+  __shared__ float orun[G][D];  // running (unnormalised) output of the current group
+  __shared__ float mrun[G], lrun[G];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int lr = blockIdx.y / a.hkv;
-  const int g = blockIdx.y - lr * a.hkv;
-  const Task k = decode_task(a, blockIdx.x);
-  const long layer = a.layer_begin + lr;
-  const int cap = k.seg ? a.cap1 : a.cap0;
-  const long lg = (k.b * a.L + layer) * a.hkv + g;
-  const float* Kb = (const float*)(k.seg ? a.k1 : a.k0) + lg * cap * D;
-  const float* Vb = (const float*)(k.seg ? a.v1 : a.v0) + lg * cap * D;
-  const long jofs = k.seg ? k.n0 : 0;
+  const long w = blockIdx.x;
+  const long P = a.total_units, W = a.workers;
+  const long p0 = w * P / W, p1 = (w + 1) * P / W;
+  long cur_group = -1;
 
-  const float* qp = (const float*)a.q + ((k.b * a.Lr + lr) * a.hq + (long)g * G) * D;
-  float* qsf = (float*)&qs4[0][0];
-  for (int i = tid; i < G * D; i += NT) qsf[i] = qp[i];
-  __syncthreads();
+  auto flush = [&]() {
+    const long rec = (w + cur_group) * G;
+    for (int i = tid; i < G * D; i += NT) {
+      const int hh = i / D;
+      a.part[(rec + hh) * D + (i - hh * D)] = orun[hh][i - hh * D];
+    }
+    if (tid < G) {
+      a.ml[(rec + tid) * 2] = mrun[tid];
+      a.ml[(rec + tid) * 2 + 1] = lrun[tid];
+    }
+  };
 
-  const int t = k.c0 + tid;
-  const bool valid = t < k.c1;
-  float s[G];
+  for (long p = p0; p < p1; ++p) {
+    const Unit u = decode_unit(a, p);
+    if (u.group != cur_group) {
+      if (cur_group >= 0) flush();
+      __syncthreads();
+      cur_group = u.group;
+      const float* qp = (const float*)a.q + ((u.b * a.Lr + u.lr) * a.hq + (long)u.g * G) * D;
+      float* qsf = (float*)&qs4[0][0];
+      for (int i = tid; i < G * D; i += NT) {
+        qsf[i] = qp[i];
+        orun[i / D][i % D] = 0.f;
+      }
+      if (tid < G) {
+        mrun[tid] = -INFINITY;
+        lrun[tid] = 0.f;
+      }
+      __syncthreads();
+    }
+    const int cap = u.seg ? a.cap1 : a.cap0;
+    const long lg = (u.b * a.L + a.layer_begin + u.lr) * a.hkv + u.g;
+    const float* Kb = (const float*)(u.seg ? a.k1 : a.k0) + lg * cap * D;
+    const float* Vb = (const float*)(u.seg ? a.v1 : a.v0) + lg * cap * D;
+    const int t = u.c0 + tid;
+    const bool valid = t < u.c1;
+    float s[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
-  if (valid) {
-    const float4* kp = (const float4*)(Kb + (long)t * D);
+    for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
+    if (valid) {
 #pragma unroll 2
-    for (int c = 0; c < D / 4; ++c) {
-      const float4 k4 = kp[c];
+      for (int c = 0; c < D / 4; ++c) {
+        // K-tiles keep 8 consecutive dimensions of a row together
+        const float4 k4 = *(const float4*)(Kb + k_off(t, 4 * c, D));
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float4 qa = qs4[hh][c];
+          float x = s[hh];
+          x = fmaf(qa.x, k4.x, x);
+          x = fmaf(qa.y, k4.y, x);
+          x = fmaf(qa.z, k4.z, x);
+          x = fmaf(qa.w, k4.w, x);
+          s[hh] = x;
+        }
+      }
+    }
+    float* lg_out = a.alpha + ((u.b * a.Lr + u.lr) * a.hq + (long)u.g * G) * a.alpha_stride +
+                    (u.seg ? u.n0 : 0);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float v = valid ? s[hh] * a.scale : -INFINITY;  // base-2 logit
+      s[hh] = v;
+      if (valid) lg_out[hh * a.alpha_stride + t] = v;
+      const float mx = wave_max(v);
+      if (lane == 0) red[hh][wid] = mx;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mx = red[tid][0];
+      for (int ww = 1; ww < NT / kWave; ++ww) mx = fmaxf(mx, red[tid][ww]);
+      mfin[tid] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float pe = valid ? __builtin_amdgcn_exp2f(s[hh] - mfin[hh]) : 0.f;
+      ps[hh][tid] = pe;
+      const float l = wave_sum(pe);
+      if (lane == 0) red[hh][wid] = l;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float l = 0.f;
+      for (int ww = 0; ww < NT / kWave; ++ww) l += red[tid][ww];
+      lfin[tid] = l;
+    }
+    // P.V over V-tiles
+    const int dp = tid % DP;
+    const int tg = tid / DP;
+    float acc[G][2];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) acc[hh][0] = acc[hh][1] = 0.f;
+    const int tend = min(TPG, u.c1 - u.c0 - tg * TPG);
+    for (int i = 0; i < tend; ++i) {
+      const int tt = tg * TPG + i;
+      const long slot = u.c0 + tt;
+      const float v0 = Vb[v_off(slot, 2 * dp, D)], v1 = Vb[v_off(slot, 2 * dp + 1, D)];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float4 qa = qs4[hh][c];
-        float x = s[hh];
-        x = fmaf(qa.x, k4.x, x);
-        x = fmaf(qa.y, k4.y, x);
-        x = fmaf(qa.z, k4.z, x);
-        x = fmaf(qa.w, k4.w, x);
-        s[hh] = x;
+        const float pe = ps[hh][tt];
+        acc[hh][0] = fmaf(pe, v0, acc[hh][0]);
+        acc[hh][1] = fmaf(pe, v1, acc[hh][1]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      pv[tg][hh][2 * dp] = acc[hh][0];
+      pv[tg][hh][2 * dp + 1] = acc[hh][1];
+    }
+    __syncthreads();
+    // merge this unit into the running state of the group
+    for (int i = tid; i < G * D; i += NT) {
+      const int hh = i / D;
+      const int d = i - hh * D;
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) sum += pv[q][hh][d];
+      const float mo = mrun[hh], mu = mfin[hh];
+      const float mn = fmaxf(mo, mu);
+      const float co = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+      const float cu = mu == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mu - mn);
+      orun[hh][d] = orun[hh][d] * co + sum * cu;
+    }
+    __syncthreads();
+    if (tid < G) {
+      const float mo = mrun[tid], mu = mfin[tid];
+      const float mn = fmaxf(mo, mu);
+      const float co = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+      const float cu = mu == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mu - mn);
+      lrun[tid] = lrun[tid] * co + lfin[tid] * cu;
+      mrun[tid] = mn;
+    }
+    __syncthreads();
+  }
+  if (cur_group >= 0) flush();
+}
+
+// ---------------------------------------------------------------------------
+// combine: one wave per (sequence, layer, query head) merges the split records
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  constexpr int PER = D / 64;
+  const int G = a.hq / a.hkv;
+  const int rows = a.Lr * a.hq;
+  const int bl = blockIdx.x / rows;
+  const int r = blockIdx.x - bl * rows;
+  const int lr = r / a.hq;
+  const int hd = r - lr * a.hq;
+  const int g = hd / G;
+  const int hh = hd - g * G;
+  const long b = a.seq.b_offset + bl;
+  const long row = b * rows + r;
+  const int per = a.seq.units[bl];
+  const long group = (long)bl * a.Lr * a.hkv + lr * a.hkv + g;
+  const long P = a.total_units, W = a.workers;
+  float M = -INFINITY, lam = 0.f;
+  float o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  if (per > 0) {
+    const long s = a.seq.base[bl] + (long)(lr * a.hkv + g) * per;
+    const long e = s + per;
+    const long wf = ((s + 1) * W - 1) / P;  // worker holding unit s
+    const long wl = (e * W - 1) / P;        // worker holding unit e-1
+    for (long w = wf; w <= wl; ++w) {
+      const long ws = w * P / W, we = (w + 1) * P / W;
+      if (ws >= we || ws >= e || we <= s) continue;
+      M = fmaxf(M, a.ml[((w + group) * G + hh) * 2]);
+    }
+    if (M != -INFINITY) {
+      for (long w = wf; w <= wl; ++w) {
+        const long ws = w * P / W, we = (w + 1) * P / W;
+        if (ws >= we || ws >= e || we <= s) continue;
+        const long rec = (w + group) * G + hh;
+        const float ms = a.ml[rec * 2];
+        const float c = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        lam = fmaf(a.ml[rec * 2 + 1], c, lam);
+        const float* pp = a.part + rec * D + threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] = fmaf(pp[64 * i], c, o[i]);
       }
     }
   }
-  float* lg_out = a.alpha + ((k.b * a.Lr + lr) * a.hq + (long)g * G) * a.alpha_stride + jofs;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float v = valid ? s[hh] * a.scale : -INFINITY;
-    s[hh] = v;
-    if (valid) lg_out[hh * a.alpha_stride + t] = v;
-    const float mx = wave_max(v);
-    if (lane == 0) red[hh][wid] = mx;
+  for (int i = 0; i < PER; ++i) a.out[row * D + threadIdx.x + 64 * i] = lam > 0.f ? o[i] / lam : 0.f;
+  if (threadIdx.x == 0) {
+    a.stat[row * 2] = M;
+    a.stat[row * 2 + 1] = lam > 0.f ? 1.0f / lam : 0.f;
   }
-  __syncthreads();
-  if (tid < G) {
-    float mx = red[tid][0];
-    for (int ww = 1; ww < NT / kWave; ++ww) mx = fmaxf(mx, red[tid][ww]);
-    mfin[tid] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float pe = valid ? exp_acc(s[hh] - mfin[hh]) : 0.f;
-    ps[hh][tid] = pe;
-    const float l = wave_sum(pe);
-    if (lane == 0) red[hh][wid] = l;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float l = 0.f;
-    for (int ww = 0; ww < NT / kWave; ++ww) l += red[tid][ww];
-    lfin[tid] = l;
-  }
-  // P.V with V in 8-slot panels: element (slot, d) at ((slot/8)*D + d)*8 + slot%8
-  const int dp = tid % DP;
-  const int tg = tid / DP;
-  float acc[G][2];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) acc[hh][0] = acc[hh][1] = 0.f;
-  const int tend = min(TPG, k.c1 - k.c0 - tg * TPG);
-  for (int i = 0; i < tend; ++i) {
-    const int tt = tg * TPG + i;
-    const long slot = k.c0 + tt;
-    const float* vp = Vb + ((slot >> 3) * D + 2 * dp) * 8 + (slot & 7);
-    const float v0 = vp[0], v1 = vp[8];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float pe = ps[hh][tt];
-      acc[hh][0] = fmaf(pe, v0, acc[hh][0]);
-      acc[hh][1] = fmaf(pe, v1, acc[hh][1]);
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    pv[tg][hh][2 * dp] = acc[hh][0];
-    pv[tg][hh][2 * dp + 1] = acc[hh][1];
-  }
-  __syncthreads();
-  const long row0 = (k.b * a.Lr + lr) * a.hq + (long)g * G;
-  const bool any = k.c1 > k.c0;
-  for (int i = tid; i < G * D; i += NT) {
-    const int hh = i / D;
-    const int d = i - hh * D;
-    float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < NG; ++q) sum += pv[q][hh][d];
-    a.part[((row0 + hh) * a.max_splits + k.split) * D + d] = any ? sum : 0.f;
-    if (d == 0) {
-      a.ml[((row0 + hh) * a.max_splits + k.split) * 2] = any ? mfin[hh] : -INFINITY;
-      a.ml[((row0 + hh) * a.max_splits + k.split) * 2 + 1] = any ? lfin[hh] : 0.f;
-    }
-  }
-  merge_if_last(a, k, lr, g, D, &flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,13 +631,13 @@ __global__ __launch_bounds__(512) void alpha_score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int rr = r + u * RG;
-          const float v = exp_acc(x[u] - st[2 * rr]) * st[2 * rr + 1];
+          const float v = __builtin_amdgcn_exp2f(x[u] - st[2 * rr]) * st[2 * rr + 1];
           ap[(long)rr * a.alpha_stride] = v;
           acc += (double)v;
         }
       }
       for (; r < rows; r += RG) {
-        const float v = exp_acc(ap[(long)r * a.alpha_stride] - st[2 * r]) * st[2 * r + 1];
+        const float v = __builtin_amdgcn_exp2f(ap[(long)r * a.alpha_stride] - st[2 * r]) * st[2 * r + 1];
         ap[(long)r * a.alpha_stride] = v;
         acc += (double)v;
       }
@@ -509,19 +686,45 @@ static bool launch_valu(const AttnArgs& a, int group, dim3 grid, hipStream_t s) 
 
 bool attn_group_supported(int group) { return (group >= 1 && group <= 8) || group == 16; }
 
-void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, int ntasks,
-                         hipStream_t s) {
+// Waves of attn_partial_mfma the device holds at once (its worker count).
+int mfma_resident_waves(int head_dim) {
+  static int cached[2] = {0, 0};
+  int& c = cached[head_dim == 128 ? 1 : 0];
+  if (c) return c;
+  int dev = 0, cus = 0, blocks = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const void* fn = head_dim == 128 ? (const void*)attn_partial_mfma_kernel<128>
+                                   : (const void*)attn_partial_mfma_kernel<64>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 256, 0) != hipSuccess || blocks < 1)
+    blocks = 1;
+  c = cus * blocks * 4 < kMaxWorkers ? cus * blocks * 4 : kMaxWorkers;
+  return c;
+}
+
+void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, hipStream_t s) {
   KernelTimer timer("attn_partial", s);
-  dim3 grid(ntasks, a.Lr * a.hkv);
   if (kv_dtype == TKV_BF16) {
+    dim3 grid((unsigned)((a.workers + 3) / 4));
     if (head_dim == 128)
       hipLaunchKernelGGL((attn_partial_mfma_kernel<128>), grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((attn_partial_mfma_kernel<64>), grid, dim3(256), 0, s, a);
   } else {
+    dim3 grid((unsigned)a.workers);
     if (head_dim == 128) launch_valu<128>(a, group, grid, s);
     else launch_valu<64>(a, group, grid, s);
   }
+}
+
+void launch_attn_combine(const AttnArgs& a, int head_dim, int nb, hipStream_t s) {
+  KernelTimer timer("attn_combine", s);
+  dim3 grid(nb * a.Lr * a.hq);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_combine_kernel<128>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<64>), grid, dim3(64), 0, s, a);
 }
 
 void launch_alpha_score(const ScoreArgs& a, int nblocks, hipStream_t s) {

@@ -22,21 +22,6 @@ __device__ __forceinline__ float to_f32(float f) { return f; }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// exp(x) with a two-constant split of log2(e) (Cody and Waite's argument
-// reduction): x*log2(e) = t + r with t = fl(x*L2E_HI) and r recovered exactly by
-// an FMA plus the low constant's term; exp(x) = 2^t * 2^r and, as |r| is below
-// one ulp of t, 2^r = 1 + r*ln2 to float precision.  2^t uses the hardware
-// base-2 exponential (v_exp_f32).  Accurate to a few ulp across the range a
-// softmax uses (x <= 0).
-__device__ __forceinline__ float exp_acc(float x) {
-  const float kL2eHi = 1.44269502162933349609375f;  // float nearest to log2(e)
-  const float kL2eLo = 1.925963033500011e-8f;        // log2(e) - kL2eHi
-  const float kLn2 = 0.693147180559945309f;
-  float t = x * kL2eHi;
-  float r = fmaf(x, kL2eHi, -t) + x * kL2eLo;
-  return __builtin_amdgcn_exp2f(t) * fmaf(r, kLn2, 1.0f);
-}
-
 // ---------------------------------------------------------------------------
 // wave64 reductions (cross-lane through ds_swizzle/bpermute as the compiler picks)
 // ---------------------------------------------------------------------------

@@ -4,8 +4,9 @@
 // Method: "Not All Thoughts Need HBM" summary pages (gist.science, paper
 // 2605.09490), Methodologie section 1: T1 tokens live in host DDR at full
 // precision and are brought to the GPU before each attention step.  The pack
-// makes the rows contiguous per (layer, KV head) so the copy is one strided 2D
-// transfer per tensor, served by the DMA engines from pinned memory.
+// writes the rows in the device window's storage order (K-tiles, V-tiles) so the
+// copy is one strided 2D transfer per tensor, served by the DMA engines from
+// pinned memory.
 #include <sched.h>
 #include <string.h>
 
@@ -15,6 +16,7 @@
 #include <vector>
 
 #include "common.h"
+#include "layout.h"
 
 namespace {
 
@@ -42,7 +44,7 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
     return fail(TKV_ERR_ARG, "bad model shape");
   if (n_t1 < 0 || cap1 < 0 || max_ctx < 0) return fail(TKV_ERR_ARG, "negative size");
   if (n_t1 > cap1) return fail(TKV_ERR_CAPACITY, "n_t1 > cap1");
-  if (cap1 % 8) return fail(TKV_ERR_ARG, "cap1 must be a multiple of 8");
+  if (cap1 % 32) return fail(TKV_ERR_ARG, "cap1 must be a multiple of 32");
   if (!staging_k || !staging_v) return fail(TKV_ERR_ARG, "staging is null");
   if ((dev_k_t1 == nullptr) != (dev_v_t1 == nullptr))
     return fail(TKV_ERR_ARG, "both or neither device windows must be given");
@@ -60,48 +62,50 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
   const long lgs = (long)model->num_layers * model->num_kv_heads;
 
   const int D = model->head_dim;
-  const long npanels = (n_t1 + 7) / 8;
+  const long nblocks = (n_t1 + 31) / 32;  // 32-slot blocks of the tile layouts
   if (positions && n_t1 > 0) {
     const long krows = lgs * n_t1;
-    const long vpanels = lgs * npanels;
+    const long vpanels = lgs * nblocks * 4;
     const long total = krows + vpanels * 8;  // work units: K rows, then V panels (8 rows each)
     const int nt = (int)std::min<long>(pack_threads(), std::max<long>(1, total / 2048));
-    auto pack_v = [&](auto* sv_base, const auto* hv_base, long lo, long hi) {
-      using E = std::remove_const_t<std::remove_pointer_t<decltype(hv_base)>>;
-      for (long i = lo; i < hi; ++i) {
-        const long lg = i / npanels;
-        const long p = i - lg * npanels;
-        E* dst = sv_base + ((size_t)lg * (cap1 / 8) + p) * D * 8;
+    auto pack = [&](auto* sk_base, auto* sv_base, const auto* hk_base, const auto* hv_base,
+                    long lo, long hi) {
+      using E = std::remove_const_t<std::remove_pointer_t<decltype(hk_base)>>;
+      // K rows in [0, krows): 8-element chunks to their K-tile places
+      for (long i = lo; i < std::min(hi, krows); ++i) {
+        const long lg = i / n_t1;
+        const long r = i - lg * n_t1;
+        const E* from = hk_base + ((size_t)lg * max_ctx + positions[r]) * D;
+        E* to = sk_base + (size_t)lg * cap1 * D;
+        for (int c = 0; c < D; c += 8) memcpy(to + k_off(r, c, D), from + c, 8 * sizeof(E));
+      }
+      // V panels: units [krows, total) in steps of 8
+      const long vlo = std::max(lo, krows);
+      if (hi <= vlo) return;
+      const long plo = (vlo - krows + 7) / 8, phi = (hi - krows + 7) / 8;
+      for (long i = plo; i < phi; ++i) {
+        const long lg = i / (nblocks * 4);
+        const long p = i - lg * nblocks * 4;  // panel: slots 8p .. 8p+7
+        E* to = sv_base + (size_t)lg * cap1 * D;
         for (int e = 0; e < 8; ++e) {
           const long r = 8 * p + e;
           if (r < n_t1) {
-            const E* src = hv_base + ((size_t)lg * max_ctx + positions[r]) * D;
-            for (int d = 0; d < D; ++d) dst[d * 8 + e] = src[d];
+            const E* from = hv_base + ((size_t)lg * max_ctx + positions[r]) * D;
+            for (int d = 0; d < D; ++d) to[v_off(r, d, D)] = from[d];
           } else {
-            for (int d = 0; d < D; ++d) dst[d * 8 + e] = E(0);
+            for (int d = 0; d < D; ++d) to[v_off(r, d, D)] = E(0);
           }
         }
       }
     };
     auto work = [&](int t) {
       const long lo = total * t / nt, hi = total * (t + 1) / nt;
-      // K rows in [0, krows)
-      for (long i = lo; i < std::min(hi, krows); ++i) {
-        const long lg = i / n_t1;
-        const long r = i - lg * n_t1;
-        const size_t so = ((size_t)lg * max_ctx + positions[r]) * row;
-        const size_t dof = ((size_t)lg * cap1 + r) * row;
-        memcpy((char*)staging_k + dof, (const char*)host_k + so, row);
-      }
-      // V panels: units [krows, total) in steps of 8
-      const long vlo = std::max(lo, krows), vhi = hi;
-      if (vhi > vlo) {
-        const long plo = (vlo - krows + 7) / 8, phi = (vhi - krows + 7) / 8;
-        if (esz == 2)
-          pack_v((uint16_t*)staging_v, (const uint16_t*)host_v, plo, phi);
-        else
-          pack_v((uint32_t*)staging_v, (const uint32_t*)host_v, plo, phi);
-      }
+      if (esz == 2)
+        pack((uint16_t*)staging_k, (uint16_t*)staging_v, (const uint16_t*)host_k,
+             (const uint16_t*)host_v, lo, hi);
+      else
+        pack((uint32_t*)staging_k, (uint32_t*)staging_v, (const uint32_t*)host_k,
+             (const uint32_t*)host_v, lo, hi);
     };
     if (nt == 1) {
       work(0);
@@ -116,13 +120,13 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
   if (dev_k_t1 && n_t1 > 0) {
     const size_t pitch = (size_t)cap1 * row;
     KernelTimer timer("gather_t1_h2d", side_stream);
-    tkv_status st = hip_check(hipMemcpy2DAsync(dev_k_t1, pitch, staging_k, pitch,
-                                               (size_t)n_t1 * row, lgs, hipMemcpyHostToDevice,
-                                               side_stream),
+    const size_t width = (size_t)nblocks * 32 * row;  // whole 32-slot blocks
+    tkv_status st = hip_check(hipMemcpy2DAsync(dev_k_t1, pitch, staging_k, pitch, width, lgs,
+                                               hipMemcpyHostToDevice, side_stream),
                               "T1 key copy");
     if (st) return st;
-    st = hip_check(hipMemcpy2DAsync(dev_v_t1, pitch, staging_v, pitch, (size_t)npanels * 8 * row,
-                                    lgs, hipMemcpyHostToDevice, side_stream),
+    st = hip_check(hipMemcpy2DAsync(dev_v_t1, pitch, staging_v, pitch, width, lgs,
+                                    hipMemcpyHostToDevice, side_stream),
                    "T1 value copy");
     if (st) return st;
   }

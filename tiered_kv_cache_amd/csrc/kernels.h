@@ -5,8 +5,9 @@
 
 namespace tkv {
 
-constexpr int kAttnChunkMin = 128;   // smallest split (bf16 path: 4 waves x 32 tokens)
-constexpr int kAttnChunkValu = 256;  // float32 path: one token per thread
+constexpr int kUnitMfma = 32;        // tokens per work unit, bf16 matrix-core path (a pair of 16-token tiles)
+constexpr int kUnitValu = 256;       // tokens per work unit, float32 path (one token per thread)
+constexpr int kMaxWorkers = 8192;    // bound on attention workers (split records <= workers + groups)
 constexpr int kScoreSlots = 16;      // attended slots per alpha_score workgroup
 
 // Per-launch sequence table: lengths and the prefix of work blocks per sequence.
@@ -15,7 +16,8 @@ struct SeqTable {
   int b_offset;  // index of the first one in the caller's batch
   int t0_len[kMaxSeqPerLaunch];
   int t1_len[kMaxSeqPerLaunch];
-  int base[kMaxSeqPerLaunch + 1];  // first work block of each sequence
+  int base[kMaxSeqPerLaunch + 1];  // first work unit (attention) or slot block (scores)
+  int units[kMaxSeqPerLaunch];     // attention: work units per (layer, KV head) group
 };
 
 struct AttnArgs {
@@ -26,16 +28,16 @@ struct AttnArgs {
   const void* v1;
   float* out;
   float* alpha;   // raw scaled logits on exit of attn_partial
-  float* part;    // [B][Lr][Hq][max_splits][D]
-  float* ml;      // [B][Lr][Hq][max_splits][2]
-  float* stat;    // [B][Lr][Hq][2]: M, 1/Lambda
-  int* counters;  // [B][Lr][Hkv] arrival counters (zero between calls)
+  float* part;    // split records: [record][head in group][D] partial P.V
+  float* ml;      // split records: [record][head in group][2] (m, l)
+  float* stat;    // [B][Lr][Hq][2]: M (base-2 logits), 1/Lambda
   long alpha_stride;
-  int chunk;      // tokens per split (multiple of kAttnChunkMin)
+  long total_units;  // work units of this launch
+  long workers;      // workers sharing them (record index = worker + group)
+  int unit;          // tokens per work unit
   int cap0, cap1;
   int L, Lr, layer_begin, hq, hkv;
-  int max_splits;
-  float scale;
+  float scale;       // softmax_scale * log2(e): logits are kept in base 2
   SeqTable seq;
 };
 
@@ -122,8 +124,9 @@ struct QuantArgs {
 };
 
 bool attn_group_supported(int group);
-void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, int ntasks,
-                         hipStream_t s);
+int mfma_resident_waves(int head_dim);
+void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, hipStream_t s);
+void launch_attn_combine(const AttnArgs& a, int head_dim, int nb, hipStream_t s);
 void launch_alpha_score(const ScoreArgs& a, int nblocks, hipStream_t s);
 void launch_append(const AppendArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
 void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s);

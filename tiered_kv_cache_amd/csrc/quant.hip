@@ -12,6 +12,7 @@
 // wave max-reduction for absmax, one division per element.
 #include "common.h"
 #include "kernels.h"
+#include "layout.h"
 
 namespace tkv {
 
@@ -38,8 +39,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int d = lane * PER + i;
-    // K rows are contiguous; V sits in 8-slot panels (head_dim-major inside a panel)
-    const long off = kv ? ((slot >> 3) * D + d) * 8 + (slot & 7) : slot * D + d;
+    const long off = kv ? v_off(slot, d, D) : k_off(slot, d, D);  // tile storage order
     v[i] = to_f32(blk[off]);
     am = fmaxf(am, fabsf(v[i]));
   }

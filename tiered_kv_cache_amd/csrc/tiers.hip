@@ -16,12 +16,14 @@
 // compact_scan  -- one workgroup per sequence: block scans over positions map
 //                  every new T0/T1 slot to its source slot in the previous
 //                  pool/window and list the positions newly in T2.
-// compact_copy  -- moves the rows (one 16-byte vector per lane, coalesced).
+// compact_copy  -- moves the rows into the new pool/window (K-tile chunks and
+//                  V-tile panels, written in destination order).
 // append        -- writes the new token's K/V row into its T0 slot.
 #include <limits.h>
 
 #include "common.h"
 #include "kernels.h"
+#include "layout.h"
 
 namespace tkv {
 
@@ -275,9 +277,8 @@ __global__ __launch_bounds__(kTierThreads) void compact_scan_kernel(CompactArgs 
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compact_copy_kernel(CopyArgs c) {
-  constexpr int ROWS = 64;                       // destination slots per workgroup (8 V panels)
-  constexpr int VPR = D * (int)sizeof(T) / 16;  // 16-byte vectors per K row
-  const int z = blockIdx.z;                      // 0: T0 destination, 1: T1 destination
+  constexpr int ROWS = 64;  // destination slots per workgroup (two 32-slot blocks)
+  const int z = blockIdx.z;  // 0: T0 destination, 1: T1 destination
   const int lgs = c.L * c.hkv;
   const int bl = blockIdx.y / lgs;
   const long lg = blockIdx.y - (long)bl * lgs;
@@ -290,46 +291,53 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(CopyArgs c) {
   const long blk0 = (b * lgs + lg) * c.cap0 * D;  // element offset of this (b, l, g) block
   const long blk1 = (b * lgs + lg) * c.cap1 * D;
   const long blkd = (b * lgs + lg) * (long)cap_d * D;
-  // K: row-major, one 16-byte vector per lane
+  // K: 8-element chunks; items ordered like the destination (block, tile, chunk, row)
   {
-    const uint4* ks0 = (const uint4*)((const T*)c.k0s + blk0);
-    const uint4* ks1 = (const uint4*)((const T*)c.k1s + blk1);
-    uint4* kd = (uint4*)((T*)(z ? c.k1d : c.k0d) + blkd);
-    for (int i = threadIdx.x; i < ROWS * VPR; i += 256) {
-      const int rr = i / VPR;
-      const int v = i - rr * VPR;
-      const int r = r0 + rr;
-      if (r >= len) break;
-      const int s = src[r];
-      kd[(long)r * VPR + v] = s >= 0 ? ks0[(long)s * VPR + v] : ks1[(long)(-s - 1) * VPR + v];
+    const T* ks0 = (const T*)c.k0s + blk0;
+    const T* ks1 = (const T*)c.k1s + blk1;
+    T* kd = (T*)(z ? c.k1d : c.k0d) + blkd;
+    constexpr int CH = D / 8;
+    for (int i = threadIdx.x; i < ROWS * CH; i += 256) {
+      const int row = i & 15;
+      const int cc = (i >> 4) % CH;
+      const int u = (i / (16 * CH)) & 1;
+      const int bk = i / (32 * CH);
+      const int r = r0 + bk * 32 + 8 * (row >> 2) + 4 * u + (row & 3);
+      if (r >= len) continue;
+      const int sidx = src[r];
+      const long ss = sidx >= 0 ? sidx : -sidx - 1;
+      const T* from = (sidx >= 0 ? ks0 : ks1) + k_off(ss, 8 * cc, D);
+      T* to = kd + k_off(r, 8 * cc, D);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) to[e] = from[e];
     }
   }
-  // V: 8-slot panels, element (slot, d) at ((slot/8)*D + d)*8 + slot%8
+  // V: 8-slot panels of one dimension; items ordered like the destination
   {
     const T* vs0 = (const T*)c.v0s + blk0;
     const T* vs1 = (const T*)c.v1s + blk1;
     T* vd = (T*)(z ? c.v1d : c.v0d) + blkd;
-    const int p0 = r0 >> 3;
     for (int i = threadIdx.x; i < (ROWS / 8) * D; i += 256) {
-      const int pl = i / D;
-      const int d = i - pl * D;
-      const int p = p0 + pl;
-      if (8 * p >= len) break;
+      const int d15 = i & 15;
+      const int pnl = (i >> 4) & 3;
+      const int dh = (i >> 6) % (D / 16);
+      const int bk = i / (4 * D);
+      const int d = dh * 16 + d15;
+      const int rb = r0 + bk * 32 + pnl * 8;
+      if (rb >= len) continue;
       T vals[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int r = 8 * p + e;
         vals[e] = T(0);
-        if (r < len) {
-          const int s = src[r];
-          const long slot = s >= 0 ? s : -s - 1;
-          const T* base = s >= 0 ? vs0 : vs1;
-          vals[e] = base[((slot >> 3) * D + d) * 8 + (slot & 7)];
+        if (rb + e < len) {
+          const int sidx = src[rb + e];
+          const long ss = sidx >= 0 ? sidx : -sidx - 1;
+          vals[e] = (sidx >= 0 ? vs0 : vs1)[v_off(ss, d, D)];
         }
       }
-      T* out = vd + ((long)p * D + d) * 8;
+      T* to = vd + v_off(rb, d, D);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = vals[e];
+      for (int e = 0; e < 8; ++e) to[e] = vals[e];
     }
   }
 }
@@ -369,11 +377,11 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int pos = a.pos[bl];
   const T* ks = (const T*)a.kn + (b * lgs + lg) * D;
   const T* vs = (const T*)a.vn + (b * lgs + lg) * D;
-  T* kd = (T*)a.k0 + ((b * lgs + lg) * a.cap0 + slot) * D;
-  T* vd = (T*)a.v0 + (b * lgs + lg) * a.cap0 * D + (long)(slot >> 3) * D * 8 + (slot & 7);
-  for (int d = threadIdx.x; d < D; d += 64) {
-    kd[d] = ks[d];
-    vd[d * 8] = vs[d];  // V is stored in 8-slot panels, head_dim-major inside a panel
+  T* kd = (T*)a.k0 + (b * lgs + lg) * a.cap0 * D;
+  T* vd = (T*)a.v0 + (b * lgs + lg) * a.cap0 * D;
+  for (int d = threadIdx.x; d < D; d += 64) {  // K-tiles / V-tiles storage order
+    kd[k_off(slot, d, D)] = ks[d];
+    vd[v_off(slot, d, D)] = vs[d];
   }
   if (lg == 0 && threadIdx.x == 0) {
     a.t0_pos[b * a.cap0 + slot] = pos;

@@ -68,20 +68,40 @@ def to_device(x: np.ndarray, dtype, device) -> torch.Tensor:
     return t.to(device=device, dtype=dtype, non_blocking=False)
 
 
-def v_rows_to_panels(v: torch.Tensor) -> torch.Tensor:
-    """Rows [..., n, D] (n a multiple of 8) -> the 8-slot panel storage order.
+# Storage order of the pools, windows and staging (see csrc/layout.h).  A tensor
+# keeps its [..., cap, D] shape as a container; every 32-slot block holds
+#   K-tiles: [tile u][D/8 chunks][16 rows][8], slot 8j + 4u + i at row 4j + i;
+#   V-tiles: [D/16][4 panels][16 dims][8 slots of the panel].
+def k_rows_to_tiles(x: torch.Tensor) -> torch.Tensor:
+    *lead, n, d = x.shape
+    t = x.reshape(*lead, n // 32, 4, 2, 4, d // 8, 8)        # blk, j, u, i, chunk, e
+    k = len(lead)
+    t = t.permute(*range(k), k, k + 2, k + 4, k + 1, k + 3, k + 5)  # blk, u, chunk, j, i, e
+    return t.contiguous().reshape(*lead, n, d)
 
-    V pools and windows keep each group of 8 consecutive slots as a [D][8] panel
-    (head_dim-major), so one 16-byte load gives 8 slots of one dimension; the
-    tensor keeps its [..., n, D] shape as a container."""
-    *lead, n, d = v.shape
-    return v.reshape(*lead, n // 8, 8, d).transpose(-1, -2).contiguous().reshape(*lead, n, d)
+
+def k_tiles_to_rows(x: torch.Tensor, n: int) -> torch.Tensor:
+    *lead, cap, d = x.shape
+    t = x.reshape(*lead, cap // 32, 2, d // 8, 4, 4, 8)      # blk, u, chunk, j, i, e
+    k = len(lead)
+    t = t.permute(*range(k), k, k + 3, k + 1, k + 4, k + 2, k + 5)  # blk, j, u, i, chunk, e
+    return t.reshape(*lead, cap, d)[..., :n, :]
 
 
-def v_panels_to_rows(v: torch.Tensor, n: int) -> torch.Tensor:
-    """Panel storage [..., cap, D] -> rows [..., n, D] (inverse of v_rows_to_panels)."""
-    *lead, cap, d = v.shape
-    return v.reshape(*lead, cap // 8, d, 8).transpose(-1, -2).reshape(*lead, cap, d)[..., :n, :]
+def v_rows_to_tiles(x: torch.Tensor) -> torch.Tensor:
+    *lead, n, d = x.shape
+    t = x.reshape(*lead, n // 32, 4, 8, d // 16, 16)         # blk, panel, e, dh, d15
+    k = len(lead)
+    t = t.permute(*range(k), k, k + 3, k + 1, k + 4, k + 2)  # blk, dh, panel, d15, e
+    return t.contiguous().reshape(*lead, n, d)
+
+
+def v_tiles_to_rows(x: torch.Tensor, n: int) -> torch.Tensor:
+    *lead, cap, d = x.shape
+    t = x.reshape(*lead, cap // 32, d // 16, 4, 16, 8)       # blk, dh, panel, d15, e
+    k = len(lead)
+    t = t.permute(*range(k), k, k + 2, k + 4, k + 1, k + 3)  # blk, panel, e, dh, d15
+    return t.reshape(*lead, cap, d)[..., :n, :]
 
 
 def to_host_bits(t: torch.Tensor) -> np.ndarray:
@@ -103,7 +123,7 @@ class TieredKVCache:
         self.batch = batch
         self.device = torch.device(device)
         self.max_ctx = _round_up(max_ctx, 64)
-        self.cap0 = _round_up(cap0 or self.max_ctx, 64)
+        self.cap0 = _round_up(cap0 or self.max_ctx, 64)   # multiples of 32 (tile blocks)
         self.cap1 = _round_up(cap1 if cap1 is not None
                               else int(math.floor(float(np.float32(policy.frac_t1)) * self.max_ctx)) + 64, 64)
         self.t2_cap = _round_up(t2_cap if t2_cap is not None
@@ -182,14 +202,16 @@ class TieredKVCache:
         n0 = K.shape[2]
         if n0 > self.cap0:
             raise ValueError("context longer than the T0 pool")
-        n0p = (n0 + 7) // 8 * 8
+        n0p = (n0 + 31) // 32 * 32
         if n0p > self.cap0:
             raise ValueError("context longer than the T0 pool")
-        self.k0[self.cur][b, :, :, :n0] = to_device(K, self.shape.torch_dtype, self.device)
-        vpad = torch.zeros(K.shape[0], K.shape[1], n0p, K.shape[3], dtype=self.shape.torch_dtype,
-                           device=self.device)
+        shape = (K.shape[0], K.shape[1], n0p, K.shape[3])
+        kpad = torch.zeros(shape, dtype=self.shape.torch_dtype, device=self.device)
+        vpad = torch.zeros(shape, dtype=self.shape.torch_dtype, device=self.device)
+        kpad[:, :, :n0] = to_device(K, self.shape.torch_dtype, self.device)
         vpad[:, :, :n0] = to_device(V, self.shape.torch_dtype, self.device)
-        self.v0[self.cur][b, :, :, :n0p] = v_rows_to_panels(vpad)
+        self.k0[self.cur][b, :, :, :n0p] = k_rows_to_tiles(kpad)
+        self.v0[self.cur][b, :, :, :n0p] = v_rows_to_tiles(vpad)
         self.pos0[self.cur][b, :n0] = torch.arange(n0, dtype=torch.int32, device=self.device)
         self.tier[self.tcur][b].zero_()
         self.scores[b].zero_()
@@ -275,14 +297,14 @@ class TieredKVCache:
     def t0_rows(self, b: int):
         """Host copies (bf16 bits or float32) of the T0 pool rows of sequence b: K, V [L][Hkv][n][D]."""
         n = self.t0_len[b]
-        return (to_host_bits(self.k_t0[b, :, :, :n]),
-                to_host_bits(v_panels_to_rows(self.v_t0[b], n)))
+        return (to_host_bits(k_tiles_to_rows(self.k_t0[b], n)),
+                to_host_bits(v_tiles_to_rows(self.v_t0[b], n)))
 
     def t1_rows(self, b: int):
         """Host copies of the T1 window rows of sequence b: K, V [L][Hkv][n][D]."""
         n = self.t1_len[b]
-        return (to_host_bits(self.k_t1[b, :, :, :n]),
-                to_host_bits(v_panels_to_rows(self.v_t1[b], n)))
+        return (to_host_bits(k_tiles_to_rows(self.k_t1[b], n)),
+                to_host_bits(v_tiles_to_rows(self.v_t1[b], n)))
 
     def alpha_of(self, b: int) -> np.ndarray:
         m = self.t0_len[b] + self.t1_len[b]
