@@ -246,6 +246,11 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   if (mfma) {
     resident = mfma_resident_waves(D);
     if (resident < 1) return fail(TKV_ERR_HIP, "cannot query the device for its occupancy");
+    static const int override_workers = [] {  // tuning sweeps: TKV_ATTN_WORKERS
+      const char* e = getenv("TKV_ATTN_WORKERS");
+      return e ? atoi(e) : 0;
+    }();
+    if (override_workers > 0) resident = std::min(override_workers, kMaxWorkers);
   }
 
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {

@@ -162,7 +162,22 @@ struct WaveState {
   bf16x8_t qop[D / 32];
   float m, lsum;  // running max (base-2 logits) and partial sum of this lane's 8 columns
   long group;     // group index within the launch of the current softmax
-  float* lg_row;  // logits row of this lane's head (null for padding heads)
+  long lrow0;     // element offset in `alpha` of the group's first query head row
+};
+
+// Logits are staged in LDS and written in bursts: stores interleaved with the
+// key/value stream cost this GPU about a fifth of its read bandwidth, while a
+// burst after the last load costs only its own bytes.  Per wave: up to
+// kStageUnits units of [G heads][32 tokens] floats, with each unit's destination.
+constexpr int kStageFloats = 4096;  // 16 KB per wave
+constexpr int kStageUnits = 64;
+
+struct Stage {
+  float* buf;   // this wave's slice of LDS
+  long* dst;    // per staged unit: element offset of (head 0, first token) in alpha
+  int* count;   // per staged unit: valid tokens
+  int n;        // units staged
+  int cap;      // capacity in units for this group size
 };
 
 template <int D>
@@ -171,8 +186,8 @@ __device__ __forceinline__ void begin_group(const AttnArgs& a, const Cursor& c, 
   constexpr int KB = D / 32, NB = D / 16;
   const long b = a.seq.b_offset + c.bl;
   st.group = (long)c.bl * a.Lr * a.hkv + c.lgl;
-  const long row = (b * a.Lr + c.lr) * a.hq + (long)c.g * G + h;
-  const uint16_t* qrow = (const uint16_t*)a.q + row * D;
+  const long row0 = (b * a.Lr + c.lr) * a.hq + (long)c.g * G;
+  const uint16_t* qrow = (const uint16_t*)a.q + (row0 + h) * D;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -183,7 +198,7 @@ __device__ __forceinline__ void begin_group(const AttnArgs& a, const Cursor& c, 
   for (int nb = 0; nb < NB; ++nb) st.acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.lsum = 0.f;
-  st.lg_row = h < G ? a.alpha + row * a.alpha_stride : nullptr;
+  st.lrow0 = row0 * a.alpha_stride;
 }
 
 // Split record of (worker, group): per head of the group, (m, l) and the partial P.V.
@@ -210,6 +225,20 @@ __device__ __forceinline__ void flush_record(const AttnArgs& a, long worker, int
   }
 }
 
+// Write every staged unit: 2 heads x 32 tokens per wave store.
+__device__ __forceinline__ void flush_stage(const AttnArgs& a, int lane, int G, Stage& sg) {
+  for (int u = 0; u < sg.n; ++u) {
+    const long dst = sg.dst[u];
+    const int n = sg.count[u];
+    const float* src = sg.buf + u * G * 32;
+    for (int hh = lane >> 5; hh < G; hh += 2) {
+      const int t = lane & 31;
+      if (t < n) a.alpha[dst + hh * a.alpha_stride + t] = src[hh * 32 + t];
+    }
+  }
+  sg.n = 0;
+}
+
 // Loads of one unit: with K-tiles and V-tiles every operand is one contiguous
 // 1 KB wave access at lane offset kb*64 + lane (K) or nb*64 + lane (V).  The
 // 32-slot block is always inside the allocation (capacities are multiples of
@@ -233,14 +262,14 @@ __device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, 
 
 template <int D, bool FULL>
 __device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
-                                        int h, int grp, WaveState<D>& st) {
+                                        int h, int grp, int G, WaveState<D>& st, Stage& sg) {
   constexpr int KB = D / 32, NB = D / 16;
   constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
   const int c1 = c.seg ? c.n1 : c.n0;
   const int tb = c.c0 + 8 * grp;  // first of this lane's 8 tokens
-  if (!FULL) {  // tail panel: zero the value slots past the end of the segment
+  if (!FULL) {  // tail: zero the value slots past the end of the segment
     const int valid = c1 - tb;
-    if (valid > 0 && valid < 8) {
+    if (valid < 8) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         uint32_t* wds = (uint32_t*)&L.v[nb];
@@ -265,17 +294,17 @@ __device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, Unit
     if (!FULL && tb + e >= c1) sv[e] = -INFINITY;
     pm = fmaxf(pm, sv[e]);
   }
-  if (st.lg_row) {
-    float* dst = st.lg_row + (c.seg ? c.n0 : 0) + tb;
-    if (FULL && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
-      reinterpret_cast<float4*>(dst)[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (FULL || tb + e < c1) dst[e] = sv[e];
-    }
+  // stage the logits of this unit: [head][32 tokens]
+  if (h < G) {
+    float4* dst = reinterpret_cast<float4*>(sg.buf + (sg.n * G + h) * 32 + 8 * grp);
+    dst[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+    dst[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
   }
+  if ((threadIdx.x & 63) == 0) {
+    sg.dst[sg.n] = st.lrow0 + (c.seg ? c.n0 : 0) + c.c0;
+    sg.count[sg.n] = min(kUnitMfma, c1 - c.c0);
+  }
+  ++sg.n;
   pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
   pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
   if (__ballot(pm > st.m + kLazy) != 0ull) {
@@ -318,68 +347,77 @@ __device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, Unit
 #define TKV_MFMA_MIN_BLOCKS 2
 #endif
 
-template <int D>
 __device__ __forceinline__ bool unit_full(const Cursor& c) {
   return c.c0 + kUnitMfma <= (c.seg ? c.n1 : c.n0);
 }
 
 template <int D>
-__device__ __forceinline__ void load_unit(const AttnArgs& a, const Cursor& c, int h, int grp,
-                                          UnitLoads<D>& L) {
-  issue_loads<D>(a, c, grp * 16 + h, L);
-}
-
-template <int D>
 __device__ __forceinline__ void step_unit(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
-                                          long w, int h, int grp, int G, WaveState<D>& st) {
+                                          long w, int h, int grp, int G, WaveState<D>& st,
+                                          Stage& sg) {
   const long group = (long)c.bl * a.Lr * a.hkv + c.lgl;
   if (group != st.group) {
     flush_record<D>(a, w, h, grp, G, st);
     begin_group<D>(a, c, h, grp, G, st);
   }
-  if (unit_full<D>(c)) consume<D, true>(a, c, L, h, grp, st);
-  else consume<D, false>(a, c, L, h, grp, st);
+  if (sg.n == sg.cap) flush_stage(a, grp * 16 + h, G, sg);
+  if (unit_full(c)) consume<D, true>(a, c, L, h, grp, G, st, sg);
+  else consume<D, false>(a, c, L, h, grp, G, st, sg);
 }
 
 template <int D>
 __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_kernel(AttnArgs a) {
+  __shared__ float stage_buf[4][kStageFloats];
+  __shared__ long stage_dst[4][kStageUnits];
+  __shared__ int stage_cnt[4][kStageUnits];
   const int lane = threadIdx.x & 63;
   const int h = lane & 15;    // head column of S^T / P row; token row of the K operand
   const int grp = lane >> 4;  // k-slice of the operands; 8-token block of the unit
-  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // The worker index is uniform across the wave; saying so keeps the whole unit
+  // cursor in scalar registers (scalar loads of the sequence table, no vector
+  // memory waits for bookkeeping).
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long w = (long)blockIdx.x * 4 + wv;
   const long P = a.total_units, W = a.workers;
   const long p0 = w * P / W, p1 = (w + 1) * P / W;
   if (p0 >= p1) return;  // this wave has no work (small launches)
   const int G = a.hq / a.hkv;
+  Stage sg;
+  sg.buf = stage_buf[wv];
+  sg.dst = stage_dst[wv];
+  sg.count = stage_cnt[wv];
+  sg.n = 0;
+  sg.cap = min(kStageUnits, kStageFloats / (32 * G));
   WaveState<D> st;
   Cursor c = cursor_at(a, p0);
   begin_group<D>(a, c, h, grp, G, st);
 #if TKV_MFMA_PIPELINE
   UnitLoads<D> A, B;
-  load_unit<D>(a, c, h, grp, A);
+  issue_loads<D>(a, c, lane, A);
   for (long p = p0; p < p1; p += 2) {
     Cursor cb = c;
     cursor_next(a, cb);
     const bool more_b = p + 1 < p1;
-    if (more_b) load_unit<D>(a, cb, h, grp, B);
-    step_unit<D>(a, c, A, w, h, grp, G, st);
+    if (more_b) issue_loads<D>(a, cb, lane, B);
+    step_unit<D>(a, c, A, w, h, grp, G, st, sg);
     if (!more_b) break;
     c = cb;
     cursor_next(a, c);
     const bool more_a = p + 2 < p1;
-    if (more_a) load_unit<D>(a, c, h, grp, A);
-    step_unit<D>(a, cb, B, w, h, grp, G, st);
+    if (more_a) issue_loads<D>(a, c, lane, A);
+    step_unit<D>(a, cb, B, w, h, grp, G, st, sg);
     if (!more_a) break;
   }
 #else
   UnitLoads<D> A;
   for (long p = p0; p < p1; ++p) {
-    load_unit<D>(a, c, h, grp, A);
-    step_unit<D>(a, c, A, w, h, grp, G, st);
+    issue_loads<D>(a, c, lane, A);
+    step_unit<D>(a, c, A, w, h, grp, G, st, sg);
     cursor_next(a, c);
   }
 #endif
   flush_record<D>(a, w, h, grp, G, st);
+  flush_stage(a, lane, G, sg);
 }
 
 // ---------------------------------------------------------------------------
