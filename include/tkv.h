@@ -298,9 +298,13 @@ tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k, const void*
  * launches is bracketed by HIP events on its own stream; tkv_timing_read
  * synchronises those events and returns the summed milliseconds and launch
  * count of one kernel (by name, e.g. "attn_partial") since the last reset.
- * Not thread-safe.
+ * tkv_timing_select restricts the timers to a comma-separated list of kernel
+ * names (NULL or "" = every kernel): each pair of events adds a few
+ * microseconds between launches, so a throughput run times only the kernel
+ * it reports.  Not thread-safe.
  */
 tkv_status tkv_timing_enable(int32_t enable);
+tkv_status tkv_timing_select(const char* kernels);
 tkv_status tkv_timing_reset(void);
 tkv_status tkv_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 

@@ -92,11 +92,14 @@ def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, st
     stats["reassignments"] += 1
 
 
-def run_lockstep(wl: Workload, n_steps: int = None, label: str = "") -> dict:
-    """Every step compared; re-sync of the ranking at each reassignment."""
+def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
+                 fused_scores: bool = True) -> dict:
+    """Every step compared; re-sync of the ranking at each reassignment.
+    fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores."""
     n_steps = n_steps or wl.total_steps
     dw = DeviceWorkload(wl)
     cache = dw.make_cache()
+    cache.fused_scores = fused_scores
     pol = oracle_policy(wl)
     seqs = []
     for b in range(wl.batch):

@@ -33,6 +33,13 @@ def test_small_gqa4_lockstep():
     assert st["reassignments"] == 3
 
 
+def test_small_standalone_score_update():
+    # the score update as its own call (tkv_update_scores on the normalised alpha)
+    wl = WORKLOADS["small"].scaled(warmup=8, steps=72)
+    st = run_lockstep(wl, fused_scores=False, label="small_standalone_scores")
+    assert st["reassignments"] == 1
+
+
 def test_ragged_batch_d64_lockstep():
     base = WORKLOADS["small"]
     wl = base.scaled(name="ragged5_L2_h8kv2_d64", layers=2, head_dim=64, batch=5,
@@ -41,6 +48,17 @@ def test_ragged_batch_d64_lockstep():
                      frac_t3=0.05)
     st = run_lockstep(wl)
     assert st["reassignments"] == 3 * 5          # counted per sequence
+
+
+def test_batch70_crosses_the_per_launch_sequence_limit():
+    # 70 ragged sequences: the library splits them over two launches of <= 64
+    base = WORKLOADS["small"]
+    ctx = tuple(int(c) for c in np.random.default_rng(7).integers(33, 400, size=70))
+    wl = base.scaled(name="batch70_L1_h4kv2_d64", layers=1, q_heads=4, kv_heads=2, head_dim=64,
+                     batch=70, ctx=ctx, warmup=4, steps=8, delta=4, prompt=8, recent=8, sinks=2,
+                     planted=(0,) * 70, frac_t1=0.3, frac_t2=0.1, frac_t3=0.1)
+    st = run_lockstep(wl)
+    assert st["reassignments"] == 3 * 70
 
 
 def test_chain8k_full_size_sampled():

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <map>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -38,6 +39,7 @@ struct TimerRec {
 };
 struct TimerState {
   bool enabled = false;
+  std::set<std::string> only;  // empty: every kernel
   std::vector<TimerRec> pending;
   std::vector<hipEvent_t> free_events;
   std::map<std::string, std::pair<double, long long>> totals;
@@ -76,6 +78,7 @@ void drain_timers() {
 
 KernelTimer::KernelTimer(const char* name, hipStream_t s) : name_(name), stream_(s), ev_(nullptr) {
   if (!timers().enabled) return;
+  if (!timers().only.empty() && !timers().only.count(name)) return;
   hipEvent_t e = take_event();
   if (e && hipEventRecord(e, s) == hipSuccess) ev_ = e;
 }
@@ -116,6 +119,29 @@ static size_t max_records(int batch, int n_layers, int hkv) {
   return (size_t)kMaxWorkers + (size_t)nb * n_layers * hkv;
 }
 
+static size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+// Decode workspace, in floats, every region 256-byte aligned:
+//   part [records][G][D] | ml [records][G][2] | gsum [nb][Lr * Hkv][gs_stride]
+struct DecodeWorkspace {
+  size_t part, ml, gsum, total, gs_stride;
+};
+
+static DecodeWorkspace decode_workspace(const tkv_model* m, int batch, int n_layers, int cap0,
+                                        int cap1) {
+  const size_t G = (size_t)(m->num_q_heads / m->num_kv_heads);
+  const size_t D = (size_t)m->head_dim;
+  const size_t recs = max_records(batch, n_layers, m->num_kv_heads);
+  const size_t nb = (size_t)(batch < kMaxSeqPerLaunch ? batch : kMaxSeqPerLaunch);
+  DecodeWorkspace w;
+  w.gs_stride = round_up((size_t)cap0 + (size_t)cap1, 4);
+  w.part = 0;
+  w.ml = round_up(w.part + recs * G * D, 64);
+  w.gsum = round_up(w.ml + recs * G * 2, 64);
+  w.total = round_up(w.gsum + nb * n_layers * m->num_kv_heads * w.gs_stride, 64);
+  return w;
+}
+
 }  // namespace tkv
 
 using namespace tkv;
@@ -128,6 +154,23 @@ const char* tkv_last_error(void) { return g_last_error.c_str(); }
 
 tkv_status tkv_timing_enable(int32_t enable) {
   timers().enabled = enable != 0;
+  return TKV_OK;
+}
+
+tkv_status tkv_timing_select(const char* kernels) {
+  auto& only = timers().only;
+  only.clear();
+  if (!kernels) return TKV_OK;
+  std::string cur;
+  for (const char* c = kernels;; ++c) {
+    if (*c == ',' || *c == '\0') {
+      if (!cur.empty()) only.insert(cur);
+      cur.clear();
+      if (*c == '\0') break;
+    } else if (*c != ' ') {
+      cur += *c;
+    }
+  }
   return TKV_OK;
 }
 
@@ -193,11 +236,8 @@ size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t
                                   int32_t cap0, int32_t cap1) {
   if (!model || batch < 0 || n_layers < 0 || cap0 < 0 || cap1 < 0) return 0;
   if (model->num_kv_heads < 1 || model->num_q_heads < 1) return 0;
-  const size_t G = (size_t)(model->num_q_heads / model->num_kv_heads);
-  const size_t D = (size_t)model->head_dim;
-  const size_t recs = max_records(batch, n_layers, model->num_kv_heads);
-  const size_t rows = (size_t)batch * n_layers * model->num_q_heads;
-  return recs * G * (D + 2) * sizeof(float) + rows * 2 * sizeof(float) + 256;
+  const DecodeWorkspace w = decode_workspace(model, batch, n_layers, cap0, cap1);
+  return w.total * sizeof(float);
 }
 
 tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
@@ -228,6 +268,9 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   if (any_t1 && (!k_t1 || !v_t1)) return fail(TKV_ERR_ARG, "T1 window is null but t1_len > 0");
   if (scores && (!t0_pos || (any_t1 && !t1_pos) || max_ctx < 1))
     return fail(TKV_ERR_ARG, "fused score update needs t0_pos, t1_pos and max_ctx");
+  if (alpha_stride % 4 || ((uintptr_t)alpha & 15) || ((uintptr_t)workspace & 255))
+    return fail(TKV_ERR_ARG,
+                "alpha_stride must be a multiple of 4, alpha 16-byte and workspace 256-byte aligned");
   const int Lr = layer_end - layer_begin;
   if (workspace_bytes < tkv_decode_workspace_bytes(model, batch, Lr, cap0, cap1))
     return fail(TKV_ERR_CAPACITY, "workspace too small");
@@ -238,10 +281,10 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   const int G = hq / hkv;
   const bool mfma = model->kv_dtype == TKV_BF16;
   const int unit = mfma ? kUnitMfma : kUnitValu;
-  const size_t recs = max_records(batch, Lr, hkv);
-  float* part = (float*)workspace;
-  float* ml = part + recs * G * D;
-  float* stat = ml + recs * G * 2;
+  const DecodeWorkspace wl = decode_workspace(model, batch, Lr, cap0, cap1);
+  float* part = (float*)workspace + wl.part;
+  float* ml = (float*)workspace + wl.ml;
+  float* gsum = (float*)workspace + wl.gsum;
   int resident = 0;
   if (mfma) {
     resident = mfma_resident_waves(D);
@@ -265,7 +308,6 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     a.alpha = alpha;
     a.part = part;
     a.ml = ml;
-    a.stat = stat;
     a.alpha_stride = alpha_stride;
     a.unit = unit;
     a.cap0 = cap0;
@@ -279,9 +321,10 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     a.scale = (float)((double)scale_of(model) * 1.4426950408889634074);
     a.seq.nb = nb;
     a.seq.b_offset = b0;
-    long units = 0;
-    int sblocks = 0;
+    MergeArgs m{};
     ScoreArgs sa{};
+    long units = 0;
+    int cblocks = 0, sblocks = 0;
     for (int i = 0; i < nb; ++i) {
       const int n0 = t0_len[b0 + i], n1 = t1_len[b0 + i];
       a.seq.t0_len[i] = n0;
@@ -289,6 +332,10 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
       a.seq.base[i] = (int)units;
       a.seq.units[i] = ceil_div(n0, unit) + ceil_div(n1, unit);
       units += (long)Lr * hkv * a.seq.units[i];
+      m.cbase[i] = cblocks;
+      cblocks += Lr * hkv * merge_alpha_blocks(n0 + n1);
+      sa.seq.t0_len[i] = n0;
+      sa.seq.t1_len[i] = n1;
       sa.seq.base[i] = sblocks;
       sblocks += ceil_div(n0 + n1, kScoreSlots);
     }
@@ -300,31 +347,43 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
       launch_attn_partial(a, model->kv_dtype, D, G, stream);
       if ((st = hip_check(hipGetLastError(), "attn_partial launch"))) return st;
     }
-    launch_attn_combine(a, D, nb, stream);
-    if ((st = hip_check(hipGetLastError(), "attn_combine launch"))) return st;
 
-    sa.alpha = alpha;
-    sa.stat = stat;
-    sa.t0_pos = t0_pos;
-    sa.t1_pos = t1_pos;
-    sa.scores = scores;
-    sa.alpha_stride = alpha_stride;
-    sa.rows = Lr * hq;
-    sa.normalise = 1;
-    sa.cap0 = cap0;
-    sa.cap1 = cap1;
-    sa.max_ctx = max_ctx;
-    sa.weight = 1.0 / ((double)model->num_layers * hq);
-    sa.seq.nb = nb;
-    sa.seq.b_offset = b0;
-    for (int i = 0; i < nb; ++i) {
-      sa.seq.t0_len[i] = t0_len[b0 + i];
-      sa.seq.t1_len[i] = t1_len[b0 + i];
-    }
-    sa.seq.base[nb] = sblocks;
-    if (sblocks > 0) {
-      launch_alpha_score(sa, sblocks, stream);
-      if ((st = hip_check(hipGetLastError(), "alpha_score launch"))) return st;
+    m.part = part;
+    m.ml = ml;
+    m.out = out;
+    m.alpha = alpha;
+    m.gsum = scores ? gsum : nullptr;
+    m.alpha_stride = alpha_stride;
+    m.gs_stride = (long)wl.gs_stride;
+    m.total_units = a.total_units;
+    m.workers = a.workers > 0 ? a.workers : 1;
+    m.Lr = Lr;
+    m.hq = hq;
+    m.hkv = hkv;
+    m.out_rows = nb * Lr * hq;
+    m.out_blocks = merge_output_blocks(m.out_rows);
+    m.seq = a.seq;
+    m.cbase[nb] = cblocks;
+    launch_attn_merge(m, D, m.out_blocks + cblocks, stream);
+    if ((st = hip_check(hipGetLastError(), "attn_merge launch"))) return st;
+
+    if (scores && sblocks > 0) {
+      sa.src = gsum;
+      sa.row_stride = (long)wl.gs_stride;
+      sa.seq_stride = (long)Lr * hkv * (long)wl.gs_stride;
+      sa.rows = Lr * hkv;
+      sa.t0_pos = t0_pos;
+      sa.t1_pos = t1_pos;
+      sa.scores = scores;
+      sa.cap0 = cap0;
+      sa.cap1 = cap1;
+      sa.max_ctx = max_ctx;
+      sa.weight = 1.0 / ((double)model->num_layers * hq);
+      sa.seq.nb = nb;
+      sa.seq.b_offset = b0;
+      sa.seq.base[nb] = sblocks;
+      launch_score_rows(sa, sblocks, "score_update", stream);
+      if ((st = hip_check(hipGetLastError(), "score_update launch"))) return st;
     }
   }
   return TKV_OK;
@@ -357,14 +416,14 @@ tkv_status tkv_update_scores(const tkv_model* model, int32_t batch, int32_t laye
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
     ScoreArgs sa{};
-    sa.alpha = const_cast<float*>(alpha);  // read only when normalise == 0
-    sa.stat = nullptr;
+    const int rows = Lr * model->num_q_heads;
+    sa.src = alpha + (size_t)b0 * rows * alpha_stride;
+    sa.row_stride = alpha_stride;
+    sa.seq_stride = (long)rows * alpha_stride;
+    sa.rows = rows;
     sa.t0_pos = t0_pos;
     sa.t1_pos = t1_pos;
     sa.scores = scores;
-    sa.alpha_stride = alpha_stride;
-    sa.rows = Lr * model->num_q_heads;
-    sa.normalise = 0;
     sa.cap0 = cap0;
     sa.cap1 = cap1;
     sa.max_ctx = max_ctx;
@@ -380,7 +439,7 @@ tkv_status tkv_update_scores(const tkv_model* model, int32_t batch, int32_t laye
     }
     sa.seq.base[nb] = sblocks;
     if (sblocks > 0) {
-      launch_alpha_score(sa, sblocks, stream);
+      launch_score_rows(sa, sblocks, "update_scores", stream);
       if ((st = hip_check(hipGetLastError(), "update_scores launch"))) return st;
     }
   }

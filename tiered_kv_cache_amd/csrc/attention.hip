@@ -25,21 +25,15 @@
 //       is permuted so that the S^T accumulator is already the A operand of
 //       P V, and keys and values are stored in the operand order (K-tiles,
 //       V-tiles: layout.h), so every operand load is one contiguous 1 KB wave
-//       access: no LDS, no barriers.  The next
-//       unit's loads are issued before the current unit is computed.  The
+//       access.  The logits of a wave's units are staged in LDS and written
+//       in bursts once its key/value stream is done (stores interleaved with
+//       the stream slow its reads down).  The
 //       logits are kept in base 2 (q.k * softmax_scale * log2 e), so every
 //       weight is one v_exp_f32; they go to `alpha` and are normalised there
-//       by alpha_score.
+//       by the merge kernels.
 //   attn_partial_valu -- float32 path (plain FMAs); a worker is a workgroup.
-//   attn_combine -- one wave per (sequence, layer, query head) merges the split
-//       records: M = max m, Lambda = sum l e^(m-M), O = sum acc e^(m-M)/Lambda;
-//       stores (M, 1/Lambda).  (A separate launch: merging in the
-//       last-arriving workgroup would need an agent-scope fence per workgroup,
-//       which on this GPU writes back the per-XCD L2.)
-//   alpha_score -- per 16 attended slots: alpha = e^(S-M)/Lambda written in
-//       place, summed in float64 over every (layer, head) and added, weighted
-//       1/(num_layers*Hq), to the score of the slot's position.  Also the
-//       standalone score update (alpha already normalised).
+// The records are merged, and the logits normalised into alpha, by the merge
+// kernels (merge.hip).
 #include "common.h"
 #include "kernels.h"
 #include "layout.h"
@@ -584,127 +578,6 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: one wave per (sequence, layer, query head) merges the split records
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
-  constexpr int PER = D / 64;
-  const int G = a.hq / a.hkv;
-  const int rows = a.Lr * a.hq;
-  const int bl = blockIdx.x / rows;
-  const int r = blockIdx.x - bl * rows;
-  const int lr = r / a.hq;
-  const int hd = r - lr * a.hq;
-  const int g = hd / G;
-  const int hh = hd - g * G;
-  const long b = a.seq.b_offset + bl;
-  const long row = b * rows + r;
-  const int per = a.seq.units[bl];
-  const long group = (long)bl * a.Lr * a.hkv + lr * a.hkv + g;
-  const long P = a.total_units, W = a.workers;
-  float M = -INFINITY, lam = 0.f;
-  float o[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  if (per > 0) {
-    const long s = a.seq.base[bl] + (long)(lr * a.hkv + g) * per;
-    const long e = s + per;
-    const long wf = ((s + 1) * W - 1) / P;  // worker holding unit s
-    const long wl = (e * W - 1) / P;        // worker holding unit e-1
-    for (long w = wf; w <= wl; ++w) {
-      const long ws = w * P / W, we = (w + 1) * P / W;
-      if (ws >= we || ws >= e || we <= s) continue;
-      M = fmaxf(M, a.ml[((w + group) * G + hh) * 2]);
-    }
-    if (M != -INFINITY) {
-      for (long w = wf; w <= wl; ++w) {
-        const long ws = w * P / W, we = (w + 1) * P / W;
-        if (ws >= we || ws >= e || we <= s) continue;
-        const long rec = (w + group) * G + hh;
-        const float ms = a.ml[rec * 2];
-        const float c = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        lam = fmaf(a.ml[rec * 2 + 1], c, lam);
-        const float* pp = a.part + rec * D + threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) o[i] = fmaf(pp[64 * i], c, o[i]);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) a.out[row * D + threadIdx.x + 64 * i] = lam > 0.f ? o[i] / lam : 0.f;
-  if (threadIdx.x == 0) {
-    a.stat[row * 2] = M;
-    a.stat[row * 2 + 1] = lam > 0.f ? 1.0f / lam : 0.f;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// alpha normalisation (optional) + score accumulation over (layer, head)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void alpha_score_kernel(ScoreArgs a) {
-  constexpr int SL = kScoreSlots;  // slots per workgroup
-  constexpr int RG = 32;           // row groups (8 waves x 4 lane groups)
-  __shared__ double red[RG][SL];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int rg = (tid >> 6) * 4 + (lane >> 4);
-  const int blk = blockIdx.x;
-  int bl = 0;
-  while (bl + 1 < a.seq.nb && a.seq.base[bl + 1] <= blk) ++bl;
-  const long b = a.seq.b_offset + bl;
-  const int n0 = a.seq.t0_len[bl];
-  const int natt = n0 + a.seq.t1_len[bl];
-  const int j = (blk - a.seq.base[bl]) * SL + (lane & 15);
-  const int rows = a.rows;
-  double acc = 0.0;
-  if (j < natt) {
-    float* ap = a.alpha + b * rows * a.alpha_stride + j;
-    const float* st = a.stat + b * rows * 2;
-    int r = rg;
-    if (a.normalise) {
-      for (; r + 3 * RG < rows; r += 4 * RG) {
-        float x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = ap[(long)(r + u * RG) * a.alpha_stride];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int rr = r + u * RG;
-          const float v = __builtin_amdgcn_exp2f(x[u] - st[2 * rr]) * st[2 * rr + 1];
-          ap[(long)rr * a.alpha_stride] = v;
-          acc += (double)v;
-        }
-      }
-      for (; r < rows; r += RG) {
-        const float v = __builtin_amdgcn_exp2f(ap[(long)r * a.alpha_stride] - st[2 * r]) * st[2 * r + 1];
-        ap[(long)r * a.alpha_stride] = v;
-        acc += (double)v;
-      }
-    } else {
-      for (; r + 3 * RG < rows; r += 4 * RG) {
-        float x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = ap[(long)(r + u * RG) * a.alpha_stride];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc += (double)x[u];
-      }
-      for (; r < rows; r += RG) acc += (double)ap[(long)r * a.alpha_stride];
-    }
-  }
-  if (!a.scores) return;  // normalisation only (block-uniform)
-  red[rg][lane & 15] = acc;
-  __syncthreads();
-  if (tid < SL && j < natt) {
-    double t = 0.0;
-    for (int q = 0; q < RG; ++q) t += red[q][tid];
-    const int pos = j < n0 ? a.t0_pos[b * a.cap0 + j] : a.t1_pos[b * a.cap1 + (j - n0)];
-    if ((unsigned)pos < (unsigned)a.max_ctx) {  // slot maps hold positions < max_ctx
-      float* sp = a.scores + b * a.max_ctx + pos;
-      *sp = *sp + (float)(t * a.weight);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 template <int D>
@@ -754,20 +627,6 @@ void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int grou
     if (head_dim == 128) launch_valu<128>(a, group, grid, s);
     else launch_valu<64>(a, group, grid, s);
   }
-}
-
-void launch_attn_combine(const AttnArgs& a, int head_dim, int nb, hipStream_t s) {
-  KernelTimer timer("attn_combine", s);
-  dim3 grid(nb * a.Lr * a.hq);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), grid, dim3(64), 0, s, a);
-}
-
-void launch_alpha_score(const ScoreArgs& a, int nblocks, hipStream_t s) {
-  KernelTimer timer(a.normalise ? "alpha_score" : "update_scores", s);
-  hipLaunchKernelGGL(alpha_score_kernel, dim3(nblocks), dim3(512), 0, s, a);
 }
 
 }  // namespace tkv

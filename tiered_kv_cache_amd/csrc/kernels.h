@@ -8,7 +8,7 @@ namespace tkv {
 constexpr int kUnitMfma = 32;        // tokens per work unit, bf16 matrix-core path (a pair of 16-token tiles)
 constexpr int kUnitValu = 256;       // tokens per work unit, float32 path (one token per thread)
 constexpr int kMaxWorkers = 8192;    // bound on attention workers (split records <= workers + groups)
-constexpr int kScoreSlots = 16;      // attended slots per alpha_score workgroup
+constexpr int kScoreSlots = 64;      // attended slots per score workgroup
 
 // Per-launch sequence table: lengths and the prefix of work blocks per sequence.
 struct SeqTable {
@@ -30,7 +30,6 @@ struct AttnArgs {
   float* alpha;   // raw scaled logits on exit of attn_partial
   float* part;    // split records: [record][head in group][D] partial P.V
   float* ml;      // split records: [record][head in group][2] (m, l)
-  float* stat;    // [B][Lr][Hq][2]: M (base-2 logits), 1/Lambda
   long alpha_stride;
   long total_units;  // work units of this launch
   long workers;      // workers sharing them (record index = worker + group)
@@ -41,18 +40,34 @@ struct AttnArgs {
   SeqTable seq;
 };
 
+// Score accumulation: s[pos(j)] += weight * sum over r of src[r][j], for the
+// attended slots j of every sequence (row r of sequence bl at
+// src + bl * seq_stride + r * row_stride).
 struct ScoreArgs {
-  float* alpha;
-  const float* stat;
+  const float* src;
+  long row_stride, seq_stride;
+  int rows;
   const int* t0_pos;
   const int* t1_pos;
   float* scores;
-  long alpha_stride;
-  int rows;  // Lr * Hq
-  int normalise;
   int cap0, cap1, max_ctx;
   double weight;  // 1 / (num_layers * Hq)
   SeqTable seq;   // base[] counts kScoreSlots-slot blocks
+};
+
+// Merge of the split records (output O), alpha normalisation, group sums.
+struct MergeArgs {
+  const float* part;
+  const float* ml;
+  float* out;
+  float* alpha;
+  float* gsum;  // [nb][Lr * Hkv][gs_stride] sums of alpha over a group's heads, or null
+  long alpha_stride, gs_stride;
+  long total_units, workers;  // as in the attention launch
+  int Lr, hq, hkv;
+  int out_rows, out_blocks;   // O rows of the launch; workgroups merging them (first)
+  SeqTable seq;               // base[] / units[] as in the attention launch
+  int cbase[kMaxSeqPerLaunch + 1];  // alpha workgroups: prefix over sequences
 };
 
 struct AppendArgs {
@@ -126,8 +141,10 @@ struct QuantArgs {
 bool attn_group_supported(int group);
 int mfma_resident_waves(int head_dim);
 void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, hipStream_t s);
-void launch_attn_combine(const AttnArgs& a, int head_dim, int nb, hipStream_t s);
-void launch_alpha_score(const ScoreArgs& a, int nblocks, hipStream_t s);
+int merge_alpha_blocks(int natt);    // alpha workgroups per (layer, KV head) group
+int merge_output_blocks(int rows);   // workgroups merging `rows` output rows
+void launch_attn_merge(const MergeArgs& a, int head_dim, int nblocks, hipStream_t s);
+void launch_score_rows(const ScoreArgs& a, int nblocks, const char* name, hipStream_t s);
 void launch_append(const AppendArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
 void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s);
 void launch_compact(const CompactArgs& a, const CopyArgs& c, int kv_dtype, int head_dim, int nb,

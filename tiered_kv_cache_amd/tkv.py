@@ -26,8 +26,8 @@ TKV_F32 = 1
 EXPORTED = (
     "tkv_abi_version", "tkv_last_error", "tkv_append", "tkv_decode_workspace_bytes",
     "tkv_decode_step", "tkv_update_scores", "tkv_assign_tiers", "tkv_compact_workspace_bytes",
-    "tkv_compact", "tkv_quantize_t2", "tkv_gather_t1", "tkv_timing_enable", "tkv_timing_reset",
-    "tkv_timing_read",
+    "tkv_compact", "tkv_quantize_t2", "tkv_gather_t1", "tkv_timing_enable", "tkv_timing_select",
+    "tkv_timing_reset", "tkv_timing_read",
 )
 
 
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
         "tkv_gather_t1": (_I, [ctypes.POINTER(tkv_model), _P, _P, _I, _P, _I, _P, _P, _I, _P,
                                _P, _P, _P]),
         "tkv_timing_enable": (_I, [_I]),
+        "tkv_timing_select": (_I, [ctypes.c_char_p]),
         "tkv_timing_reset": (_I, []),
         "tkv_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_int64)]),
@@ -252,6 +253,12 @@ def tkv_gather_t1(model, host_k, host_v, max_ctx, positions, n_t1, staging_k, st
 
 def tkv_timing_enable(enable: bool) -> None:
     _check(lib().tkv_timing_enable(1 if enable else 0), "tkv_timing_enable")
+
+
+def tkv_timing_select(kernels=None) -> None:
+    """Time only the named kernels (an iterable of names, or None for every kernel)."""
+    arg = None if kernels is None else ",".join(kernels).encode()
+    _check(lib().tkv_timing_select(arg), "tkv_timing_select")
 
 
 def tkv_timing_reset() -> None:

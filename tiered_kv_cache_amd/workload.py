@@ -29,12 +29,14 @@ class DeviceWorkload:
         self.streams = [SequenceStream(wl, b) for b in range(wl.batch)]
         self.dtype = shape_of(wl).torch_dtype
 
-    def make_cache(self, **kw) -> TieredKVCache:
+    def make_cache(self, contexts=None, **kw) -> TieredKVCache:
+        """A cache holding every sequence's initial context (regenerated unless
+        `contexts`, a list of (K, V) host arrays per sequence, is given)."""
         wl = self.wl
         cache = TieredKVCache(shape_of(wl), policy_of(wl), wl.batch, wl.max_ctx,
                               device=str(self.device), **kw)
         for b, st in enumerate(self.streams):
-            K, V = st.context()
+            K, V = contexts[b] if contexts is not None else st.context()
             cache.load_context(b, K, V)
         return cache
 
