@@ -73,6 +73,33 @@ def reassign_bytes(wl, n: int, n0: int, n1: int, r2: int) -> int:
     return tiers + compact + quant
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_partial_{workload}_hbm_counters.md")
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per attn_partial launch from the committed counter summary, or None when
+    there is none for this workload or the kernel sources changed since it was taken."""
+    import hashlib
+    path = COUNTERS_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in fields["source_files"].split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != fields["source_sha256"]:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -254,7 +281,7 @@ def main():
                    "delta": wl.delta, "reassignments_timed": len(re_info)},
         "roofline": {"bound": "hbm", "kernel": "attn_partial", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": None, "bytes_per_launch": attn_bytes,
+                     "traffic": counter_traffic(args.workload), "bytes_per_launch": attn_bytes,
                      "avg_launch_us": attn["avg_us"]},
         "step_hbm": {"algorithmic_bytes_per_step": alg_bytes,
                      "achieved_gbps": alg_bytes * steps_per_s / 1e9,
