@@ -238,41 +238,53 @@ __device__ __forceinline__ void flush_stage(const AttnArgs& a, int lane, int G, 
 // 32-slot block is always inside the allocation (capacities are multiples of
 // 32); slots past the segment end are masked when consumed.
 template <int D>
-__device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, int lane,
-                                            UnitLoads<D>& L) {
-  constexpr int KB = D / 32, NB = D / 16;
+__device__ __forceinline__ long unit_base(const AttnArgs& a, const Cursor& c) {
   const long b = a.seq.b_offset + c.bl;
   const int cap = c.seg ? a.cap1 : a.cap0;
-  const long blk = ((b * a.L + a.layer_begin + c.lr) * a.hkv + c.g) * (long)cap * D + (long)c.c0 * D;
-  const uint4* Ku = (const uint4*)((const uint16_t*)(c.seg ? a.k1 : a.k0) + blk);
-  const uint4* Vu = (const uint4*)((const uint16_t*)(c.seg ? a.v1 : a.v0) + blk);
+  return ((b * a.L + a.layer_begin + c.lr) * a.hkv + c.g) * (long)cap * D + (long)c.c0 * D;
+}
+
+template <int D>
+__device__ __forceinline__ void issue_k(const AttnArgs& a, const Cursor& c, int lane,
+                                        UnitLoads<D>& L) {
+  constexpr int KB = D / 32;
+  const uint4* Ku = (const uint4*)((const uint16_t*)(c.seg ? a.k1 : a.k0) + unit_base<D>(a, c));
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) L.k[u][kb] = Ku[u * 2 * D + kb * 64 + lane];
+}
+
+template <int D>
+__device__ __forceinline__ void issue_v(const AttnArgs& a, const Cursor& c, int lane,
+                                        UnitLoads<D>& L) {
+  constexpr int NB = D / 16;
+  const uint4* Vu = (const uint4*)((const uint16_t*)(c.seg ? a.v1 : a.v0) + unit_base<D>(a, c));
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) L.v[nb] = Vu[nb * 64 + lane];
 }
 
+// Loads of one unit: with K-tiles and V-tiles every operand is one contiguous
+// 1 KB wave access at lane offset kb*64 + lane (K) or nb*64 + lane (V).  The
+// 32-slot block is always inside the allocation (capacities are multiples of
+// 32); slots past the segment end are masked when consumed.
+template <int D>
+__device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, int lane,
+                                            UnitLoads<D>& L) {
+  issue_k<D>(a, c, lane, L);
+  issue_v<D>(a, c, lane, L);
+}
+
+// Logits of one unit from its keys: S^T = K Q^T, staged in LDS, the online
+// softmax update, and P (bf16 high part + bf16 remainder) for P.V.
 template <int D, bool FULL>
-__device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
-                                        int h, int grp, int G, WaveState<D>& st, Stage& sg) {
+__device__ __forceinline__ void unit_scores(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
+                                            int h, int grp, int G, WaveState<D>& st, Stage& sg,
+                                            bf16x8_t& phi, bf16x8_t& plo) {
   constexpr int KB = D / 32, NB = D / 16;
   constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
   const int c1 = c.seg ? c.n1 : c.n0;
   const int tb = c.c0 + 8 * grp;  // first of this lane's 8 tokens
-  if (!FULL) {  // tail: zero the value slots past the end of the segment
-    const int valid = c1 - tb;
-    if (valid < 8) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        uint32_t* wds = (uint32_t*)&L.v[nb];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= valid) wds[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      }
-    }
-  }
   // S^T = K Q^T: this lane gets tokens tb + e (e = 0..7) of head h
   f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -313,7 +325,6 @@ __device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, Unit
     }
     st.m = mn;
   }
-  bf16x8_t phi, plo;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float pe = __builtin_amdgcn_exp2f(sv[e] - st.m);  // masked slots: exp2(-inf) = 0
@@ -322,7 +333,26 @@ __device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, Unit
     phi[e] = hb;
     plo[e] = (__bf16)(pe - (float)hb);
   }
-  // O += P V (high part, then the remainder)
+}
+
+// O += P V (high part, then the remainder).
+template <int D, bool FULL>
+__device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, int grp,
+                                            const bf16x8_t& phi, const bf16x8_t& plo,
+                                            WaveState<D>& st) {
+  constexpr int NB = D / 16;
+  if (!FULL) {  // tail: zero the value slots past the end of the segment (they may hold NaN)
+    const int valid = (c.seg ? c.n1 : c.n0) - (c.c0 + 8 * grp);
+    if (valid < 8) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t* wds = (uint32_t*)&L.v[nb];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= valid) wds[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      }
+    }
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, as_bf16x8(L.v[nb]), st.acc[nb], 0, 0, 0);
@@ -330,11 +360,24 @@ __device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, Unit
   }
 }
 
-// Prefetch depth of the matrix-core kernel: 1 issues the next unit's loads before
-// computing the current one (two register buffers, fewer waves per SIMD); 0 loads
-// and computes one unit at a time (one buffer, more waves per SIMD).
+template <int D, bool FULL>
+__device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
+                                        int h, int grp, int G, WaveState<D>& st, Stage& sg) {
+  bf16x8_t phi, plo;
+  unit_scores<D, FULL>(a, c, L, h, grp, G, st, sg, phi, plo);
+  unit_values<D, FULL>(c, L, grp, phi, plo, st);
+}
+
+// Prefetch scheme of the matrix-core kernel:
+//  2 (default): rolling -- the next unit's keys are loaded as soon as Q.K of the
+//     current unit has consumed the key registers, its values as soon as P.V has
+//     consumed the value registers; one register buffer, and a unit's worth of
+//     loads stays in flight while the wave computes;
+//  1: two register buffers (next unit loaded before the current is computed;
+//     more registers, fewer waves per SIMD);
+//  0: load and compute one unit at a time.
 #ifndef TKV_MFMA_PIPELINE
-#define TKV_MFMA_PIPELINE 0
+#define TKV_MFMA_PIPELINE 2
 #endif
 // Minimum workgroups per CU the compiler must fit (register budget).
 #ifndef TKV_MFMA_MIN_BLOCKS
@@ -385,7 +428,30 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
   WaveState<D> st;
   Cursor c = cursor_at(a, p0);
   begin_group<D>(a, c, h, grp, G, st);
-#if TKV_MFMA_PIPELINE
+#if TKV_MFMA_PIPELINE == 2
+  UnitLoads<D> L;
+  issue_loads<D>(a, c, lane, L);
+  for (long p = p0; p < p1; ++p) {
+    const bool more = p + 1 < p1;
+    Cursor cn = c;
+    if (more) cursor_next(a, cn);
+    const long group = (long)c.bl * a.Lr * a.hkv + c.lgl;
+    if (group != st.group) {
+      flush_record<D>(a, w, h, grp, G, st);
+      begin_group<D>(a, c, h, grp, G, st);
+    }
+    if (sg.n == sg.cap) flush_stage(a, lane, G, sg);
+    bf16x8_t phi, plo;
+    const bool full = unit_full(c);
+    if (full) unit_scores<D, true>(a, c, L, h, grp, G, st, sg, phi, plo);
+    else unit_scores<D, false>(a, c, L, h, grp, G, st, sg, phi, plo);
+    if (more) issue_k<D>(a, cn, lane, L);
+    if (full) unit_values<D, true>(c, L, grp, phi, plo, st);
+    else unit_values<D, false>(c, L, grp, phi, plo, st);
+    if (more) issue_v<D>(a, cn, lane, L);
+    c = cn;
+  }
+#elif TKV_MFMA_PIPELINE == 1
   UnitLoads<D> A, B;
   issue_loads<D>(a, c, lane, A);
   for (long p = p0; p < p1; p += 2) {

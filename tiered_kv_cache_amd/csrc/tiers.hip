@@ -16,8 +16,9 @@
 // compact_scan  -- one workgroup per sequence: block scans over positions map
 //                  every new T0/T1 slot to its source slot in the previous
 //                  pool/window and list the positions newly in T2.
-// compact_copy  -- moves the rows into the new pool/window (K-tile chunks and
-//                  V-tile panels, written in destination order).
+// compact_copy  -- moves the rows into the new pool/window, one 32-slot
+//                  destination block per workgroup: 16-byte key chunks and
+//                  8-slot value panels, written in destination order.
 // append        -- writes the new token's K/V row into its T0 slot.
 #include <limits.h>
 
@@ -46,6 +47,47 @@ __device__ __forceinline__ bool in_sel(const Sel& s, uint32_t key, int p) {
   return key < s.T || (key == s.T && p >= s.cut);
 }
 
+// hist[bin] += 1 for every active lane, one LDS atomic per distinct bin of the
+// wave (scores of a tail cluster in few bins of the leading digits).
+__device__ __forceinline__ void wave_hist_add(unsigned* hist, unsigned bin, bool active) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t todo = __ballot(active);
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const unsigned lb = (unsigned)__shfl((int)bin, leader, kWave);
+    const uint64_t same = __ballot(active && bin == lb);
+    if (lane == leader) atomicAdd(&hist[lb], (unsigned)__popcll(same));
+    todo &= ~same;
+    if (bin == lb) active = false;
+  }
+}
+
+// Digit of the k-th smallest key: the first bin whose inclusive prefix count
+// reaches kk.  sh[0] = bin, sh[1] = kk minus the count below that bin.
+// Every thread of the block calls it (barriers); hist holds 256 counts.
+__device__ __forceinline__ void pick_digit(const unsigned* hist, int kk, int* tmp, int* sh) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int v = tid < 256 ? (int)hist[tid] : 0;
+  int incl = wave_incl_scan_i(v);
+  if (wid < 256 / kWave && lane == kWave - 1) tmp[wid] = incl;
+  if (tid == 0) {
+    sh[0] = 255;
+    sh[1] = kk;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    for (int w = 0; w < wid; ++w) incl += tmp[w];
+    const int excl = incl - v;
+    if (excl < kk && kk <= incl) {
+      sh[0] = tid;
+      sh[1] = kk - excl;
+    }
+  }
+  __syncthreads();
+}
+
 // k (block-uniform) least important candidates among positions [0, n).
 template <class Cand>
 __device__ Sel radix_select(int k, int n, const float* sc, const uint8_t* tp, Cand cand,
@@ -61,23 +103,20 @@ __device__ Sel radix_select(int k, int n, const float* sc, const uint8_t* tp, Ca
     for (int i = tid; i < 256; i += kTierThreads) hist[i] = 0u;
     __syncthreads();
     const uint32_t himask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int p = tid; p < n; p += kTierThreads) {
-      const uint32_t key = score_key(sc[p]);
-      if ((key & himask) == prefix && cand(p, tp[p], key))
-        atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int cum = 0, d = 0;
-      for (; d < 255; ++d) {
-        const int h = (int)hist[d];
-        if (cum + h >= kk) break;
-        cum += h;
+    // the trip count is the same for every lane of a wave (n is block-uniform and
+    // the stride is the block size), so the ballots below see the whole wave
+    for (int p0 = tid - (tid & (kWave - 1)); p0 < n; p0 += kTierThreads) {
+      const int p = p0 + (tid & (kWave - 1));
+      bool act = false;
+      uint32_t key = 0u;
+      if (p < n) {
+        key = score_key(sc[p]);
+        act = (key & himask) == prefix && cand(p, tp[p], key);
       }
-      sh[0] = d;
-      sh[1] = kk - cum;
+      wave_hist_add(hist, (key >> shift) & 255u, act);
     }
     __syncthreads();
+    pick_digit(hist, kk, tmp, sh);
     prefix |= (uint32_t)sh[0] << shift;
     kk = sh[1];
     __syncthreads();
@@ -88,22 +127,40 @@ __device__ Sel radix_select(int k, int n, const float* sc, const uint8_t* tp, Ca
   const int seg = (n + kTierThreads - 1) / kTierThreads;
   const int hi = max(0, n - tid * seg);
   const int lo = max(0, n - (tid + 1) * seg);
+  constexpr int kBatch = 16;  // positions whose loads are issued together
   int cnt = 0;
-  for (int p = lo; p < hi; ++p) {
-    const uint32_t key = score_key(sc[p]);
-    if (key == prefix && cand(p, tp[p], key)) ++cnt;
+  for (int base = lo; base < hi; base += kBatch) {
+    bool tie[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = base + i;
+      tie[i] = false;
+      if (p < hi) {
+        const uint32_t key = score_key(sc[p]);
+        tie[i] = key == prefix && cand(p, tp[p], key);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) cnt += tie[i] ? 1 : 0;
   }
   int total;
   const int excl = block_excl_scan(cnt, tmp, &total);
   if (excl < kk && kk <= excl + cnt) {
-    int need = kk - excl;
-    for (int p = hi - 1; p >= lo; --p) {
-      const uint32_t key = score_key(sc[p]);
-      if (key == prefix && cand(p, tp[p], key)) {
-        if (--need == 0) {
-          sh[2] = p;
-          break;
+    int need = kk - excl;  // the need-th tie counted from the top of this segment
+    for (int top = hi - 1; top >= lo && need > 0; top -= kBatch) {
+      bool tie[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int p = top - i;
+        tie[i] = false;
+        if (p >= lo) {
+          const uint32_t key = score_key(sc[p]);
+          tie[i] = key == prefix && cand(p, tp[p], key);
         }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (need > 0 && tie[i] && --need == 0) sh[2] = top - i;
       }
     }
   }
@@ -275,69 +332,94 @@ __global__ __launch_bounds__(kTierThreads) void compact_scan_kernel(CompactArgs 
   }
 }
 
+// Eight consecutive elements: one 16-byte vector for bf16, two for float32.
+template <typename T>
+struct Vec8 {
+  uint4 w[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ Vec8<T> load8(const T* p) {
+  Vec8<T> v;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) v.w[i] = reinterpret_cast<const uint4*>(p)[i];
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const Vec8<T>& v) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) reinterpret_cast<uint4*>(p)[i] = v.w[i];
+}
+
+// One workgroup per destination 32-slot block of one (sequence, layer, KV head).
+// Keys move as 8-element chunks (a chunk of a row is contiguous in a K-tile);
+// values are gathered 8 slots at a time into one V-tile panel of one dimension.
+// Items are numbered in destination order, so the stores of a wave are
+// contiguous; slots at or past the new length are written as zero.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void compact_copy_kernel(CopyArgs c) {
-  constexpr int ROWS = 64;  // destination slots per workgroup (two 32-slot blocks)
+  constexpr int CH = D / 8;  // 8-element key chunks per row
   const int z = blockIdx.z;  // 0: T0 destination, 1: T1 destination
   const int lgs = c.L * c.hkv;
   const int bl = blockIdx.y / lgs;
   const long lg = blockIdx.y - (long)bl * lgs;
   const long b = c.b_offset + bl;
   const int len = c.new_lens[b * 3 + z];
-  const int r0 = blockIdx.x * ROWS;
+  const int r0 = blockIdx.x * 32;
   if (len <= r0) return;
   const int cap_d = z ? c.cap1 : c.cap0;
-  const int* src = z ? c.src1 + b * c.cap1 : c.src0 + b * c.cap0;
+  const int* src = (z ? c.src1 + b * c.cap1 : c.src0 + b * c.cap0) + r0;
+  const int nrow = min(32, len - r0);
   const long blk0 = (b * lgs + lg) * c.cap0 * D;  // element offset of this (b, l, g) block
   const long blk1 = (b * lgs + lg) * c.cap1 * D;
-  const long blkd = (b * lgs + lg) * (long)cap_d * D;
-  // K: 8-element chunks; items ordered like the destination (block, tile, chunk, row)
+  const long blkd = (b * lgs + lg) * (long)cap_d * D + (long)r0 * D;
+  // keys: item i -> (tile u, chunk cc, tile row) in destination order
   {
     const T* ks0 = (const T*)c.k0s + blk0;
     const T* ks1 = (const T*)c.k1s + blk1;
     T* kd = (T*)(z ? c.k1d : c.k0d) + blkd;
-    constexpr int CH = D / 8;
-    for (int i = threadIdx.x; i < ROWS * CH; i += 256) {
+    for (int i = threadIdx.x; i < 32 * CH; i += 256) {
       const int row = i & 15;
       const int cc = (i >> 4) % CH;
-      const int u = (i / (16 * CH)) & 1;
-      const int bk = i / (32 * CH);
-      const int r = r0 + bk * 32 + 8 * (row >> 2) + 4 * u + (row & 3);
-      if (r >= len) continue;
-      const int sidx = src[r];
-      const long ss = sidx >= 0 ? sidx : -sidx - 1;
-      const T* from = (sidx >= 0 ? ks0 : ks1) + k_off(ss, 8 * cc, D);
-      T* to = kd + k_off(r, 8 * cc, D);
+      const int u = i / (16 * CH);
+      const int r = 8 * (row >> 2) + 4 * u + (row & 3);
+      Vec8<T> v;
+      if (r < nrow) {
+        const int sidx = src[r];
+        const long ss = sidx >= 0 ? sidx : -sidx - 1;
+        v = load8((sidx >= 0 ? ks0 : ks1) + k_off(ss, 8 * cc, D));
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) to[e] = from[e];
+        for (int w = 0; w < (int)(sizeof(T) / 2); ++w) v.w[w] = make_uint4(0, 0, 0, 0);
+      }
+      store8(kd + k_off(r, 8 * cc, D), v);
     }
   }
-  // V: 8-slot panels of one dimension; items ordered like the destination
+  // values: item i -> (dimension group dh, panel, dimension) in destination order
   {
     const T* vs0 = (const T*)c.v0s + blk0;
     const T* vs1 = (const T*)c.v1s + blk1;
     T* vd = (T*)(z ? c.v1d : c.v0d) + blkd;
-    for (int i = threadIdx.x; i < (ROWS / 8) * D; i += 256) {
+    for (int i = threadIdx.x; i < 4 * D; i += 256) {
       const int d15 = i & 15;
       const int pnl = (i >> 4) & 3;
-      const int dh = (i >> 6) % (D / 16);
-      const int bk = i / (4 * D);
+      const int dh = i >> 6;
       const int d = dh * 16 + d15;
-      const int rb = r0 + bk * 32 + pnl * 8;
-      if (rb >= len) continue;
       T vals[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        const int r = pnl * 8 + e;
         vals[e] = T(0);
-        if (rb + e < len) {
-          const int sidx = src[rb + e];
+        if (r < nrow) {
+          const int sidx = src[r];
           const long ss = sidx >= 0 ? sidx : -sidx - 1;
           vals[e] = (sidx >= 0 ? vs0 : vs1)[v_off(ss, d, D)];
         }
       }
-      T* to = vd + v_off(rb, d, D);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) to[e] = vals[e];
+      Vec8<T> packed;
+      __builtin_memcpy(&packed, vals, sizeof(packed));
+      store8(vd + v_off(pnl * 8, d, D), packed);
     }
   }
 }
@@ -349,7 +431,7 @@ void launch_compact(const CompactArgs& a, const CopyArgs& c, int kv_dtype, int h
     hipLaunchKernelGGL(compact_scan_kernel, dim3(nb), dim3(kTierThreads), 0, s, a);
   }
   const int rows = max(1, min(max_n, max(c.cap0, c.cap1)));
-  dim3 grid(ceil_div(rows, 64), nb * c.L * c.hkv, 2);
+  dim3 grid(ceil_div(rows, 32), nb * c.L * c.hkv, 2);
   KernelTimer timer("compact_copy", s);
   if (kv_dtype == TKV_BF16) {
     if (head_dim == 128)
