@@ -8,8 +8,11 @@ import numpy as np
 import pytest
 import torch
 
-from tests.parity import run_lockstep, run_sampled, say
+from oracle import attention
+from tests.parity import check_alpha, check_output, check_scores, run_lockstep, run_sampled, say
+from tiered_kv_cache_amd.driver import to_device
 from tiered_kv_cache_amd.synth import WORKLOADS
+from tiered_kv_cache_amd.workload import DeviceWorkload
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +62,40 @@ def test_batch70_crosses_the_per_launch_sequence_limit():
                      planted=(0,) * 70, frac_t1=0.3, frac_t2=0.1, frac_t3=0.1)
     st = run_lockstep(wl)
     assert st["reassignments"] == 3 * 70
+
+
+def test_empty_sequence_in_batch():
+    # one sequence of the batch has no attended token: its output rows are zero and the
+    # other sequences are unaffected (one attention call, no append)
+    from collections import defaultdict
+    wl = WORKLOADS["small"].scaled(name="empty_mix_L2_h8kv2_d128", layers=2, batch=3,
+                                   ctx=(300, 0, 77), planted=(0, 0, 0), warmup=0, steps=1,
+                                   prompt=8, recent=8, sinks=2)
+    dw = DeviceWorkload(wl)
+    cache = dw.make_cache()
+    q, _, _ = dw.host_step(1)
+    cache.out.fill_(float("nan"))
+    cache.attend(to_device(q, dw.dtype, dw.device))
+    torch.cuda.synchronize()
+    out = cache.out.cpu().numpy()
+    stats = defaultdict(float)
+    scale = 1.0 / np.sqrt(wl.head_dim)
+    for b, n in enumerate(wl.ctx):
+        if n == 0:
+            assert np.all(out[b] == 0.0), "rows of the empty sequence must be zero"
+            continue
+        K, V = dw.streams[b].context()
+        alpha_gpu = cache.alpha_of(b)
+        inc = np.zeros(n)
+        for l in range(wl.layers):
+            for h in range(wl.q_heads):
+                g = h // wl.group
+                O, a = attention(q[b][l][h:h + 1], K[l][g:g + 1], V[l][g:g + 1], scale)
+                check_output(out[b, l, h][None], O, stats)
+                check_alpha(alpha_gpu[l, h][None], a, stats)
+                inc += a[0]
+        check_scores(cache.scores[b, :n].cpu().numpy(), inc / (wl.layers * wl.q_heads), stats)
+    say(f"[empty sequence] ok: " + ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))
 
 
 def test_chain8k_full_size_sampled():

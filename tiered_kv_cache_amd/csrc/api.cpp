@@ -293,7 +293,7 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
       const char* e = getenv("TKV_ATTN_WORKERS");
       return e ? atoi(e) : 0;
     }();
-    if (override_workers > 0) resident = std::min(override_workers, kMaxWorkers);
+    if (override_workers > 0) resident = std::min(override_workers, resident);
   }
 
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {

@@ -416,6 +416,7 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const long w = (long)blockIdx.x * 4 + wv;
   const long P = a.total_units, W = a.workers;
+  if (w >= W) return;  // the last workgroup may hold waves past the worker count
   const long p0 = w * P / W, p1 = (w + 1) * P / W;
   if (p0 >= p1) return;  // this wave has no work (small launches)
   const int G = a.hq / a.hkv;
