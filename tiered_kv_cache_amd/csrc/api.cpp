@@ -136,7 +136,7 @@ static DecodeWorkspace decode_workspace(const tkv_model* m, int batch, int n_lay
   DecodeWorkspace w;
   w.gs_stride = round_up((size_t)cap0 + (size_t)cap1, 4);
   w.part = 0;
-  w.ml = round_up(w.part + recs * G * D, 64);
+  w.ml = round_up(w.part + recs * (size_t)part_rec_floats((int)G, (int)D), 64);
   w.gsum = round_up(w.ml + recs * G * 2, 64);
   w.total = round_up(w.gsum + nb * n_layers * m->num_kv_heads * w.gs_stride, 64);
   return w;

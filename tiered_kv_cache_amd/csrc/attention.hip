@@ -208,14 +208,12 @@ __device__ __forceinline__ void flush_record(const AttnArgs& a, long worker, int
     a.ml[(rec + h) * 2] = st.m;
     a.ml[(rec + h) * 2 + 1] = l;
   }
+  if (grp < (G + 3) / 4) {  // lane groups holding real heads; one whole row per store
+    float* base = a.part + (worker + st.group) * part_rec_floats(G, D);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int head = grp * 4 + r;
-    if (head < G) {
-      float* dst = a.part + (rec + head) * D + h;
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) dst[nb * 16] = st.acc[nb][r];
-    }
+      for (int nb = 0; nb < NB; ++nb) base[part_off(G, D, grp * 4 + r, nb * 16 + h)] = st.acc[nb][r];
   }
 }
 
@@ -509,9 +507,10 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
 
   auto flush = [&]() {
     const long rec = (w + cur_group) * G;
+    float* base = a.part + (w + cur_group) * part_rec_floats(G, D);
     for (int i = tid; i < G * D; i += NT) {
       const int hh = i / D;
-      a.part[(rec + hh) * D + (i - hh * D)] = orun[hh][i - hh * D];
+      base[part_off(G, D, hh, i - hh * D)] = orun[hh][i - hh * D];
     }
     if (tid < G) {
       a.ml[(rec + tid) * 2] = mrun[tid];

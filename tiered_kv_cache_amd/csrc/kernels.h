@@ -20,6 +20,18 @@ struct SeqTable {
   int units[kMaxSeqPerLaunch];     // attention: work units per (layer, KV head) group
 };
 
+// Split records of the partial P.V: per record (worker + group) the G heads'
+// D values, stored in the order the matrix-core kernel holds them, so that its
+// stores are whole 64-byte (G <= 4), 128-byte (G <= 8) or 256-byte rows:
+// [head % 4][D / 16][ceil(G / 4)][16], head h at (h % 4, h / 4), dim d at
+// (d / 16, d % 16).  Heads past G (padding up to 4 * ceil(G / 4)) are written
+// but never read.
+__host__ __device__ inline long part_rec_floats(int G, int D) { return 4L * D * ((G + 3) / 4); }
+__host__ __device__ inline long part_off(int G, int D, int head, int d) {
+  const int GR = (G + 3) / 4;
+  return ((long)((head & 3) * (D / 16) + (d >> 4)) * GR + (head >> 2)) * 16 + (d & 15);
+}
+
 struct AttnArgs {
   const void* q;
   const void* k0;
@@ -28,8 +40,8 @@ struct AttnArgs {
   const void* v1;
   float* out;
   float* alpha;   // raw scaled logits on exit of attn_partial
-  float* part;    // split records: [record][head in group][D] partial P.V
-  float* ml;      // split records: [record][head in group][2] (m, l)
+  float* part;    // split records: [worker + group][part_rec_floats] partial P.V
+  float* ml;      // split records: [worker + group][head in group][2] (m, l)
   long alpha_stride;
   long total_units;  // work units of this launch
   long workers;      // workers sharing them (record index = worker + group)

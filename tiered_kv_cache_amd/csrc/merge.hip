@@ -127,9 +127,10 @@ __device__ void merge_output_row(const MergeArgs& a, int row_in_launch) {
           const int src = k + u < cnt ? k + u : k;
           const int ru = __shfl(rec, src, kWave);
           cu[u] = k + u < cnt ? __shfl(c, src, kWave) : 0.f;
-          const float* pp = a.part + (long)ru * D + lane;
+          const float* pp = a.part + (long)(ru / G) * part_rec_floats(G, D);
 #pragma unroll
-          for (int i = 0; i < PER; ++i) v[u][i] = cu[u] != 0.f ? pp[kWave * i] : 0.f;
+          for (int i = 0; i < PER; ++i)
+            v[u][i] = cu[u] != 0.f ? pp[part_off(G, D, hh, lane + kWave * i)] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
