@@ -155,14 +155,16 @@ class HostStore:
 
 
 def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=(),
-                label: str = "") -> dict:
+                label: str = "", byte_seqs=None) -> dict:
     """Full-size run, checked on samples the oracle computes one at a time:
     * O and alpha of the sampled (layer, head) pairs over the GPU's attended set;
     * the whole score increment at `full_inc_steps` (all layers and heads);
     * total score mass == steps (any size);
     * at every reassignment: tiers from the oracle ranking of the GPU's scores, the
-      counts, slot maps, T1 window bytes and the int8 rows of new T2 positions.
+      counts and slot maps of every sequence; the T0/T1 row bytes and the int8 rows of
+      new T2 positions of the sequences in `byte_seqs` (default: all).
     """
+    byte_seqs = set(range(wl.batch)) if byte_seqs is None else set(byte_seqs)
     dw = DeviceWorkload(wl)
     cache = dw.make_cache()
     store = HostStore(dw, cache.max_ctx)
@@ -223,6 +225,9 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                 t1 = np.nonzero(t_ref == 1)[0]
                 assert np.array_equal(cache.t0_pos[b, :cache.t0_len[b]].cpu().numpy(), t0)
                 assert np.array_equal(cache.t1_pos[b, :cache.t1_len[b]].cpu().numpy(), t1)
+                stats["reassignments"] += 1
+                if b not in byte_seqs:
+                    continue
                 k1, v1 = cache.t1_rows(b)
                 assert k1.tobytes() == np.ascontiguousarray(store.K[b][:, :, t1]).tobytes()
                 assert v1.tobytes() == np.ascontiguousarray(store.V[b][:, :, t1]).tobytes()
@@ -241,7 +246,6 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                     assert np.array_equal(codes, ref_codes), "int8 codes differ"
                     assert np.array_equal(scales.view(np.uint32), ref_scales.view(np.uint32))
                 stats["t2_rows"] += len(pos)
-                stats["reassignments"] += 1
     stats["steps"] = n_steps
     say(f"[{label or wl.name}] sampled ok: " +
         ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))

@@ -104,3 +104,21 @@ def test_chain8k_full_size_sampled():
     st = run_sampled(wl, n_steps=130, sample_steps={1, 63, 64, 65, 100, 128, 129},
                      heads=heads, full_inc_steps={2, 66})
     assert st["reassignments"] == 2
+
+
+def test_batch16_ragged_full_size_sampled():
+    # 16 sequences with contexts from 1024 to 8192 tokens, the 7B-class shape
+    wl = WORKLOADS["batch16"]
+    heads = [(0, 0), (11, 13), (27, 27)]
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 64, 65, 97, 128},
+                     heads=heads, full_inc_steps={2, 70}, byte_seqs={0, 7, 15})
+    assert st["reassignments"] == 2 * 16
+
+
+def test_chain32k_full_size_sampled():
+    # 4 sequences of 32768 tokens, 32 layers, 32 query / 8 KV heads
+    wl = WORKLOADS["chain32k"]
+    heads = [(0, 3), (17, 20), (31, 31)]
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 64, 65, 128},
+                     heads=heads, full_inc_steps={66}, byte_seqs={1})
+    assert st["reassignments"] == 2 * 4

@@ -33,6 +33,8 @@ q, K and V.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from functools import lru_cache
 from typing import Optional, Tuple
@@ -229,12 +231,30 @@ class SequenceStream:
         return _query_cache(self.wl, self.b, step)
 
     def context(self) -> Tuple[np.ndarray, np.ndarray]:
-        """Whole initial context: K, V each [L][Hkv][n0][D]."""
-        ks, vs = zip(*(self.context_layer(l) for l in range(self.wl.layers)))
+        """Whole initial context: K, V each [L][Hkv][n0][D].  Layers are independent
+        streams, generated on a few host threads (NumPy's generators release the GIL)."""
+        wl = self.wl
+        e = 2 if wl.dtype == "bf16" else 4
+        if wl.layers * 2 * wl.kv_heads * self.n0 * wl.head_dim * e < (16 << 20):
+            parts = [self.context_layer(l) for l in range(wl.layers)]
+        else:
+            for t in sorted(set(self.planted()[1].tolist())):
+                self._query_cached(t)          # fill the shared cache before the threads
+            with ThreadPoolExecutor(max_workers=_host_threads()) as ex:
+                parts = list(ex.map(self.context_layer, range(wl.layers)))
+        ks, vs = zip(*parts)
         return np.stack(ks), np.stack(vs)
 
 
-@lru_cache(maxsize=64)
+def _host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+@lru_cache(maxsize=256)
 def _query_cache(wl: Workload, b: int, step: int) -> np.ndarray:
     return SequenceStream(wl, b).query_f32(step)
 
