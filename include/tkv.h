@@ -162,6 +162,29 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
                            hipStream_t stream);
 
 /*
+ * tkv_append_decode_step -- tkv_append followed by tkv_decode_step over all
+ * layers, as one pass over the key/value rows: each generated token adds one
+ * key/value pair (Enonce du probleme), which enters T0 and is attended in the
+ * same step.  With bf16 data the attention kernel reads the new rows from
+ * k_new/v_new, writes them into the T0 pool at slot t0_len[b] and records
+ * t0_pos[b][t0_len[b]] = position[b], score 0 and tier 0 (when scores / tier are
+ * given); float32 data run the two calls.
+ *
+ * Arguments as for tkv_append and tkv_decode_step, with t0_len the lengths
+ * BEFORE the append (the call attends t0_len[b] + 1 T0 rows, so
+ * t0_len[b] + 1 <= cap0); layer_begin = 0 and layer_end = num_layers.
+ * The caller adds one to its t0_len after the call.
+ */
+tkv_status tkv_append_decode_step(const tkv_model* model, int32_t batch, const void* k_new,
+                                  const void* v_new, const int32_t* position, uint8_t* tier,
+                                  const void* q, void* k_t0, void* v_t0, const int32_t* t0_len,
+                                  int32_t cap0, const void* k_t1, const void* v_t1,
+                                  const int32_t* t1_len, int32_t cap1, float* out, float* alpha,
+                                  int32_t alpha_stride, int32_t* t0_pos, const int32_t* t1_pos,
+                                  float* scores, int32_t max_ctx, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * tkv_update_scores -- the importance-score recurrence (Methodologie section 2):
  * scores[b][pos(j)] += (1/(num_layers*Hq)) * sum over layers in
  * [layer_begin, layer_end) and heads of alpha[b][l][h][j], for every attended

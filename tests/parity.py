@@ -92,10 +92,23 @@ def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, st
     stats["reassignments"] += 1
 
 
+def step_inputs(cache, dw, q, kn, vn, fused_append: bool) -> None:
+    """Append the step's new rows and attend, fused or as two calls."""
+    qd = to_device(q, dw.dtype, dw.device)
+    kd, vd = to_device(kn, dw.dtype, dw.device), to_device(vn, dw.dtype, dw.device)
+    if fused_append:
+        cache.append_attend(qd, kd, vd)
+    else:
+        cache.append(kd, vd)
+        cache.attend(qd)
+
+
 def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
-                 fused_scores: bool = True) -> dict:
+                 fused_scores: bool = True, fused_append: bool = True) -> dict:
     """Every step compared; re-sync of the ranking at each reassignment.
-    fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores."""
+    fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores;
+    fused_append=False appends with tkv_append before tkv_decode_step instead of
+    tkv_append_decode_step."""
     n_steps = n_steps or wl.total_steps
     dw = DeviceWorkload(wl)
     cache = dw.make_cache()
@@ -108,8 +121,7 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
     stats = defaultdict(float)
     for k in range(1, n_steps + 1):
         q, kn, vn = dw.host_step(k)
-        cache.append(to_device(kn, dw.dtype, dw.device), to_device(vn, dw.dtype, dw.device))
-        cache.attend(to_device(q, dw.dtype, dw.device))
+        step_inputs(cache, dw, q, kn, vn, fused_append)
         cache.steps += 1
         torch.cuda.synchronize()
         out = cache.out.cpu().numpy()
@@ -177,8 +189,7 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
         for b in range(wl.batch):
             store.put(b, cache.n[b], kn[b], vn[b])
         s_before = cache.scores.cpu().numpy() if k in full_inc_steps else None
-        cache.append(to_device(kn, dw.dtype, dw.device), to_device(vn, dw.dtype, dw.device))
-        cache.attend(to_device(q, dw.dtype, dw.device))
+        step_inputs(cache, dw, q, kn, vn, True)
         cache.steps += 1
         if k in sample_steps or k in full_inc_steps:
             torch.cuda.synchronize()

@@ -89,6 +89,26 @@ def test_decode_step_validation():
     assert "negative" in msg
 
 
+def append_decode(m, **kw):
+    args = dict(batch=1, k_new=FAKE, v_new=FAKE, position=[10], tier=FAKE, q=FAKE, k_t0=FAKE,
+                v_t0=FAKE, t0_len=[10], cap0=32, k_t1=FAKE, v_t1=FAKE, t1_len=[2], cap1=32,
+                out=FAKE, alpha=FAKE, alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE, scores=FAKE,
+                max_ctx=64, workspace=FAKE, workspace_bytes=1 << 30, stream=0)
+    args.update(kw)
+    return tkv.tkv_append_decode_step(m, **args)
+
+
+def test_append_decode_step_validation():
+    m = model()
+    assert status_of(append_decode, m, t0_len=[32]) == tkv.TKV_ERR_CAPACITY   # no slot left
+    assert status_of(append_decode, m, k_new=NULL) == tkv.TKV_ERR_ARG
+    assert status_of(append_decode, m, t0_pos=NULL) == tkv.TKV_ERR_ARG
+    assert status_of(append_decode, m, position=[-1]) == tkv.TKV_ERR_ARG
+    assert status_of(append_decode, m, position=[64]) == tkv.TKV_ERR_CAPACITY
+    assert status_of(append_decode, m, alpha_stride=12) == tkv.TKV_ERR_CAPACITY  # 10 + 1 + 2
+    assert status_of(append_decode, model(head_dim=96)) == tkv.TKV_ERR_ARG
+
+
 def test_workspace_size_formula():
     m = model()
     a = tkv.tkv_decode_workspace_bytes(m, 1, 2, 256, 256)

@@ -36,6 +36,13 @@ def test_small_gqa4_lockstep():
     assert st["reassignments"] == 3
 
 
+def test_small_separate_append_call():
+    # tkv_append then tkv_decode_step (the other tests use tkv_append_decode_step)
+    wl = WORKLOADS["small"].scaled(warmup=8, steps=72)
+    st = run_lockstep(wl, fused_append=False, label="small_separate_append")
+    assert st["reassignments"] == 1
+
+
 def test_small_standalone_score_update():
     # the score update as its own call (tkv_update_scores on the normalised alpha)
     wl = WORKLOADS["small"].scaled(warmup=8, steps=72)

@@ -240,13 +240,29 @@ size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t
   return w.total * sizeof(float);
 }
 
-tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
-                           int32_t layer_end, const void* q, const void* k_t0, const void* v_t0,
-                           const int32_t* t0_len, int32_t cap0, const void* k_t1,
-                           const void* v_t1, const int32_t* t1_len, int32_t cap1, float* out,
-                           float* alpha, int32_t alpha_stride, const int32_t* t0_pos,
-                           const int32_t* t1_pos, float* scores, int32_t max_ctx,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace tkv {
+
+// The token each sequence appends in this call (tkv_append_decode_step).
+struct AppendInfo {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* position;  // host [B]
+  int32_t* t0_pos;
+  uint8_t* tier;
+};
+
+// tkv_decode_step; with `app`, t0_len are the lengths before the append and the
+// attention kernel performs the append (bf16; the float32 path appends first).
+static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                              int32_t layer_end, const void* q, const void* k_t0,
+                              const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                              const void* k_t1, const void* v_t1, const int32_t* t1_len,
+                              int32_t cap1, float* out, float* alpha, int32_t alpha_stride,
+                              const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
+                              int32_t max_ctx, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const AppendInfo* app) {
   tkv_status st = check_model(model);
   if (st) return st;
   if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
@@ -258,12 +274,25 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   if (cap0 < 0 || cap1 < 0 || alpha_stride < 1) return fail(TKV_ERR_ARG, "bad capacity or stride");
   if (cap0 % 32 || cap1 % 32) return fail(TKV_ERR_ARG, "cap0 and cap1 must be multiples of 32");
   bool any_t1 = false;
+  const int grow = app ? 1 : 0;  // T0 rows added by the append
   for (int b = 0; b < batch; ++b) {
     if (t0_len[b] < 0 || t1_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
-    if (t0_len[b] > cap0 || t1_len[b] > cap1) return fail(TKV_ERR_CAPACITY, "length > capacity");
-    if ((long)t0_len[b] + t1_len[b] > alpha_stride)
+    if (t0_len[b] + grow > cap0 || t1_len[b] > cap1)
+      return fail(TKV_ERR_CAPACITY, "length > capacity");
+    if ((long)t0_len[b] + grow + t1_len[b] > alpha_stride)
       return fail(TKV_ERR_CAPACITY, "alpha_stride < t0_len + t1_len");
     any_t1 |= t1_len[b] > 0;
+  }
+  if (app) {
+    if (layer_begin != 0 || layer_end != model->num_layers)
+      return fail(TKV_ERR_ARG, "the fused append needs all layers");
+    if (!app->k_new || !app->v_new || !app->position || !app->t0_pos)
+      return fail(TKV_ERR_ARG, "null pointer");
+    for (int b = 0; b < batch; ++b) {
+      if (app->position[b] < 0) return fail(TKV_ERR_ARG, "negative position");
+      if ((scores || app->tier) && app->position[b] >= max_ctx)
+        return fail(TKV_ERR_CAPACITY, "position >= max_ctx");
+    }
   }
   if (any_t1 && (!k_t1 || !v_t1)) return fail(TKV_ERR_ARG, "T1 window is null but t1_len > 0");
   if (scores && (!t0_pos || (any_t1 && !t1_pos) || max_ctx < 1))
@@ -280,6 +309,18 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   const int D = model->head_dim;
   const int G = hq / hkv;
   const bool mfma = model->kv_dtype == TKV_BF16;
+  std::vector<int32_t> len_after;
+  if (app) {
+    len_after.assign(t0_len, t0_len + batch);
+    for (auto& n : len_after) ++n;
+    if (!mfma) {  // float32 path: the separate append kernel first
+      if ((st = tkv_append(model, batch, app->k_new, app->v_new, const_cast<void*>(k_t0),
+                           const_cast<void*>(v_t0), cap0, t0_len, app->t0_pos, app->position,
+                           scores, app->tier, max_ctx, stream)))
+        return st;
+    }
+  }
+  const int32_t* att_len = app ? len_after.data() : t0_len;  // attended T0 rows
   const int unit = mfma ? kUnitMfma : kUnitValu;
   const DecodeWorkspace wl = decode_workspace(model, batch, Lr, cap0, cap1);
   float* part = (float*)workspace + wl.part;
@@ -325,8 +366,20 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     ScoreArgs sa{};
     long units = 0;
     int cblocks = 0, sblocks = 0;
+    if (app && mfma) {
+      a.kn = app->k_new;
+      a.vn = app->v_new;
+      a.app_t0_pos = app->t0_pos;
+      a.app_scores = scores;
+      a.app_tier = app->tier;
+      a.app_max_ctx = max_ctx;
+      for (int i = 0; i < nb; ++i) {
+        a.app_slot[i] = t0_len[b0 + i];
+        a.app_pos[i] = app->position[b0 + i];
+      }
+    }
     for (int i = 0; i < nb; ++i) {
-      const int n0 = t0_len[b0 + i], n1 = t1_len[b0 + i];
+      const int n0 = att_len[b0 + i], n1 = t1_len[b0 + i];
       a.seq.t0_len[i] = n0;
       a.seq.t1_len[i] = n1;
       a.seq.base[i] = (int)units;
@@ -387,6 +440,37 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
     }
   }
   return TKV_OK;
+}
+
+}  // namespace tkv
+
+extern "C" {
+
+tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                           int32_t layer_end, const void* q, const void* k_t0, const void* v_t0,
+                           const int32_t* t0_len, int32_t cap0, const void* k_t1,
+                           const void* v_t1, const int32_t* t1_len, int32_t cap1, float* out,
+                           float* alpha, int32_t alpha_stride, const int32_t* t0_pos,
+                           const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1,
+                     v_t1, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
+                     max_ctx, workspace, workspace_bytes, stream, nullptr);
+}
+
+tkv_status tkv_append_decode_step(const tkv_model* model, int32_t batch, const void* k_new,
+                                  const void* v_new, const int32_t* position, uint8_t* tier,
+                                  const void* q, void* k_t0, void* v_t0, const int32_t* t0_len,
+                                  int32_t cap0, const void* k_t1, const void* v_t1,
+                                  const int32_t* t1_len, int32_t cap1, float* out, float* alpha,
+                                  int32_t alpha_stride, int32_t* t0_pos, const int32_t* t1_pos,
+                                  float* scores, int32_t max_ctx, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (!model) return fail(TKV_ERR_ARG, "model is null");
+  const AppendInfo app{k_new, v_new, position, t0_pos, tier};
+  return decode_step(model, batch, 0, model->num_layers, q, k_t0, v_t0, t0_len, cap0, k_t1, v_t1,
+                     t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores, max_ctx,
+                     workspace, workspace_bytes, stream, &app);
 }
 
 tkv_status tkv_update_scores(const tkv_model* model, int32_t batch, int32_t layer_begin,

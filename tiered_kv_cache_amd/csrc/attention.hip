@@ -262,10 +262,88 @@ __device__ __forceinline__ void issue_v(const AttnArgs& a, const Cursor& c, int 
   for (int nb = 0; nb < NB; ++nb) L.v[nb] = Vu[nb * 64 + lane];
 }
 
-// Loads of one unit: with K-tiles and V-tiles every operand is one contiguous
-// 1 KB wave access at lane offset kb*64 + lane (K) or nb*64 + lane (V).  The
-// 32-slot block is always inside the allocation (capacities are multiples of
-// 32); slots past the segment end are masked when consumed.
+// Append fused into the attention launch: the wave that owns the T0 unit holding
+// a sequence's new slot writes the new key/value rows of that (layer, KV head)
+// into the pool; only that wave reads the unit.  The rows are fetched first, the
+// wave's first unit is requested, and only then are the rows stored (the store
+// waits for the fetch, not for the unit), so the stream starts without a bubble.
+// A wave reads the stored rows with later instructions of its own (in order for
+// the same wave), except when the appended unit is its very first unit: then the
+// rows are stored before that unit is requested.  The wave of layer 0 / KV head
+// 0 also records the token's position, score 0 and tier T0.
+struct AppendRow {
+  long blk;     // element offset of the 32-slot pool block
+  long row;     // element offset of the new row in k_new / v_new
+  int rn;       // slot within the block
+  int bl, lgl;  // sequence within the launch; layer * Hkv + KV head
+};
+
+// The appended row in this wave's unit range (a range holds at most one T0 tail
+// unit per group; the first one is taken, the others are written at once).
+template <int D>
+__device__ bool find_append(const AttnArgs& a, long p0, long p1, int lane, AppendRow& r,
+                            long& pu_first) {
+  const int per_seq = a.Lr * a.hkv;
+  const Cursor first = cursor_at(a, p0);
+  const Cursor last = cursor_at(a, p1 - 1);
+  const long g0 = (long)first.bl * per_seq + first.lgl;
+  const long g1 = (long)last.bl * per_seq + last.lgl;
+  bool found = false;
+  for (long g = g0; g <= g1; ++g) {
+    const int bl = (int)(g / per_seq);
+    const int lgl = (int)(g - (long)bl * per_seq);
+    const int per = a.seq.units[bl];
+    if (per == 0) continue;
+    const int slot = a.app_slot[bl];
+    const long pu = a.seq.base[bl] + (long)lgl * per + slot / kUnitMfma;  // unit holding it
+    if (pu < p0 || pu >= p1) continue;
+    const long b = a.seq.b_offset + bl;
+    const int lr = lgl / a.hkv, gk = lgl - lr * a.hkv;
+    AppendRow x;
+    x.row = ((b * a.L + a.layer_begin + lr) * a.hkv + gk) * (long)D;
+    x.blk = x.row * a.cap0 + (long)(slot & ~(kUnitMfma - 1)) * D;
+    x.rn = slot & (kUnitMfma - 1);
+    x.bl = bl;
+    x.lgl = lgl;
+    if (!found) {
+      r = x;
+      pu_first = pu;
+      found = true;
+    } else {  // more than one (short segments): write it now, blocking
+      const uint16_t* kn = (const uint16_t*)a.kn + x.row;
+      const uint16_t* vn = (const uint16_t*)a.vn + x.row;
+      if (lane < D / 8)
+        *reinterpret_cast<uint4*>((uint16_t*)a.k0 + x.blk + k_off(x.rn, 8 * lane, D)) =
+            *reinterpret_cast<const uint4*>(kn + 8 * lane);
+#pragma unroll
+      for (int d = lane; d < D; d += 64) ((uint16_t*)a.v0)[x.blk + v_off(x.rn, d, D)] = vn[d];
+      if (lgl == 0 && lane == 0) {
+        const int pos = a.app_pos[bl];
+        a.app_t0_pos[b * a.cap0 + slot] = pos;
+        if (a.app_scores) a.app_scores[b * a.app_max_ctx + pos] = 0.f;
+        if (a.app_tier) a.app_tier[b * a.app_max_ctx + pos] = 0;
+      }
+    }
+  }
+  return found;
+}
+
+template <int D>
+__device__ __forceinline__ void store_append(const AttnArgs& a, const AppendRow& r, int lane,
+                                             const uint4& kx, const uint16_t (&vx)[D / 64]) {
+  if (lane < D / 8)
+    *reinterpret_cast<uint4*>((uint16_t*)a.k0 + r.blk + k_off(r.rn, 8 * lane, D)) = kx;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) ((uint16_t*)a.v0)[r.blk + v_off(r.rn, lane + 64 * i, D)] = vx[i];
+  if (r.lgl == 0 && lane == 0) {
+    const long b = a.seq.b_offset + r.bl;
+    const int pos = a.app_pos[r.bl];
+    a.app_t0_pos[b * a.cap0 + a.app_slot[r.bl]] = pos;
+    if (a.app_scores) a.app_scores[b * a.app_max_ctx + pos] = 0.f;
+    if (a.app_tier) a.app_tier[b * a.app_max_ctx + pos] = 0;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, int lane,
                                             UnitLoads<D>& L) {
@@ -358,25 +436,6 @@ __device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, in
   }
 }
 
-template <int D, bool FULL>
-__device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
-                                        int h, int grp, int G, WaveState<D>& st, Stage& sg) {
-  bf16x8_t phi, plo;
-  unit_scores<D, FULL>(a, c, L, h, grp, G, st, sg, phi, plo);
-  unit_values<D, FULL>(c, L, grp, phi, plo, st);
-}
-
-// Prefetch scheme of the matrix-core kernel:
-//  2 (default): rolling -- the next unit's keys are loaded as soon as Q.K of the
-//     current unit has consumed the key registers, its values as soon as P.V has
-//     consumed the value registers; one register buffer, and a unit's worth of
-//     loads stays in flight while the wave computes;
-//  1: two register buffers (next unit loaded before the current is computed;
-//     more registers, fewer waves per SIMD);
-//  0: load and compute one unit at a time.
-#ifndef TKV_MFMA_PIPELINE
-#define TKV_MFMA_PIPELINE 2
-#endif
 // Minimum workgroups per CU the compiler must fit (register budget).
 #ifndef TKV_MFMA_MIN_BLOCKS
 #define TKV_MFMA_MIN_BLOCKS 2
@@ -384,20 +443,6 @@ __device__ __forceinline__ void consume(const AttnArgs& a, const Cursor& c, Unit
 
 __device__ __forceinline__ bool unit_full(const Cursor& c) {
   return c.c0 + kUnitMfma <= (c.seg ? c.n1 : c.n0);
-}
-
-template <int D>
-__device__ __forceinline__ void step_unit(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
-                                          long w, int h, int grp, int G, WaveState<D>& st,
-                                          Stage& sg) {
-  const long group = (long)c.bl * a.Lr * a.hkv + c.lgl;
-  if (group != st.group) {
-    flush_record<D>(a, w, h, grp, G, st);
-    begin_group<D>(a, c, h, grp, G, st);
-  }
-  if (sg.n == sg.cap) flush_stage(a, grp * 16 + h, G, sg);
-  if (unit_full(c)) consume<D, true>(a, c, L, h, grp, G, st, sg);
-  else consume<D, false>(a, c, L, h, grp, G, st, sg);
 }
 
 template <int D>
@@ -424,12 +469,29 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
   sg.count = stage_cnt[wv];
   sg.n = 0;
   sg.cap = min(kStageUnits, kStageFloats / (32 * G));
+  AppendRow ar;
+  long pu = -1;
+  const bool app = a.kn && find_append<D>(a, p0, p1, lane, ar, pu);
+  uint4 kx = make_uint4(0, 0, 0, 0);
+  uint16_t vx[D / 64];
+  if (app) {  // fetch the new rows
+    if (lane < D / 8) kx = *reinterpret_cast<const uint4*>((const uint16_t*)a.kn + ar.row + 8 * lane);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vx[i] = ((const uint16_t*)a.vn)[ar.row + lane + 64 * i];
+    if (pu == p0) {  // the first unit is the appended one: in place before it is requested
+      store_append<D>(a, ar, lane, kx, vx);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
   WaveState<D> st;
   Cursor c = cursor_at(a, p0);
   begin_group<D>(a, c, h, grp, G, st);
-#if TKV_MFMA_PIPELINE == 2
+  // Rolling prefetch: the next unit's keys are requested as soon as Q.K of this
+  // unit has consumed the key registers, its values as soon as P.V has consumed
+  // the value registers, so a unit's worth of loads stays in flight.
   UnitLoads<D> L;
   issue_loads<D>(a, c, lane, L);
+  if (app && pu != p0) store_append<D>(a, ar, lane, kx, vx);  // read back units later
   for (long p = p0; p < p1; ++p) {
     const bool more = p + 1 < p1;
     Cursor cn = c;
@@ -450,31 +512,6 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
     if (more) issue_v<D>(a, cn, lane, L);
     c = cn;
   }
-#elif TKV_MFMA_PIPELINE == 1
-  UnitLoads<D> A, B;
-  issue_loads<D>(a, c, lane, A);
-  for (long p = p0; p < p1; p += 2) {
-    Cursor cb = c;
-    cursor_next(a, cb);
-    const bool more_b = p + 1 < p1;
-    if (more_b) issue_loads<D>(a, cb, lane, B);
-    step_unit<D>(a, c, A, w, h, grp, G, st, sg);
-    if (!more_b) break;
-    c = cb;
-    cursor_next(a, c);
-    const bool more_a = p + 2 < p1;
-    if (more_a) issue_loads<D>(a, c, lane, A);
-    step_unit<D>(a, cb, B, w, h, grp, G, st, sg);
-    if (!more_a) break;
-  }
-#else
-  UnitLoads<D> A;
-  for (long p = p0; p < p1; ++p) {
-    issue_loads<D>(a, c, lane, A);
-    step_unit<D>(a, c, A, w, h, grp, G, st, sg);
-    cursor_next(a, c);
-  }
-#endif
   flush_record<D>(a, w, h, grp, G, st);
   flush_stage(a, lane, G, sg);
 }

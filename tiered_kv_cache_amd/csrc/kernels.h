@@ -50,6 +50,17 @@ struct AttnArgs {
   int L, Lr, layer_begin, hq, hkv;
   float scale;       // softmax_scale * log2(e): logits are kept in base 2
   SeqTable seq;
+  // append fused into the bf16 kernel (kn null: none).  The new row of sequence i
+  // sits at T0 slot app_slot[i] (< seq.t0_len[i]); the kernel reads it from kn/vn
+  // ([B][L][Hkv][D]), writes it into the pool, and records its position.
+  const void* kn;
+  const void* vn;
+  int* app_t0_pos;
+  float* app_scores;
+  uint8_t* app_tier;
+  int app_max_ctx;
+  int app_slot[kMaxSeqPerLaunch];
+  int app_pos[kMaxSeqPerLaunch];
 };
 
 // Score accumulation: s[pos(j)] += weight * sum over r of src[r][j], for the

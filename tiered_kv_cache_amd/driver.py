@@ -166,6 +166,7 @@ class TieredKVCache:
         self.t2_new = [0] * B   # rows quantised at the last reassignment
         self.steps = 0
         self.fused_scores = True
+        self.fused_append = True   # step(): tkv_append_decode_step rather than the two calls
 
     # ---- views -------------------------------------------------------------
     @property
@@ -253,11 +254,29 @@ class TieredKVCache:
                                   self.t1_pos, self.t1_len, self.cap1, self.scores,
                                   self.max_ctx, stream)
 
+    def append_attend(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      stream=None) -> None:
+        """append() then attend() over all layers, as one pass (tkv_append_decode_step)."""
+        if not self.fused_scores:
+            self.append(k_new, v_new, stream)
+            self.attend(q, stream)
+            return
+        tkv.tkv_append_decode_step(self.model, self.batch, k_new, v_new, self.n, self.tiers, q,
+                                   self.k_t0, self.v_t0, self.t0_len, self.cap0, self.k_t1,
+                                   self.v_t1, self.t1_len, self.cap1, self.out, self.alpha,
+                                   self.alpha_stride, self.t0_pos, self.t1_pos, self.scores,
+                                   self.max_ctx, self.ws, self.ws_bytes, stream)
+        self.n = [x + 1 for x in self.n]
+        self.t0_len = [x + 1 for x in self.t0_len]
+
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None,
              reassign: bool = True) -> bool:
         """One decode step; returns True when it ended with a reassignment."""
-        self.append(k_new, v_new, stream)
-        self.attend(q, stream)
+        if self.fused_append:
+            self.append_attend(q, k_new, v_new, stream)
+        else:
+            self.append(k_new, v_new, stream)
+            self.attend(q, stream)
         self.steps += 1
         if reassign and self.steps % self.policy.delta == 0:
             self.reassign(stream)
