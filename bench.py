@@ -210,15 +210,16 @@ def main():
     contexts = [st.context() for st in dw.streams]
     inputs = dw.preload(1, wl.total_steps)
 
-    def run(timed_kernels):
+    def run(timed_kernels, every=1):
         """Fresh cache, W warm-up steps, then exactly K steps between two syncs with the
-        kernel timers on for `timed_kernels` (None = all)."""
+        kernel timers on for `timed_kernels` (None = all) on every `every`-th step (each
+        pair of events adds a few microseconds around the launch it brackets)."""
         cache = dw.make_cache(contexts=contexts)
         torch.cuda.synchronize()
         for k in range(1, args.warmup + 1):
             cache.step(*inputs[k - 1])
         torch.cuda.synchronize()
-        n_att, n_all, re = [], [], []
+        n_att, n_all, re, sampled = [], [], [], []
         tkv.tkv_timing_select(timed_kernels)
         tkv.tkv_timing_reset()
         tkv.tkv_timing_enable(True)
@@ -227,6 +228,11 @@ def main():
         for k in range(args.warmup + 1, args.warmup + args.steps + 1):
             n_att.append(sum(cache.t0_len) + sum(cache.t1_len) + wl.batch)
             n_all.append(sum(cache.n) + wl.batch)
+            if every > 1:
+                on = (k - args.warmup - 1) % every == 0
+                tkv.tkv_timing_enable(on)
+                if on:
+                    sampled.append(n_att[-1])
             if cache.step(*inputs[k - 1]):
                 re.append((sum(cache.n), sum(cache.t0_len), sum(cache.t1_len), sum(cache.t2_new)))
         torch.cuda.synchronize()
@@ -239,24 +245,25 @@ def main():
             if cnt:
                 kernels[name] = {"launches": cnt, "avg_us": ms * 1e3 / cnt, "total_ms": ms}
         tkv.tkv_timing_select(None)
-        return cache, elapsed, n_att, n_all, re, kernels
+        return cache, elapsed, n_att, n_all, re, kernels, (sampled or n_att)
 
     # the measured run: only the reported kernel carries timers
     print(f"[bench] warm-up {args.warmup} steps, {args.steps} timed steps", file=sys.stderr,
           flush=True)
-    cache, elapsed, n_att_steps, n_steps, re_info, timed = run(["attn_partial"])
+    cache, elapsed, n_att_steps, n_steps, re_info, timed, n_att_timed = run(["attn_partial"],
+                                                                             every=8)
     del cache
     torch.cuda.empty_cache()
     # a second, identical run with every kernel timed (the per-kernel breakdown only)
     print("[bench] breakdown run", file=sys.stderr, flush=True)
-    cache, elapsed_bd, _, _, _, kernels = run(None)
+    cache, elapsed_bd, _, _, _, kernels, _ = run(None)
 
     steps_per_s = args.steps / elapsed
     step_b = [step_bytes(wl, n_att, n)["total"] for n_att, n in zip(n_att_steps, n_steps)]
     re_b = sum(reassign_bytes(wl, *r) for r in re_info)
     alg_bytes = (sum(step_b) + re_b) / args.steps
     attn = timed.get("attn_partial", {"launches": 1, "avg_us": float("nan"), "total_ms": float("nan")})
-    attn_bytes = float(np.mean([attn_partial_bytes(wl, n) for n in n_att_steps]))
+    attn_bytes = float(np.mean([attn_partial_bytes(wl, n) for n in n_att_timed]))
     achieved = attn_bytes / (attn["avg_us"] * 1e-6) / 1e9
 
     out = {
@@ -291,7 +298,7 @@ def main():
         "kernels_note": ("per-kernel averages from a second identical run with every kernel "
                          "timed (events between launches slow that run to "
                          f"{args.steps / elapsed_bd:.0f} steps/s); value and roofline come "
-                         "from the run that times attn_partial only"),
+                         "from the run that times attn_partial only, on every 8th step"),
     }
     if not args.no_pcie:
         try:
