@@ -334,7 +334,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
       const char* e = getenv("TKV_ATTN_WORKERS");
       return e ? atoi(e) : 0;
     }();
-    if (override_workers > 0) resident = std::min(override_workers, resident);
+    if (override_workers > 0) resident = std::min(override_workers, kMaxWorkers);
   }
 
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
