@@ -50,6 +50,20 @@ def test_small_standalone_score_update():
     assert st["reassignments"] == 1
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(16, 1, 128), (4, 4, 64), (6, 2, 128), (8, 1, 64)],
+                         ids=["group16_d128", "mha_d64", "group3_d128", "group8_d64"])
+def test_head_groupings_lockstep(hq, hkv, d):
+    # every query-head grouping the matrix-core kernel supports shape-wise: 1, 3, 8, 16
+    # query heads per KV head, both head sizes, a ragged pair of sequences
+    base = WORKLOADS["small"]
+    wl = base.scaled(name=f"groups_h{hq}kv{hkv}_d{d}", layers=2, q_heads=hq, kv_heads=hkv,
+                     head_dim=d, batch=2, ctx=(190, 333), warmup=4, steps=8, delta=4, prompt=8,
+                     recent=8, sinks=2, planted=(3, 5), frac_t1=0.3, frac_t2=0.15,
+                     frac_t3=0.05)
+    st = run_lockstep(wl)
+    assert st["reassignments"] == 3 * 2
+
+
 def test_ragged_batch_d64_lockstep():
     base = WORKLOADS["small"]
     wl = base.scaled(name="ragged5_L2_h8kv2_d64", layers=2, head_dim=64, batch=5,
