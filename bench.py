@@ -33,6 +33,8 @@ def parse():
     p.add_argument("--workload", default="chain8k")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-pcie", action="store_true")
+    p.add_argument("--no-flush-run", action="store_true",
+                   help="skip the run that reads a 512 MB buffer before every step")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's timed CPU work")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -210,10 +212,13 @@ def main():
     contexts = [st.context() for st in dw.streams]
     inputs = dw.preload(1, wl.total_steps)
 
-    def run(timed_kernels, every=1):
+    flush_buf = None
+
+    def run(timed_kernels, every=1, flush=False):
         """Fresh cache, W warm-up steps, then exactly K steps between two syncs with the
         kernel timers on for `timed_kernels` (None = all) on every `every`-th step (each
-        pair of events adds a few microseconds around the launch it brackets)."""
+        pair of events adds a few microseconds around the launch it brackets).  With
+        `flush`, a 512 MB buffer is read before every step (outside the kernel timers)."""
         cache = dw.make_cache(contexts=contexts)
         torch.cuda.synchronize()
         for k in range(1, args.warmup + 1):
@@ -228,6 +233,8 @@ def main():
         for k in range(args.warmup + 1, args.warmup + args.steps + 1):
             n_att.append(sum(cache.t0_len) + sum(cache.t1_len) + wl.batch)
             n_all.append(sum(cache.n) + wl.batch)
+            if flush:
+                flush_buf.sum()
             if every > 1:
                 on = (k - args.warmup - 1) % every == 0
                 tkv.tkv_timing_enable(on)
@@ -300,6 +307,23 @@ def main():
                          f"{args.steps / elapsed_bd:.0f} steps/s); value and roofline come "
                          "from the run that times attn_partial only, on every 8th step"),
     }
+    if not args.no_flush_run:
+        # a real decode streams the model weights between two visits of a layer, which
+        # evicts the memory-side cache: the same steps with 512 MB read before each one
+        del cache
+        torch.cuda.empty_cache()
+        print("[bench] cache-flushed run", file=sys.stderr, flush=True)
+        flush_buf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        cache, elapsed_fl, _, _, _, fl_kernels, fl_att = run(["attn_partial"], flush=True)
+        fa = fl_kernels.get("attn_partial")
+        if fa:
+            fb = float(np.mean([attn_partial_bytes(wl, n) for n in fl_att]))
+            out["flushed"] = {"attn_partial_avg_us": fa["avg_us"],
+                              "achieved_gbps": fb / (fa["avg_us"] * 1e-6) / 1e9,
+                              "frac": fb / (fa["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                              "note": "512 MB read before every step (memory-side cache "
+                                      "cold, as after a model's weight stream)"}
+        del flush_buf
     if not args.no_pcie:
         try:
             t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()
