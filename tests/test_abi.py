@@ -189,3 +189,31 @@ def test_gather_host_pack_without_device():
     for r in range(len(pos), 8):                 # the rest of the last value panel is cleared
         vo = [((d // 16) * 4 + r // 8) * 128 + (d % 16) * 8 + r % 8 for d in range(64)]
         assert not sv.reshape(2, 2, -1)[:, :, vo].any()
+
+
+def test_gather_host_pack_blocks_d128():
+    # several 32-slot blocks with a ragged last one, head_dim 128: every staged element
+    # against the element-wise storage order, padding slots zero
+    m = model(layers=3, kv_heads=2, q_heads=4, head_dim=128)
+    r = np.random.default_rng(1)
+    max_ctx, cap1, D = 300, 96, 128
+    hk = r.integers(0, 65535, size=(3, 2, max_ctx, D)).astype(np.uint16)
+    hv = r.integers(0, 65535, size=(3, 2, max_ctx, D)).astype(np.uint16)
+    sk = np.full((3, 2, cap1, D), 7, np.uint16)
+    sv = np.full((3, 2, cap1, D), 7, np.uint16)
+    pos = sorted(r.choice(max_ctx, 77, replace=False).tolist())
+    tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), sk, sv, cap1)
+    n = len(pos)
+    slots = np.arange(96)[:, None]
+    d = np.arange(D)[None, :]
+    rr = slots % 32
+    ko = (slots // 32) * 32 * D + ((rr // 4) % 2) * 16 * D + ((d // 8) * 16 + 4 * (rr // 8) + rr % 4) * 8 + d % 8
+    vo = (slots // 32) * 32 * D + ((d // 16) * 4 + rr // 8) * 128 + (d % 16) * 8 + rr % 8
+    exp_k = np.zeros((3, 2, 96, D), np.uint16)
+    exp_v = np.zeros((3, 2, 96, D), np.uint16)
+    exp_k[:, :, :n] = hk[:, :, pos]
+    exp_v[:, :, :n] = hv[:, :, pos]
+    got_k = sk.reshape(3, 2, -1)[:, :, ko]
+    got_v = sv.reshape(3, 2, -1)[:, :, vo]
+    assert np.array_equal(got_k, exp_k)
+    assert np.array_equal(got_v, exp_v)

@@ -7,6 +7,7 @@
 // writes the rows in the device window's storage order (K-tiles, V-tiles) so the
 // copy is one strided 2D transfer per tensor, served by the DMA engines from
 // pinned memory.
+#include <emmintrin.h>
 #include <sched.h>
 #include <string.h>
 
@@ -26,6 +27,45 @@ int pack_threads() {
   if (sched_getaffinity(0, sizeof(set), &set) == 0) n = CPU_COUNT(&set);
   if (n <= 0) n = (int)std::thread::hardware_concurrency();
   return std::max(1, std::min(n, 16));
+}
+
+// One 8-slot value panel group: dims [dg, dg + 16) of 8 source rows, written as
+// 16 dimensions x 8 slots (256 contiguous bytes).  bf16: an SSE2 8x8 transpose of
+// 16-bit lanes, twice; other element types: element by element.
+template <typename E>
+inline void panel16(E* out, const E* const* rows, int nr, int dg) {
+  for (int d = 0; d < 16; ++d) {
+    E vals[8];
+    for (int e = 0; e < 8; ++e) vals[e] = e < nr ? rows[e][dg + d] : E(0);
+    memcpy(out + d * 8, vals, sizeof(vals));
+  }
+}
+
+template <>
+inline void panel16<uint16_t>(uint16_t* out, const uint16_t* const* rows, int nr, int dg) {
+  for (int half = 0; half < 2; ++half) {
+    __m128i a[8];
+    for (int e = 0; e < 8; ++e)
+      a[e] = e < nr ? _mm_loadu_si128(reinterpret_cast<const __m128i*>(rows[e] + dg + 8 * half))
+                    : _mm_setzero_si128();
+    const __m128i t0 = _mm_unpacklo_epi16(a[0], a[1]), t1 = _mm_unpackhi_epi16(a[0], a[1]);
+    const __m128i t2 = _mm_unpacklo_epi16(a[2], a[3]), t3 = _mm_unpackhi_epi16(a[2], a[3]);
+    const __m128i t4 = _mm_unpacklo_epi16(a[4], a[5]), t5 = _mm_unpackhi_epi16(a[4], a[5]);
+    const __m128i t6 = _mm_unpacklo_epi16(a[6], a[7]), t7 = _mm_unpackhi_epi16(a[6], a[7]);
+    const __m128i u0 = _mm_unpacklo_epi32(t0, t2), u1 = _mm_unpackhi_epi32(t0, t2);
+    const __m128i u2 = _mm_unpacklo_epi32(t1, t3), u3 = _mm_unpackhi_epi32(t1, t3);
+    const __m128i u4 = _mm_unpacklo_epi32(t4, t6), u5 = _mm_unpackhi_epi32(t4, t6);
+    const __m128i u6 = _mm_unpacklo_epi32(t5, t7), u7 = _mm_unpackhi_epi32(t5, t7);
+    __m128i* o = reinterpret_cast<__m128i*>(out + 64 * half);  // dims 8 half + 0..7
+    _mm_storeu_si128(o + 0, _mm_unpacklo_epi64(u0, u4));
+    _mm_storeu_si128(o + 1, _mm_unpackhi_epi64(u0, u4));
+    _mm_storeu_si128(o + 2, _mm_unpacklo_epi64(u1, u5));
+    _mm_storeu_si128(o + 3, _mm_unpackhi_epi64(u1, u5));
+    _mm_storeu_si128(o + 4, _mm_unpacklo_epi64(u2, u6));
+    _mm_storeu_si128(o + 5, _mm_unpackhi_epi64(u2, u6));
+    _mm_storeu_si128(o + 6, _mm_unpacklo_epi64(u3, u7));
+    _mm_storeu_si128(o + 7, _mm_unpackhi_epi64(u3, u7));
+  }
 }
 
 }  // namespace
@@ -64,38 +104,42 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
   const int D = model->head_dim;
   const long nblocks = (n_t1 + 31) / 32;  // 32-slot blocks of the tile layouts
   if (positions && n_t1 > 0) {
-    const long krows = lgs * n_t1;
-    const long vpanels = lgs * nblocks * 4;
-    const long total = krows + vpanels * 8;  // work units: K rows, then V panels (8 rows each)
-    const int nt = (int)std::min<long>(pack_threads(), std::max<long>(1, total / 2048));
+    // Work item: one 32-slot block of one (layer, KV head), keys and values.  Both
+    // are written in storage order -- a K-tile as [tile][chunk][16 rows] of 8-element
+    // chunks, a V-tile as [dim group][panel][16 dims] of 8-slot panels -- so the
+    // staging stores are sequential and the 32 source rows stay in the L1 cache.
+    const long total = lgs * nblocks;
+    const int nt = (int)std::min<long>(pack_threads(), std::max<long>(1, total / 16));
     auto pack = [&](auto* sk_base, auto* sv_base, const auto* hk_base, const auto* hv_base,
                     long lo, long hi) {
       using E = std::remove_const_t<std::remove_pointer_t<decltype(hk_base)>>;
-      // K rows in [0, krows): 8-element chunks to their K-tile places
-      for (long i = lo; i < std::min(hi, krows); ++i) {
-        const long lg = i / n_t1;
-        const long r = i - lg * n_t1;
-        const E* from = hk_base + ((size_t)lg * max_ctx + positions[r]) * D;
-        E* to = sk_base + (size_t)lg * cap1 * D;
-        for (int c = 0; c < D; c += 8) memcpy(to + k_off(r, c, D), from + c, 8 * sizeof(E));
-      }
-      // V panels: units [krows, total) in steps of 8
-      const long vlo = std::max(lo, krows);
-      if (hi <= vlo) return;
-      const long plo = (vlo - krows + 7) / 8, phi = (hi - krows + 7) / 8;
-      for (long i = plo; i < phi; ++i) {
-        const long lg = i / (nblocks * 4);
-        const long p = i - lg * nblocks * 4;  // panel: slots 8p .. 8p+7
-        E* to = sv_base + (size_t)lg * cap1 * D;
-        for (int e = 0; e < 8; ++e) {
-          const long r = 8 * p + e;
-          if (r < n_t1) {
-            const E* from = hv_base + ((size_t)lg * max_ctx + positions[r]) * D;
-            for (int d = 0; d < D; ++d) to[v_off(r, d, D)] = from[d];
-          } else {
-            for (int d = 0; d < D; ++d) to[v_off(r, d, D)] = E(0);
-          }
+      const E* rk[32];
+      const E* rv[32];
+      for (long it = lo; it < hi; ++it) {
+        const long lg = it / nblocks;
+        const long blk = it - lg * nblocks;
+        const long r0 = blk * 32;
+        const int nr = (int)std::min<long>(32, n_t1 - r0);
+        for (int i = 0; i < nr; ++i) {
+          const size_t src = ((size_t)lg * max_ctx + positions[r0 + i]) * D;
+          rk[i] = hk_base + src;
+          rv[i] = hv_base + src;
         }
+        E* tk = sk_base + ((size_t)lg * cap1 + r0) * D;
+        E* tv = sv_base + ((size_t)lg * cap1 + r0) * D;
+        // keys: slot r = 8j + 4u + i is row 4j + i of tile u
+        for (int u = 0; u < 2; ++u)
+          for (int c = 0; c < D; c += 8)
+            for (int row = 0; row < 16; ++row) {
+              const int r = ((row >> 2) << 3) + 4 * u + (row & 3);
+              E* to = tk + k_off(r, c, D);
+              if (r < nr) memcpy(to, rk[r] + c, 8 * sizeof(E));
+              else memset(to, 0, 8 * sizeof(E));
+            }
+        // values: the 8 slots of a panel for one dimension are contiguous
+        for (int dg = 0; dg < D; dg += 16)
+          for (int pn = 0; pn < 4; ++pn)
+            panel16<E>(tv + v_off(8 * pn, dg, D), rv + 8 * pn, nr - 8 * pn, dg);
       }
     };
     auto work = [&](int t) {
