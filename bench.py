@@ -65,12 +65,14 @@ def attn_partial_bytes(wl, n_att: int) -> int:
     return 2 * L * Hkv * n_att * D * e + L * Hq * D * e + L * Hq * n_att * 4
 
 
-def reassign_bytes(wl, n: int, n0: int, n1: int, r2: int) -> int:
+def reassign_bytes(wl, n: int, n0: int, n1: int, r2: int, moved: int) -> int:
     """Algorithmic bytes of one reassignment (amortised over Delta steps)."""
     L, Hkv, D = wl.layers, wl.kv_heads, wl.head_dim
     e = 2 if wl.dtype == "bf16" else 4
     tiers = n * (4 + 1 + 1)                    # scores + previous map read, new map write
-    compact = (n0 + n1) * 2 * L * Hkv * D * e * 2 + n * 2
+    # maps: two tier maps and an inverse map over positions, the slot maps;
+    # rows: each copy reads and writes a K and a V row of every (layer, KV head)
+    compact = n * (2 + 8) + (n0 + n1) * 8 + moved * 2 * L * Hkv * D * e * 2
     quant = r2 * L * Hkv * 2 * (D * e + D + 4)
     return tiers + compact + quant
 
@@ -241,13 +243,14 @@ def main():
                 if on:
                     sampled.append(n_att[-1])
             if cache.step(*inputs[k - 1]):
-                re.append((sum(cache.n), sum(cache.t0_len), sum(cache.t1_len), sum(cache.t2_new)))
+                re.append((sum(cache.n), sum(cache.t0_len), sum(cache.t1_len), sum(cache.t2_new),
+                           sum(cache.moved)))
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         tkv.tkv_timing_enable(False)
         kernels = {}
         for name in ("append", "attn_partial", "attn_merge", "score_update", "assign_tiers",
-                     "compact_scan", "compact_copy", "quantize_t2"):
+                     "reloc_scan", "quantize_t2", "reloc_stage", "reloc_to_t1", "reloc_to_t0"):
             ms, cnt = tkv.tkv_timing_read(name)
             if cnt:
                 kernels[name] = {"launches": cnt, "avg_us": ms * 1e3 / cnt, "total_ms": ms}
@@ -326,7 +329,7 @@ def main():
         del flush_buf
     if not args.no_pcie:
         try:
-            t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()
+            t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()   # window slot order
             out["pcie"] = pcie_leg(wl, cache, t1)
             out["pcie"]["note"] = ("host-link path of T1, not part of value: host pack into "
                                    "pinned staging, then hipMemcpy2DAsync on a side stream")

@@ -38,10 +38,12 @@
  *     values (V-tiles): (slot/32)*32*D + ((d/16)*4 + r/8)*128 + (d%16)*8 + r%8.
  *   With it every operand load of the attention kernel is one contiguous
  *   1 KB wave access.  Capacities (cap0, cap1) must be multiples of 32.
- *   Per sequence, the T0 pool holds the T0 positions in ascending order in
- *   slots [0, t0_len) and the T1 window holds the T1 positions in ascending
- *   order in slots [0, t1_len).  The "attended index" j of a sequence runs over
- *   T0 slots then T1 slots: j < t0_len is T0 slot j, otherwise T1 slot
+ *   Per sequence, the T0 pool holds the T0 positions in slots [0, t0_len) and
+ *   the T1 window holds the T1 positions in slots [0, t1_len), in any order:
+ *   the slot -> position maps t0_pos / t1_pos [B][cap] say which position a
+ *   slot holds (an appended token takes slot t0_len; tkv_compact fills the
+ *   holes a reassignment leaves).  The "attended index" j of a sequence runs
+ *   over T0 slots then T1 slots: j < t0_len is T0 slot j, otherwise T1 slot
  *   j - t0_len.
  * - Query head h reads KV head h / (Hq / Hkv) (contiguous grouping).
  * - Supported shapes: head_dim 64 or 128; 1 <= Hq / Hkv <= 16.
@@ -228,46 +230,57 @@ tkv_status tkv_assign_tiers(int32_t batch, const int32_t* ctx_len, int32_t max_c
                             const uint8_t* tier_prev, uint8_t* tier_next, int32_t* counts,
                             hipStream_t stream);
 
-/* Bytes of device workspace tkv_compact needs. */
-size_t tkv_compact_workspace_bytes(int32_t batch, int32_t cap0, int32_t cap1);
+/* Bytes of device workspace tkv_compact needs (0 for an invalid model or a
+ * negative size).  It grows with batch * (max_ctx + cap0 + cap1) words plus a
+ * staging area of batch * cap1 rows of L * Hkv * 2 * D elements. */
+size_t tkv_compact_workspace_bytes(const tkv_model* model, int32_t batch, int32_t max_ctx,
+                                   int32_t cap0, int32_t cap1);
 
 /*
- * tkv_compact -- after a reassignment, rebuild the resident T0 pool and the
- * T1 window in ascending position order from the previous pool and window,
- * and list the positions that newly entered T2 (Methodologie section 4:
- * tiers change every Delta steps; only tokens that change tier move).
- * Positions newly in T3 are simply not copied.  Every new T0/T1 row is found
- * on the device, because T2 and T3 never return to T0/T1.
+ * tkv_compact -- after a reassignment, bring the resident T0 pool and the T1
+ * window in line with the new tier map, in place, and turn the rows that
+ * newly entered T2 into 8-bit rows (Methodologie section 4: tiers change every
+ * Delta steps and only the tokens whose tier changed move; section 1: T2 holds
+ * low-importance tokens at reduced precision).
  *
- * Preconditions: the *_src pools/windows hold exactly the tier_prev T0 / T1
- * positions in ascending order (t0_len_src[b] / t1_len_src[b] of them), and
- * the *_dst buffers do not overlap the *_src ones.
- * ctx_len           : host [B]
- * tier_prev/next    : device [B][max_ctx]
- * k/v_t0_src, t0_len_src (host [B]), cap0 : previous T0 pool [B][L][Hkv][cap0][D]
- * k/v_t1_src, t1_len_src (host [B]), cap1 : previous T1 window [B][L][Hkv][cap1][D]
- *                                           (tiles, here and below)
- * k/v_t0_dst, t0_pos_dst : new T0 pool and its slot -> position map [B][cap0]
- * k/v_t1_dst, t1_pos_dst : new T1 window and its map [B][cap1]
- * t2_src    : device [B][t2_cap]: source of each newly-T2 row, in ascending
- *             position order: s >= 0 is previous T0 slot s, s < 0 is previous
- *             T1 slot -s-1 (the encoding tkv_quantize_t2 reads)
- * t2_pos    : device [B][t2_cap]: their positions
- * new_lens  : device [B][3] int32: new T0 length, new T1 length, newly-T2 count.
- *             If a capacity would be exceeded or the tier maps disagree with
- *             the source lengths (a T2/T3 position marked T0/T1 again, or
- *             counts not matching t0_len_src/t1_len_src), new_lens[b] is
- *             {-1,-1,-1} and the destination contents are unspecified.
+ * Slot order inside the pool and the window is not position order: the slot
+ * -> position maps t0_pos / t1_pos say which position each slot holds.  A row
+ * moves only if its tier changed, or if it stays but sits at or past the new
+ * length of its pool; each mover fills a hole (a slot below the new length
+ * whose row left or which was past the old length), the i-th mover in
+ * position order taking the i-th hole in slot order.  Rows leaving for T3 are
+ * dropped.  Every new T0/T1 row is already resident, because T2 and T3 never
+ * return to T0/T1.  Slots at or past the new lengths keep stale rows.
+ *
+ * ctx_len          : host [B]
+ * tier_prev/next   : device [B][max_ctx] uint8, distinct buffers
+ * k/v_t0, cap0     : T0 pool [B][L][Hkv][cap0][D] (tiles), updated in place
+ * t0_pos           : device [B][cap0] slot -> position, updated in place
+ * t0_len           : host [B] current T0 lengths
+ * k/v_t1, t1_pos, t1_len, cap1 : the T1 window, likewise
+ * t2_src, t2_pos   : device [B][t2_cap]: the old slot code of each newly-T2 row
+ *                    (s >= 0 T0 slot s, s < 0 T1 slot -s-1) and its position,
+ *                    in ascending position order
+ * t2_codes/scales  : device, as tkv_quantize_t2's codes/scales with max_rows =
+ *                    t2_cap; filled for the newly-T2 rows (may be null if
+ *                    t2_cap is 0)
+ * new_lens         : device [B][4] int32: new T0 length, new T1 length,
+ *                    newly-T2 count, row copies made (moves into T1 and T0
+ *                    plus promoted rows staged).  If a capacity would be exceeded or the
+ *                    maps disagree with tier_prev and the lengths (a position
+ *                    without its slot, a slot pointing outside the context,
+ *                    a T2/T3 position marked T0/T1 again), new_lens[b] is
+ *                    {-1,-1,-1,-1} and nothing of sequence b is changed.
+ * workspace        : device, tkv_compact_workspace_bytes() bytes
+ * Calls that overlap on the same buffers race.
  */
 tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
                        int32_t max_ctx, const uint8_t* tier_prev, const uint8_t* tier_next,
-                       const void* k_t0_src, const void* v_t0_src, const int32_t* t0_len_src,
-                       int32_t cap0, const void* k_t1_src, const void* v_t1_src,
-                       const int32_t* t1_len_src, int32_t cap1, void* k_t0_dst,
-                       void* v_t0_dst, int32_t* t0_pos_dst, void* k_t1_dst, void* v_t1_dst,
-                       int32_t* t1_pos_dst, int32_t* t2_src, int32_t* t2_pos, int32_t t2_cap,
-                       int32_t* new_lens, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream);
+                       void* k_t0, void* v_t0, int32_t* t0_pos, const int32_t* t0_len,
+                       int32_t cap0, void* k_t1, void* v_t1, int32_t* t1_pos,
+                       const int32_t* t1_len, int32_t cap1, int32_t* t2_src, int32_t* t2_pos,
+                       int32_t t2_cap, int8_t* t2_codes, float* t2_scales, int32_t* new_lens,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * tkv_quantize_t2 -- 8-bit rows of the tokens that enter T2 (Methodologie
@@ -280,7 +293,7 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
  * k/v_t0, cap0, k/v_t1, cap1 : the pool and window the rows are read from
  * src     : device [B][max_rows]: s >= 0 is T0 slot s, s < 0 is T1 slot -s-1
  * n_rows  : device int32, element b * n_rows_stride is the row count of
- *           sequence b (tkv_compact's new_lens with stride 3, offset 2, fits)
+ *           sequence b (tkv_compact's new_lens with stride 4, offset 2, fits)
  * max_rows: host bound on every row count (rows at or beyond it are ignored)
  * codes   : device [B][max_rows][L][Hkv][2][D] int8 (index 0 = K, 1 = V)
  * scales  : device [B][max_rows][L][Hkv][2] float32
@@ -295,14 +308,16 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
  * tkv_gather_t1 -- bring one sequence's T1 rows to the GPU (Methodologie
  * section 1: T1 stays in host DDR at full precision and is brought to the GPU
  * before each attention step).  Packs the rows of the host store at the given
- * positions, in the given (ascending) order, into contiguous pinned staging
+ * positions, in the given order, into contiguous pinned staging
  * with host threads, then queues the host-to-device copy of the staging on
  * side_stream and records `ready` there.  The attention stream must wait on
  * `ready` before reading the window.
  *
  * host_k, host_v   : host [L][Hkv][max_ctx][D] full-precision store
- * positions        : host [n_t1], strictly ascending, each < max_ctx; null
- *                    re-sends the staging as it is (no pack)
+ * positions        : host [n_t1], distinct, each < max_ctx: window slot i
+ *                    receives positions[i] (pass the window's slot ->
+ *                    position map); null re-sends the staging as it is
+ *                    (no pack)
  * staging_k/v      : pinned host [L][Hkv][cap1][D] tiles (n_t1 <= cap1), written in
  *                    the device window's storage order (value slots past n_t1
  *                    in the last panel are zeroed), so the copy is a plain

@@ -75,8 +75,8 @@ def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, st
     assert counts.tolist() == [int((seq.tier[:n] == t).sum()) for t in range(4)]
     t0 = np.nonzero(seq.tier[:n] == 0)[0]
     assert cache.t0_len[b] == len(t0) and cache.t1_len[b] == len(seq.t1_positions)
-    assert np.array_equal(cache.t0_pos[b, :len(t0)].cpu().numpy(), t0)
-    assert np.array_equal(cache.t1_pos[b, :cache.t1_len[b]].cpu().numpy(), seq.t1_positions)
+    assert np.array_equal(cache.t0_positions(b), t0)
+    assert np.array_equal(cache.t1_positions(b), seq.t1_positions)
     k1, v1 = cache.t1_rows(b)
     assert k1.tobytes() == np.ascontiguousarray(seq.t1_K).tobytes(), "T1 window keys differ"
     assert v1.tobytes() == np.ascontiguousarray(seq.t1_V).tobytes(), "T1 window values differ"
@@ -234,8 +234,8 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                 assert cache.counts[b].cpu().numpy().tolist() == counts.tolist()
                 t0 = np.nonzero(t_ref == 0)[0]
                 t1 = np.nonzero(t_ref == 1)[0]
-                assert np.array_equal(cache.t0_pos[b, :cache.t0_len[b]].cpu().numpy(), t0)
-                assert np.array_equal(cache.t1_pos[b, :cache.t1_len[b]].cpu().numpy(), t1)
+                assert np.array_equal(cache.t0_positions(b), t0)
+                assert np.array_equal(cache.t1_positions(b), t1)
                 stats["reassignments"] += 1
                 if b not in byte_seqs:
                     continue

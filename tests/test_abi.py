@@ -131,17 +131,22 @@ def test_assign_tiers_validation():
 
 def test_compact_and_quant_validation():
     m = model()
-    args = dict(model=m, batch=1, ctx_len=[10], max_ctx=16, tier_prev=FAKE, tier_next=FAKE,
-                k_t0_src=FAKE, v_t0_src=FAKE, t0_len_src=[6], cap0=32, k_t1_src=FAKE,
-                v_t1_src=FAKE, t1_len_src=[3], cap1=32, k_t0_dst=FAKE + 64, v_t0_dst=FAKE + 64,
-                t0_pos_dst=FAKE, k_t1_dst=FAKE + 64, v_t1_dst=FAKE + 64, t1_pos_dst=FAKE,
-                t2_src=FAKE, t2_pos=FAKE, t2_cap=8, new_lens=FAKE, workspace=FAKE,
-                workspace_bytes=1 << 20, stream=0)
-    assert status_of(tkv.tkv_compact, **{**args, "t0_len_src": [8]}) == tkv.TKV_ERR_STATE
-    assert status_of(tkv.tkv_compact, **{**args, "t1_len_src": [33], "ctx_len": [40],
+    ws = tkv.tkv_compact_workspace_bytes(m, 1, 16, 32, 32)
+    args = dict(model=m, batch=1, ctx_len=[10], max_ctx=16, tier_prev=FAKE, tier_next=FAKE + 64,
+                k_t0=FAKE, v_t0=FAKE, t0_pos=FAKE, t0_len=[6], cap0=32, k_t1=FAKE, v_t1=FAKE,
+                t1_pos=FAKE, t1_len=[3], cap1=32, t2_src=FAKE, t2_pos=FAKE, t2_cap=8,
+                t2_codes=FAKE, t2_scales=FAKE, new_lens=FAKE, workspace=FAKE,
+                workspace_bytes=ws, stream=0)
+    assert ws > 0 and tkv.tkv_compact_workspace_bytes(m, -1, 16, 32, 32) == 0
+    assert status_of(tkv.tkv_compact, **{**args, "t0_len": [8]}) == tkv.TKV_ERR_STATE
+    assert status_of(tkv.tkv_compact, **{**args, "t1_len": [33], "ctx_len": [40],
                                           "max_ctx": 64}) == tkv.TKV_ERR_CAPACITY
-    assert status_of(tkv.tkv_compact, **{**args, "k_t0_dst": FAKE}) == tkv.TKV_ERR_ARG
-    assert status_of(tkv.tkv_compact, **{**args, "workspace_bytes": 8}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_compact, **{**args, "tier_next": FAKE}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_compact, **{**args, "t2_codes": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_compact, **{**args, "t1_pos": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_compact, **{**args, "cap0": 40}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_compact, **{**args, "workspace_bytes": ws - 1}) == \
+        tkv.TKV_ERR_CAPACITY
     qargs = dict(model=m, batch=1, k_t0=FAKE, v_t0=FAKE, cap0=32, k_t1=FAKE, v_t1=FAKE, cap1=32,
                  src=FAKE, n_rows=FAKE, n_rows_stride=3, max_rows=4, codes=FAKE, scales=FAKE,
                  stream=0)
@@ -162,7 +167,8 @@ def test_append_validation():
 
 
 def test_gather_host_pack_without_device():
-    # positions ascending check, then a pack-only call (no device pointers -> no HIP call)
+    # position checks (repeats, range, capacity), then a pack-only call (no device
+    # pointers -> no HIP call) with positions in window-slot order, not sorted
     m = model(layers=2, kv_heads=2, q_heads=2, head_dim=64)
     r = np.random.default_rng(0)
     max_ctx, cap1 = 40, 32
@@ -170,13 +176,13 @@ def test_gather_host_pack_without_device():
     hv = r.integers(0, 65535, size=(2, 2, max_ctx, 64)).astype(np.uint16)
     sk = np.zeros((2, 2, cap1, 64), np.uint16)
     sv = np.zeros((2, 2, cap1, 64), np.uint16)
-    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 2], 2, sk, sv, cap1) == \
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 2, 3], 3, sk, sv, cap1) == \
         tkv.TKV_ERR_ARG
     assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 40], 2, sk, sv, cap1) == \
         tkv.TKV_ERR_ARG
     assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, list(range(33)), 33, sk, sv, cap1) == \
         tkv.TKV_ERR_CAPACITY
-    pos = [1, 5, 6, 17, 39]
+    pos = [17, 5, 39, 1, 6]
     tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), sk, sv, cap1)
     # storage order of 32-slot blocks: K-tiles and V-tiles (element-wise definition)
     for r in range(len(pos)):

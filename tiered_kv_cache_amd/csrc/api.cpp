@@ -575,58 +575,87 @@ tkv_status tkv_assign_tiers(int32_t batch, const int32_t* ctx_len, int32_t max_c
   return TKV_OK;
 }
 
-size_t tkv_compact_workspace_bytes(int32_t batch, int32_t cap0, int32_t cap1) {
-  if (batch < 0 || cap0 < 0 || cap1 < 0) return 0;
-  return (size_t)batch * ((size_t)cap0 + cap1) * sizeof(int32_t) + 256;
+// Relocation workspace, every region 256-byte aligned:
+//   inv [B][max_ctx] | holes0 [B][cap0] | holes1 [B][cap1] | to_t0 [B][cap0] int2 |
+//   to_t1 [B][cap1] int2 | staged [B][cap1] int2 | cnt [B][4] | staging [B][cap1][L*Hkv][2][D]
+struct RelocWorkspace {
+  size_t inv, holes0, holes1, to_t0, to_t1, staged, cnt, staging, total;
+};
+
+static RelocWorkspace reloc_workspace(const tkv_model* m, int batch, int max_ctx, int cap0,
+                                      int cap1) {
+  const size_t B = (size_t)batch;
+  const size_t elem = m->kv_dtype == TKV_BF16 ? 2 : 4;
+  RelocWorkspace w;
+  w.inv = 0;
+  w.holes0 = round_up(w.inv + B * max_ctx * 4, 256);
+  w.holes1 = round_up(w.holes0 + B * cap0 * 4, 256);
+  w.to_t0 = round_up(w.holes1 + B * cap1 * 4, 256);
+  w.to_t1 = round_up(w.to_t0 + B * cap0 * 8, 256);
+  w.staged = round_up(w.to_t1 + B * cap1 * 8, 256);
+  w.cnt = round_up(w.staged + B * cap1 * 8, 256);
+  w.staging = round_up(w.cnt + B * 16, 256);
+  w.total = round_up(w.staging + B * cap1 * (size_t)m->num_layers * m->num_kv_heads * 2 *
+                                     m->head_dim * elem,
+                     256);
+  return w;
+}
+
+size_t tkv_compact_workspace_bytes(const tkv_model* model, int32_t batch, int32_t max_ctx,
+                                   int32_t cap0, int32_t cap1) {
+  if (check_model(model) || batch < 0 || max_ctx < 0 || cap0 < 0 || cap1 < 0) return 0;
+  return reloc_workspace(model, batch, max_ctx, cap0, cap1).total;
 }
 
 tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
                        int32_t max_ctx, const uint8_t* tier_prev, const uint8_t* tier_next,
-                       const void* k_t0_src, const void* v_t0_src, const int32_t* t0_len_src,
-                       int32_t cap0, const void* k_t1_src, const void* v_t1_src,
-                       const int32_t* t1_len_src, int32_t cap1, void* k_t0_dst, void* v_t0_dst,
-                       int32_t* t0_pos_dst, void* k_t1_dst, void* v_t1_dst, int32_t* t1_pos_dst,
-                       int32_t* t2_src, int32_t* t2_pos, int32_t t2_cap, int32_t* new_lens,
+                       void* k_t0, void* v_t0, int32_t* t0_pos, const int32_t* t0_len,
+                       int32_t cap0, void* k_t1, void* v_t1, int32_t* t1_pos,
+                       const int32_t* t1_len, int32_t cap1, int32_t* t2_src, int32_t* t2_pos,
+                       int32_t t2_cap, int8_t* t2_codes, float* t2_scales, int32_t* new_lens,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   tkv_status st = check_model(model);
   if (st) return st;
   if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
   if (batch == 0) return TKV_OK;
-  if (!ctx_len || !tier_prev || !tier_next || !k_t0_src || !v_t0_src || !t0_len_src ||
-      !t1_len_src || !k_t0_dst || !v_t0_dst || !t0_pos_dst || !t2_src || !t2_pos ||
-      !new_lens || !workspace)
+  if (!ctx_len || !tier_prev || !tier_next || !k_t0 || !v_t0 || !t0_pos || !t0_len || !t1_len ||
+      !t2_src || !t2_pos || !new_lens || !workspace)
     return fail(TKV_ERR_ARG, "null pointer");
-  if (cap1 > 0 && (!k_t1_src || !v_t1_src || !k_t1_dst || !v_t1_dst || !t1_pos_dst))
+  if (cap1 > 0 && (!k_t1 || !v_t1 || !t1_pos))
     return fail(TKV_ERR_ARG, "null T1 pointer with cap1 > 0");
+  if (t2_cap > 0 && (!t2_codes || !t2_scales))
+    return fail(TKV_ERR_ARG, "null T2 codes or scales with t2_cap > 0");
   if (cap0 < 1 || cap1 < 0 || t2_cap < 0 || max_ctx < 1 || cap0 % 32 || cap1 % 32)
     return fail(TKV_ERR_ARG, "bad capacity (cap0, cap1 multiples of 32)");
-  if (k_t0_src == k_t0_dst || v_t0_src == v_t0_dst || (cap1 > 0 && (k_t1_src == k_t1_dst ||
-                                                                    v_t1_src == v_t1_dst)))
-    return fail(TKV_ERR_ARG, "source and destination buffers must differ");
-  int max_n = 0;
+  if (t2_cap > 65535) return fail(TKV_ERR_CAPACITY, "t2_cap above 65535");
+  if (tier_prev == tier_next) return fail(TKV_ERR_ARG, "tier_prev and tier_next must differ");
   for (int b = 0; b < batch; ++b) {
-    if (ctx_len[b] < 0 || t0_len_src[b] < 0 || t1_len_src[b] < 0)
+    if (ctx_len[b] < 0 || t0_len[b] < 0 || t1_len[b] < 0)
       return fail(TKV_ERR_ARG, "negative length");
     if (ctx_len[b] > max_ctx) return fail(TKV_ERR_CAPACITY, "ctx_len > max_ctx");
-    if (t0_len_src[b] > cap0 || t1_len_src[b] > cap1)
-      return fail(TKV_ERR_CAPACITY, "source length > capacity");
-    if ((long)t0_len_src[b] + t1_len_src[b] > ctx_len[b])
+    if (t0_len[b] > cap0 || t1_len[b] > cap1)
+      return fail(TKV_ERR_CAPACITY, "length > capacity");
+    if ((long)t0_len[b] + t1_len[b] > ctx_len[b])
       return fail(TKV_ERR_STATE, "t0_len + t1_len > ctx_len");
-    max_n = std::max(max_n, ctx_len[b]);
   }
-  if (workspace_bytes < tkv_compact_workspace_bytes(batch, cap0, cap1))
-    return fail(TKV_ERR_CAPACITY, "workspace too small");
-  int* src0 = (int*)workspace;
-  int* src1 = src0 + (size_t)batch * cap0;
+  const RelocWorkspace w = reloc_workspace(model, batch, max_ctx, cap0, cap1);
+  if (workspace_bytes < w.total) return fail(TKV_ERR_CAPACITY, "workspace too small");
+  char* base = (char*)workspace;
+  const int lgs = model->num_layers * model->num_kv_heads;
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
-    CompactArgs a{};
+    RelocArgs a{};
     a.tprev = tier_prev;
     a.tnext = tier_next;
-    a.t0_pos_dst = t0_pos_dst;
-    a.t1_pos_dst = t1_pos_dst;
-    a.src0 = src0;
-    a.src1 = src1;
+    a.t0_pos = t0_pos;
+    a.t1_pos = t1_pos;
+    a.inv = (int*)(base + w.inv);
+    a.holes0 = (int*)(base + w.holes0);
+    a.holes1 = (int*)(base + w.holes1);
+    a.to_t0 = (int2*)(base + w.to_t0);
+    a.to_t1 = (int2*)(base + w.to_t1);
+    a.staged = (int2*)(base + w.staged);
+    a.cnt = (int*)(base + w.cnt);
     a.t2_src = t2_src;
     a.t2_pos = t2_pos;
     a.new_lens = new_lens;
@@ -635,35 +664,62 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
     a.cap1 = cap1;
     a.t2_cap = t2_cap;
     a.b_offset = b0;
-    int mx = 0;
     for (int i = 0; i < nb; ++i) {
       a.n[i] = ctx_len[b0 + i];
-      a.len0[i] = t0_len_src[b0 + i];
-      a.len1[i] = t1_len_src[b0 + i];
-      mx = std::max(mx, ctx_len[b0 + i]);
+      a.len0[i] = t0_len[b0 + i];
+      a.len1[i] = t1_len[b0 + i];
     }
-    CopyArgs c{};
-    c.k0s = k_t0_src;
-    c.v0s = v_t0_src;
-    c.k1s = k_t1_src;
-    c.v1s = v_t1_src;
-    c.k0d = k_t0_dst;
-    c.v0d = v_t0_dst;
-    c.k1d = k_t1_dst;
-    c.v1d = v_t1_dst;
-    c.src0 = src0;
-    c.src1 = src1;
-    c.new_lens = new_lens;
-    c.cap0 = cap0;
-    c.cap1 = cap1;
-    c.L = model->num_layers;
-    c.hkv = model->num_kv_heads;
-    c.b_offset = b0;
-    c.nb = nb;
-    launch_compact(a, c, model->kv_dtype, model->head_dim, nb, mx, stream);
-    if ((st = hip_check(hipGetLastError(), "compact launch"))) return st;
+    launch_reloc_scan(a, nb, stream);
+    if ((st = hip_check(hipGetLastError(), "reloc_scan launch"))) return st;
+    // the rows entering T2 are quantised from their old slots, before any row moves
+    if (t2_cap > 0) {
+      QuantArgs q{};
+      q.k0 = k_t0;
+      q.v0 = v_t0;
+      q.k1 = k_t1;
+      q.v1 = v_t1;
+      q.src = t2_src;
+      q.n_rows = new_lens + 2;
+      q.codes = t2_codes;
+      q.scales = t2_scales;
+      q.n_rows_stride = 4;
+      q.max_rows = t2_cap;
+      q.cap0 = cap0;
+      q.cap1 = cap1;
+      q.L = model->num_layers;
+      q.hkv = model->num_kv_heads;
+      q.b_offset = b0;
+      launch_quantize(q, model->kv_dtype, model->head_dim, nb, stream);
+      if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
+    }
+    // promoted T1 rows to staging, then every row into the T1 window (its
+    // sources are T0 slots and T1 slots at or past the new T1 length, never a
+    // T1 hole), then every row into the T0 pool (sources: T0 slots at or past
+    // the new T0 length, and staging)
+    MoveArgs mv{};
+    mv.k0 = k_t0;
+    mv.v0 = v_t0;
+    mv.k1 = k_t1;
+    mv.v1 = v_t1;
+    mv.staging = base + w.staging;
+    mv.cnt = a.cnt;
+    mv.cap0 = cap0;
+    mv.cap1 = cap1;
+    mv.lgs = lgs;
+    mv.b_offset = b0;
+    mv.nb = nb;
+    const int2* lists[3] = {a.staged, a.to_t1, a.to_t0};
+    const int strides[3] = {cap1, cap1, cap0};
+    const int order[3] = {kMoveStage, kMoveToT1, kMoveToT0};
+    for (int k = 0; k < 3; ++k) {
+      if (cap1 == 0 && order[k] != kMoveToT0) continue;
+      mv.which = order[k];
+      mv.list = lists[order[k]];
+      mv.list_stride = strides[order[k]];
+      launch_reloc_move(mv, model->kv_dtype, model->head_dim, stream);
+      if ((st = hip_check(hipGetLastError(), "reloc_move launch"))) return st;
+    }
   }
-  (void)max_n;
   return TKV_OK;
 }
 

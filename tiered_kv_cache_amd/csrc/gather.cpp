@@ -90,11 +90,11 @@ extern "C" tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k,
     return fail(TKV_ERR_ARG, "both or neither device windows must be given");
   if (positions) {
     if (!host_k || !host_v) return fail(TKV_ERR_ARG, "host store is null");
+    std::vector<uint8_t> seen((size_t)max_ctx, 0);
     for (int i = 0; i < n_t1; ++i) {
       if (positions[i] < 0 || positions[i] >= max_ctx)
         return fail(TKV_ERR_ARG, "position outside [0, max_ctx)");
-      if (i > 0 && positions[i] <= positions[i - 1])
-        return fail(TKV_ERR_ARG, "positions must be strictly ascending");
+      if (seen[positions[i]]++) return fail(TKV_ERR_ARG, "repeated position");
     }
   }
   const size_t esz = model->kv_dtype == TKV_BF16 ? 2 : 4;

@@ -118,13 +118,23 @@ struct TierArgs {
   int n3[kMaxSeqPerLaunch];
 };
 
-struct CompactArgs {
+// Relocation after a reassignment, in place.  Per sequence the workspace holds
+// an inverse map (position -> slot code), the low holes of the T0 pool and of
+// the T1 window, three move lists of (source, destination) pairs and their
+// counts.  Slot codes: s >= 0 is T0 slot s, s < 0 is T1 slot -s-1; in the
+// T0-destination list a negative source is staging row -s-1.
+struct RelocArgs {
   const uint8_t* tprev;
   const uint8_t* tnext;
-  int* t0_pos_dst;
-  int* t1_pos_dst;
-  int* src0;  // workspace [B][cap0]
-  int* src1;  // workspace [B][cap1]
+  int* t0_pos;   // in/out [B][cap0]
+  int* t1_pos;   // in/out [B][cap1]
+  int* inv;      // [B][max_ctx]
+  int* holes0;   // [B][cap0]
+  int* holes1;   // [B][cap1]
+  int2* to_t0;   // [B][cap0]  (T0 slot or staging row, T0 slot)
+  int2* to_t1;   // [B][cap1]  (T0 or T1 slot code, T1 slot)
+  int2* staged;  // [B][cap1]  (T1 slot code, staging row): promotions
+  int* cnt;      // [B][4]  |to_t0|, |to_t1|, |staged|, 0
   int* t2_src;
   int* t2_pos;
   int* new_lens;
@@ -134,19 +144,17 @@ struct CompactArgs {
   int len1[kMaxSeqPerLaunch];
 };
 
-struct CopyArgs {
-  const void* k0s;
-  const void* v0s;
-  const void* k1s;
-  const void* v1s;
-  void* k0d;
-  void* v0d;
-  void* k1d;
-  void* v1d;
-  const int* src0;
-  const int* src1;
-  const int* new_lens;
-  int cap0, cap1, L, hkv, b_offset, nb;
+enum MoveList { kMoveStage = 0, kMoveToT1 = 1, kMoveToT0 = 2 };
+
+struct MoveArgs {
+  void* k0;
+  void* v0;
+  void* k1;
+  void* v1;
+  void* staging;      // [B][cap1][L * Hkv][2][D] elements, plain rows (K then V)
+  const int2* list;   // [B][list_stride]
+  const int* cnt;     // [B][4]
+  int list_stride, which, cap0, cap1, lgs, b_offset, nb;
 };
 
 struct QuantArgs {
@@ -170,8 +178,8 @@ void launch_attn_merge(const MergeArgs& a, int head_dim, int nblocks, hipStream_
 void launch_score_rows(const ScoreArgs& a, int nblocks, const char* name, hipStream_t s);
 void launch_append(const AppendArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
 void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s);
-void launch_compact(const CompactArgs& a, const CopyArgs& c, int kv_dtype, int head_dim, int nb,
-                    int max_n, hipStream_t s);
+void launch_reloc_scan(const RelocArgs& a, int nb, hipStream_t s);
+void launch_reloc_move(const MoveArgs& m, int kv_dtype, int head_dim, hipStream_t s);
 void launch_quantize(const QuantArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
 
 }  // namespace tkv

@@ -13,12 +13,13 @@
 //                  monotone uint32 key of the float32 score, with ties at the
 //                  threshold resolved by position (the higher positions leave
 //                  first) through a block scan.  No sort is materialised.
-// compact_scan  -- one workgroup per sequence: block scans over positions map
-//                  every new T0/T1 slot to its source slot in the previous
-//                  pool/window and list the positions newly in T2.
-// compact_copy  -- moves the rows into the new pool/window, one 32-slot
-//                  destination block per workgroup: 16-byte key chunks and
-//                  8-slot value panels, written in destination order.
+// reloc_scan    -- one workgroup per sequence: block scans over positions and
+//                  slots list the holes of the pool and window, the rows that
+//                  move into them, and the positions newly in T2.  The slot ->
+//                  position maps are updated in place.
+// reloc_move    -- copies the listed rows (one wave per row and layer x KV
+//                  head); three launches: promoted T1 rows to staging, rows
+//                  into the T1 window, rows into the T0 pool.
 // append        -- writes the new token's K/V row into its T0 slot.
 #include <limits.h>
 
@@ -265,70 +266,156 @@ void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// compaction
+// relocation (in place)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kTierThreads) void compact_scan_kernel(CompactArgs a) {
+constexpr int kNoSlot = INT_MIN;
+
+// One workgroup per sequence.  Only the rows whose tier changed, and the rows
+// left above the new length of their pool, move: each fills a "hole", a slot
+// below the new length whose row left (or which was past the old length).
+// The i-th mover in position order takes the i-th hole in slot order.
+__global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
   __shared__ int tmp[kTierThreads / kWave + 1];
   const int tid = threadIdx.x;
   const int bl = blockIdx.x;
   const long b = a.b_offset + bl;
-  const int n = a.n[bl];
+  const int n = a.n[bl], len0 = a.len0[bl], len1 = a.len1[bl];
   const uint8_t* tp = a.tprev + b * a.max_ctx;
   const uint8_t* tn = a.tnext + b * a.max_ctx;
+  int* pos0 = a.t0_pos + b * a.cap0;
+  int* pos1 = a.t1_pos + b * a.cap1;
+  int* inv = a.inv + b * a.max_ctx;
+  int* cnt = a.cnt + b * 4;
+  int* lens = a.new_lens + b * 4;
+
+  // inverse map of the current pool and window
+  for (int p = tid; p < n; p += kTierThreads) inv[p] = kNoSlot;
+  __syncthreads();
+  int bad = 0;
+  for (int s = tid; s < len0; s += kTierThreads) {
+    const int p = pos0[s];
+    if (p < 0 || p >= n) ++bad;
+    else inv[p] = s;
+  }
+  for (int s = tid; s < len1; s += kTierThreads) {
+    const int p = pos1[s];
+    if (p < 0 || p >= n) ++bad;
+    else inv[p] = -s - 1;
+  }
+  __syncthreads();
+
+  // new sizes, and a consistency check of the maps against the previous tiers:
+  // with len0 T0 slots and len0 T0 positions, every T0 position holding a T0
+  // slot makes the map a bijection (likewise for T1)
   const int seg = (n + kTierThreads - 1) / kTierThreads;
   const int lo = min(n, tid * seg);
   const int hi = min(n, lo + seg);
-
-  int cp0 = 0, cp1 = 0, cn0 = 0, cn1 = 0, ct2 = 0, bad = 0;
+  int cp0 = 0, cp1 = 0, cn0 = 0, cn1 = 0, ct2 = 0;
   for (int p = lo; p < hi; ++p) {
-    const int o = tp[p], w = tn[p];
-    if (o > 3 || w > 3) ++bad;
-    if (o == 0) ++cp0;
-    else if (o == 1) ++cp1;
-    if (w == 0) ++cn0;
-    else if (w == 1) ++cn1;
-    else if (w == 2 && o <= 1) ++ct2;
-    if (w <= 1 && o > 1) ++bad;  // T2/T3 never return to full precision
+    const int o = tp[p], w = tn[p], v = inv[p];
+    if (o > 3 || w > 3 || (w <= 1 && o > 1)) ++bad;  // T2/T3 never return to full precision
+    if (o == 0) {
+      ++cp0;
+      if (v < 0) ++bad;
+    } else if (o == 1) {
+      ++cp1;
+      if (v >= 0 || v == kNoSlot) ++bad;
+    } else if (v != kNoSlot) {
+      ++bad;
+    }
+    cn0 += w == 0;
+    cn1 += w == 1;
+    ct2 += (w == 2 && o <= 1);
   }
-  int tp0, tp1, tn0, tn1, tt2;
-  int bp0 = block_excl_scan(cp0, tmp, &tp0);
-  int bp1 = block_excl_scan(cp1, tmp, &tp1);
-  int bn0 = block_excl_scan(cn0, tmp, &tn0);
-  int bn1 = block_excl_scan(cn1, tmp, &tn1);
-  int bt2 = block_excl_scan(ct2, tmp, &tt2);
   bad = block_sum_i(bad, tmp);
-  int* lens = a.new_lens + b * 3;
-  if (bad || tp0 != a.len0[bl] || tp1 != a.len1[bl] || tn0 > a.cap0 || tn1 > a.cap1 ||
-      tt2 > a.t2_cap) {
-    if (tid < 3) lens[tid] = -1;
+  cp0 = block_sum_i(cp0, tmp);
+  cp1 = block_sum_i(cp1, tmp);
+  const int n0 = block_sum_i(cn0, tmp);
+  const int n1 = block_sum_i(cn1, tmp);
+  const int nt2 = block_sum_i(ct2, tmp);
+  if (bad || cp0 != len0 || cp1 != len1 || n0 > a.cap0 || n1 > a.cap1 || nt2 > a.t2_cap) {
+    if (tid < 4) lens[tid] = -1;
+    if (tid < 4) cnt[tid] = 0;
     return;
   }
-  int* pos0 = a.t0_pos_dst + b * a.cap0;
-  int* pos1 = a.t1_pos_dst + b * a.cap1;
-  int* src0 = a.src0 + b * a.cap0;
-  int* src1 = a.src1 + b * a.cap1;
+
+  // holes, in slot order
+  int* holes0 = a.holes0 + b * a.cap0;
+  int* holes1 = a.holes1 + b * a.cap1;
+  int h0, h1;
+  {
+    const int sg = (n0 + kTierThreads - 1) / kTierThreads;
+    const int s0 = min(n0, tid * sg), s1 = min(n0, s0 + sg);
+    int c = 0;
+    for (int s = s0; s < s1; ++s) c += (s >= len0 || tn[pos0[s]] != 0);
+    int k = block_excl_scan(c, tmp, &h0);
+    for (int s = s0; s < s1; ++s)
+      if (s >= len0 || tn[pos0[s]] != 0) holes0[k++] = s;
+  }
+  {
+    const int sg = (n1 + kTierThreads - 1) / kTierThreads;
+    const int s0 = min(n1, tid * sg), s1 = min(n1, s0 + sg);
+    int c = 0;
+    for (int s = s0; s < s1; ++s) c += (s >= len1 || tn[pos1[s]] != 1);
+    int k = block_excl_scan(c, tmp, &h1);
+    for (int s = s0; s < s1; ++s)
+      if (s >= len1 || tn[pos1[s]] != 1) holes1[k++] = s;
+  }
+
+  // movers, in position order
+  int m0 = 0, m1 = 0, mp = 0;
+  for (int p = lo; p < hi; ++p) {
+    const int o = tp[p], w = tn[p], v = inv[p];
+    m0 += (w == 0 && (o == 1 || (o == 0 && v >= n0)));
+    m1 += (w == 1 && (o == 0 || (o == 1 && -v - 1 >= n1)));
+    mp += (w == 0 && o == 1);
+  }
+  int M0, M1, MP, T2;
+  int i0 = block_excl_scan(m0, tmp, &M0);
+  int i1 = block_excl_scan(m1, tmp, &M1);
+  int ip = block_excl_scan(mp, tmp, &MP);
+  int it2 = block_excl_scan(ct2, tmp, &T2);
+  if (M0 != h0 || M1 != h1) {  // cannot happen once the checks above hold
+    if (tid < 4) lens[tid] = -1;
+    if (tid < 4) cnt[tid] = 0;
+    return;
+  }
+  __syncthreads();  // every read of the old slot -> position maps is done
+  int2* to0 = a.to_t0 + b * a.cap0;
+  int2* to1 = a.to_t1 + b * a.cap1;
+  int2* stg = a.staged + b * a.cap1;
   int* t2s = a.t2_src + b * a.t2_cap;
   int* t2p = a.t2_pos + b * a.t2_cap;
   for (int p = lo; p < hi; ++p) {
-    const int o = tp[p], w = tn[p];
-    int loc = 0;
-    if (o == 0) loc = bp0++;
-    else if (o == 1) loc = -(bp1++) - 1;
-    if (w == 0) {
-      pos0[bn0] = p;
-      src0[bn0++] = loc;
-    } else if (w == 1) {
-      pos1[bn1] = p;
-      src1[bn1++] = loc;
+    const int o = tp[p], w = tn[p], v = inv[p];
+    if (w == 0 && o == 1) {
+      const int j = ip++;
+      stg[j] = make_int2(v, j);
+      const int d = holes0[i0];
+      to0[i0++] = make_int2(-j - 1, d);
+      pos0[d] = p;
+    } else if (w == 0 && o == 0 && v >= n0) {
+      const int d = holes0[i0];
+      to0[i0++] = make_int2(v, d);
+      pos0[d] = p;
+    } else if (w == 1 && (o == 0 || -v - 1 >= n1)) {
+      const int d = holes1[i1];
+      to1[i1++] = make_int2(v, d);
+      pos1[d] = p;
     } else if (w == 2 && o <= 1) {
-      t2s[bt2] = loc;
-      t2p[bt2++] = p;
+      t2s[it2] = v;
+      t2p[it2++] = p;
     }
   }
   if (tid == 0) {
-    lens[0] = tn0;
-    lens[1] = tn1;
-    lens[2] = tt2;
+    lens[0] = n0;
+    lens[1] = n1;
+    lens[2] = nt2;
+    lens[3] = M0 + M1 + MP;
+    cnt[kMoveToT0] = M0;
+    cnt[kMoveToT1] = M1;
+    cnt[kMoveStage] = MP;
+    cnt[3] = 0;
   }
 }
 
@@ -352,97 +439,83 @@ __device__ __forceinline__ void store8(T* p, const Vec8<T>& v) {
   for (int i = 0; i < (int)(sizeof(T) / 2); ++i) reinterpret_cast<uint4*>(p)[i] = v.w[i];
 }
 
-// One workgroup per destination 32-slot block of one (sequence, layer, KV head).
-// Keys move as 8-element chunks (a chunk of a row is contiguous in a K-tile);
-// values are gathered 8 slots at a time into one V-tile panel of one dimension.
-// Items are numbered in destination order, so the stores of a wave are
-// contiguous; slots at or past the new length are written as zero.
+// One row of one (layer, KV head): a slot of a pool (K-tile / V-tile order) or
+// a plain staging row (D keys then D values).
+template <typename T>
+struct RowRef {
+  T* k;
+  T* v;
+  long slot;  // < 0: plain row
+};
+
+// One wave per (move, layer x KV head) item; consecutive waves take consecutive
+// moves of one (layer, KV head), whose destinations are in slot order.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void compact_copy_kernel(CopyArgs c) {
-  constexpr int CH = D / 8;  // 8-element key chunks per row
-  const int z = blockIdx.z;  // 0: T0 destination, 1: T1 destination
-  const int lgs = c.L * c.hkv;
-  const int bl = blockIdx.y / lgs;
-  const long lg = blockIdx.y - (long)bl * lgs;
-  const long b = c.b_offset + bl;
-  const int len = c.new_lens[b * 3 + z];
-  const int r0 = blockIdx.x * 32;
-  if (len <= r0) return;
-  const int cap_d = z ? c.cap1 : c.cap0;
-  const int* src = (z ? c.src1 + b * c.cap1 : c.src0 + b * c.cap0) + r0;
-  const int nrow = min(32, len - r0);
-  const long blk0 = (b * lgs + lg) * c.cap0 * D;  // element offset of this (b, l, g) block
-  const long blk1 = (b * lgs + lg) * c.cap1 * D;
-  const long blkd = (b * lgs + lg) * (long)cap_d * D + (long)r0 * D;
-  // keys: item i -> (tile u, chunk cc, tile row) in destination order
-  {
-    const T* ks0 = (const T*)c.k0s + blk0;
-    const T* ks1 = (const T*)c.k1s + blk1;
-    T* kd = (T*)(z ? c.k1d : c.k0d) + blkd;
-    for (int i = threadIdx.x; i < 32 * CH; i += 256) {
-      const int row = i & 15;
-      const int cc = (i >> 4) % CH;
-      const int u = i / (16 * CH);
-      const int r = 8 * (row >> 2) + 4 * u + (row & 3);
-      Vec8<T> v;
-      if (r < nrow) {
-        const int sidx = src[r];
-        const long ss = sidx >= 0 ? sidx : -sidx - 1;
-        v = load8((sidx >= 0 ? ks0 : ks1) + k_off(ss, 8 * cc, D));
-      } else {
-#pragma unroll
-        for (int w = 0; w < (int)(sizeof(T) / 2); ++w) v.w[w] = make_uint4(0, 0, 0, 0);
-      }
-      store8(kd + k_off(r, 8 * cc, D), v);
-    }
-  }
-  // values: item i -> (dimension group dh, panel, dimension) in destination order
-  {
-    const T* vs0 = (const T*)c.v0s + blk0;
-    const T* vs1 = (const T*)c.v1s + blk1;
-    T* vd = (T*)(z ? c.v1d : c.v0d) + blkd;
-    for (int i = threadIdx.x; i < 4 * D; i += 256) {
-      const int d15 = i & 15;
-      const int pnl = (i >> 4) & 3;
-      const int dh = i >> 6;
-      const int d = dh * 16 + d15;
-      T vals[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = pnl * 8 + e;
-        vals[e] = T(0);
-        if (r < nrow) {
-          const int sidx = src[r];
-          const long ss = sidx >= 0 ? sidx : -sidx - 1;
-          vals[e] = (sidx >= 0 ? vs0 : vs1)[v_off(ss, d, D)];
+__global__ __launch_bounds__(256) void reloc_move_kernel(MoveArgs m) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const long gw = (long)blockIdx.x * (256 / kWave) + (threadIdx.x / kWave);
+  const long nw = (long)gridDim.x * (256 / kWave);
+  for (int bl = 0; bl < m.nb; ++bl) {
+    const long b = m.b_offset + bl;
+    const int cnt = m.cnt[b * 4 + m.which];
+    const long items = (long)cnt * m.lgs;
+    const int2* list = m.list + b * m.list_stride;
+    for (long it = gw; it < items; it += nw) {
+      const int lg = (int)(it / cnt);
+      const int i = (int)(it - (long)lg * cnt);
+      const int2 mv = list[i];
+      const long g = b * m.lgs + lg;
+      T* p0k = (T*)m.k0 + g * m.cap0 * D;
+      T* p0v = (T*)m.v0 + g * m.cap0 * D;
+      T* p1k = (T*)m.k1 + g * m.cap1 * D;
+      T* p1v = (T*)m.v1 + g * m.cap1 * D;
+      RowRef<T> src, dst;
+      if (m.which == kMoveStage) {  // T1 slot -> staging row
+        src = {p1k, p1v, (long)(-mv.x - 1)};
+        T* r = (T*)m.staging + ((b * m.cap1 + mv.y) * m.lgs + lg) * 2 * D;
+        dst = {r, r + D, -1};
+      } else if (m.which == kMoveToT1) {  // T0 or T1 slot -> T1 slot
+        src = mv.x >= 0 ? RowRef<T>{p0k, p0v, (long)mv.x} : RowRef<T>{p1k, p1v, (long)(-mv.x - 1)};
+        dst = {p1k, p1v, (long)mv.y};
+      } else {  // T0 slot or staging row -> T0 slot
+        if (mv.x >= 0) {
+          src = {p0k, p0v, (long)mv.x};
+        } else {
+          T* r = (T*)m.staging + ((b * m.cap1 + (-mv.x - 1)) * m.lgs + lg) * 2 * D;
+          src = {r, r + D, -1};
         }
+        dst = {p0k, p0v, (long)mv.y};
       }
-      Vec8<T> packed;
-      __builtin_memcpy(&packed, vals, sizeof(packed));
-      store8(vd + v_off(pnl * 8, d, D), packed);
+      if (lane < D / 8) {
+        const int d = 8 * lane;
+        const Vec8<T> kv = load8(src.slot >= 0 ? src.k + k_off(src.slot, d, D) : src.k + d);
+        store8(dst.slot >= 0 ? dst.k + k_off(dst.slot, d, D) : dst.k + d, kv);
+      }
+#pragma unroll
+      for (int d = lane; d < D; d += kWave) {
+        const T x = src.slot >= 0 ? src.v[v_off(src.slot, d, D)] : src.v[d];
+        if (dst.slot >= 0) dst.v[v_off(dst.slot, d, D)] = x;
+        else dst.v[d] = x;
+      }
     }
   }
 }
 
-void launch_compact(const CompactArgs& a, const CopyArgs& c, int kv_dtype, int head_dim, int nb,
-                    int max_n, hipStream_t s) {
-  {
-    KernelTimer timer("compact_scan", s);
-    hipLaunchKernelGGL(compact_scan_kernel, dim3(nb), dim3(kTierThreads), 0, s, a);
-  }
-  const int rows = max(1, min(max_n, max(c.cap0, c.cap1)));
-  dim3 grid(ceil_div(rows, 32), nb * c.L * c.hkv, 2);
-  KernelTimer timer("compact_copy", s);
+void launch_reloc_scan(const RelocArgs& a, int nb, hipStream_t s) {
+  KernelTimer timer("reloc_scan", s);
+  hipLaunchKernelGGL(reloc_scan_kernel, dim3(nb), dim3(kTierThreads), 0, s, a);
+}
+
+void launch_reloc_move(const MoveArgs& m, int kv_dtype, int head_dim, hipStream_t s) {
+  static const char* names[3] = {"reloc_stage", "reloc_to_t1", "reloc_to_t0"};
+  KernelTimer timer(names[m.which], s);
+  const dim3 grid(2048);
   if (kv_dtype == TKV_BF16) {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((compact_copy_kernel<uint16_t, 128>), grid, dim3(256), 0, s, c);
-    else
-      hipLaunchKernelGGL((compact_copy_kernel<uint16_t, 64>), grid, dim3(256), 0, s, c);
+    if (head_dim == 128) hipLaunchKernelGGL((reloc_move_kernel<uint16_t, 128>), grid, dim3(256), 0, s, m);
+    else hipLaunchKernelGGL((reloc_move_kernel<uint16_t, 64>), grid, dim3(256), 0, s, m);
   } else {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((compact_copy_kernel<float, 128>), grid, dim3(256), 0, s, c);
-    else
-      hipLaunchKernelGGL((compact_copy_kernel<float, 64>), grid, dim3(256), 0, s, c);
+    if (head_dim == 128) hipLaunchKernelGGL((reloc_move_kernel<float, 128>), grid, dim3(256), 0, s, m);
+    else hipLaunchKernelGGL((reloc_move_kernel<float, 64>), grid, dim3(256), 0, s, m);
   }
 }
 

@@ -8,12 +8,14 @@ memory and supplies the stream):
                fused importance-score update)
     every Delta steps (Methodologie section 4 of the "Not All Thoughts Need
     HBM" summary pages, gist.science paper 2605.09490):
-               tkv_assign_tiers -> tkv_compact (new T0 pool / T1 window, list of
-               new T2 rows) -> tkv_quantize_t2 -> one host sync for the new
-               lengths.
+               tkv_assign_tiers -> tkv_compact (the new T2 rows quantised, then
+               only the rows whose tier changed move, in place) -> one host
+               sync for the new lengths.
 
-The T0 pool and the T1 window are double-buffered: compaction reads one copy
-and writes the other.  The tier map is double-buffered the same way.
+The T0 pool and the T1 window are single copies whose slot order is not
+position order (t0_pos / t1_pos map slots to positions); the read-back helpers
+return rows in ascending position order.  The tier map is double-buffered:
+the relocation reads the previous map and the new one.
 """
 from __future__ import annotations
 
@@ -138,61 +140,38 @@ class TieredKVCache:
         dt, dev, B = shape.torch_dtype, self.device, batch
         pool0 = (B, L, Hkv, self.cap0, D)
         pool1 = (B, L, Hkv, self.cap1, D)
-        self.k0 = [torch.zeros(pool0, dtype=dt, device=dev) for _ in range(2)]
-        self.v0 = [torch.zeros(pool0, dtype=dt, device=dev) for _ in range(2)]
-        self.k1 = [torch.zeros(pool1, dtype=dt, device=dev) for _ in range(2)]
-        self.v1 = [torch.zeros(pool1, dtype=dt, device=dev) for _ in range(2)]
-        self.pos0 = [torch.zeros((B, self.cap0), dtype=torch.int32, device=dev) for _ in range(2)]
-        self.pos1 = [torch.zeros((B, self.cap1), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.k_t0 = torch.zeros(pool0, dtype=dt, device=dev)
+        self.v_t0 = torch.zeros(pool0, dtype=dt, device=dev)
+        self.k_t1 = torch.zeros(pool1, dtype=dt, device=dev)
+        self.v_t1 = torch.zeros(pool1, dtype=dt, device=dev)
+        self.t0_pos = torch.zeros((B, self.cap0), dtype=torch.int32, device=dev)
+        self.t1_pos = torch.zeros((B, self.cap1), dtype=torch.int32, device=dev)
         self.tier = [torch.zeros((B, self.max_ctx), dtype=torch.uint8, device=dev) for _ in range(2)]
         self.scores = torch.zeros((B, self.max_ctx), dtype=torch.float32, device=dev)
         self.alpha = torch.zeros((B, L, Hq, self.alpha_stride), dtype=torch.float32, device=dev)
         self.out = torch.zeros((B, L, Hq, D), dtype=torch.float32, device=dev)
         self.counts = torch.zeros((B, 4), dtype=torch.int32, device=dev)
-        self.new_lens = torch.zeros((B, 3), dtype=torch.int32, device=dev)
+        self.new_lens = torch.zeros((B, 4), dtype=torch.int32, device=dev)
         self.t2_src = torch.zeros((B, self.t2_cap), dtype=torch.int32, device=dev)
         self.t2_pos = torch.zeros((B, self.t2_cap), dtype=torch.int32, device=dev)
         self.t2_codes = torch.zeros((B, self.t2_cap, L, Hkv, 2, D), dtype=torch.int8, device=dev)
         self.t2_scales = torch.zeros((B, self.t2_cap, L, Hkv, 2), dtype=torch.float32, device=dev)
         self.ws_bytes = tkv.tkv_decode_workspace_bytes(self.model, B, L, self.cap0, self.cap1)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
-        self.cws_bytes = tkv.tkv_compact_workspace_bytes(B, self.cap0, self.cap1)
+        self.cws_bytes = tkv.tkv_compact_workspace_bytes(self.model, B, self.max_ctx, self.cap0,
+                                                         self.cap1)
         self.cws = torch.zeros(self.cws_bytes, dtype=torch.uint8, device=dev)
-        self.cur = 0       # which pool/window copy is live
         self.tcur = 0      # which tier map is live
         self.n = [0] * B
         self.t0_len = [0] * B
         self.t1_len = [0] * B
         self.t2_new = [0] * B   # rows quantised at the last reassignment
+        self.moved = [0] * B    # row copies of the last relocation
         self.steps = 0
         self.fused_scores = True
         self.fused_append = True   # step(): tkv_append_decode_step rather than the two calls
 
     # ---- views -------------------------------------------------------------
-    @property
-    def k_t0(self):
-        return self.k0[self.cur]
-
-    @property
-    def v_t0(self):
-        return self.v0[self.cur]
-
-    @property
-    def k_t1(self):
-        return self.k1[self.cur]
-
-    @property
-    def v_t1(self):
-        return self.v1[self.cur]
-
-    @property
-    def t0_pos(self):
-        return self.pos0[self.cur]
-
-    @property
-    def t1_pos(self):
-        return self.pos1[self.cur]
-
     @property
     def tiers(self):
         return self.tier[self.tcur]
@@ -211,9 +190,9 @@ class TieredKVCache:
         vpad = torch.zeros(shape, dtype=self.shape.torch_dtype, device=self.device)
         kpad[:, :, :n0] = to_device(K, self.shape.torch_dtype, self.device)
         vpad[:, :, :n0] = to_device(V, self.shape.torch_dtype, self.device)
-        self.k0[self.cur][b, :, :, :n0p] = k_rows_to_tiles(kpad)
-        self.v0[self.cur][b, :, :, :n0p] = v_rows_to_tiles(vpad)
-        self.pos0[self.cur][b, :n0] = torch.arange(n0, dtype=torch.int32, device=self.device)
+        self.k_t0[b, :, :, :n0p] = k_rows_to_tiles(kpad)
+        self.v_t0[b, :, :, :n0p] = v_rows_to_tiles(vpad)
+        self.t0_pos[b, :n0] = torch.arange(n0, dtype=torch.int32, device=self.device)
         self.tier[self.tcur][b].zero_()
         self.scores[b].zero_()
         self.n[b] = n0
@@ -284,50 +263,66 @@ class TieredKVCache:
         return False
 
     def reassign(self, stream=None) -> None:
-        """Rank, compact, quantise new T2 rows; one host sync for the new lengths."""
-        nxt, tnx = 1 - self.cur, 1 - self.tcur
+        """Rank, quantise the new T2 rows, relocate in place; one host sync for the new lengths."""
+        tnx = 1 - self.tcur
         B = self.batch
         tkv.tkv_assign_tiers(B, self.n, self.max_ctx, self.scores, self.tpolicy,
                              self.tier[self.tcur], self.tier[tnx], self.counts, stream)
         tkv.tkv_compact(self.model, B, self.n, self.max_ctx, self.tier[self.tcur], self.tier[tnx],
-                        self.k0[self.cur], self.v0[self.cur], self.t0_len, self.cap0,
-                        self.k1[self.cur], self.v1[self.cur], self.t1_len, self.cap1,
-                        self.k0[nxt], self.v0[nxt], self.pos0[nxt], self.k1[nxt], self.v1[nxt],
-                        self.pos1[nxt], self.t2_src, self.t2_pos, self.t2_cap, self.new_lens,
-                        self.cws, self.cws_bytes, stream)
-        tkv.tkv_quantize_t2(self.model, B, self.k0[self.cur], self.v0[self.cur], self.cap0,
-                            self.k1[self.cur], self.v1[self.cur], self.cap1, self.t2_src,
-                            self.new_lens[:, 2:], 3, self.t2_cap, self.t2_codes, self.t2_scales,
-                            stream)
+                        self.k_t0, self.v_t0, self.t0_pos, self.t0_len, self.cap0,
+                        self.k_t1, self.v_t1, self.t1_pos, self.t1_len, self.cap1,
+                        self.t2_src, self.t2_pos, self.t2_cap, self.t2_codes, self.t2_scales,
+                        self.new_lens, self.cws, self.cws_bytes, stream)
         lens = self.new_lens.cpu().numpy()          # the one sync per reassignment
         if (lens < 0).any():
             raise RuntimeError(f"tier state error reported by the device: {lens.tolist()}")
         self.t0_len = lens[:, 0].tolist()
         self.t1_len = lens[:, 1].tolist()
         self.t2_new = lens[:, 2].tolist()
-        self.cur, self.tcur = nxt, tnx
+        self.moved = lens[:, 3].tolist()
+        self.tcur = tnx
 
-    # ---- read-back helpers (tests, tools) ---------------------------------------
-    def attended_positions(self, b: int) -> np.ndarray:
+    # ---- read-back helpers (tests, tools): ascending position order -------------
+    def _order(self, b: int):
+        """Slot orders of the pool and the window that sort their positions."""
         p0 = self.t0_pos[b, :self.t0_len[b]].cpu().numpy()
         p1 = self.t1_pos[b, :self.t1_len[b]].cpu().numpy()
-        return np.concatenate([p0, p1]).astype(np.int64)
+        return np.argsort(p0, kind="stable"), np.argsort(p1, kind="stable"), p0, p1
+
+    def t0_positions(self, b: int) -> np.ndarray:
+        o0, _, p0, _ = self._order(b)
+        return p0[o0].astype(np.int64)
+
+    def t1_positions(self, b: int) -> np.ndarray:
+        _, o1, _, p1 = self._order(b)
+        return p1[o1].astype(np.int64)
+
+    def attended_positions(self, b: int) -> np.ndarray:
+        """T0 positions then T1 positions, each ascending."""
+        o0, o1, p0, p1 = self._order(b)
+        return np.concatenate([p0[o0], p1[o1]]).astype(np.int64)
 
     def t0_rows(self, b: int):
-        """Host copies (bf16 bits or float32) of the T0 pool rows of sequence b: K, V [L][Hkv][n][D]."""
+        """Host copies (bf16 bits or float32) of the T0 rows of sequence b in ascending
+        position order: K, V [L][Hkv][n][D]."""
+        o0 = self._order(b)[0]
         n = self.t0_len[b]
-        return (to_host_bits(k_tiles_to_rows(self.k_t0[b], n)),
-                to_host_bits(v_tiles_to_rows(self.v_t0[b], n)))
+        return (to_host_bits(k_tiles_to_rows(self.k_t0[b], n))[:, :, o0],
+                to_host_bits(v_tiles_to_rows(self.v_t0[b], n))[:, :, o0])
 
     def t1_rows(self, b: int):
-        """Host copies of the T1 window rows of sequence b: K, V [L][Hkv][n][D]."""
+        """Host copies of the T1 rows of sequence b in ascending position order."""
+        o1 = self._order(b)[1]
         n = self.t1_len[b]
-        return (to_host_bits(k_tiles_to_rows(self.k_t1[b], n)),
-                to_host_bits(v_tiles_to_rows(self.v_t1[b], n)))
+        return (to_host_bits(k_tiles_to_rows(self.k_t1[b], n))[:, :, o1],
+                to_host_bits(v_tiles_to_rows(self.v_t1[b], n))[:, :, o1])
 
     def alpha_of(self, b: int) -> np.ndarray:
+        """alpha [L][Hq][n_att] in attended_positions() order."""
+        o0, o1, _, _ = self._order(b)
         m = self.t0_len[b] + self.t1_len[b]
-        return self.alpha[b, :, :, :m].cpu().numpy()
+        a = self.alpha[b, :, :, :m].cpu().numpy()
+        return a[:, :, np.concatenate([o0, self.t0_len[b] + o1])]
 
     def last_t2(self, b: int):
         r = self.t2_new[b]

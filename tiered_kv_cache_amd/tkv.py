@@ -84,9 +84,10 @@ def lib() -> ctypes.CDLL:
         "tkv_update_scores": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _I, _P, _P, _I,
                                    _P, _P, _I, _P, _I, _P]),
         "tkv_assign_tiers": (_I, [_I, _P, _I, _P, ctypes.POINTER(tkv_policy), _P, _P, _P, _P]),
-        "tkv_compact_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
-        "tkv_compact": (_I, [ctypes.POINTER(tkv_model), _I, _P, _I, _P, _P, _P, _P, _P, _I,
-                             _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+        "tkv_compact_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(tkv_model), _I, _I,
+                                                          _I, _I]),
+        "tkv_compact": (_I, [ctypes.POINTER(tkv_model), _I, _P, _I, _P, _P, _P, _P, _P, _P,
+                             _I, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P,
                              ctypes.c_size_t, _P]),
         "tkv_quantize_t2": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _I, _P, _P, _I, _P,
                                  _P, _I, _I, _P, _P, _P]),
@@ -233,21 +234,19 @@ def tkv_assign_tiers(batch, ctx_len, max_ctx, scores, policy, tier_prev, tier_ne
                                   _stream(stream)), "tkv_assign_tiers")
 
 
-def tkv_compact_workspace_bytes(batch, cap0, cap1) -> int:
-    return lib().tkv_compact_workspace_bytes(batch, cap0, cap1)
+def tkv_compact_workspace_bytes(model, batch, max_ctx, cap0, cap1) -> int:
+    return lib().tkv_compact_workspace_bytes(ctypes.byref(model), batch, max_ctx, cap0, cap1)
 
 
-def tkv_compact(model, batch, ctx_len, max_ctx, tier_prev, tier_next, k_t0_src, v_t0_src,
-                t0_len_src, cap0, k_t1_src, v_t1_src, t1_len_src, cap1, k_t0_dst, v_t0_dst,
-                t0_pos_dst, k_t1_dst, v_t1_dst, t1_pos_dst, t2_src, t2_pos, t2_cap, new_lens,
-                workspace, workspace_bytes, stream=None) -> None:
-    a, b, c = _HostInts(ctx_len), _HostInts(t0_len_src), _HostInts(t1_len_src)
+def tkv_compact(model, batch, ctx_len, max_ctx, tier_prev, tier_next, k_t0, v_t0, t0_pos,
+                t0_len, cap0, k_t1, v_t1, t1_pos, t1_len, cap1, t2_src, t2_pos, t2_cap,
+                t2_codes, t2_scales, new_lens, workspace, workspace_bytes, stream=None) -> None:
+    a, b, c = _HostInts(ctx_len), _HostInts(t0_len), _HostInts(t1_len)
     _check(lib().tkv_compact(ctypes.byref(model), batch, a.ptr, max_ctx, _ptr(tier_prev),
-                             _ptr(tier_next), _ptr(k_t0_src), _ptr(v_t0_src), b.ptr, cap0,
-                             _ptr(k_t1_src), _ptr(v_t1_src), c.ptr, cap1, _ptr(k_t0_dst),
-                             _ptr(v_t0_dst), _ptr(t0_pos_dst), _ptr(k_t1_dst), _ptr(v_t1_dst),
-                             _ptr(t1_pos_dst), _ptr(t2_src), _ptr(t2_pos), t2_cap,
-                             _ptr(new_lens), _ptr(workspace), workspace_bytes,
+                             _ptr(tier_next), _ptr(k_t0), _ptr(v_t0), _ptr(t0_pos), b.ptr,
+                             cap0, _ptr(k_t1), _ptr(v_t1), _ptr(t1_pos), c.ptr, cap1,
+                             _ptr(t2_src), _ptr(t2_pos), t2_cap, _ptr(t2_codes),
+                             _ptr(t2_scales), _ptr(new_lens), _ptr(workspace), workspace_bytes,
                              _stream(stream)), "tkv_compact")
 
 
