@@ -163,7 +163,10 @@ struct WaveState {
 // key/value stream cost this GPU about a fifth of its read bandwidth, while a
 // burst after the last load costs only its own bytes.  Per wave: up to
 // kStageUnits units of [G heads][32 tokens] floats, with each unit's destination.
-constexpr int kStageFloats = 4096;  // 16 KB per wave
+// 24 KB per wave (four waves per workgroup, one per SIMD: 99 KB of LDS) holds the
+// 27 units of seven heads, so at chain-8K sizes every logit goes out after the
+// wave's last load.
+constexpr int kStageFloats = 6144;
 constexpr int kStageUnits = 64;
 
 struct Stage {

@@ -145,6 +145,21 @@ __device__ void merge_output_row(const MergeArgs& a, int row_in_launch) {
   for (int i = 0; i < PER; ++i) a.out[orow * D + lane + kWave * i] = o[i] * inv;
 }
 
+// The logits are read once and alpha is written once per step: both go
+// through non-temporal accesses, so they do not displace lines in the caches
+// (measured: ~2 us of the ~15 us launch at chain 8K).
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 ld_stream4(const float* p) {
+  const f32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void st_stream4(float* p, const float4& y) {
+  const f32x4v_t v = {y.x, y.y, y.z, y.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4v_t*>(p));
+}
+
 template <int GM>
 __device__ void normalise_chunk(const MergeArgs& a, int cb) {
   __shared__ float sM[GM], sI[GM];
@@ -172,7 +187,7 @@ __device__ void normalise_chunk(const MergeArgs& a, int cb) {
     if (h < G) {
       const float* p = arow + (long)h * a.alpha_stride;
       if (full) {
-        x[h] = *reinterpret_cast<const float4*>(p);
+        x[h] = ld_stream4(p);
       } else if (j0 < natt) {
         x[h].x = p[0];
         if (j0 + 1 < natt) x[h].y = p[1];
@@ -206,7 +221,7 @@ __device__ void normalise_chunk(const MergeArgs& a, int cb) {
       y.w = __builtin_amdgcn_exp2f(x[h].w - m) * inv;
       float* p = arow + (long)h * a.alpha_stride;
       if (full) {
-        *reinterpret_cast<float4*>(p) = y;
+        st_stream4(p, y);
       } else {
         p[0] = y.x;
         if (j0 + 1 < natt) p[1] = y.y;
