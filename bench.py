@@ -50,11 +50,12 @@ def step_bytes(wl, n_att: int, n: int) -> dict:
     kv = 2 * L * Hkv * n_att * D * e          # K and V rows of the attended set
     q = L * Hq * D * e
     o = L * Hq * D * 4
-    alpha = L * Hq * n_att * 4                 # normalised weights, written once
+    alpha = 2 * L * Hq * n_att * 4             # weights: written, read back by the score
     s = 8 * n_att                              # score read-modify-write
     append = 2 * 2 * L * Hkv * D * e           # new row read + pool write
+    minimal = kv + q + o + s + append
     return {"kv": kv, "q": q, "o": o, "alpha": alpha, "scores": s, "append": append,
-            "total": kv + q + o + alpha + s + append}
+            "minimal": minimal, "total": minimal + alpha}
 
 
 def attn_partial_bytes(wl, n_att: int) -> int:
@@ -269,9 +270,10 @@ def main():
     cache, elapsed_bd, _, _, _, kernels, _ = run(None)
 
     steps_per_s = args.steps / elapsed
-    step_b = [step_bytes(wl, n_att, n)["total"] for n_att, n in zip(n_att_steps, n_steps)]
+    step_b = [step_bytes(wl, n_att, n) for n_att, n in zip(n_att_steps, n_steps)]
     re_b = sum(reassign_bytes(wl, *r) for r in re_info)
-    alg_bytes = (sum(step_b) + re_b) / args.steps
+    alg_bytes = (sum(x["total"] for x in step_b) + re_b) / args.steps
+    min_bytes = (sum(x["minimal"] for x in step_b) + re_b) / args.steps
     attn = timed.get("attn_partial", {"launches": 1, "avg_us": float("nan"), "total_ms": float("nan")})
     attn_bytes = float(np.mean([attn_partial_bytes(wl, n) for n in n_att_timed]))
     achieved = attn_bytes / (attn["avg_us"] * 1e-6) / 1e9
@@ -303,6 +305,11 @@ def main():
         "step_hbm": {"algorithmic_bytes_per_step": alg_bytes,
                      "achieved_gbps": alg_bytes * steps_per_s / 1e9,
                      "frac": alg_bytes * steps_per_s / 1e9 / PEAK_HBM_GBS,
+                     "minimal_bytes_per_step": min_bytes,
+                     "frac_minimal": min_bytes * steps_per_s / 1e9 / PEAK_HBM_GBS,
+                     "note": "bytes with the alpha round trip (written, read by the score "
+                             "update) and minimal bytes (K/V, q, O, score RMW, append), "
+                             "plus the per-Delta terms amortised",
                      "mean_attended_tokens": float(np.mean(n_att_steps))},
         "kernels": kernels,
         "kernels_note": ("per-kernel averages from a second identical run with every kernel "
