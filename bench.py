@@ -297,7 +297,8 @@ def main():
                    "head_dim": wl.head_dim,
                    "tiers_t0_t1_t2_t3": [round(1 - wl.frac_t1 - wl.frac_t2 - wl.frac_t3, 4),
                                          wl.frac_t1, wl.frac_t2, wl.frac_t3],
-                   "delta": wl.delta, "reassignments_timed": len(re_info)},
+                   "delta": wl.delta, "reassignments_timed": len(re_info),
+                   "rows_copied_per_reassignment": [r[4] for r in re_info]},
         "roofline": {"bound": "hbm", "kernel": "attn_partial", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": counter_traffic(args.workload), "bytes_per_launch": attn_bytes,

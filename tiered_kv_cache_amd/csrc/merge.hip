@@ -269,6 +269,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(ScoreArgs a) 
   const int n0 = a.seq.t0_len[bl];
   const int natt = n0 + a.seq.t1_len[bl];
   const int j = (blk - a.seq.base[bl]) * kScoreSlots + lane;
+  // the first row group also owns the score of its slot: its position and the
+  // current score are fetched before the rows, so the three loads overlap
+  float* sp = nullptr;
+  float s_old = 0.f;
+  if (rg == 0 && j < natt) {
+    const int pos = j < n0 ? a.t0_pos[b * a.cap0 + j] : a.t1_pos[b * a.cap1 + (j - n0)];
+    if ((unsigned)pos < (unsigned)a.max_ctx) {  // slot maps hold positions < max_ctx
+      sp = a.scores + b * a.max_ctx + pos;
+      s_old = *sp;
+    }
+  }
   double acc = 0.0;
   if (j < natt) {
     const float* src = a.src + (long)bl * a.seq_stride + j;
@@ -285,14 +296,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(ScoreArgs a) 
   }
   red[rg][lane] = acc;
   __syncthreads();
-  if (tid < kScoreSlots && j < natt) {
+  if (sp) {
     double t = 0.0;
     for (int q = 0; q < kScoreRowGroups; ++q) t += red[q][tid];
-    const int pos = j < n0 ? a.t0_pos[b * a.cap0 + j] : a.t1_pos[b * a.cap1 + (j - n0)];
-    if ((unsigned)pos < (unsigned)a.max_ctx) {  // slot maps hold positions < max_ctx
-      float* sp = a.scores + b * a.max_ctx + pos;
-      *sp = *sp + (float)(t * a.weight);
-    }
+    *sp = s_old + (float)(t * a.weight);
   }
 }
 

@@ -48,19 +48,11 @@ __device__ __forceinline__ bool in_sel(const Sel& s, uint32_t key, int p) {
   return key < s.T || (key == s.T && p >= s.cut);
 }
 
-// hist[bin] += 1 for every active lane, one LDS atomic per distinct bin of the
-// wave (scores of a tail cluster in few bins of the leading digits).
-__device__ __forceinline__ void wave_hist_add(unsigned* hist, unsigned bin, bool active) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint64_t todo = __ballot(active);
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const unsigned lb = (unsigned)__shfl((int)bin, leader, kWave);
-    const uint64_t same = __ballot(active && bin == lb);
-    if (lane == leader) atomicAdd(&hist[lb], (unsigned)__popcll(same));
-    todo &= ~same;
-    if (bin == lb) active = false;
-  }
+// hist[bin] += 1 for every active lane: one LDS atomic per lane.  (Aggregating
+// equal bins of a wave first with ballots costs a serial round per distinct bin,
+// and after the leading digit the candidates spread over many bins.)
+__device__ __forceinline__ void hist_add(unsigned* hist, unsigned bin, bool active) {
+  if (active) atomicAdd(&hist[bin], 1u);
 }
 
 // Digit of the k-th smallest key: the first bin whose inclusive prefix count
@@ -89,6 +81,33 @@ __device__ __forceinline__ void pick_digit(const unsigned* hist, int kk, int* tm
   __syncthreads();
 }
 
+// Positions [0, n) of the block in strides of its size, kPassBatch per thread
+// at a time: the score and tier loads of a batch are issued before any is used.
+constexpr int kPassBatch = 8;
+
+template <class F>
+__device__ __forceinline__ void for_positions(int n, const float* sc, const uint8_t* tp, F f) {
+  for (int p0 = threadIdx.x; p0 < n; p0 += kTierThreads * kPassBatch) {
+    uint32_t key[kPassBatch];
+    int t[kPassBatch];
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) {
+      const int p = p0 + i * kTierThreads;
+      key[i] = 0u;
+      t[i] = 0;
+      if (p < n) {
+        key[i] = score_key(sc[p]);
+        t[i] = tp[p];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) {
+      const int p = p0 + i * kTierThreads;
+      if (p < n) f(p, t[i], key[i]);
+    }
+  }
+}
+
 // k (block-uniform) least important candidates among positions [0, n).
 template <class Cand>
 __device__ Sel radix_select(int k, int n, const float* sc, const uint8_t* tp, Cand cand,
@@ -104,18 +123,9 @@ __device__ Sel radix_select(int k, int n, const float* sc, const uint8_t* tp, Ca
     for (int i = tid; i < 256; i += kTierThreads) hist[i] = 0u;
     __syncthreads();
     const uint32_t himask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
-    // the trip count is the same for every lane of a wave (n is block-uniform and
-    // the stride is the block size), so the ballots below see the whole wave
-    for (int p0 = tid - (tid & (kWave - 1)); p0 < n; p0 += kTierThreads) {
-      const int p = p0 + (tid & (kWave - 1));
-      bool act = false;
-      uint32_t key = 0u;
-      if (p < n) {
-        key = score_key(sc[p]);
-        act = (key & himask) == prefix && cand(p, tp[p], key);
-      }
-      wave_hist_add(hist, (key >> shift) & 255u, act);
-    }
+    for_positions(n, sc, tp, [&](int p, int t, uint32_t key) {
+      hist_add(hist, (key >> shift) & 255u, (key & himask) == prefix && cand(p, t, key));
+    });
     __syncthreads();
     pick_digit(hist, kk, tmp, sh);
     prefix |= (uint32_t)sh[0] << shift;
@@ -189,15 +199,12 @@ __global__ __launch_bounds__(kTierThreads) void assign_tiers_kernel(TierArgs a) 
   auto prot = [=](int p) { return p < prot_lo || p >= prot_hi; };
 
   int cE = 0, cT2 = 0, cPool = 0, cBad = 0;
-  for (int p = tid; p < n; p += kTierThreads) {
-    const int t = tp[p];
-    if (t > 3) ++cBad;
-    else if (t == 3) ++cE;
-    else {
-      if (t == 2) ++cT2;
-      if (!prot(p)) ++cPool;
-    }
-  }
+  for_positions(n, sc, tp, [&](int p, int t, uint32_t) {
+    cBad += t > 3;
+    cE += t == 3;
+    cT2 += t == 2;
+    cPool += t <= 2 && !prot(p);
+  });
   cBad = block_sum_i(cBad, tmp);
   if (cBad) {
     if (tid < 4) counts[tid] = -1;
@@ -213,13 +220,12 @@ __global__ __launch_bounds__(kTierThreads) void assign_tiers_kernel(TierArgs a) 
   const Sel s1 = radix_select(e, n, sc, tp, cand1, hist, tmp, sh);
 
   int cEvT2 = 0, cLive = 0;
-  for (int p = tid; p < n; p += kTierThreads) {
-    const int t = tp[p];
-    if (t > 2 || prot(p)) continue;
-    const bool ev = in_sel(s1, score_key(sc[p]), p);
-    if (t == 2 && ev) ++cEvT2;
-    if (t <= 1 && !ev) ++cLive;
-  }
+  for_positions(n, sc, tp, [&](int p, int t, uint32_t key) {
+    const bool pool = t <= 2 && !prot(p);
+    const bool ev = in_sel(s1, key, p);
+    cEvT2 += pool && t == 2 && ev;
+    cLive += pool && t <= 1 && !ev;
+  });
   cEvT2 = block_sum_i(cEvT2, tmp);
   cLive = block_sum_i(cLive, tmp);
 
@@ -238,10 +244,8 @@ __global__ __launch_bounds__(kTierThreads) void assign_tiers_kernel(TierArgs a) 
   };
   const Sel s3 = radix_select(r1, n, sc, tp, cand3, hist, tmp, sh);
 
-  int c[4] = {0, 0, 0, 0};
-  for (int p = tid; p < n; p += kTierThreads) {
-    const int t = tp[p];
-    const uint32_t key = score_key(sc[p]);
+  int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  for_positions(n, sc, tp, [&](int p, int t, uint32_t key) {
     const bool np = !prot(p);
     int nt;
     if (t == 3) nt = 3;
@@ -251,12 +255,20 @@ __global__ __launch_bounds__(kTierThreads) void assign_tiers_kernel(TierArgs a) 
     else if (np && in_sel(s3, key, p)) nt = 1;
     else nt = 0;
     tn[p] = (uint8_t)nt;
-    ++c[nt];
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int v = block_sum_i(c[t], tmp);
-    if (tid == 0) counts[t] = v;
+    c0 += nt == 0;
+    c1 += nt == 1;
+    c2 += nt == 2;
+    c3 += nt == 3;
+  });
+  c0 = block_sum_i(c0, tmp);
+  c1 = block_sum_i(c1, tmp);
+  c2 = block_sum_i(c2, tmp);
+  c3 = block_sum_i(c3, tmp);
+  if (tid == 0) {
+    counts[0] = c0;
+    counts[1] = c1;
+    counts[2] = c2;
+    counts[3] = c3;
   }
 }
 
@@ -269,6 +281,71 @@ void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s) {
 // relocation (in place)
 // ---------------------------------------------------------------------------
 constexpr int kNoSlot = INT_MIN;
+
+// Helpers of the relocation scan: kPassBatch entries per thread at a time, the
+// loads of a batch issued before any is used, f called in index order.
+
+// Slot -> position map entries [0, len), strided by the block: f(slot, position).
+template <class F>
+__device__ __forceinline__ void for_map(int len, const int* pos, F f) {
+  for (int s0 = threadIdx.x; s0 < len; s0 += kTierThreads * kPassBatch) {
+    int p[kPassBatch];
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) {
+      const int s = s0 + i * kTierThreads;
+      p[i] = s < len ? pos[s] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i)
+      if (s0 + i * kTierThreads < len) f(s0 + i * kTierThreads, p[i]);
+  }
+}
+
+// Positions [lo, hi): f(position, previous tier, new tier, slot code).
+template <class F>
+__device__ __forceinline__ void for_segment(int lo, int hi, const uint8_t* tp, const uint8_t* tn,
+                                            const int* inv, F f) {
+  for (int base = lo; base < hi; base += kPassBatch) {
+    int o[kPassBatch], w[kPassBatch], v[kPassBatch];
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) {
+      const int p = base + i;
+      o[i] = 0;
+      w[i] = 0;
+      v[i] = kNoSlot;
+      if (p < hi) {
+        o[i] = tp[p];
+        w[i] = tn[p];
+        v[i] = inv[p];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i)
+      if (base + i < hi) f(base + i, o[i], w[i], v[i]);
+  }
+}
+
+// Slots [s0, s1) of a pool with `len` rows: f(slot, hole).  A hole is a slot at
+// or past the old length, or one whose row leaves `tier`.  Positions of slots
+// below len are known to lie in [0, n).
+template <class F>
+__device__ __forceinline__ void for_slots(int s0, int s1, int len, const int* pos,
+                                          const uint8_t* tn, int tier, F f) {
+  for (int base = s0; base < s1; base += kPassBatch) {
+    int p[kPassBatch];
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) {
+      const int s = base + i;
+      p[i] = (s < s1 && s < len) ? pos[s] : -1;
+    }
+    int t[kPassBatch];
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i) t[i] = p[i] >= 0 ? (int)tn[p[i]] : -1;
+#pragma unroll
+    for (int i = 0; i < kPassBatch; ++i)
+      if (base + i < s1) f(base + i, t[i] != tier);
+  }
+}
 
 // One workgroup per sequence.  Only the rows whose tier changed, and the rows
 // left above the new length of their pool, move: each fills a "hole", a slot
@@ -292,16 +369,14 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
   for (int p = tid; p < n; p += kTierThreads) inv[p] = kNoSlot;
   __syncthreads();
   int bad = 0;
-  for (int s = tid; s < len0; s += kTierThreads) {
-    const int p = pos0[s];
+  for_map(len0, pos0, [&](int s, int p) {
     if (p < 0 || p >= n) ++bad;
     else inv[p] = s;
-  }
-  for (int s = tid; s < len1; s += kTierThreads) {
-    const int p = pos1[s];
+  });
+  for_map(len1, pos1, [&](int s, int p) {
     if (p < 0 || p >= n) ++bad;
     else inv[p] = -s - 1;
-  }
+  });
   __syncthreads();
 
   // new sizes, and a consistency check of the maps against the previous tiers:
@@ -311,22 +386,17 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
   const int lo = min(n, tid * seg);
   const int hi = min(n, lo + seg);
   int cp0 = 0, cp1 = 0, cn0 = 0, cn1 = 0, ct2 = 0;
-  for (int p = lo; p < hi; ++p) {
-    const int o = tp[p], w = tn[p], v = inv[p];
-    if (o > 3 || w > 3 || (w <= 1 && o > 1)) ++bad;  // T2/T3 never return to full precision
-    if (o == 0) {
-      ++cp0;
-      if (v < 0) ++bad;
-    } else if (o == 1) {
-      ++cp1;
-      if (v >= 0 || v == kNoSlot) ++bad;
-    } else if (v != kNoSlot) {
-      ++bad;
-    }
+  for_segment(lo, hi, tp, tn, inv, [&](int, int o, int w, int v) {
+    bad += o > 3 || w > 3 || (w <= 1 && o > 1);  // T2/T3 never return to full precision
+    bad += o == 0 && v < 0;
+    bad += o == 1 && (v >= 0 || v == kNoSlot);
+    bad += o > 1 && v != kNoSlot;
+    cp0 += o == 0;
+    cp1 += o == 1;
     cn0 += w == 0;
     cn1 += w == 1;
-    ct2 += (w == 2 && o <= 1);
-  }
+    ct2 += w == 2 && o <= 1;
+  });
   bad = block_sum_i(bad, tmp);
   cp0 = block_sum_i(cp0, tmp);
   cp1 = block_sum_i(cp1, tmp);
@@ -347,29 +417,30 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
     const int sg = (n0 + kTierThreads - 1) / kTierThreads;
     const int s0 = min(n0, tid * sg), s1 = min(n0, s0 + sg);
     int c = 0;
-    for (int s = s0; s < s1; ++s) c += (s >= len0 || tn[pos0[s]] != 0);
+    for_slots(s0, s1, len0, pos0, tn, 0, [&](int, bool hole) { c += hole; });
     int k = block_excl_scan(c, tmp, &h0);
-    for (int s = s0; s < s1; ++s)
-      if (s >= len0 || tn[pos0[s]] != 0) holes0[k++] = s;
+    for_slots(s0, s1, len0, pos0, tn, 0, [&](int s, bool hole) {
+      if (hole) holes0[k++] = s;
+    });
   }
   {
     const int sg = (n1 + kTierThreads - 1) / kTierThreads;
     const int s0 = min(n1, tid * sg), s1 = min(n1, s0 + sg);
     int c = 0;
-    for (int s = s0; s < s1; ++s) c += (s >= len1 || tn[pos1[s]] != 1);
+    for_slots(s0, s1, len1, pos1, tn, 1, [&](int, bool hole) { c += hole; });
     int k = block_excl_scan(c, tmp, &h1);
-    for (int s = s0; s < s1; ++s)
-      if (s >= len1 || tn[pos1[s]] != 1) holes1[k++] = s;
+    for_slots(s0, s1, len1, pos1, tn, 1, [&](int s, bool hole) {
+      if (hole) holes1[k++] = s;
+    });
   }
 
   // movers, in position order
   int m0 = 0, m1 = 0, mp = 0;
-  for (int p = lo; p < hi; ++p) {
-    const int o = tp[p], w = tn[p], v = inv[p];
-    m0 += (w == 0 && (o == 1 || (o == 0 && v >= n0)));
-    m1 += (w == 1 && (o == 0 || (o == 1 && -v - 1 >= n1)));
-    mp += (w == 0 && o == 1);
-  }
+  for_segment(lo, hi, tp, tn, inv, [&](int, int o, int w, int v) {
+    m0 += w == 0 && (o == 1 || (o == 0 && v >= n0));
+    m1 += w == 1 && (o == 0 || (o == 1 && -v - 1 >= n1));
+    mp += w == 0 && o == 1;
+  });
   int M0, M1, MP, T2;
   int i0 = block_excl_scan(m0, tmp, &M0);
   int i1 = block_excl_scan(m1, tmp, &M1);
@@ -386,8 +457,7 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
   int2* stg = a.staged + b * a.cap1;
   int* t2s = a.t2_src + b * a.t2_cap;
   int* t2p = a.t2_pos + b * a.t2_cap;
-  for (int p = lo; p < hi; ++p) {
-    const int o = tp[p], w = tn[p], v = inv[p];
+  for_segment(lo, hi, tp, tn, inv, [&](int p, int o, int w, int v) {
     if (w == 0 && o == 1) {
       const int j = ip++;
       stg[j] = make_int2(v, j);
@@ -406,7 +476,7 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
       t2s[it2] = v;
       t2p[it2++] = p;
     }
-  }
+  });
   if (tid == 0) {
     lens[0] = n0;
     lens[1] = n1;
@@ -448,10 +518,42 @@ struct RowRef {
   long slot;  // < 0: plain row
 };
 
-// One wave per (move, layer x KV head) item; consecutive waves take consecutive
-// moves of one (layer, KV head), whose destinations are in slot order.
+// Source and destination rows of one move of one (layer, KV head).
+template <typename T, int D>
+__device__ __forceinline__ void move_rows(const MoveArgs& m, long b, int lg, int2 mv,
+                                          RowRef<T>& src, RowRef<T>& dst) {
+  const long g = b * m.lgs + lg;
+  T* p0k = (T*)m.k0 + g * m.cap0 * D;
+  T* p0v = (T*)m.v0 + g * m.cap0 * D;
+  T* p1k = (T*)m.k1 + g * m.cap1 * D;
+  T* p1v = (T*)m.v1 + g * m.cap1 * D;
+  if (m.which == kMoveStage) {  // T1 slot -> staging row
+    src = {p1k, p1v, (long)(-mv.x - 1)};
+    T* r = (T*)m.staging + ((b * m.cap1 + mv.y) * m.lgs + lg) * 2 * D;
+    dst = {r, r + D, -1};
+  } else if (m.which == kMoveToT1) {  // T0 or T1 slot -> T1 slot
+    src = mv.x >= 0 ? RowRef<T>{p0k, p0v, (long)mv.x} : RowRef<T>{p1k, p1v, (long)(-mv.x - 1)};
+    dst = {p1k, p1v, (long)mv.y};
+  } else {  // T0 slot or staging row -> T0 slot
+    if (mv.x >= 0) {
+      src = {p0k, p0v, (long)mv.x};
+    } else {
+      T* r = (T*)m.staging + ((b * m.cap1 + (-mv.x - 1)) * m.lgs + lg) * 2 * D;
+      src = {r, r + D, -1};
+    }
+    dst = {p0k, p0v, (long)mv.y};
+  }
+}
+
+// One wave per (move, layer x KV head) item, kMoveBatch items of a wave in
+// flight together (list entries first, then every row load, then the stores);
+// consecutive waves take consecutive moves of one (layer, KV head), whose
+// destinations are in slot order.
+constexpr int kMoveBatch = 4;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void reloc_move_kernel(MoveArgs m) {
+  constexpr int VE = D / kWave;  // value elements per lane
   const int lane = threadIdx.x & (kWave - 1);
   const long gw = (long)blockIdx.x * (256 / kWave) + (threadIdx.x / kWave);
   const long nw = (long)gridDim.x * (256 / kWave);
@@ -460,42 +562,49 @@ __global__ __launch_bounds__(256) void reloc_move_kernel(MoveArgs m) {
     const int cnt = m.cnt[b * 4 + m.which];
     const long items = (long)cnt * m.lgs;
     const int2* list = m.list + b * m.list_stride;
-    for (long it = gw; it < items; it += nw) {
-      const int lg = (int)(it / cnt);
-      const int i = (int)(it - (long)lg * cnt);
-      const int2 mv = list[i];
-      const long g = b * m.lgs + lg;
-      T* p0k = (T*)m.k0 + g * m.cap0 * D;
-      T* p0v = (T*)m.v0 + g * m.cap0 * D;
-      T* p1k = (T*)m.k1 + g * m.cap1 * D;
-      T* p1v = (T*)m.v1 + g * m.cap1 * D;
-      RowRef<T> src, dst;
-      if (m.which == kMoveStage) {  // T1 slot -> staging row
-        src = {p1k, p1v, (long)(-mv.x - 1)};
-        T* r = (T*)m.staging + ((b * m.cap1 + mv.y) * m.lgs + lg) * 2 * D;
-        dst = {r, r + D, -1};
-      } else if (m.which == kMoveToT1) {  // T0 or T1 slot -> T1 slot
-        src = mv.x >= 0 ? RowRef<T>{p0k, p0v, (long)mv.x} : RowRef<T>{p1k, p1v, (long)(-mv.x - 1)};
-        dst = {p1k, p1v, (long)mv.y};
-      } else {  // T0 slot or staging row -> T0 slot
-        if (mv.x >= 0) {
-          src = {p0k, p0v, (long)mv.x};
-        } else {
-          T* r = (T*)m.staging + ((b * m.cap1 + (-mv.x - 1)) * m.lgs + lg) * 2 * D;
-          src = {r, r + D, -1};
+    for (long it0 = gw; it0 < items; it0 += nw * kMoveBatch) {
+      int2 mv[kMoveBatch];
+      int lg[kMoveBatch];
+#pragma unroll
+      for (int k = 0; k < kMoveBatch; ++k) {
+        const long it = it0 + k * nw;
+        lg[k] = 0;
+        mv[k] = make_int2(0, 0);
+        if (it < items) {
+          lg[k] = (int)(it / cnt);
+          mv[k] = list[it - (long)lg[k] * cnt];
         }
-        dst = {p0k, p0v, (long)mv.y};
       }
-      if (lane < D / 8) {
-        const int d = 8 * lane;
-        const Vec8<T> kv = load8(src.slot >= 0 ? src.k + k_off(src.slot, d, D) : src.k + d);
-        store8(dst.slot >= 0 ? dst.k + k_off(dst.slot, d, D) : dst.k + d, kv);
+      RowRef<T> src[kMoveBatch], dst[kMoveBatch];
+      Vec8<T> kv[kMoveBatch];
+      T x[kMoveBatch][VE];
+#pragma unroll
+      for (int k = 0; k < kMoveBatch; ++k) {
+        if (it0 + k * nw >= items) continue;
+        move_rows<T, D>(m, b, lg[k], mv[k], src[k], dst[k]);
+        if (lane < D / 8) {
+          const int d = 8 * lane;
+          kv[k] = load8(src[k].slot >= 0 ? src[k].k + k_off(src[k].slot, d, D) : src[k].k + d);
+        }
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const int d = lane + e * kWave;
+          x[k][e] = src[k].slot >= 0 ? src[k].v[v_off(src[k].slot, d, D)] : src[k].v[d];
+        }
       }
 #pragma unroll
-      for (int d = lane; d < D; d += kWave) {
-        const T x = src.slot >= 0 ? src.v[v_off(src.slot, d, D)] : src.v[d];
-        if (dst.slot >= 0) dst.v[v_off(dst.slot, d, D)] = x;
-        else dst.v[d] = x;
+      for (int k = 0; k < kMoveBatch; ++k) {
+        if (it0 + k * nw >= items) continue;
+        if (lane < D / 8) {
+          const int d = 8 * lane;
+          store8(dst[k].slot >= 0 ? dst[k].k + k_off(dst[k].slot, d, D) : dst[k].k + d, kv[k]);
+        }
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const int d = lane + e * kWave;
+          if (dst[k].slot >= 0) dst[k].v[v_off(dst[k].slot, d, D)] = x[k][e];
+          else dst[k].v[d] = x[k][e];
+        }
       }
     }
   }
