@@ -151,8 +151,13 @@ def cpu_baseline(wl, seconds: float) -> dict:
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
-def pcie_leg(wl, cache, positions) -> dict:
-    """Host-link path of T1: host pack into pinned staging + H2D on a side stream."""
+def pcie_leg(wl, cache, positions, device_step_s: float) -> dict:
+    """Host-link path of T1: host pack into pinned staging + H2D on a side stream.
+
+    Also the end-to-end rate if T1 were streamed from host memory every step (the pack
+    redone at each reassignment only, since T1 membership changes only then), next to
+    the link bytes of the persistent device window, which moves changed rows on the
+    device and sends nothing over the link."""
     import numpy as np
     import torch
     from tiered_kv_cache_amd import tkv
@@ -183,9 +188,14 @@ def pcie_leg(wl, cache, positions) -> dict:
     ev1.record(side)
     ev1.synchronize()
     t_h2d = ev0.elapsed_time(ev1) / 1e3 / reps
+    streamed_step_s = max(t_h2d + t_pack / wl.delta, device_step_s)
     return {"t1_rows": n1, "t1_bytes": bytes_t1, "pack_ms": t_pack * 1e3,
             "pack_gbps": bytes_t1 / t_pack / 1e9, "h2d_ms": t_h2d * 1e3,
-            "h2d_gbps": bytes_t1 / t_h2d / 1e9}
+            "h2d_gbps": bytes_t1 / t_h2d / 1e9,
+            "link_bytes_per_step_streamed": bytes_t1,
+            "link_bytes_per_step_device_window": 0,
+            "streamed_steps_per_s": 1.0 / streamed_step_s,
+            "streamed_bound": "host link" if t_h2d + t_pack / wl.delta > device_step_s else "device"}
 
 
 def main():
@@ -338,7 +348,7 @@ def main():
     if not args.no_pcie:
         try:
             t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()   # window slot order
-            out["pcie"] = pcie_leg(wl, cache, t1)
+            out["pcie"] = pcie_leg(wl, cache, t1, 1.0 / steps_per_s)
             out["pcie"]["note"] = ("host-link path of T1, not part of value: host pack into "
                                    "pinned staging, then hipMemcpy2DAsync on a side stream")
         except Exception as e:  # reported, never fatal for the device number

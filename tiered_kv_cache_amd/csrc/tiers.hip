@@ -133,8 +133,17 @@ __device__ Sel radix_select(int k, int n, const float* sc, const uint8_t* tp, Ca
     __syncthreads();
   }
   // kk candidates with key == prefix remain to be taken: the highest positions.
-  // Thread t owns positions [n - (t+1)*seg, n - t*seg): a forward scan over
-  // threads counts ties above each segment.
+  // The last histogram still holds how many candidates have key == prefix; when
+  // all of them are taken (the usual case for distinct scores) no scan is needed.
+  const int ties = (int)hist[prefix & 255u];
+  __syncthreads();
+  if (kk == ties) {
+    r.T = prefix;
+    r.cut = 0;
+    return r;
+  }
+  // Otherwise thread t owns positions [n - (t+1)*seg, n - t*seg): a forward scan
+  // over threads counts ties above each segment.
   const int seg = (n + kTierThreads - 1) / kTierThreads;
   const int hi = max(0, n - tid * seg);
   const int lo = max(0, n - (tid + 1) * seg);
