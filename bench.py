@@ -37,6 +37,10 @@ def parse():
                    help="skip the run that reads a 512 MB buffer before every step")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's timed CPU work")
+    p.add_argument("--eviction-curve", action="store_true",
+                   help="instead of the bench line: output error against full attention, per "
+                        "step, for eviction-only policies and tiered policies that keep the same "
+                        "share of the context in HBM (one JSON line)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one plain 256 MiB read + 256 MiB write elementwise kernel first "
                         "(scale reference for HBM byte counters)")
@@ -198,6 +202,60 @@ def pcie_leg(wl, cache, positions, device_step_s: float) -> dict:
             "streamed_bound": "host link" if t_h2d + t_pack / wl.delta > device_step_s else "device"}
 
 
+def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
+    """Mechanism-level accuracy of the tiers on synthetic inputs.
+
+    For each share x of the context kept out of HBM, four policies run the same
+    inputs as a full-attention run (every position in T0): eviction only (T3 = x),
+    tiered (T1 = x, nothing evicted), T2 = x (8-bit rows, not attended, so at the
+    attention level the same as evicting them), and a fixed eviction with the rest
+    offloaded (T1 = x - 0.05, T3 = 0.05), which Proposition 1 of the pages says
+    must match eviction only at 0.05.  Error of one step: max over (sequence,
+    layer, head) rows of max|O - O_full| / max|O_full|."""
+    import numpy as np
+    import torch
+    from tiered_kv_cache_amd.workload import DeviceWorkload
+
+    dw = DeviceWorkload(wl.with_fractions(0.0, 0.0, 0.0, "_full"))
+    contexts = [st.context() for st in dw.streams]
+    inputs = dw.preload(1, wl.total_steps)
+
+    def run(f1, f2, f3):
+        cache = DeviceWorkload(wl.with_fractions(f1, f2, f3)).make_cache(contexts=contexts)
+        outs = []
+        for k in range(1, wl.total_steps + 1):
+            cache.step(*inputs[k - 1])
+            if k > wl.warmup:
+                outs.append(cache.out.clone())
+        torch.cuda.synchronize()
+        return outs
+
+    full = run(0.0, 0.0, 0.0)
+
+    def err(outs):
+        e = []
+        for o, r in zip(outs, full):
+            num = (o - r).abs().amax(dim=-1)
+            den = r.abs().amax(dim=-1).clamp_min(1e-30)
+            e.append(float((num / den).max()))
+        return {"mean": float(np.mean(e)), "max": float(np.max(e))}
+
+    rows = []
+    for x in shares:
+        row = {"off_hbm_share": x,
+               "eviction_only": err(run(0.0, 0.0, x)),
+               "tiered_t1": err(run(x, 0.0, 0.0)),
+               "t2_not_attended": err(run(0.0, x, 0.0))}
+        if x > 0.05:
+            row["t1_plus_fixed_eviction_0.05"] = err(run(x - 0.05, 0.0, 0.05))
+        rows.append(row)
+        print(f"[curve] {x}: {row}", file=sys.stderr, flush=True)
+    return {"eviction_curve": rows, "workload": f"{wl.name}: {wl.description}",
+            "timed_steps": wl.steps, "warmup": wl.warmup, "delta": wl.delta,
+            "error": "per step: max over (sequence, layer, head) of max|O - O_full| / "
+                     "max|O_full|; mean and max over the timed steps"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -220,6 +278,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = WORKLOADS[args.workload].scaled(steps=args.steps, warmup=args.warmup)
+    if args.eviction_curve:
+        print(json.dumps(eviction_curve(wl)), flush=True)
+        return
     print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
     dw = DeviceWorkload(wl)
     contexts = [st.context() for st in dw.streams]

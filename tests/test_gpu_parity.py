@@ -30,6 +30,14 @@ def test_tiny_prop1_no_eviction_equals_full_attention():
     assert st["reassignments"] == 4 and st["t2_rows"] == 0
 
 
+def test_small_eviction_only_lockstep():
+    # the eviction-only baseline mode (T1 = T2 = 0, 30% evicted): the same path with
+    # only T0 and T3, checked step by step like the tiered policy
+    wl = WORKLOADS["small"].with_fractions(0.0, 0.0, 0.3, "_evict30").scaled(warmup=8, steps=72)
+    st = run_lockstep(wl, label="small_eviction_only")
+    assert st["reassignments"] == 1 and st["t2_rows"] == 0
+
+
 def test_small_gqa4_lockstep():
     wl = WORKLOADS["small"]
     st = run_lockstep(wl)
