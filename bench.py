@@ -321,7 +321,7 @@ def main():
         elapsed = time.perf_counter() - t0
         tkv.tkv_timing_enable(False)
         kernels = {}
-        for name in ("append", "attn_partial", "attn_merge", "score_update", "assign_tiers",
+        for name in ("append", "attn_partial", "attn_merge", "alpha_score", "score_update", "assign_tiers",
                      "reloc_scan", "quantize_t2", "reloc_stage", "reloc_to_t1", "reloc_to_t0"):
             ms, cnt = tkv.tkv_timing_read(name)
             if cnt:

@@ -76,18 +76,22 @@ void drain_timers() {
 }
 }  // namespace
 
-KernelTimer::KernelTimer(const char* name, hipStream_t s) : name_(name), stream_(s), ev_(nullptr) {
+KernelTimer::KernelTimer(const char* name, hipStream_t)
+    : name_(name), start_(nullptr), stop_(nullptr) {
   if (!timers().enabled) return;
   if (!timers().only.empty() && !timers().only.count(name)) return;
-  hipEvent_t e = take_event();
-  if (e && hipEventRecord(e, s) == hipSuccess) ev_ = e;
+  start_ = take_event();
+  stop_ = take_event();
+  if (!start_ || !stop_) {
+    if (start_) timers().free_events.push_back(start_);
+    if (stop_) timers().free_events.push_back(stop_);
+    start_ = stop_ = nullptr;
+  }
 }
 
 KernelTimer::~KernelTimer() {
-  if (!ev_) return;
-  hipEvent_t stop = take_event();
-  if (!stop || hipEventRecord(stop, stream_) != hipSuccess) return;
-  timers().pending.push_back({name_, (hipEvent_t)ev_, stop});
+  if (!start_) return;
+  timers().pending.push_back({name_, start_, stop_});
   if (timers().pending.size() > 4096) drain_timers();
 }
 

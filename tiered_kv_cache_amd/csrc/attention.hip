@@ -708,11 +708,13 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
 // host launchers
 // ---------------------------------------------------------------------------
 template <int D>
-static bool launch_valu(const AttnArgs& a, int group, dim3 grid, hipStream_t s) {
+static bool launch_valu(const AttnArgs& a, int group, dim3 grid, hipStream_t s,
+                        const KernelTimer& timer) {
   switch (group) {
 #define TKV_CASE(G)                                                                 \
   case G:                                                                           \
-    hipLaunchKernelGGL((attn_partial_valu_kernel<D, G>), grid, dim3(256), 0, s, a); \
+    hipExtLaunchKernelGGL((attn_partial_valu_kernel<D, G>), grid, dim3(256), 0, s,    \
+                          timer.start(), timer.stop(), 0, a);                     \
     return true;
     TKV_CASE(1) TKV_CASE(2) TKV_CASE(3) TKV_CASE(4) TKV_CASE(5) TKV_CASE(6) TKV_CASE(7)
     TKV_CASE(8) TKV_CASE(16)
@@ -745,13 +747,15 @@ void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int grou
   if (kv_dtype == TKV_BF16) {
     dim3 grid((unsigned)((a.workers + 3) / 4));
     if (head_dim == 128)
-      hipLaunchKernelGGL((attn_partial_mfma_kernel<128>), grid, dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((attn_partial_mfma_kernel<128>), grid, dim3(256), 0, s,
+                            timer.start(), timer.stop(), 0, a);
     else
-      hipLaunchKernelGGL((attn_partial_mfma_kernel<64>), grid, dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((attn_partial_mfma_kernel<64>), grid, dim3(256), 0, s,
+                            timer.start(), timer.stop(), 0, a);
   } else {
     dim3 grid((unsigned)a.workers);
-    if (head_dim == 128) launch_valu<128>(a, group, grid, s);
-    else launch_valu<64>(a, group, grid, s);
+    if (head_dim == 128) launch_valu<128>(a, group, grid, s, timer);
+    else launch_valu<64>(a, group, grid, s, timer);
   }
 }
 

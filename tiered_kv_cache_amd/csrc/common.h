@@ -1,6 +1,7 @@
 // Internal helpers of libtkv (device math, launch bookkeeping).  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,12 +92,15 @@ tkv_status fail(tkv_status code, const std::string& msg);
 tkv_status hip_check(hipError_t e, const char* what);
 
 // Optional event timing around each launch (see tkv_timing_*).
+// The two events go to hipExtLaunchKernelGGL, which records them when the
+// kernel itself starts and ends (no launch gap inside the interval).
 struct KernelTimer {
   KernelTimer(const char* name, hipStream_t s);
   ~KernelTimer();
+  hipEvent_t start() const { return start_; }
+  hipEvent_t stop() const { return stop_; }
   const char* name_;
-  hipStream_t stream_;
-  void* ev_;  // opaque; null when timing is off
+  hipEvent_t start_, stop_;  // null when timing is off
 };
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }

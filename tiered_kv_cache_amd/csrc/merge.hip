@@ -314,17 +314,22 @@ void launch_attn_merge(const MergeArgs& a, int head_dim, int nblocks, hipStream_
   const int G = a.hq / a.hkv;
   dim3 grid(nblocks), block(kMergeThreads);
   if (head_dim == 128) {
-    if (G <= 8) hipLaunchKernelGGL((attn_merge_kernel<128, 8>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_merge_kernel<128, 16>), grid, block, 0, s, a);
+    if (G <= 8) hipExtLaunchKernelGGL((attn_merge_kernel<128, 8>), grid, block, 0, s,
+                                      timer.start(), timer.stop(), 0, a);
+    else hipExtLaunchKernelGGL((attn_merge_kernel<128, 16>), grid, block, 0, s,
+                               timer.start(), timer.stop(), 0, a);
   } else {
-    if (G <= 8) hipLaunchKernelGGL((attn_merge_kernel<64, 8>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_merge_kernel<64, 16>), grid, block, 0, s, a);
+    if (G <= 8) hipExtLaunchKernelGGL((attn_merge_kernel<64, 8>), grid, block, 0, s,
+                                      timer.start(), timer.stop(), 0, a);
+    else hipExtLaunchKernelGGL((attn_merge_kernel<64, 16>), grid, block, 0, s,
+                               timer.start(), timer.stop(), 0, a);
   }
 }
 
 void launch_score_rows(const ScoreArgs& a, int nblocks, const char* name, hipStream_t s) {
   KernelTimer timer(name, s);
-  hipLaunchKernelGGL(score_rows_kernel, dim3(nblocks), dim3(kScoreThreads), 0, s, a);
+  hipExtLaunchKernelGGL(score_rows_kernel, dim3(nblocks), dim3(kScoreThreads), 0, s,
+                        timer.start(), timer.stop(), 0, a);
 }
 
 }  // namespace tkv

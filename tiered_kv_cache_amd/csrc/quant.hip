@@ -60,11 +60,15 @@ void launch_quantize(const QuantArgs& a, int kv_dtype, int head_dim, int nb, hip
   KernelTimer timer("quantize_t2", s);
   dim3 grid(ceil_div(a.L * a.hkv * 2, 4), a.max_rows, nb);
   if (kv_dtype == TKV_BF16) {
-    if (head_dim == 128) hipLaunchKernelGGL((quantize_kernel<uint16_t, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((quantize_kernel<uint16_t, 64>), grid, dim3(256), 0, s, a);
+    if (head_dim == 128) hipExtLaunchKernelGGL((quantize_kernel<uint16_t, 128>), grid, dim3(256), 0, s,
+                                               timer.start(), timer.stop(), 0, a);
+    else hipExtLaunchKernelGGL((quantize_kernel<uint16_t, 64>), grid, dim3(256), 0, s,
+                               timer.start(), timer.stop(), 0, a);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((quantize_kernel<float, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((quantize_kernel<float, 64>), grid, dim3(256), 0, s, a);
+    if (head_dim == 128) hipExtLaunchKernelGGL((quantize_kernel<float, 128>), grid, dim3(256), 0, s,
+                                               timer.start(), timer.stop(), 0, a);
+    else hipExtLaunchKernelGGL((quantize_kernel<float, 64>), grid, dim3(256), 0, s,
+                               timer.start(), timer.stop(), 0, a);
   }
 }
 

@@ -283,7 +283,8 @@ __global__ __launch_bounds__(kTierThreads) void assign_tiers_kernel(TierArgs a) 
 
 void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s) {
   KernelTimer timer("assign_tiers", s);
-  hipLaunchKernelGGL(assign_tiers_kernel, dim3(nb), dim3(kTierThreads), 0, s, a);
+  hipExtLaunchKernelGGL(assign_tiers_kernel, dim3(nb), dim3(kTierThreads), 0, s,
+                        timer.start(), timer.stop(), 0, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -621,7 +622,8 @@ __global__ __launch_bounds__(256) void reloc_move_kernel(MoveArgs m) {
 
 void launch_reloc_scan(const RelocArgs& a, int nb, hipStream_t s) {
   KernelTimer timer("reloc_scan", s);
-  hipLaunchKernelGGL(reloc_scan_kernel, dim3(nb), dim3(kTierThreads), 0, s, a);
+  hipExtLaunchKernelGGL(reloc_scan_kernel, dim3(nb), dim3(kTierThreads), 0, s,
+                        timer.start(), timer.stop(), 0, a);
 }
 
 void launch_reloc_move(const MoveArgs& m, int kv_dtype, int head_dim, hipStream_t s) {
@@ -629,11 +631,15 @@ void launch_reloc_move(const MoveArgs& m, int kv_dtype, int head_dim, hipStream_
   KernelTimer timer(names[m.which], s);
   const dim3 grid(2048);
   if (kv_dtype == TKV_BF16) {
-    if (head_dim == 128) hipLaunchKernelGGL((reloc_move_kernel<uint16_t, 128>), grid, dim3(256), 0, s, m);
-    else hipLaunchKernelGGL((reloc_move_kernel<uint16_t, 64>), grid, dim3(256), 0, s, m);
+    if (head_dim == 128) hipExtLaunchKernelGGL((reloc_move_kernel<uint16_t, 128>), grid, dim3(256), 0, s,
+                                               timer.start(), timer.stop(), 0, m);
+    else hipExtLaunchKernelGGL((reloc_move_kernel<uint16_t, 64>), grid, dim3(256), 0, s,
+                               timer.start(), timer.stop(), 0, m);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((reloc_move_kernel<float, 128>), grid, dim3(256), 0, s, m);
-    else hipLaunchKernelGGL((reloc_move_kernel<float, 64>), grid, dim3(256), 0, s, m);
+    if (head_dim == 128) hipExtLaunchKernelGGL((reloc_move_kernel<float, 128>), grid, dim3(256), 0, s,
+                                               timer.start(), timer.stop(), 0, m);
+    else hipExtLaunchKernelGGL((reloc_move_kernel<float, 64>), grid, dim3(256), 0, s,
+                               timer.start(), timer.stop(), 0, m);
   }
 }
 
@@ -667,11 +673,15 @@ void launch_append(const AppendArgs& a, int kv_dtype, int head_dim, int nb, hipS
   KernelTimer timer("append", s);
   dim3 grid(a.L * a.hkv, nb);
   if (kv_dtype == TKV_BF16) {
-    if (head_dim == 128) hipLaunchKernelGGL((append_kernel<uint16_t, 128>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((append_kernel<uint16_t, 64>), grid, dim3(64), 0, s, a);
+    if (head_dim == 128) hipExtLaunchKernelGGL((append_kernel<uint16_t, 128>), grid, dim3(64), 0, s,
+                                               timer.start(), timer.stop(), 0, a);
+    else hipExtLaunchKernelGGL((append_kernel<uint16_t, 64>), grid, dim3(64), 0, s,
+                               timer.start(), timer.stop(), 0, a);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((append_kernel<float, 128>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((append_kernel<float, 64>), grid, dim3(64), 0, s, a);
+    if (head_dim == 128) hipExtLaunchKernelGGL((append_kernel<float, 128>), grid, dim3(64), 0, s,
+                                               timer.start(), timer.stop(), 0, a);
+    else hipExtLaunchKernelGGL((append_kernel<float, 64>), grid, dim3(64), 0, s,
+                               timer.start(), timer.stop(), 0, a);
   }
 }
 
