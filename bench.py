@@ -37,6 +37,8 @@ def parse():
                    help="skip the run that reads a 512 MB buffer before every step")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's timed CPU work")
+    p.add_argument("--repeats", type=int, default=5,
+                   help="repetitions of the measured run; value and roofline are their medians")
     p.add_argument("--eviction-curve", action="store_true",
                    help="instead of the bench line: output error against full attention, per "
                         "step, for eviction-only policies and tiered policies that keep the same "
@@ -138,6 +140,21 @@ def cpu_baseline(wl, seconds: float) -> dict:
     seq.reassign()
     t_re = time.perf_counter() - t0
     step_s = float(np.mean(times)) + t_re / wl.delta
+    # the same oracle with its BLAS pool limited to one thread, a few more steps
+    one = []
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t_one = time.perf_counter()
+            while len(one) < 3 and (time.perf_counter() - t_one) < seconds / 2:
+                k += 1
+                q = st.query(k)
+                kn, vn = st.new_kv(k)
+                t0 = time.perf_counter()
+                seq.step(q, kn, vn, reassign=False)
+                one.append(time.perf_counter() - t0)
+    except Exception:  # pragma: no cover
+        one = []
     model = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -146,7 +163,12 @@ def cpu_baseline(wl, seconds: float) -> dict:
                 break
     except OSError:
         pass
+    out_one = ({"value": 1.0 / (float(np.mean(one)) + t_re / wl.delta), "cores": 1,
+                "steps_timed": len(one),
+                "note": "BLAS limited to one thread; reassignment cost from the run above"}
+               if one else None)
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(blas_threads),
+            "blas_threads": int(blas_threads), "one_thread": out_one,
             "kind": "oracle",
             "sample": (f"first {len(times)} decode steps of {wl.name} (full cache, "
                        f"{seq.n - len(times)}+ attended tokens, float64 NumPy) plus one "
@@ -332,10 +354,16 @@ def main():
     # the measured run: only the reported kernel carries timers
     print(f"[bench] warm-up {args.warmup} steps, {args.steps} timed steps", file=sys.stderr,
           flush=True)
-    cache, elapsed, n_att_steps, n_steps, re_info, timed, n_att_timed = run(["attn_partial"],
-                                                                             every=8)
-    del cache
-    torch.cuda.empty_cache()
+    # repeated: the reported figures are the medians over the repetitions
+    reps = []
+    for _ in range(max(1, args.repeats)):
+        cache, elapsed, n_att_steps, n_steps, re_info, timed, n_att_timed = run(["attn_partial"],
+                                                                                 every=8)
+        reps.append((elapsed, timed.get("attn_partial", {}).get("avg_us", float("nan"))))
+        del cache
+        torch.cuda.empty_cache()
+    elapsed = float(np.median([r[0] for r in reps]))
+    attn_med = float(np.median([r[1] for r in reps]))
     # a second, identical run with every kernel timed (the per-kernel breakdown only)
     print("[bench] breakdown run", file=sys.stderr, flush=True)
     cache, elapsed_bd, _, _, _, kernels, _ = run(None)
@@ -345,7 +373,9 @@ def main():
     re_b = sum(reassign_bytes(wl, *r) for r in re_info)
     alg_bytes = (sum(x["total"] for x in step_b) + re_b) / args.steps
     min_bytes = (sum(x["minimal"] for x in step_b) + re_b) / args.steps
-    attn = timed.get("attn_partial", {"launches": 1, "avg_us": float("nan"), "total_ms": float("nan")})
+    attn = dict(timed.get("attn_partial", {"launches": 1, "avg_us": float("nan"),
+                                           "total_ms": float("nan")}))
+    attn["avg_us"] = attn_med
     attn_bytes = float(np.mean([attn_partial_bytes(wl, n) for n in n_att_timed]))
     achieved = attn_bytes / (attn["avg_us"] * 1e-6) / 1e9
 
@@ -370,6 +400,9 @@ def main():
                                          wl.frac_t1, wl.frac_t2, wl.frac_t3],
                    "delta": wl.delta, "reassignments_timed": len(re_info),
                    "rows_copied_per_reassignment": [r[4] for r in re_info]},
+        "repetitions": {"count": len(reps),
+                        "steps_per_s": [args.steps / r[0] for r in reps],
+                        "attn_partial_avg_us": [r[1] for r in reps]},
         "roofline": {"bound": "hbm", "kernel": "attn_partial", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": counter_traffic(args.workload), "bytes_per_launch": attn_bytes,
