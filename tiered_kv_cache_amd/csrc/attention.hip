@@ -1,4 +1,4 @@
-// Decode attention over T0 u T1 and the importance-score accumulation.
+// Decode attention over T0 u T1 (with the append of the step's new token).
 //
 // Method: "Not All Thoughts Need HBM" summary pages (gist.science, paper
 // 2605.09490).  Methodologie section 1: T1 rows reach the GPU before the
@@ -16,8 +16,8 @@
 // W + groups records).
 //
 // Kernels:
-//   attn_partial_mfma -- bf16 path; a worker is one wave, the grid holds as
-//       many waves as fit on the GPU at once.  Per 32-token unit:
+//   attn_partial_mfma -- bf16 path; a worker is one wave, one wave per SIMD
+//       (the grid is resident at once).  Per 32-token unit:
 //       S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the group's query heads padded
 //       to 16 columns), an online softmax with lazy rescaling, and O += P V on
 //       the same MFMA with P split into a bf16 high part and a bf16 remainder
@@ -25,12 +25,15 @@
 //       is permuted so that the S^T accumulator is already the A operand of
 //       P V, and keys and values are stored in the operand order (K-tiles,
 //       V-tiles: layout.h), so every operand load is one contiguous 1 KB wave
-//       access.  The logits of a wave's units are staged in LDS and written
-//       in bursts once its key/value stream is done (stores interleaved with
-//       the stream slow its reads down).  The
-//       logits are kept in base 2 (q.k * softmax_scale * log2 e), so every
-//       weight is one v_exp_f32; they go to `alpha` and are normalised there
-//       by the merge kernels.
+//       access, marked non-temporal (read once).  The next unit's keys and
+//       values are requested as soon as this unit has consumed its own.  The
+//       logits of a wave's units are staged in LDS and written in bursts once
+//       its key/value stream is done (stores interleaved with the stream slow
+//       its reads down).  The logits are kept in base 2 (q.k * softmax_scale *
+//       log2 e), so every weight is one v_exp_f32; they go to `alpha` and are
+//       normalised there by the merge kernels.  With a new token, the wave
+//       whose range holds the T0 unit of its slot also writes its key and
+//       value rows there (and its position, score 0, tier T0).
 //   attn_partial_valu -- float32 path (plain FMAs); a worker is a workgroup.
 // The records are merged, and the logits normalised into alpha, by the merge
 // kernels (merge.hip).
@@ -728,8 +731,8 @@ bool attn_group_supported(int group) { return (group >= 1 && group <= 8) || grou
 
 // Worker count of attn_partial_mfma: one wave per SIMD (4 per CU).  The kernel
 // fits two waves per SIMD, but one streams the keys and values as fast (measured
-// on chain8k: 88.5 us against 90 us) and halves the split records and the work
-// of the merge.
+// on chain8k: 76.1 us against 77.4 us), halves the split records and the work
+// of the merge, and leaves LDS for a logit stage that holds a whole wave's share.
 int mfma_resident_waves(int head_dim) {
   static int cached = 0;
   (void)head_dim;
