@@ -260,10 +260,18 @@ class TieredSequence:
     Attention runs over the T0 rows (resident) followed by the T1 staging
     rows gathered at the last reassignment, exactly as the two halves arrive
     on the device.
+
+    With ``attend_t2`` the T2 rows are attended too, in their reduced
+    precision: each is rebuilt as code * scale from the 8-bit row stored when
+    it entered T2 (Methodologie section 1 keeps T2 at reduced precision; the
+    accuracy the pages report for offloading to T2 is that of this variant).
+    They follow T1 in ascending position order, enter the same softmax, and
+    their scores grow like any attended position's.  T2 still never returns
+    to full precision.
     """
 
     def __init__(self, K0: np.ndarray, V0: np.ndarray, policy: Policy, cap: int,
-                 scale: Optional[float] = None):
+                 scale: Optional[float] = None, attend_t2: bool = False):
         L, hkv, n0, d = K0.shape
         self.policy = policy
         self.layers, self.kv_heads, self.head_dim = L, hkv, d
@@ -279,13 +287,35 @@ class TieredSequence:
         self.t1_K = np.zeros((L, hkv, 0, d), dtype=K0.dtype)
         self.t1_V = np.zeros((L, hkv, 0, d), dtype=V0.dtype)
         self.t2_codes: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
+        self.attend_t2 = attend_t2
         self.steps_done = 0
 
     # ---- helpers -------------------------------------------------------
+    def t2_positions(self) -> np.ndarray:
+        """Attended T2 positions (ascending); empty unless ``attend_t2``."""
+        if not self.attend_t2:
+            return np.zeros(0, dtype=np.int64)
+        return np.nonzero(self.tier[:self.n] == T2)[0].astype(np.int64)
+
+    def t2_rows(self, positions: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        """Rebuilt T2 rows, the exact products code * scale (float64):
+        K, V [L][Hkv][len(positions)][D]."""
+        L, hkv, d = self.layers, self.kv_heads, self.head_dim
+        K = np.zeros((L, hkv, len(positions), d))
+        V = np.zeros((L, hkv, len(positions), d))
+        for j, p in enumerate(positions.tolist()):
+            codes, scales = self.t2_codes[p]          # [L][Hkv][2][D], [L][Hkv][2]
+            c = codes.astype(np.float64)
+            sc = scales.astype(np.float64)
+            K[:, :, j, :] = c[:, :, 0] * sc[:, :, 0, None]
+            V[:, :, j, :] = c[:, :, 1] * sc[:, :, 1, None]
+        return K, V
+
     def attended_positions(self) -> np.ndarray:
-        """Device order: T0 positions ascending, then the T1 staging order."""
+        """Device order: T0 positions ascending, then the T1 staging order, then the
+        attended T2 positions ascending."""
         t0 = np.nonzero(self.tier[:self.n] == T0)[0]
-        return np.concatenate([t0, self.t1_positions]).astype(np.int64)
+        return np.concatenate([t0, self.t1_positions, self.t2_positions()]).astype(np.int64)
 
     def _poison(self, i: int) -> None:
         nan = BF16_NAN if self.K.dtype == np.uint16 else np.float32(np.nan)
@@ -310,11 +340,13 @@ class TieredSequence:
         positions of those m attended rows.
         """
         t0 = np.nonzero(self.tier[:self.n] == T0)[0]
-        pos = np.concatenate([t0, self.t1_positions]).astype(np.int64)
+        t2 = self.t2_positions()
+        pos = np.concatenate([t0, self.t1_positions, t2]).astype(np.int64)
+        K2, V2 = self.t2_rows(t2)
         outs, alphas = [], []
         for l in range(self.layers):
-            K_att = np.concatenate([self.K[l][:, t0, :], self.t1_K[l]], axis=1)
-            V_att = np.concatenate([self.V[l][:, t0, :], self.t1_V[l]], axis=1)
+            K_att = np.concatenate([widen(self.K[l][:, t0, :]), widen(self.t1_K[l]), K2[l]], axis=1)
+            V_att = np.concatenate([widen(self.V[l][:, t0, :]), widen(self.t1_V[l]), V2[l]], axis=1)
             O, a = attention(q[l], K_att, V_att, self.scale)
             outs.append(O)
             alphas.append(a)

@@ -129,3 +129,74 @@ def test_t2_t3_rows_are_poisoned_and_never_attended():
     assert np.isnan(widen(seq.K[:, :, np.nonzero(t >= 2)[0]])).all()
     for O, *_ in outs:
         assert np.all(np.isfinite(O))
+
+
+def _exact_rows(r, shape):
+    """Rows of multiples of 2^-7 with |x| <= 127 * 2^-7 and the bound reached in every
+    row: the 8-bit format holds them exactly (scale 2^-7, codes the integers)."""
+    k = r.integers(-127, 128, size=shape)
+    k[..., 0] = np.where(r.random(shape[:-1]) < 0.5, 127, -127)
+    return (k / 128.0).astype(np.float32)
+
+
+def test_attended_t2_exact_rows_equal_full_attention():
+    # attend_t2 rebuilds T2 rows from their 8-bit codes; with rows the format holds
+    # exactly and nothing evicted, every step must equal full attention over the whole
+    # cache (library SDPA), whatever the T0/T1/T2 split
+    L, hkv, hq, d, n0 = 2, 2, 4, 64, 48
+    r = np.random.default_rng(99)
+    K0 = _exact_rows(r, (L, hkv, n0, d))
+    V0 = _exact_rows(r, (L, hkv, n0, d))
+    pol = Policy(4, 2, 4, 0.25, 0.30, 0.0, 2)
+    seq = TieredSequence(K0, V0, pol, cap=64, attend_t2=True)
+    Kall, Vall = [K0], [V0]
+    seen_t2 = 0
+    for step in range(1, 9):
+        q = r.standard_normal((L, hq, d)).astype(np.float32)
+        kn = _exact_rows(r, (L, hkv, d))
+        vn = _exact_rows(r, (L, hkv, d))
+        O, alpha, pos = seq.step(q, kn, vn)
+        Kall.append(kn[:, :, None, :])
+        Vall.append(vn[:, :, None, :])
+        Kf = np.concatenate(Kall, axis=2)
+        Vf = np.concatenate(Vall, axis=2)
+        assert sorted(pos.tolist()) == list(range(seq.n))            # nothing evicted
+        for l in range(L):
+            np.testing.assert_allclose(O[l], sdpa(q[l], Kf[l], Vf[l]), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(alpha.sum(axis=2), 1.0, atol=1e-12)
+        seen_t2 = max(seen_t2, int((seq.tier[:seq.n] == 2).sum()))
+    assert seen_t2 > 0                                               # T2 rows were attended
+
+
+def test_attended_t2_rows_are_the_dequantised_codes():
+    # with arbitrary rows, the attended T2 rows are code * scale of the quantiser,
+    # not the full-precision rows: the output equals library attention over T0/T1
+    # at full precision and T2 rebuilt by hand from quantize_rows
+    from oracle import quantize_rows
+    L, hkv, hq, d, n0 = 1, 2, 4, 64, 40
+    r = np.random.default_rng(5)
+    K0 = r.standard_normal((L, hkv, n0, d)).astype(np.float32)
+    V0 = r.standard_normal((L, hkv, n0, d)).astype(np.float32)
+    pol = Policy(4, 2, 4, 0.2, 0.4, 0.0, 2)
+    seq = TieredSequence(K0, V0, pol, cap=48, attend_t2=True)
+    Kf, Vf = K0.copy(), V0.copy()
+    for step in range(1, 5):
+        q = r.standard_normal((L, hq, d)).astype(np.float32)
+        kn = r.standard_normal((L, hkv, d)).astype(np.float32)
+        vn = r.standard_normal((L, hkv, d)).astype(np.float32)
+        tiers_before = seq.tier[:seq.n].copy()
+        O, alpha, pos = seq.step(q, kn, vn, reassign=False)
+        Kf = np.concatenate([Kf, kn[:, :, None, :]], axis=2)
+        Vf = np.concatenate([Vf, vn[:, :, None, :]], axis=2)
+        t2 = np.nonzero(tiers_before == 2)[0]
+        Kh, Vh = Kf[:, :, pos].astype(np.float64), Vf[:, :, pos].astype(np.float64)
+        for j, p in enumerate(pos.tolist()):
+            if p in set(t2.tolist()):
+                ck, sk = quantize_rows(Kf[:, :, p])
+                cv, sv = quantize_rows(Vf[:, :, p])
+                Kh[:, :, j] = ck.astype(np.float64) * sk[..., None].astype(np.float64)
+                Vh[:, :, j] = cv.astype(np.float64) * sv[..., None].astype(np.float64)
+        np.testing.assert_allclose(O[0], sdpa(q[0], Kh[0], Vh[0]), rtol=1e-12, atol=1e-12)
+        if step % 2 == 0:
+            seq.reassign()
+    assert (seq.tier[:seq.n] == 2).sum() > 0
