@@ -35,6 +35,9 @@ def parse():
     p.add_argument("--no-pcie", action="store_true")
     p.add_argument("--no-flush-run", action="store_true",
                    help="skip the run that reads a 512 MB buffer before every step")
+    p.add_argument("--no-t2-leg", action="store_true",
+                   help="skip the run that also attends the 8-bit T2 rows (reported under "
+                        "\"attend_t2\", never in value)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the oracle's timed CPU work")
     p.add_argument("--repeats", type=int, default=5,
@@ -64,12 +67,15 @@ def step_bytes(wl, n_att: int, n: int) -> dict:
             "minimal": minimal, "total": minimal + alpha}
 
 
-def attn_partial_bytes(wl, n_att: int) -> int:
+def attn_partial_bytes(wl, n_att: int, n_t2: int = 0) -> int:
     """Algorithmic bytes of one attn_partial launch: K/V of the attended set, the
-    queries, and the raw logits it writes (read back once to normalise)."""
+    queries, and the raw logits it writes (read back once to normalise).  n_att counts
+    the full-precision rows (T0, T1); the n_t2 attended 8-bit rows read D one-byte codes
+    and one float32 scale for K and for V per (layer, KV head)."""
     L, Hq, Hkv, D = wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim
     e = 2 if wl.dtype == "bf16" else 4
-    return 2 * L * Hkv * n_att * D * e + L * Hq * D * e + L * Hq * n_att * 4
+    return (2 * L * Hkv * n_att * D * e + 2 * L * Hkv * n_t2 * (D + 4) + L * Hq * D * e
+            + L * Hq * (n_att + n_t2) * 4)
 
 
 def reassign_bytes(wl, n: int, n0: int, n1: int, r2: int, moved: int) -> int:
@@ -310,12 +316,14 @@ def main():
 
     flush_buf = None
 
-    def run(timed_kernels, every=1, flush=False):
+    def run(timed_kernels, every=1, flush=False, attend_t2=False):
         """Fresh cache, W warm-up steps, then exactly K steps between two syncs with the
         kernel timers on for `timed_kernels` (None = all) on every `every`-th step (each
         pair of events adds a few microseconds around the launch it brackets).  With
-        `flush`, a 512 MB buffer is read before every step (outside the kernel timers)."""
-        cache = dw.make_cache(contexts=contexts)
+        `flush`, a 512 MB buffer is read before every step (outside the kernel timers).
+        With `attend_t2`, the 8-bit T2 rows are attended too; the attended counts are
+        then (full-precision rows, T2 rows) pairs."""
+        cache = dw.make_cache(contexts=contexts, attend_t2=attend_t2)
         torch.cuda.synchronize()
         for k in range(1, args.warmup + 1):
             cache.step(*inputs[k - 1])
@@ -327,7 +335,8 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.warmup + 1, args.warmup + args.steps + 1):
-            n_att.append(sum(cache.t0_len) + sum(cache.t1_len) + wl.batch)
+            full_rows = sum(cache.t0_len) + sum(cache.t1_len) + wl.batch
+            n_att.append((full_rows, sum(cache.t2_len)) if attend_t2 else full_rows)
             n_all.append(sum(cache.n) + wl.batch)
             if flush:
                 flush_buf.sum()
@@ -343,8 +352,9 @@ def main():
         elapsed = time.perf_counter() - t0
         tkv.tkv_timing_enable(False)
         kernels = {}
-        for name in ("append", "attn_partial", "attn_merge", "alpha_score", "score_update", "assign_tiers",
-                     "reloc_scan", "quantize_t2", "reloc_stage", "reloc_to_t1", "reloc_to_t0"):
+        for name in ("append", "attn_partial", "attn_merge", "alpha_score", "score_update",
+                     "assign_tiers", "reloc_scan", "quantize_t2", "reloc_stage", "reloc_to_t1",
+                     "reloc_to_t0", "t2_scan", "t2_move"):
             ms, cnt = tkv.tkv_timing_read(name)
             if cnt:
                 kernels[name] = {"launches": cnt, "avg_us": ms * 1e3 / cnt, "total_ms": ms}
@@ -439,6 +449,23 @@ def main():
                               "note": "512 MB read before every step (memory-side cache "
                                       "cold, as after a model's weight stream)"}
         del flush_buf
+    if not args.no_t2_leg:
+        # the variant that attends the 8-bit T2 rows after T1: same inputs and policy
+        del cache
+        torch.cuda.empty_cache()
+        print("[bench] attended-T2 run", file=sys.stderr, flush=True)
+        cache, el_t2, att_t2, _, re_t2, k_t2, smp_t2 = run(["attn_partial"], every=8,
+                                                           attend_t2=True)
+        a2 = k_t2.get("attn_partial")
+        if a2:
+            b2 = float(np.mean([attn_partial_bytes(wl, f, t) for f, t in smp_t2]))
+            out["attend_t2"] = {
+                "steps_per_s": args.steps / el_t2, "attn_partial_avg_us": a2["avg_us"],
+                "bytes_per_launch": b2, "achieved_gbps": b2 / (a2["avg_us"] * 1e-6) / 1e9,
+                "frac": b2 / (a2["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                "mean_t2_rows": float(np.mean([t for _, t in att_t2])),
+                "note": "T0 u T1 u T2 attended, T2 as int8 code x float32 scale per row "
+                        "(one run, attn_partial timed on every 8th step); not part of value"}
     if not args.no_pcie:
         try:
             t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()   # window slot order

@@ -187,6 +187,68 @@ tkv_status tkv_append_decode_step(const tkv_model* model, int32_t batch, const v
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Attended T2 pool (optional variant of the decode step).  Methodologie
+ * section 1 keeps T2 tokens at reduced precision (8-bit quantisation), and the
+ * accuracy the pages report for offloading to T2 ("Resultats cles") is that of
+ * a model still attending them: each T2 row enters the same softmax as
+ * code * scale of its 8-bit row (the format of tkv_quantize_t2), after the T1
+ * rows.  The pool lives in device memory:
+ *
+ * k_codes, v_codes : device [B][L][Hkv][cap2][D] int8, in the K-tile / V-tile
+ *                    element order of the bf16 pools (one byte per element),
+ *                    16-byte aligned
+ * k_scale, v_scale : device [B][L][Hkv][cap2] float32 (one scale per row),
+ *                    16-byte aligned
+ * t2_pos           : device [B][cap2] slot -> position map (read by the fused
+ *                    score update; may be null when scores are not updated)
+ * t2_len           : host [B], T2 rows in slots [0, t2_len) (<= cap2)
+ * cap2             : multiple of 32
+ * With a T2 pool, the attended index j runs over T0 slots, then T1 slots, then
+ * T2 slots (j - t0_len - t1_len), alpha_stride must cover t0_len + t1_len +
+ * t2_len, and the decode workspace is
+ * tkv_decode_workspace_bytes(model, batch, Lr, cap0, cap1 + cap2).
+ */
+typedef struct {
+  const int8_t* k_codes;
+  const int8_t* v_codes;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* t2_pos;
+  const int32_t* t2_len;
+  int32_t cap2;
+} tkv_t2_pool;
+
+/*
+ * tkv_decode_step_t2 / tkv_append_decode_step_t2 -- tkv_decode_step and
+ * tkv_append_decode_step over the attended set T0 u T1 u T2, with the T2 rows
+ * read from the 8-bit pool `t2` (non-null; see tkv_t2_pool).  Other arguments,
+ * outputs and errors as for the calls without _t2.  Numerics: bf16 data widen
+ * the int8 codes exactly to bf16 for the matrix-core products; the key scale
+ * multiplies the row's logit and the value scale its weight in P.V (the
+ * softmax sum uses the plain weight); float32 data use code * scale in
+ * float32.
+ */
+tkv_status tkv_decode_step_t2(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                              int32_t layer_end, const void* q, const void* k_t0,
+                              const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                              const void* k_t1, const void* v_t1, const int32_t* t1_len,
+                              int32_t cap1, const tkv_t2_pool* t2, float* out, float* alpha,
+                              int32_t alpha_stride, const int32_t* t0_pos,
+                              const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+tkv_status tkv_append_decode_step_t2(const tkv_model* model, int32_t batch, const void* k_new,
+                                     const void* v_new, const int32_t* position, uint8_t* tier,
+                                     const void* q, void* k_t0, void* v_t0,
+                                     const int32_t* t0_len, int32_t cap0, const void* k_t1,
+                                     const void* v_t1, const int32_t* t1_len, int32_t cap1,
+                                     const tkv_t2_pool* t2, float* out, float* alpha,
+                                     int32_t alpha_stride, int32_t* t0_pos,
+                                     const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
  * tkv_update_scores -- the importance-score recurrence (Methodologie section 2):
  * scores[b][pos(j)] += (1/(num_layers*Hq)) * sum over layers in
  * [layer_begin, layer_end) and heads of alpha[b][l][h][j], for every attended
@@ -303,6 +365,47 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
                            int32_t cap1, const int32_t* src, const int32_t* n_rows,
                            int32_t n_rows_stride, int32_t max_rows, int8_t* codes,
                            float* scales, hipStream_t stream);
+
+/* Bytes of device workspace tkv_t2_update needs (hole and move lists). */
+size_t tkv_t2_update_workspace_bytes(int32_t batch, int32_t cap2);
+
+/*
+ * tkv_t2_update -- after a reassignment, bring the attended T2 pool in line
+ * with the new tier map, in place (Methodologie section 4: only the tokens
+ * whose tier changed move; section 1: T2 keeps 8-bit rows).  T2 is left only
+ * for T3 (those rows are dropped), and receives the rows tkv_compact has just
+ * quantised.  Holes are slots below the new length whose row left or which
+ * were past the old length, in slot order; movers are rows that stay but sit
+ * at or past the new length (slot order), then the new rows in their list
+ * order; the i-th mover fills the i-th hole.  Rows that stay below the new
+ * length keep their slots.  Call it after tkv_compact on the same stream.
+ *
+ * ctx_len          : host [B]
+ * tier_next        : device [B][max_ctx], the new tier map
+ * k/v_codes, k/v_scale, t2_pos, cap2 : the pool (see tkv_t2_pool), in/out
+ * t2_len           : host [B], current pool lengths
+ * new_pos          : device [B][max_rows] positions of the new rows
+ *                    (tkv_compact's t2_pos, max_rows = its t2_cap)
+ * new_codes/scales : device [B][max_rows][L][Hkv][2][D] int8 and
+ *                    [B][max_rows][L][Hkv][2] float32 (tkv_compact's output)
+ * n_new            : device int32, element b * n_new_stride is the new row count
+ *                    of sequence b (tkv_compact's new_lens + 2 with stride 4)
+ * new_t2_len       : device [B][2] int32: the new pool length and the row moves
+ *                    made.  If a slot of the old pool maps to a position >= n or
+ *                    to one whose new tier is T0/T1, if the new row count is
+ *                    negative or above max_rows, if the new length exceeds cap2,
+ *                    or if it differs from the number of T2 positions of
+ *                    tier_next, new_t2_len[b] is {-1,-1} and nothing of
+ *                    sequence b is changed.
+ * workspace        : device, tkv_t2_update_workspace_bytes(batch, cap2) bytes
+ */
+tkv_status tkv_t2_update(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
+                         int32_t max_ctx, const uint8_t* tier_next, int8_t* k_codes,
+                         int8_t* v_codes, float* k_scale, float* v_scale, int32_t* t2_pos,
+                         const int32_t* t2_len, int32_t cap2, const int32_t* new_pos,
+                         const int8_t* new_codes, const float* new_scales, const int32_t* n_new,
+                         int32_t n_new_stride, int32_t max_rows, int32_t* new_t2_len,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * tkv_gather_t1 -- bring one sequence's T1 rows to the GPU (Methodologie

@@ -90,6 +90,24 @@ def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, st
             f"scales differ at position {p}"
     stats["t2_rows"] += len(pos)
     stats["reassignments"] += 1
+    if cache.attend_t2:
+        check_t2_pool(cache, b, seq, stats)
+
+
+def check_t2_pool(cache, b, seq: TieredSequence, stats):
+    """The attended T2 pool holds exactly the oracle's T2 positions, each with the
+    int8 codes and scales the oracle stored when it entered T2 (bit-exact)."""
+    t2 = np.nonzero(seq.tier[:seq.n] == 2)[0]
+    assert cache.t2_len[b] == len(t2), f"T2 pool length {cache.t2_len[b]} != {len(t2)}"
+    assert np.array_equal(cache.t2_positions(b), t2), "T2 pool positions differ"
+    kc, vc, ks, vs = cache.t2_pool_rows(b)
+    for j, p in enumerate(t2.tolist()):
+        rc, rs = seq.t2_codes[p]                    # [L][Hkv][2][D], [L][Hkv][2]
+        assert np.array_equal(kc[:, :, j], rc[:, :, 0]), f"T2 pool key codes differ at {p}"
+        assert np.array_equal(vc[:, :, j], rc[:, :, 1]), f"T2 pool value codes differ at {p}"
+        assert np.array_equal(ks[:, :, j].view(np.uint32), rs[:, :, 0].view(np.uint32))
+        assert np.array_equal(vs[:, :, j].view(np.uint32), rs[:, :, 1].view(np.uint32))
+    stats["t2_pool_rows"] = max(stats["t2_pool_rows"], len(t2))
 
 
 def step_inputs(cache, dw, q, kn, vn, fused_append: bool) -> None:
@@ -104,20 +122,22 @@ def step_inputs(cache, dw, q, kn, vn, fused_append: bool) -> None:
 
 
 def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
-                 fused_scores: bool = True, fused_append: bool = True) -> dict:
+                 fused_scores: bool = True, fused_append: bool = True,
+                 attend_t2: bool = False) -> dict:
     """Every step compared; re-sync of the ranking at each reassignment.
     fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores;
     fused_append=False appends with tkv_append before tkv_decode_step instead of
-    tkv_append_decode_step."""
+    tkv_append_decode_step; attend_t2 attends the 8-bit T2 rows after T1 on both sides
+    (the _t2 entry points and the oracle's attend_t2 mode)."""
     n_steps = n_steps or wl.total_steps
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache()
+    cache = dw.make_cache(attend_t2=attend_t2)
     cache.fused_scores = fused_scores
     pol = oracle_policy(wl)
     seqs = []
     for b in range(wl.batch):
         K, V = dw.streams[b].context()
-        seqs.append(TieredSequence(K, V, pol, cap=cache.max_ctx))
+        seqs.append(TieredSequence(K, V, pol, cap=cache.max_ctx, attend_t2=attend_t2))
     stats = defaultdict(float)
     for k in range(1, n_steps + 1):
         q, kn, vn = dw.host_step(k)

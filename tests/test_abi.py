@@ -155,6 +155,68 @@ def test_compact_and_quant_validation():
     assert status_of(tkv.tkv_quantize_t2, **{**qargs, "max_rows": 70000}) == tkv.TKV_ERR_CAPACITY
 
 
+def t2pool(**kw):
+    d = dict(k_codes=FAKE, v_codes=FAKE, k_scale=FAKE, v_scale=FAKE, t2_pos=FAKE, t2_len=[5],
+             cap2=32)
+    d.update(kw)
+    return tkv.T2Pool(**d)
+
+
+def test_decode_step_t2_validation():
+    m = model()
+
+    def call(t2, fused_append=False, **kw):
+        if fused_append:
+            args = dict(batch=1, k_new=FAKE, v_new=FAKE, position=[10], tier=FAKE, q=FAKE,
+                        k_t0=FAKE, v_t0=FAKE, t0_len=[10], cap0=32, k_t1=FAKE, v_t1=FAKE,
+                        t1_len=[2], cap1=32, t2=t2, out=FAKE, alpha=FAKE, alpha_stride=24,
+                        t0_pos=FAKE, t1_pos=FAKE, scores=FAKE, max_ctx=64, workspace=FAKE,
+                        workspace_bytes=1 << 30, stream=0)
+            args.update(kw)
+            return tkv.tkv_append_decode_step_t2(m, **args)
+        args = dict(batch=1, layer_begin=0, layer_end=2, q=FAKE, k_t0=FAKE, v_t0=FAKE,
+                    t0_len=[10], cap0=32, k_t1=FAKE, v_t1=FAKE, t1_len=[2], cap1=32, t2=t2,
+                    out=FAKE, alpha=FAKE, alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE,
+                    scores=FAKE, max_ctx=64, workspace=FAKE, workspace_bytes=1 << 30, stream=0)
+        args.update(kw)
+        return tkv.tkv_decode_step_t2(m, **args)
+
+    assert status_of(call, None) == tkv.TKV_ERR_ARG                         # pool required
+    assert status_of(call, t2pool(t2_len=[33])) == tkv.TKV_ERR_CAPACITY     # > cap2
+    assert status_of(call, t2pool(cap2=40)) == tkv.TKV_ERR_ARG              # 32-slot blocks
+    assert status_of(call, t2pool(t2_len=[-1])) == tkv.TKV_ERR_ARG
+    assert status_of(call, t2pool(k_codes=NULL)) == tkv.TKV_ERR_ARG
+    assert status_of(call, t2pool(v_scale=FAKE + 4)) == tkv.TKV_ERR_ARG     # 16-byte aligned
+    assert status_of(call, t2pool(t2_pos=NULL)) == tkv.TKV_ERR_ARG          # fused scores
+    assert status_of(call, t2pool(t2_len=[13])) == tkv.TKV_ERR_CAPACITY     # stride < 10+2+13
+    ws = tkv.tkv_decode_workspace_bytes(m, 1, 2, 32, 32)
+    assert status_of(call, t2pool(), alpha_stride=64,
+                     workspace_bytes=ws) == tkv.TKV_ERR_CAPACITY            # gsum covers T2
+    assert status_of(call, t2pool(), fused_append=True, t0_len=[32]) == tkv.TKV_ERR_CAPACITY
+    assert status_of(call, t2pool(t2_len=[12]), fused_append=True) == tkv.TKV_ERR_CAPACITY
+    assert status_of(call, None, fused_append=True) == tkv.TKV_ERR_ARG
+
+
+def test_t2_update_validation():
+    m = model()
+    ws = tkv.tkv_t2_update_workspace_bytes(2, 64)
+    assert ws > tkv.tkv_t2_update_workspace_bytes(1, 64) > 0
+    assert tkv.tkv_t2_update_workspace_bytes(-1, 64) == 0
+    args = dict(model=m, batch=2, ctx_len=[100, 50], max_ctx=128, tier_next=FAKE, k_codes=FAKE,
+                v_codes=FAKE, k_scale=FAKE, v_scale=FAKE, t2_pos=FAKE, t2_len=[10, 0], cap2=64,
+                new_pos=FAKE, new_codes=FAKE, new_scales=FAKE, n_new=FAKE, n_new_stride=4,
+                max_rows=16, new_t2_len=FAKE, workspace=FAKE, workspace_bytes=ws, stream=0)
+    assert status_of(tkv.tkv_t2_update, **{**args, "t2_len": [65, 0]}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_t2_update, **{**args, "ctx_len": [129, 0]}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(tkv.tkv_t2_update, **{**args, "cap2": 48}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_t2_update, **{**args, "n_new_stride": 0}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_t2_update, **{**args, "new_codes": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_t2_update, **{**args, "t2_pos": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_t2_update, **{**args, "t2_len": [-2, 0]}) == tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_t2_update, **{**args, "workspace_bytes": ws - 1}) == \
+        tkv.TKV_ERR_CAPACITY
+
+
 def test_append_validation():
     m = model()
     args = dict(model=m, batch=1, k_new=FAKE, v_new=FAKE, k_t0=FAKE, v_t0=FAKE, cap0=32,

@@ -1,0 +1,160 @@
+"""Attended T2 rows on the GPU (tkv_decode_step_t2, tkv_append_decode_step_t2,
+tkv_t2_update) against the oracle's attend_t2 mode: every step compared in lock step
+(output, weights and scores within the tolerances of tests/parity.py; the T2 pool's
+positions, int8 codes and scales bit-exact after every reassignment), and the pool
+update called directly on adversarial transitions."""
+import numpy as np
+import pytest
+import torch
+
+from tests.parity import run_lockstep, say
+from tiered_kv_cache_amd import tkv
+from tiered_kv_cache_amd.driver import (k_rows_to_tiles, k_tiles_to_rows, v_rows_to_tiles,
+                                        v_tiles_to_rows)
+from tiered_kv_cache_amd.synth import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fp32_attend_t2_lockstep():
+    # float32 path (D 64), 40/30/20/10: T2 grows and loses rows to T3 over 4 reassignments
+    st = run_lockstep(WORKLOADS["tiny"], attend_t2=True, label="tiny_attend_t2")
+    assert st["reassignments"] == 4 and st["t2_pool_rows"] > 0
+
+
+def test_small_gqa4_attend_t2_lockstep():
+    # bf16 matrix-core path (D 128, 4 query heads per KV head), 50/30/10/10
+    st = run_lockstep(WORKLOADS["small"], attend_t2=True, label="small_attend_t2")
+    assert st["reassignments"] == 3 and st["t2_pool_rows"] > 0
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 1, 128), (8, 1, 64), (6, 2, 128)],
+                         ids=["group16_d128", "group8_d64", "group3_d128"])
+def test_head_groupings_attend_t2_lockstep(hq, hkv, d):
+    # ragged pair, short tails in every segment (T2 lengths not multiples of 32)
+    base = WORKLOADS["small"]
+    wl = base.scaled(name=f"t2_groups_h{hq}kv{hkv}_d{d}", layers=2, q_heads=hq, kv_heads=hkv,
+                     head_dim=d, batch=2, ctx=(190, 333), warmup=4, steps=8, delta=4, prompt=8,
+                     recent=8, sinks=2, planted=(3, 5), frac_t1=0.3, frac_t2=0.15,
+                     frac_t3=0.05)
+    st = run_lockstep(wl, attend_t2=True)
+    assert st["reassignments"] == 3 * 2 and st["t2_pool_rows"] > 0
+
+
+def test_ragged_batch_attend_t2_lockstep():
+    # five sequences, one too short for any T2 row; T2 twice the T3 share
+    base = WORKLOADS["small"]
+    wl = base.scaled(name="t2_ragged5_L2_h8kv2_d64", layers=2, head_dim=64, batch=5,
+                     ctx=(130, 700, 257, 1100, 12), warmup=8, steps=16, delta=8, prompt=16,
+                     recent=16, sinks=4, planted=(2, 8, 4, 10, 0), frac_t1=0.3, frac_t2=0.2,
+                     frac_t3=0.1)
+    st = run_lockstep(wl, attend_t2=True)
+    assert st["reassignments"] == 3 * 5
+
+
+# ---------------------------------------------------------------------------
+# tkv_t2_update called directly
+# ---------------------------------------------------------------------------
+L, HKV, HQ, D = 2, 3, 6, 128
+CAP2, MAX_ROWS, MAX_CTX = 256, 112, 640
+
+
+def t2_case(rng, kind, n):
+    """Old pool (positions in slot order), the new tier map and the new rows' positions."""
+    tn = rng.choice([0, 1], size=n).astype(np.uint8)
+    old = rng.permutation(rng.choice(n, size=min(n // 3, 150), replace=False)).astype(np.int32)
+    if kind == "mixed":         # about a third of the pool leaves for T3, new rows come in
+        leave = rng.random(len(old)) < 0.35
+    elif kind == "all_leave":   # the pool empties, then refills from new rows only
+        leave = np.ones(len(old), bool)
+    elif kind == "fill":        # nothing leaves; new rows fill the pool to capacity
+        leave = np.zeros(len(old), bool)
+    else:                       # "no_change"
+        leave = np.zeros(len(old), bool)
+    tn[old] = np.where(leave, 3, 2).astype(np.uint8)
+    rest = np.setdiff1d(np.arange(n), old)
+    stay = int((~leave).sum())
+    want = {"mixed": 40, "all_leave": 70, "fill": CAP2 - stay, "no_change": 0}[kind]
+    want = min(want, MAX_ROWS, len(rest))
+    new = np.sort(rng.choice(rest, size=want, replace=False)).astype(np.int32)
+    tn[new] = 2
+    return dict(n=n, old=old, tn=tn, new=new)
+
+
+def test_t2_update_adversarial():
+    rng = np.random.default_rng(20261216)
+    kinds = ["mixed", "all_leave", "fill", "no_change"]
+    seqs = [t2_case(rng, k, n) for k, n in zip(kinds, (600, 400, 640, 300))]
+    # an inconsistent sequence: one old slot points at a position the new map puts in T1
+    bad = t2_case(rng, "mixed", 500)
+    bad["tn"][bad["old"][3]] = 1
+    seqs.append(bad)
+    B = len(seqs)
+    # the old pool: per position a distinct code row and scale (garbage past the lengths)
+    codes = {}
+    pool_k = rng.integers(-127, 128, size=(B, L, HKV, CAP2, D)).astype(np.int8)
+    pool_v = rng.integers(-127, 128, size=(B, L, HKV, CAP2, D)).astype(np.int8)
+    sk = rng.random((B, L, HKV, CAP2)).astype(np.float32)
+    sv = rng.random((B, L, HKV, CAP2)).astype(np.float32)
+    pos = np.full((B, CAP2), -5, np.int32)
+    new_codes = rng.integers(-127, 128, size=(B, MAX_ROWS, L, HKV, 2, D)).astype(np.int8)
+    new_scales = rng.random((B, MAX_ROWS, L, HKV, 2)).astype(np.float32)
+    new_pos = np.zeros((B, MAX_ROWS), np.int32)
+    n_new = np.zeros((B, 4), np.int32)
+    tn = np.zeros((B, MAX_CTX), np.uint8)
+    for b, sq in enumerate(seqs):
+        m = len(sq["old"])
+        pos[b, :m] = sq["old"]
+        for s, p in enumerate(sq["old"].tolist()):
+            codes[(b, p)] = (pool_k[b, :, :, s].copy(), pool_v[b, :, :, s].copy(),
+                             sk[b, :, :, s].copy(), sv[b, :, :, s].copy())
+        r = len(sq["new"])
+        new_pos[b, :r] = sq["new"]
+        n_new[b, 2] = r
+        for i, p in enumerate(sq["new"].tolist()):
+            codes[(b, p)] = (new_codes[b, i, :, :, 0], new_codes[b, i, :, :, 1],
+                             new_scales[b, i, :, :, 0], new_scales[b, i, :, :, 1])
+        tn[b, :sq["n"]] = sq["tn"]
+    dev = dict(
+        k=k_rows_to_tiles(torch.from_numpy(pool_k)).cuda(),
+        v=v_rows_to_tiles(torch.from_numpy(pool_v)).cuda(),
+        sk=torch.from_numpy(sk).cuda(), sv=torch.from_numpy(sv).cuda(),
+        pos=torch.from_numpy(pos).cuda())
+    before = {k: t.clone() for k, t in dev.items()}
+    model = tkv.make_model(L, HQ, HKV, D, tkv.TKV_BF16)
+    ws_bytes = tkv.tkv_t2_update_workspace_bytes(B, CAP2)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.zeros((B, 2), dtype=torch.int32, device="cuda")
+    n_new_d = torch.from_numpy(n_new).cuda()
+    tkv.tkv_t2_update(model, B, [s["n"] for s in seqs], MAX_CTX, torch.from_numpy(tn).cuda(),
+                      dev["k"], dev["v"], dev["sk"], dev["sv"], dev["pos"],
+                      [len(s["old"]) for s in seqs], CAP2, torch.from_numpy(new_pos).cuda(),
+                      torch.from_numpy(new_codes).cuda(), torch.from_numpy(new_scales).cuda(),
+                      n_new_d[:, 2:], 4, MAX_ROWS, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    got_len = out.cpu().numpy()
+    gk = k_tiles_to_rows(dev["k"], CAP2).cpu().numpy()
+    gv = v_tiles_to_rows(dev["v"], CAP2).cpu().numpy()
+    gsk, gsv, gpos = dev["sk"].cpu().numpy(), dev["sv"].cpu().numpy(), dev["pos"].cpu().numpy()
+    for b, sq in enumerate(seqs[:-1]):
+        want = np.nonzero(sq["tn"] == 2)[0]
+        new_len = len(want)
+        stay_low = [s for s, p in enumerate(sq["old"].tolist()) if s < new_len and sq["tn"][p] == 2]
+        moves = new_len - len(stay_low)
+        assert got_len[b].tolist() == [new_len, moves], (kinds[b], got_len[b])
+        slots = gpos[b, :new_len]
+        assert np.array_equal(np.sort(slots), want), kinds[b]
+        for s in stay_low:                      # stayers below the new length keep their slot
+            assert slots[s] == sq["old"][s], (kinds[b], s)
+        for s, p in enumerate(slots.tolist()):  # every slot holds its position's row
+            ck, cv, ssk, ssv = codes[(b, p)]
+            assert np.array_equal(gk[b, :, :, s], ck) and np.array_equal(gv[b, :, :, s], cv), \
+                (kinds[b], s, p)
+            assert np.array_equal(gsk[b, :, :, s].view(np.uint32), ssk.view(np.uint32))
+            assert np.array_equal(gsv[b, :, :, s].view(np.uint32), ssv.view(np.uint32))
+    b = B - 1
+    assert got_len[b].tolist() == [-1, -1]
+    for k in dev:
+        assert torch.equal(dev[k][b], before[k][b]), k
+    say(f"[t2 update] {B - 1} sequences exact (lengths/moves {got_len[:-1].tolist()}), "
+        f"inconsistent one rejected")

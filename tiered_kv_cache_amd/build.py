@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtkv.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "gather.cpp", "attention.hip", "merge.hip", "tiers.hip", "quant.hip"]
+SOURCES = ["api.cpp", "gather.cpp", "attention.hip", "merge.hip", "tiers.hip", "quant.hip",
+           "t2pool.hip"]
 
 ARCH = os.environ.get("TKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

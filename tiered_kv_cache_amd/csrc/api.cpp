@@ -258,7 +258,8 @@ struct AppendInfo {
 };
 
 // tkv_decode_step; with `app`, t0_len are the lengths before the append and the
-// attention kernel performs the append (bf16; the float32 path appends first).
+// attention kernel performs the append (bf16; the float32 path appends first);
+// with `t2`, the 8-bit T2 rows are attended after T1.
 static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
                               int32_t layer_end, const void* q, const void* k_t0,
                               const void* v_t0, const int32_t* t0_len, int32_t cap0,
@@ -266,7 +267,8 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
                               int32_t cap1, float* out, float* alpha, int32_t alpha_stride,
                               const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
                               int32_t max_ctx, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream, const AppendInfo* app) {
+                              hipStream_t stream, const AppendInfo* app,
+                              const tkv_t2_pool* t2) {
   tkv_status st = check_model(model);
   if (st) return st;
   if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
@@ -277,15 +279,28 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap0 < 0 || cap1 < 0 || alpha_stride < 1) return fail(TKV_ERR_ARG, "bad capacity or stride");
   if (cap0 % 32 || cap1 % 32) return fail(TKV_ERR_ARG, "cap0 and cap1 must be multiples of 32");
-  bool any_t1 = false;
+  const int cap2 = t2 ? t2->cap2 : 0;
+  if (t2 && (!t2->t2_len || cap2 < 0 || cap2 % 32))
+    return fail(TKV_ERR_ARG, "T2 pool: t2_len is null or cap2 is not a multiple of 32");
+  bool any_t1 = false, any_t2 = false;
   const int grow = app ? 1 : 0;  // T0 rows added by the append
   for (int b = 0; b < batch; ++b) {
-    if (t0_len[b] < 0 || t1_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
-    if (t0_len[b] + grow > cap0 || t1_len[b] > cap1)
+    const int n2 = t2 ? t2->t2_len[b] : 0;
+    if (t0_len[b] < 0 || t1_len[b] < 0 || n2 < 0) return fail(TKV_ERR_ARG, "negative length");
+    if (t0_len[b] + grow > cap0 || t1_len[b] > cap1 || n2 > cap2)
       return fail(TKV_ERR_CAPACITY, "length > capacity");
-    if ((long)t0_len[b] + grow + t1_len[b] > alpha_stride)
-      return fail(TKV_ERR_CAPACITY, "alpha_stride < t0_len + t1_len");
+    if ((long)t0_len[b] + grow + t1_len[b] + n2 > alpha_stride)
+      return fail(TKV_ERR_CAPACITY, "alpha_stride < t0_len + t1_len + t2_len");
     any_t1 |= t1_len[b] > 0;
+    any_t2 |= n2 > 0;
+  }
+  if (any_t2) {
+    if (!t2->k_codes || !t2->v_codes || !t2->k_scale || !t2->v_scale)
+      return fail(TKV_ERR_ARG, "T2 pool pointer is null but t2_len > 0");
+    if (((uintptr_t)t2->k_codes | (uintptr_t)t2->v_codes | (uintptr_t)t2->k_scale |
+         (uintptr_t)t2->v_scale) & 15)
+      return fail(TKV_ERR_ARG, "T2 codes and scales must be 16-byte aligned");
+    if (scores && !t2->t2_pos) return fail(TKV_ERR_ARG, "fused score update needs t2_pos");
   }
   if (app) {
     if (layer_begin != 0 || layer_end != model->num_layers)
@@ -305,7 +320,8 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     return fail(TKV_ERR_ARG,
                 "alpha_stride must be a multiple of 4, alpha 16-byte and workspace 256-byte aligned");
   const int Lr = layer_end - layer_begin;
-  if (workspace_bytes < tkv_decode_workspace_bytes(model, batch, Lr, cap0, cap1))
+  // the group sums cover every attended slot: T2 slots follow T1
+  if (workspace_bytes < tkv_decode_workspace_bytes(model, batch, Lr, cap0, cap1 + cap2))
     return fail(TKV_ERR_CAPACITY, "workspace too small");
 
   const int hq = model->num_q_heads;
@@ -326,7 +342,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
   }
   const int32_t* att_len = app ? len_after.data() : t0_len;  // attended T0 rows
   const int unit = mfma ? kUnitMfma : kUnitValu;
-  const DecodeWorkspace wl = decode_workspace(model, batch, Lr, cap0, cap1);
+  const DecodeWorkspace wl = decode_workspace(model, batch, Lr, cap0, cap1 + cap2);
   float* part = (float*)workspace + wl.part;
   float* ml = (float*)workspace + wl.ml;
   float* gsum = (float*)workspace + wl.gsum;
@@ -349,6 +365,12 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     a.v0 = v_t0;
     a.k1 = k_t1;
     a.v1 = v_t1;
+    if (any_t2) {
+      a.k2 = t2->k_codes;
+      a.v2 = t2->v_codes;
+      a.ks2 = t2->k_scale;
+      a.vs2 = t2->v_scale;
+    }
     a.out = out;
     a.alpha = alpha;
     a.part = part;
@@ -357,6 +379,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     a.unit = unit;
     a.cap0 = cap0;
     a.cap1 = cap1;
+    a.cap2 = cap2;
     a.L = model->num_layers;
     a.Lr = Lr;
     a.layer_begin = layer_begin;
@@ -384,17 +407,20 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     }
     for (int i = 0; i < nb; ++i) {
       const int n0 = att_len[b0 + i], n1 = t1_len[b0 + i];
+      const int n2 = t2 ? t2->t2_len[b0 + i] : 0;
       a.seq.t0_len[i] = n0;
       a.seq.t1_len[i] = n1;
+      a.seq.t2_len[i] = n2;
       a.seq.base[i] = (int)units;
-      a.seq.units[i] = ceil_div(n0, unit) + ceil_div(n1, unit);
+      a.seq.units[i] = ceil_div(n0, unit) + ceil_div(n1, unit) + ceil_div(n2, unit);
       units += (long)Lr * hkv * a.seq.units[i];
       m.cbase[i] = cblocks;
-      cblocks += Lr * hkv * merge_alpha_blocks(n0 + n1);
+      cblocks += Lr * hkv * merge_alpha_blocks(n0 + n1 + n2);
       sa.seq.t0_len[i] = n0;
       sa.seq.t1_len[i] = n1;
+      sa.seq.t2_len[i] = n2;
       sa.seq.base[i] = sblocks;
-      sblocks += ceil_div(n0 + n1, kScoreSlots);
+      sblocks += ceil_div(n0 + n1 + n2, kScoreSlots);
     }
     if (units > (1L << 30)) return fail(TKV_ERR_CAPACITY, "too many attention work units");
     a.seq.base[nb] = (int)units;
@@ -431,9 +457,11 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
       sa.rows = Lr * hkv;
       sa.t0_pos = t0_pos;
       sa.t1_pos = t1_pos;
+      sa.t2_pos = any_t2 ? t2->t2_pos : nullptr;
       sa.scores = scores;
       sa.cap0 = cap0;
       sa.cap1 = cap1;
+      sa.cap2 = cap2;
       sa.max_ctx = max_ctx;
       sa.weight = 1.0 / ((double)model->num_layers * hq);
       sa.seq.nb = nb;
@@ -459,7 +487,21 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1,
                      v_t1, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
-                     max_ctx, workspace, workspace_bytes, stream, nullptr);
+                     max_ctx, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+tkv_status tkv_decode_step_t2(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                              int32_t layer_end, const void* q, const void* k_t0,
+                              const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                              const void* k_t1, const void* v_t1, const int32_t* t1_len,
+                              int32_t cap1, const tkv_t2_pool* t2, float* out, float* alpha,
+                              int32_t alpha_stride, const int32_t* t0_pos,
+                              const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!t2) return fail(TKV_ERR_ARG, "T2 pool is null");
+  return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1,
+                     v_t1, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
+                     max_ctx, workspace, workspace_bytes, stream, nullptr, t2);
 }
 
 tkv_status tkv_append_decode_step(const tkv_model* model, int32_t batch, const void* k_new,
@@ -474,7 +516,25 @@ tkv_status tkv_append_decode_step(const tkv_model* model, int32_t batch, const v
   const AppendInfo app{k_new, v_new, position, t0_pos, tier};
   return decode_step(model, batch, 0, model->num_layers, q, k_t0, v_t0, t0_len, cap0, k_t1, v_t1,
                      t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores, max_ctx,
-                     workspace, workspace_bytes, stream, &app);
+                     workspace, workspace_bytes, stream, &app, nullptr);
+}
+
+tkv_status tkv_append_decode_step_t2(const tkv_model* model, int32_t batch, const void* k_new,
+                                     const void* v_new, const int32_t* position, uint8_t* tier,
+                                     const void* q, void* k_t0, void* v_t0,
+                                     const int32_t* t0_len, int32_t cap0, const void* k_t1,
+                                     const void* v_t1, const int32_t* t1_len, int32_t cap1,
+                                     const tkv_t2_pool* t2, float* out, float* alpha,
+                                     int32_t alpha_stride, int32_t* t0_pos,
+                                     const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!model) return fail(TKV_ERR_ARG, "model is null");
+  if (!t2) return fail(TKV_ERR_ARG, "T2 pool is null");
+  const AppendInfo app{k_new, v_new, position, t0_pos, tier};
+  return decode_step(model, batch, 0, model->num_layers, q, k_t0, v_t0, t0_len, cap0, k_t1, v_t1,
+                     t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores, max_ctx,
+                     workspace, workspace_bytes, stream, &app, t2);
 }
 
 tkv_status tkv_update_scores(const tkv_model* model, int32_t batch, int32_t layer_begin,
@@ -762,6 +822,85 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
     a.b_offset = b0;
     launch_quantize(a, model->kv_dtype, model->head_dim, nb, stream);
     if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
+  }
+  return TKV_OK;
+}
+
+// T2 update workspace, 256-byte aligned regions: holes [B][cap2] | list [B][cap2] int2 | cnt [B]
+static size_t t2_ws_list(int batch, int cap2) { return round_up((size_t)batch * cap2 * 4, 256); }
+static size_t t2_ws_cnt(int batch, int cap2) {
+  return round_up(t2_ws_list(batch, cap2) + (size_t)batch * cap2 * 8, 256);
+}
+
+size_t tkv_t2_update_workspace_bytes(int32_t batch, int32_t cap2) {
+  if (batch < 0 || cap2 < 0) return 0;
+  return round_up(t2_ws_cnt(batch, cap2) + (size_t)batch * 4, 256);
+}
+
+tkv_status tkv_t2_update(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
+                         int32_t max_ctx, const uint8_t* tier_next, int8_t* k_codes,
+                         int8_t* v_codes, float* k_scale, float* v_scale, int32_t* t2_pos,
+                         const int32_t* t2_len, int32_t cap2, const int32_t* new_pos,
+                         const int8_t* new_codes, const float* new_scales, const int32_t* n_new,
+                         int32_t n_new_stride, int32_t max_rows, int32_t* new_t2_len,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (batch == 0) return TKV_OK;
+  if (!ctx_len || !tier_next || !k_codes || !v_codes || !k_scale || !v_scale || !t2_pos ||
+      !t2_len || !new_pos || !n_new || !new_t2_len || !workspace)
+    return fail(TKV_ERR_ARG, "null pointer");
+  if (max_rows > 0 && (!new_codes || !new_scales))
+    return fail(TKV_ERR_ARG, "null new codes or scales with max_rows > 0");
+  if (cap2 < 1 || cap2 % 32 || max_ctx < 1 || max_rows < 0 || n_new_stride < 1)
+    return fail(TKV_ERR_ARG, "bad capacity, size or stride (cap2 a positive multiple of 32)");
+  for (int b = 0; b < batch; ++b) {
+    if (ctx_len[b] < 0 || t2_len[b] < 0) return fail(TKV_ERR_ARG, "negative length");
+    if (ctx_len[b] > max_ctx || t2_len[b] > cap2)
+      return fail(TKV_ERR_CAPACITY, "ctx_len > max_ctx or t2_len > cap2");
+  }
+  if (workspace_bytes < tkv_t2_update_workspace_bytes(batch, cap2))
+    return fail(TKV_ERR_CAPACITY, "workspace too small");
+  char* base = (char*)workspace;
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    T2ScanArgs a{};
+    a.tnext = tier_next;
+    a.t2_pos = t2_pos;
+    a.new_pos = new_pos;
+    a.n_new = n_new;
+    a.holes = (int*)base;
+    a.list = (int2*)(base + t2_ws_list(batch, cap2));
+    a.cnt = (int*)(base + t2_ws_cnt(batch, cap2));
+    a.out_len = new_t2_len;
+    a.max_ctx = max_ctx;
+    a.cap2 = cap2;
+    a.max_rows = max_rows;
+    a.n_new_stride = n_new_stride;
+    a.b_offset = b0;
+    for (int i = 0; i < nb; ++i) {
+      a.n[i] = ctx_len[b0 + i];
+      a.len2[i] = t2_len[b0 + i];
+    }
+    launch_t2_scan(a, nb, stream);
+    if ((st = hip_check(hipGetLastError(), "t2_scan launch"))) return st;
+    T2MoveArgs m{};
+    m.k2 = k_codes;
+    m.v2 = v_codes;
+    m.ks2 = k_scale;
+    m.vs2 = v_scale;
+    m.new_codes = new_codes;
+    m.new_scales = new_scales;
+    m.list = a.list;
+    m.cnt = a.cnt;
+    m.cap2 = cap2;
+    m.max_rows = max_rows;
+    m.lgs = model->num_layers * model->num_kv_heads;
+    m.b_offset = b0;
+    m.nb = nb;
+    launch_t2_move(m, model->head_dim, stream);
+    if ((st = hip_check(hipGetLastError(), "t2_move launch"))) return st;
   }
   return TKV_OK;
 }

@@ -8,7 +8,10 @@
 // averaged over heads and layers.
 //
 // Work decomposition (stream-K): each (sequence, layer, KV head) "group" has a
-// T0 segment and a T1 segment, cut into work units of U tokens (U = 32 on the
+// T0 segment, a T1 segment and, when the caller attends T2, a T2 segment of
+// 8-bit rows (Methodologie section 1 keeps T2 at reduced precision: each row is
+// attended as code x scale of its stored int8 codes and float32 scale), cut
+// into work units of U tokens (U = 32 on the
 // matrix-core path, 256 on the float32 path); units are numbered group after
 // group.  Worker w of W owns units [w*P/W, (w+1)*P/W) -- an equal share, so the
 // launch has no tail -- runs one online softmax per group it touches and writes
@@ -55,9 +58,9 @@ struct Unit {
   long b;      // sequence in the caller's batch
   long group;  // group index within the launch
   int lr, g;   // layer (relative) and KV head
-  int seg;     // 0: T0 pool, 1: T1 window
+  int seg;     // 0: T0 pool, 1: T1 window, 2: T2 pool (int8)
   int c0, c1;  // slot range inside the segment
-  int n0;      // T0 length (attended index of T1 slot 0)
+  int off;     // attended index of the segment's slot 0
 };
 
 __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long p) {
@@ -65,8 +68,7 @@ __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long p) {
   while (bl + 1 < a.seq.nb && a.seq.base[bl + 1] <= p) ++bl;
   Unit u;
   u.b = a.seq.b_offset + bl;
-  const int n0 = a.seq.t0_len[bl], n1 = a.seq.t1_len[bl];
-  u.n0 = n0;
+  const int n0 = a.seq.t0_len[bl], n1 = a.seq.t1_len[bl], n2 = a.seq.t2_len[bl];
   const long local = p - a.seq.base[bl];
   const int per = a.seq.units[bl];
   const int lgl = (int)(local / per);
@@ -75,14 +77,22 @@ __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long p) {
   u.g = lgl - u.lr * a.hkv;
   u.group = (long)bl * a.Lr * a.hkv + lgl;
   const int nu0 = (n0 + a.unit - 1) / a.unit;
+  const int nu1 = (n1 + a.unit - 1) / a.unit;
   if (q < nu0) {
     u.seg = 0;
     u.c0 = q * a.unit;
     u.c1 = min(n0, u.c0 + a.unit);
-  } else {
+    u.off = 0;
+  } else if (q < nu0 + nu1) {
     u.seg = 1;
     u.c0 = (q - nu0) * a.unit;
     u.c1 = min(n1, u.c0 + a.unit);
+    u.off = n0;
+  } else {
+    u.seg = 2;
+    u.c0 = (q - nu0 - nu1) * a.unit;
+    u.c1 = min(n2, u.c0 + a.unit);
+    u.off = n0 + n1;
   }
   return u;
 }
@@ -96,11 +106,29 @@ struct Cursor {
   int bl;      // sequence within the launch
   int lgl;     // group within the sequence: layer * Hkv + KV head
   int lr, g;
-  int seg;     // 0: T0 pool, 1: T1 window
+  int seg;     // 0: T0 pool, 1: T1 window, 2: T2 pool (int8)
   int c0;      // first slot of the unit inside the segment
-  int n0, n1;
+  int n0, n1, n2;
 };
 
+// The cursor helpers take T2 (the launch has T2 units) as a template flag: the
+// launches without T2 rows keep the two-segment walk, whose scalar code the
+// compiler schedules around the key/value stream best (a three-way segment
+// select there measurably slowed the stream on chain-8K sizes).
+template <bool T2>
+__device__ __forceinline__ int seg_len(const Cursor& c) {
+  if constexpr (T2) return c.seg == 0 ? c.n0 : (c.seg == 1 ? c.n1 : c.n2);
+  else return c.seg ? c.n1 : c.n0;
+}
+
+// attended index of the unit's segment slot 0: T0, then T1, then T2
+template <bool T2>
+__device__ __forceinline__ int seg_off(const Cursor& c) {
+  if constexpr (T2) return c.seg == 0 ? 0 : (c.seg == 1 ? c.n0 : c.n0 + c.n1);
+  else return c.seg ? c.n0 : 0;
+}
+
+template <bool T2>
 __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
   Cursor c;
   int bl = 0;
@@ -108,6 +136,7 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
   c.bl = bl;
   c.n0 = a.seq.t0_len[bl];
   c.n1 = a.seq.t1_len[bl];
+  c.n2 = T2 ? a.seq.t2_len[bl] : 0;
   const long local = p - a.seq.base[bl];
   const int per = a.seq.units[bl];
   c.lgl = (int)(local / per);
@@ -115,19 +144,33 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
   c.lr = c.lgl / a.hkv;
   c.g = c.lgl - c.lr * a.hkv;
   const int nu0 = (c.n0 + kUnitMfma - 1) / kUnitMfma;
-  c.seg = q < nu0 ? 0 : 1;
-  c.c0 = (q < nu0 ? q : q - nu0) * kUnitMfma;
+  if constexpr (T2) {
+    const int nu1 = (c.n1 + kUnitMfma - 1) / kUnitMfma;
+    c.seg = q < nu0 ? 0 : (q < nu0 + nu1 ? 1 : 2);
+    c.c0 = (q < nu0 ? q : (q < nu0 + nu1 ? q - nu0 : q - nu0 - nu1)) * kUnitMfma;
+  } else {
+    c.seg = q < nu0 ? 0 : 1;
+    c.c0 = (q < nu0 ? q : q - nu0) * kUnitMfma;
+  }
   return c;
 }
 
-// Next unit in the global order (T0 units, then T1 units, group after group).
+// Next unit in the global order (T0 units, then T1 units, then T2 units,
+// group after group).
+template <bool T2>
 __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   c.c0 += kUnitMfma;
-  if (c.c0 < (c.seg ? c.n1 : c.n0)) return;
+  if (c.c0 < seg_len<T2>(c)) return;
   c.c0 = 0;
   if (c.seg == 0 && c.n1 > 0) {
     c.seg = 1;
     return;
+  }
+  if constexpr (T2) {
+    if (c.seg <= 1 && c.n2 > 0) {
+      c.seg = 2;
+      return;
+    }
   }
   if (++c.g == a.hkv) {
     c.g = 0;
@@ -142,15 +185,21 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
     if (c.bl < a.seq.nb) {
       c.n0 = a.seq.t0_len[c.bl];
       c.n1 = a.seq.t1_len[c.bl];
+      if constexpr (T2) c.n2 = a.seq.t2_len[c.bl];
     }
   }
-  c.seg = c.n0 > 0 ? 0 : 1;
+  if constexpr (T2) c.seg = c.n0 > 0 ? 0 : (c.n1 > 0 ? 1 : 2);
+  else c.seg = c.n0 > 0 ? 0 : 1;
 }
 
+// Operand registers of one unit.  T2 units hold 8 int8 codes per operand in
+// .x/.y (widened to bf16 when consumed) and the key / value scales of the
+// lane's 8 tokens.
 template <int D>
 struct UnitLoads {
   uint4 k[2][D / 32];
   uint4 v[D / 16];
+  float4 ks[2], vs[2];
 };
 
 template <int D>
@@ -252,29 +301,82 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
   return make_uint4(x.x, x.y, x.z, x.w);
 }
 
-template <int D>
-__device__ __forceinline__ long unit_base(const AttnArgs& a, const Cursor& c) {
-  const long b = a.seq.b_offset + c.bl;
-  const int cap = c.seg ? a.cap1 : a.cap0;
-  return ((b * a.L + a.layer_begin + c.lr) * a.hkv + c.g) * (long)cap * D + (long)c.c0 * D;
+// 8 int8 codes of a T2 operand (the same element order at one byte each: every
+// operand load is one contiguous 512-byte wave access), kept in .x/.y.
+__device__ __forceinline__ uint4 ld_stream8(const uint2* p) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint4(x.x, x.y, 0u, 0u);
 }
 
-template <int D>
-__device__ __forceinline__ void issue_k(const AttnArgs& a, const Cursor& c, int lane,
+// int8 codes -> bf16, exactly (|code| <= 127 needs 7 significant bits): the
+// float32 conversion of the code, truncated to its upper half.
+__device__ __forceinline__ uint32_t bf16_pair_of_codes(uint32_t w, int sh) {
+  const float lo = (float)(int)(int8_t)(w >> sh);
+  const float hi = (float)(int)(int8_t)(w >> (sh + 8));
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+__device__ __forceinline__ bf16x8_t widen_codes(const uint4& x) {
+  return as_bf16x8(make_uint4(bf16_pair_of_codes(x.x, 0), bf16_pair_of_codes(x.x, 16),
+                              bf16_pair_of_codes(x.y, 0), bf16_pair_of_codes(x.y, 16)));
+}
+
+// Row index (sequence, layer, KV head) of the unit's group, and its first slot
+// as an element offset inside the segment's storage.
+__device__ __forceinline__ long unit_row(const AttnArgs& a, const Cursor& c) {
+  const long b = a.seq.b_offset + c.bl;
+  return (b * a.L + a.layer_begin + c.lr) * a.hkv + c.g;
+}
+
+template <int D, bool T2>
+__device__ __forceinline__ long unit_base(const AttnArgs& a, const Cursor& c) {
+  int cap;
+  if constexpr (T2) cap = c.seg == 0 ? a.cap0 : (c.seg == 1 ? a.cap1 : a.cap2);
+  else cap = c.seg ? a.cap1 : a.cap0;
+  return unit_row(a, c) * (long)cap * D + (long)c.c0 * D;
+}
+
+// T2: the launch has T2 units.  A separate instantiation, because loads of two
+// formats into the same prefetch registers behind a branch make the compiler
+// wait for them early and the key/value stream loses its overlap.
+template <int D, bool T2>
+__device__ __forceinline__ void issue_k(const AttnArgs& a, const Cursor& c, int lane, int grp,
                                         UnitLoads<D>& L) {
   constexpr int KB = D / 32;
-  const uint4* Ku = (const uint4*)((const uint16_t*)(c.seg ? a.k1 : a.k0) + unit_base<D>(a, c));
+  if (T2 && c.seg == 2) {  // int8 codes, and both scales of the lane's 8 tokens
+    const uint2* Ku = (const uint2*)(a.k2 + unit_base<D, T2>(a, c));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) L.k[u][kb] = ld_stream8(&Ku[u * 2 * D + kb * 64 + lane]);
+    const long so = unit_row(a, c) * (long)a.cap2 + c.c0 + 8 * grp;
+    const float4* ks = (const float4*)(a.ks2 + so);
+    const float4* vs = (const float4*)(a.vs2 + so);
+    L.ks[0] = ks[0];
+    L.ks[1] = ks[1];
+    L.vs[0] = vs[0];
+    L.vs[1] = vs[1];
+    return;
+  }
+  const uint4* Ku = (const uint4*)((const uint16_t*)(c.seg ? a.k1 : a.k0) + unit_base<D, T2>(a, c));
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) L.k[u][kb] = ld_stream(&Ku[u * 2 * D + kb * 64 + lane]);
 }
 
-template <int D>
+template <int D, bool T2>
 __device__ __forceinline__ void issue_v(const AttnArgs& a, const Cursor& c, int lane,
                                         UnitLoads<D>& L) {
   constexpr int NB = D / 16;
-  const uint4* Vu = (const uint4*)((const uint16_t*)(c.seg ? a.v1 : a.v0) + unit_base<D>(a, c));
+  if (T2 && c.seg == 2) {
+    const uint2* Vu = (const uint2*)(a.v2 + unit_base<D, T2>(a, c));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) L.v[nb] = ld_stream8(&Vu[nb * 64 + lane]);
+    return;
+  }
+  const uint4* Vu = (const uint4*)((const uint16_t*)(c.seg ? a.v1 : a.v0) + unit_base<D, T2>(a, c));
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) L.v[nb] = ld_stream(&Vu[nb * 64 + lane]);
 }
@@ -297,12 +399,12 @@ struct AppendRow {
 
 // The appended row in this wave's unit range (a range holds at most one T0 tail
 // unit per group; the first one is taken, the others are written at once).
-template <int D>
+template <int D, bool T2>
 __device__ bool find_append(const AttnArgs& a, long p0, long p1, int lane, AppendRow& r,
                             long& pu_first) {
   const int per_seq = a.Lr * a.hkv;
-  const Cursor first = cursor_at(a, p0);
-  const Cursor last = cursor_at(a, p1 - 1);
+  const Cursor first = cursor_at<T2>(a, p0);
+  const Cursor last = cursor_at<T2>(a, p1 - 1);
   const long g0 = (long)first.bl * per_seq + first.lgl;
   const long g1 = (long)last.bl * per_seq + last.lgl;
   bool found = false;
@@ -361,31 +463,43 @@ __device__ __forceinline__ void store_append(const AttnArgs& a, const AppendRow&
   }
 }
 
-template <int D>
-__device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, int lane,
+template <int D, bool T2>
+__device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, int lane, int grp,
                                             UnitLoads<D>& L) {
-  issue_k<D>(a, c, lane, L);
-  issue_v<D>(a, c, lane, L);
+  issue_k<D, T2>(a, c, lane, grp, L);
+  issue_v<D, T2>(a, c, lane, L);
 }
 
 // Logits of one unit from its keys: S^T = K Q^T, staged in LDS, the online
 // softmax update, and P (bf16 high part + bf16 remainder) for P.V.
-template <int D, bool FULL>
+// Q8 (a T2 unit): the keys are int8 codes, widened exactly to bf16, so the
+// product is q.code; the row's key scale turns it into q.(code x scale).  The
+// values are codes too: P enters P.V multiplied by each row's value scale,
+// while the softmax sum keeps the plain weights.
+template <int D, bool FULL, bool Q8, bool T2>
 __device__ __forceinline__ void unit_scores(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
                                             int h, int grp, int G, WaveState<D>& st, Stage& sg,
                                             bf16x8_t& phi, bf16x8_t& plo) {
   constexpr int KB = D / 32, NB = D / 16;
   constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
-  const int c1 = c.seg ? c.n1 : c.n0;
+  const int c1 = seg_len<T2>(c);
   const int tb = c.c0 + 8 * grp;  // first of this lane's 8 tokens
   // S^T = K Q^T: this lane gets tokens tb + e (e = 0..7) of head h
   f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.k[0][kb]), st.qop[kb], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.k[1][kb]), st.qop[kb], s1, 0, 0, 0);
+    const bf16x8_t k0 = Q8 ? widen_codes(L.k[0][kb]) : as_bf16x8(L.k[0][kb]);
+    const bf16x8_t k1 = Q8 ? widen_codes(L.k[1][kb]) : as_bf16x8(L.k[1][kb]);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, st.qop[kb], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, st.qop[kb], s1, 0, 0, 0);
   }
   float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  if (Q8) {
+    const float ks[8] = {L.ks[0].x, L.ks[0].y, L.ks[0].z, L.ks[0].w,
+                         L.ks[1].x, L.ks[1].y, L.ks[1].z, L.ks[1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] *= ks[e];
+  }
   float pm = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -400,7 +514,7 @@ __device__ __forceinline__ void unit_scores(const AttnArgs& a, const Cursor& c, 
     dst[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
   }
   if ((threadIdx.x & 63) == 0) {
-    sg.dst[sg.n] = st.lrow0 + (c.seg ? c.n0 : 0) + c.c0;
+    sg.dst[sg.n] = st.lrow0 + seg_off<T2>(c) + c.c0;
     sg.count[sg.n] = min(kUnitMfma, c1 - c.c0);
   }
   ++sg.n;
@@ -418,24 +532,42 @@ __device__ __forceinline__ void unit_scores(const AttnArgs& a, const Cursor& c, 
     }
     st.m = mn;
   }
+  float vsc[8];
+  if (Q8) {
+    vsc[0] = L.vs[0].x; vsc[1] = L.vs[0].y; vsc[2] = L.vs[0].z; vsc[3] = L.vs[0].w;
+    vsc[4] = L.vs[1].x; vsc[5] = L.vs[1].y; vsc[6] = L.vs[1].z; vsc[7] = L.vs[1].w;
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float pe = __builtin_amdgcn_exp2f(sv[e] - st.m);  // masked slots: exp2(-inf) = 0
     st.lsum += pe;
-    const __bf16 hb = (__bf16)pe;
+    float pv = pe;
+    // masked T2 slots: P is 0 whatever the stale scale past the segment end holds
+    if (Q8) pv = (FULL || tb + e < c1) ? pe * vsc[e] : 0.f;
+    const __bf16 hb = (__bf16)pv;
     phi[e] = hb;
-    plo[e] = (__bf16)(pe - (float)hb);
+    plo[e] = (__bf16)(pv - (float)hb);
   }
 }
 
-// O += P V (high part, then the remainder).
-template <int D, bool FULL>
+// O += P V (high part, then the remainder).  Q8: the values are int8 codes,
+// widened exactly; P already carries the value scales.
+template <int D, bool FULL, bool Q8, bool T2>
 __device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, int grp,
                                             const bf16x8_t& phi, const bf16x8_t& plo,
                                             WaveState<D>& st) {
   constexpr int NB = D / 16;
+  if (Q8) {  // codes are finite, and P is 0 on masked slots: nothing to clear
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8_t v = widen_codes(L.v[nb]);
+      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, v, st.acc[nb], 0, 0, 0);
+      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, v, st.acc[nb], 0, 0, 0);
+    }
+    return;
+  }
   if (!FULL) {  // tail: zero the value slots past the end of the segment (they may hold NaN)
-    const int valid = (c.seg ? c.n1 : c.n0) - (c.c0 + 8 * grp);
+    const int valid = seg_len<T2>(c) - (c.c0 + 8 * grp);
     if (valid < 8) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -458,12 +590,13 @@ __device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, in
 #define TKV_MFMA_MIN_BLOCKS 2
 #endif
 
+template <bool T2>
 __device__ __forceinline__ bool unit_full(const Cursor& c) {
-  return c.c0 + kUnitMfma <= (c.seg ? c.n1 : c.n0);
+  return c.c0 + kUnitMfma <= seg_len<T2>(c);
 }
 
 // One unit: group change, staging, Q.K, the next unit's keys, P.V, its values.
-template <int D>
+template <int D, bool T2>
 __device__ __forceinline__ void process_unit(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
                                              const Cursor& cn, bool more, long w, int lane,
                                              int h, int grp, int G, WaveState<D>& st, Stage& sg) {
@@ -474,17 +607,25 @@ __device__ __forceinline__ void process_unit(const AttnArgs& a, const Cursor& c,
   }
   if (sg.n == sg.cap) flush_stage(a, lane, G, sg);
   bf16x8_t phi, plo;
-  const bool full = unit_full(c);
-  if (full) unit_scores<D, true>(a, c, L, h, grp, G, st, sg, phi, plo);
-  else unit_scores<D, false>(a, c, L, h, grp, G, st, sg, phi, plo);
-  if (more) issue_k<D>(a, cn, lane, L);
-  if (full) unit_values<D, true>(c, L, grp, phi, plo, st);
-  else unit_values<D, false>(c, L, grp, phi, plo, st);
-  if (more) issue_v<D>(a, cn, lane, L);
+  const bool full = unit_full<T2>(c);
+  if (T2 && c.seg == 2) {  // 8-bit T2 rows
+    if (full) unit_scores<D, true, true, T2>(a, c, L, h, grp, G, st, sg, phi, plo);
+    else unit_scores<D, false, true, T2>(a, c, L, h, grp, G, st, sg, phi, plo);
+    if (more) issue_k<D, T2>(a, cn, lane, grp, L);
+    unit_values<D, true, true, T2>(c, L, grp, phi, plo, st);
+    if (more) issue_v<D, T2>(a, cn, lane, L);
+    return;
+  }
+  if (full) unit_scores<D, true, false, T2>(a, c, L, h, grp, G, st, sg, phi, plo);
+  else unit_scores<D, false, false, T2>(a, c, L, h, grp, G, st, sg, phi, plo);
+  if (more) issue_k<D, T2>(a, cn, lane, grp, L);
+  if (full) unit_values<D, true, false, T2>(c, L, grp, phi, plo, st);
+  else unit_values<D, false, false, T2>(c, L, grp, phi, plo, st);
+  if (more) issue_v<D, T2>(a, cn, lane, L);
 }
 
 
-template <int D>
+template <int D, bool T2>
 __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_kernel(AttnArgs a) {
   __shared__ float stage_buf[4][kStageFloats];
   __shared__ long stage_dst[4][kStageUnits];
@@ -510,7 +651,7 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
   sg.cap = min(kStageUnits, kStageFloats / (32 * G));
   AppendRow ar;
   long pu = -1;
-  const bool app = a.kn && find_append<D>(a, p0, p1, lane, ar, pu);
+  const bool app = a.kn && find_append<D, T2>(a, p0, p1, lane, ar, pu);
   uint4 kx = make_uint4(0, 0, 0, 0);
   uint16_t vx[D / 64];
   if (app) {  // fetch the new rows
@@ -524,19 +665,19 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
     }
   }
   WaveState<D> st;
-  Cursor c = cursor_at(a, p0);
+  Cursor c = cursor_at<T2>(a, p0);
   begin_group<D>(a, c, h, grp, G, st);
   // Rolling prefetch: the next unit's keys are requested as soon as Q.K of this
   // unit has consumed the key registers, its values as soon as P.V has consumed
   // the value registers, so a unit's worth of loads stays in flight.
   UnitLoads<D> L;
-  issue_loads<D>(a, c, lane, L);
+  issue_loads<D, T2>(a, c, lane, grp, L);
   if (app && pu != p0) store_append<D>(a, ar, lane, kx, vx);  // read back units later
   for (long p = p0; p < p1; ++p) {
     const bool more = p + 1 < p1;
     Cursor cn = c;
-    if (more) cursor_next(a, cn);
-    process_unit<D>(a, c, L, cn, more, w, lane, h, grp, G, st, sg);
+    if (more) cursor_next<T2>(a, cn);
+    process_unit<D, T2>(a, c, L, cn, more, w, lane, h, grp, G, st, sg);
     c = cn;
   }
   flush_record<D>(a, w, h, grp, G, st);
@@ -600,10 +741,13 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
       }
       __syncthreads();
     }
-    const int cap = u.seg ? a.cap1 : a.cap0;
+    const bool q8 = u.seg == 2;  // 8-bit T2 rows: code x scale
+    const int cap = u.seg == 0 ? a.cap0 : (u.seg == 1 ? a.cap1 : a.cap2);
     const long lg = (u.b * a.L + a.layer_begin + u.lr) * a.hkv + u.g;
     const float* Kb = (const float*)(u.seg ? a.k1 : a.k0) + lg * cap * D;
     const float* Vb = (const float*)(u.seg ? a.v1 : a.v0) + lg * cap * D;
+    const int8_t* Kc = a.k2 + lg * cap * D;
+    const int8_t* Vc = a.v2 + lg * cap * D;
     const int t = u.c0 + tid;
     const bool valid = t < u.c1;
     float s[G];
@@ -613,7 +757,13 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
 #pragma unroll 2
       for (int c = 0; c < D / 4; ++c) {
         // K-tiles keep 8 consecutive dimensions of a row together
-        const float4 k4 = *(const float4*)(Kb + k_off(t, 4 * c, D));
+        float4 k4;
+        if (q8) {
+          const char4 k8 = *(const char4*)(Kc + k_off(t, 4 * c, D));
+          k4 = make_float4((float)k8.x, (float)k8.y, (float)k8.z, (float)k8.w);
+        } else {
+          k4 = *(const float4*)(Kb + k_off(t, 4 * c, D));
+        }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float4 qa = qs4[hh][c];
@@ -625,9 +775,14 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
           s[hh] = x;
         }
       }
+      if (q8) {  // q.code x key scale
+        const float ksc = a.ks2[lg * cap + t];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) s[hh] *= ksc;
+      }
     }
     float* lg_out = a.alpha + ((u.b * a.Lr + u.lr) * a.hq + (long)u.g * G) * a.alpha_stride +
-                    (u.seg ? u.n0 : 0);
+                    u.off;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float v = valid ? s[hh] * a.scale : -INFINITY;  // base-2 logit
@@ -666,7 +821,15 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
     for (int i = 0; i < tend; ++i) {
       const int tt = tg * TPG + i;
       const long slot = u.c0 + tt;
-      const float v0 = Vb[v_off(slot, 2 * dp, D)], v1 = Vb[v_off(slot, 2 * dp + 1, D)];
+      float v0, v1;
+      if (q8) {  // code x value scale
+        const float vsc = a.vs2[lg * cap + slot];
+        v0 = (float)Vc[v_off(slot, 2 * dp, D)] * vsc;
+        v1 = (float)Vc[v_off(slot, 2 * dp + 1, D)] * vsc;
+      } else {
+        v0 = Vb[v_off(slot, 2 * dp, D)];
+        v1 = Vb[v_off(slot, 2 * dp + 1, D)];
+      }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         const float pe = ps[hh][tt];
@@ -749,12 +912,18 @@ void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int grou
   KernelTimer timer("attn_partial", s);
   if (kv_dtype == TKV_BF16) {
     dim3 grid((unsigned)((a.workers + 3) / 4));
-    if (head_dim == 128)
-      hipExtLaunchKernelGGL((attn_partial_mfma_kernel<128>), grid, dim3(256), 0, s,
-                            timer.start(), timer.stop(), 0, a);
-    else
-      hipExtLaunchKernelGGL((attn_partial_mfma_kernel<64>), grid, dim3(256), 0, s,
-                            timer.start(), timer.stop(), 0, a);
+    const bool t2 = a.k2 != nullptr;  // a T2 pool with rows in this launch
+#define TKV_MFMA(DD, TT)                                                                 \
+  hipExtLaunchKernelGGL((attn_partial_mfma_kernel<DD, TT>), grid, dim3(256), 0, s,       \
+                        timer.start(), timer.stop(), 0, a)
+    if (head_dim == 128) {
+      if (t2) TKV_MFMA(128, true);
+      else TKV_MFMA(128, false);
+    } else {
+      if (t2) TKV_MFMA(64, true);
+      else TKV_MFMA(64, false);
+    }
+#undef TKV_MFMA
   } else {
     dim3 grid((unsigned)a.workers);
     if (head_dim == 128) launch_valu<128>(a, group, grid, s, timer);

@@ -16,6 +16,7 @@ struct SeqTable {
   int b_offset;  // index of the first one in the caller's batch
   int t0_len[kMaxSeqPerLaunch];
   int t1_len[kMaxSeqPerLaunch];
+  int t2_len[kMaxSeqPerLaunch];    // attended 8-bit T2 rows (0 unless a T2 pool is given)
   int base[kMaxSeqPerLaunch + 1];  // first work unit (attention) or slot block (scores)
   int units[kMaxSeqPerLaunch];     // attention: work units per (layer, KV head) group
 };
@@ -38,6 +39,12 @@ struct AttnArgs {
   const void* v0;
   const void* k1;
   const void* v1;
+  // attended T2 pool (null when no sequence has T2 rows): int8 codes in the
+  // K-tile / V-tile order of the pools, one float32 scale per row
+  const int8_t* k2;
+  const int8_t* v2;
+  const float* ks2;  // [B][L][Hkv][cap2]
+  const float* vs2;  // [B][L][Hkv][cap2]
   float* out;
   float* alpha;   // raw scaled logits on exit of attn_partial
   float* part;    // split records: [worker + group][part_rec_floats] partial P.V
@@ -46,7 +53,7 @@ struct AttnArgs {
   long total_units;  // work units of this launch
   long workers;      // workers sharing them (record index = worker + group)
   int unit;          // tokens per work unit
-  int cap0, cap1;
+  int cap0, cap1, cap2;
   int L, Lr, layer_begin, hq, hkv;
   float scale;       // softmax_scale * log2(e): logits are kept in base 2
   SeqTable seq;
@@ -72,8 +79,9 @@ struct ScoreArgs {
   int rows;
   const int* t0_pos;
   const int* t1_pos;
+  const int* t2_pos;  // attended T2 slots (after T1), or null
   float* scores;
-  int cap0, cap1, max_ctx;
+  int cap0, cap1, cap2, max_ctx;
   double weight;  // 1 / (num_layers * Hq)
   SeqTable seq;   // base[] counts kScoreSlots-slot blocks
 };
@@ -169,6 +177,37 @@ struct QuantArgs {
   int n_rows_stride, max_rows, cap0, cap1, L, hkv, b_offset;
 };
 
+// In-place update of the attended T2 pool after a reassignment: rows whose
+// position left T2 (for T3) free their slots; rows left at or past the new
+// length and the newly quantised rows fill the holes below it.  Move list
+// entries are (source, destination slot): source >= 0 an old pool slot,
+// source < 0 new row -source-1.
+struct T2ScanArgs {
+  const uint8_t* tnext;     // [B][max_ctx]
+  int* t2_pos;              // in/out [B][cap2]
+  const int* new_pos;       // [B][max_rows] positions of the new rows
+  const int* n_new;         // element b * n_new_stride: new row count of sequence b
+  int* holes;               // [B][cap2]
+  int2* list;               // [B][cap2]
+  int* cnt;                 // [B]
+  int* out_len;             // [B][2]: new length, moves (or -1, -1)
+  int max_ctx, cap2, max_rows, n_new_stride, b_offset;
+  int n[kMaxSeqPerLaunch];
+  int len2[kMaxSeqPerLaunch];
+};
+
+struct T2MoveArgs {
+  int8_t* k2;
+  int8_t* v2;
+  float* ks2;
+  float* vs2;
+  const int8_t* new_codes;  // [B][max_rows][L * Hkv][2][D]
+  const float* new_scales;  // [B][max_rows][L * Hkv][2]
+  const int2* list;
+  const int* cnt;
+  int cap2, max_rows, lgs, b_offset, nb;
+};
+
 bool attn_group_supported(int group);
 int mfma_resident_waves(int head_dim);
 void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, hipStream_t s);
@@ -181,5 +220,7 @@ void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s);
 void launch_reloc_scan(const RelocArgs& a, int nb, hipStream_t s);
 void launch_reloc_move(const MoveArgs& m, int kv_dtype, int head_dim, hipStream_t s);
 void launch_quantize(const QuantArgs& a, int kv_dtype, int head_dim, int nb, hipStream_t s);
+void launch_t2_scan(const T2ScanArgs& a, int nb, hipStream_t s);
+void launch_t2_move(const T2MoveArgs& a, int head_dim, hipStream_t s);
 
 }  // namespace tkv

@@ -6,7 +6,8 @@
 // 2605.09490).  Methodologie section 2: the score of a position grows, every
 // decode step, by its attention weight averaged over the heads and the layers;
 // section 3: T1 rows are attended exactly like T0 rows, so one softmax runs over
-// the attended set T0 u T1.
+// the attended set T0 u T1 (followed, when the caller attends them, by the
+// 8-bit T2 rows).
 //
 // Every (sequence, layer, KV head) group was split between consecutive waves of
 // the attention kernel; wave w left, per query head of the group, a record
@@ -165,8 +166,7 @@ __device__ void normalise_chunk(const MergeArgs& a, int cb) {
   __shared__ float sM[GM], sI[GM];
   int bl = 0;
   while (bl + 1 < a.seq.nb && a.cbase[bl + 1] <= cb) ++bl;
-  const int n0 = a.seq.t0_len[bl];
-  const int natt = n0 + a.seq.t1_len[bl];
+  const int natt = a.seq.t0_len[bl] + a.seq.t1_len[bl] + a.seq.t2_len[bl];
   const int nch = (natt + kMergeChunk - 1) / kMergeChunk;
   const int local = cb - a.cbase[bl];
   const int gi = local / nch;
@@ -267,14 +267,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(ScoreArgs a) 
   while (bl + 1 < a.seq.nb && a.seq.base[bl + 1] <= blk) ++bl;
   const long b = a.seq.b_offset + bl;
   const int n0 = a.seq.t0_len[bl];
-  const int natt = n0 + a.seq.t1_len[bl];
+  const int n01 = n0 + a.seq.t1_len[bl];
+  const int natt = n01 + a.seq.t2_len[bl];
   const int j = (blk - a.seq.base[bl]) * kScoreSlots + lane;
   // the first row group also owns the score of its slot: its position and the
   // current score are fetched before the rows, so the three loads overlap
   float* sp = nullptr;
   float s_old = 0.f;
   if (rg == 0 && j < natt) {
-    const int pos = j < n0 ? a.t0_pos[b * a.cap0 + j] : a.t1_pos[b * a.cap1 + (j - n0)];
+    const int pos = j < n0    ? a.t0_pos[b * a.cap0 + j]
+                    : j < n01 ? a.t1_pos[b * a.cap1 + (j - n0)]
+                              : a.t2_pos[b * a.cap2 + (j - n01)];
     if ((unsigned)pos < (unsigned)a.max_ctx) {  // slot maps hold positions < max_ctx
       sp = a.scores + b * a.max_ctx + pos;
       s_old = *sp;

@@ -16,6 +16,11 @@ The T0 pool and the T1 window are single copies whose slot order is not
 position order (t0_pos / t1_pos map slots to positions); the read-back helpers
 return rows in ascending position order.  The tier map is double-buffered:
 the relocation reads the previous map and the new one.
+
+With ``attend_t2`` the 8-bit rows of T2 stay on the device in a pool of their
+own and are attended after T1 as code x scale (the variant whose accuracy the
+pages report for offloading to T2, Methodologie section 1); each reassignment
+then also runs tkv_t2_update, in the same single host sync.
 """
 from __future__ import annotations
 
@@ -119,7 +124,7 @@ class TieredKVCache:
 
     def __init__(self, shape: Shape, policy: PolicyCfg, batch: int, max_ctx: int,
                  device: str = "cuda", cap0: Optional[int] = None, cap1: Optional[int] = None,
-                 t2_cap: Optional[int] = None):
+                 t2_cap: Optional[int] = None, attend_t2: bool = False):
         self.shape = shape
         self.policy = policy
         self.batch = batch
@@ -130,7 +135,10 @@ class TieredKVCache:
                               else int(math.floor(float(np.float32(policy.frac_t1)) * self.max_ctx)) + 64, 64)
         self.t2_cap = _round_up(t2_cap if t2_cap is not None
                                 else int(math.floor(float(np.float32(policy.frac_t2)) * self.max_ctx)) + 64, 64)
-        self.alpha_stride = _round_up(self.cap0 + self.cap1, 64)
+        self.attend_t2 = attend_t2
+        # the attended T2 pool holds at most as many rows as one reassignment can quantise
+        self.cap2 = self.t2_cap if attend_t2 else 0
+        self.alpha_stride = _round_up(self.cap0 + self.cap1 + self.cap2, 64)
         self.model = tkv.make_model(shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim,
                                     shape.kv_code)
         self.tpolicy = tkv.make_policy(policy.prompt, policy.sinks, policy.recent,
@@ -156,7 +164,18 @@ class TieredKVCache:
         self.t2_pos = torch.zeros((B, self.t2_cap), dtype=torch.int32, device=dev)
         self.t2_codes = torch.zeros((B, self.t2_cap, L, Hkv, 2, D), dtype=torch.int8, device=dev)
         self.t2_scales = torch.zeros((B, self.t2_cap, L, Hkv, 2), dtype=torch.float32, device=dev)
-        self.ws_bytes = tkv.tkv_decode_workspace_bytes(self.model, B, L, self.cap0, self.cap1)
+        if attend_t2:
+            pool2 = (B, L, Hkv, self.cap2, D)
+            self.k_t2 = torch.zeros(pool2, dtype=torch.int8, device=dev)
+            self.v_t2 = torch.zeros(pool2, dtype=torch.int8, device=dev)
+            self.ks_t2 = torch.zeros(pool2[:-1], dtype=torch.float32, device=dev)
+            self.vs_t2 = torch.zeros(pool2[:-1], dtype=torch.float32, device=dev)
+            self.t2_slot_pos = torch.zeros((B, self.cap2), dtype=torch.int32, device=dev)
+            self.t2_lens_dev = torch.zeros((B, 2), dtype=torch.int32, device=dev)
+            self.t2ws_bytes = tkv.tkv_t2_update_workspace_bytes(B, self.cap2)
+            self.t2ws = torch.zeros(self.t2ws_bytes, dtype=torch.uint8, device=dev)
+        self.ws_bytes = tkv.tkv_decode_workspace_bytes(self.model, B, L, self.cap0,
+                                                       self.cap1 + self.cap2)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
         self.cws_bytes = tkv.tkv_compact_workspace_bytes(self.model, B, self.max_ctx, self.cap0,
                                                          self.cap1)
@@ -165,6 +184,7 @@ class TieredKVCache:
         self.n = [0] * B
         self.t0_len = [0] * B
         self.t1_len = [0] * B
+        self.t2_len = [0] * B   # rows in the attended T2 pool
         self.t2_new = [0] * B   # rows quantised at the last reassignment
         self.moved = [0] * B    # row copies of the last relocation
         self.steps = 0
@@ -175,6 +195,13 @@ class TieredKVCache:
     @property
     def tiers(self):
         return self.tier[self.tcur]
+
+    def t2_pool(self):
+        """The attended T2 pool as the C ABI sees it (None unless attend_t2)."""
+        if not self.attend_t2:
+            return None
+        return tkv.T2Pool(self.k_t2, self.v_t2, self.ks_t2, self.vs_t2, self.t2_slot_pos,
+                          self.t2_len, self.cap2)
 
     # ---- set-up ------------------------------------------------------------
     def load_context(self, b: int, K: np.ndarray, V: np.ndarray) -> None:
@@ -198,6 +225,7 @@ class TieredKVCache:
         self.n[b] = n0
         self.t0_len[b] = n0
         self.t1_len[b] = 0
+        self.t2_len[b] = 0
 
     # ---- the step ------------------------------------------------------------
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
@@ -222,6 +250,15 @@ class TieredKVCache:
             if not full:
                 raise ValueError("a layer subset needs caller-supplied out and alpha buffers")
             out, alpha = self.out, self.alpha
+        if self.attend_t2:
+            if not fused:
+                raise ValueError("attended T2 rows need the fused score update")
+            tkv.tkv_decode_step_t2(self.model, self.batch, layer_begin, le, q, self.k_t0,
+                                   self.v_t0, self.t0_len, self.cap0, self.k_t1, self.v_t1,
+                                   self.t1_len, self.cap1, self.t2_pool(), out, alpha,
+                                   self.alpha_stride, self.t0_pos, self.t1_pos, self.scores,
+                                   self.max_ctx, self.ws, self.ws_bytes, stream)
+            return
         tkv.tkv_decode_step(self.model, self.batch, layer_begin, le, q, self.k_t0, self.v_t0,
                             self.t0_len, self.cap0, self.k_t1, self.v_t1, self.t1_len, self.cap1,
                             out, alpha, self.alpha_stride, self.t0_pos, self.t1_pos,
@@ -239,6 +276,17 @@ class TieredKVCache:
         if not self.fused_scores:
             self.append(k_new, v_new, stream)
             self.attend(q, stream)
+            return
+        if self.attend_t2:
+            tkv.tkv_append_decode_step_t2(self.model, self.batch, k_new, v_new, self.n,
+                                          self.tiers, q, self.k_t0, self.v_t0, self.t0_len,
+                                          self.cap0, self.k_t1, self.v_t1, self.t1_len,
+                                          self.cap1, self.t2_pool(), self.out, self.alpha,
+                                          self.alpha_stride, self.t0_pos, self.t1_pos,
+                                          self.scores, self.max_ctx, self.ws, self.ws_bytes,
+                                          stream)
+            self.n = [x + 1 for x in self.n]
+            self.t0_len = [x + 1 for x in self.t0_len]
             return
         tkv.tkv_append_decode_step(self.model, self.batch, k_new, v_new, self.n, self.tiers, q,
                                    self.k_t0, self.v_t0, self.t0_len, self.cap0, self.k_t1,
@@ -273,7 +321,19 @@ class TieredKVCache:
                         self.k_t1, self.v_t1, self.t1_pos, self.t1_len, self.cap1,
                         self.t2_src, self.t2_pos, self.t2_cap, self.t2_codes, self.t2_scales,
                         self.new_lens, self.cws, self.cws_bytes, stream)
-        lens = self.new_lens.cpu().numpy()          # the one sync per reassignment
+        if self.attend_t2:
+            tkv.tkv_t2_update(self.model, B, self.n, self.max_ctx, self.tier[tnx], self.k_t2,
+                              self.v_t2, self.ks_t2, self.vs_t2, self.t2_slot_pos, self.t2_len,
+                              self.cap2, self.t2_pos, self.t2_codes, self.t2_scales,
+                              self.new_lens[:, 2:], 4, self.t2_cap, self.t2_lens_dev, self.t2ws,
+                              self.t2ws_bytes, stream)
+            both = torch.cat([self.new_lens, self.t2_lens_dev], dim=1).cpu().numpy()
+            lens, t2l = both[:, :4], both[:, 4:]    # the one sync per reassignment
+            if (t2l < 0).any():
+                raise RuntimeError(f"T2 pool state error reported by the device: {t2l.tolist()}")
+            self.t2_len = t2l[:, 0].tolist()
+        else:
+            lens = self.new_lens.cpu().numpy()      # the one sync per reassignment
         if (lens < 0).any():
             raise RuntimeError(f"tier state error reported by the device: {lens.tolist()}")
         self.t0_len = lens[:, 0].tolist()
@@ -297,10 +357,22 @@ class TieredKVCache:
         _, o1, _, p1 = self._order(b)
         return p1[o1].astype(np.int64)
 
+    def t2_order(self, b: int):
+        """Slot order of the attended T2 pool that sorts its positions, and the positions."""
+        if not self.attend_t2 or self.t2_len[b] == 0:
+            return np.zeros(0, dtype=np.int64), np.zeros(0, dtype=np.int64)
+        p2 = self.t2_slot_pos[b, :self.t2_len[b]].cpu().numpy()
+        return np.argsort(p2, kind="stable"), p2
+
+    def t2_positions(self, b: int) -> np.ndarray:
+        o2, p2 = self.t2_order(b)
+        return p2[o2].astype(np.int64)
+
     def attended_positions(self, b: int) -> np.ndarray:
-        """T0 positions then T1 positions, each ascending."""
+        """T0 positions, then T1 positions, then attended T2 positions, each ascending."""
         o0, o1, p0, p1 = self._order(b)
-        return np.concatenate([p0[o0], p1[o1]]).astype(np.int64)
+        o2, p2 = self.t2_order(b)
+        return np.concatenate([p0[o0], p1[o1], p2[o2]]).astype(np.int64)
 
     def t0_rows(self, b: int):
         """Host copies (bf16 bits or float32) of the T0 rows of sequence b in ascending
@@ -320,9 +392,22 @@ class TieredKVCache:
     def alpha_of(self, b: int) -> np.ndarray:
         """alpha [L][Hq][n_att] in attended_positions() order."""
         o0, o1, _, _ = self._order(b)
-        m = self.t0_len[b] + self.t1_len[b]
+        o2, _ = self.t2_order(b)
+        n01 = self.t0_len[b] + self.t1_len[b]
+        m = n01 + len(o2)
         a = self.alpha[b, :, :, :m].cpu().numpy()
-        return a[:, :, np.concatenate([o0, self.t0_len[b] + o1])]
+        return a[:, :, np.concatenate([o0, self.t0_len[b] + o1, n01 + o2]).astype(np.int64)]
+
+    def t2_pool_rows(self, b: int):
+        """Attended T2 rows of sequence b in ascending position order: codes
+        [L][Hkv][n2][D] int8 for K and V, and scales [L][Hkv][n2] for K and V."""
+        o2, _ = self.t2_order(b)
+        n = self.t2_len[b]
+        kc = k_tiles_to_rows(self.k_t2[b], n).cpu().numpy()[:, :, o2]
+        vc = v_tiles_to_rows(self.v_t2[b], n).cpu().numpy()[:, :, o2]
+        ks = self.ks_t2[b, :, :, :n].cpu().numpy()[:, :, o2]
+        vs = self.vs_t2[b, :, :, :n].cpu().numpy()[:, :, o2]
+        return kc, vc, ks, vs
 
     def last_t2(self, b: int):
         r = self.t2_new[b]

@@ -25,9 +25,11 @@ TKV_F32 = 1
 
 EXPORTED = (
     "tkv_abi_version", "tkv_last_error", "tkv_append", "tkv_decode_workspace_bytes",
-    "tkv_decode_step", "tkv_append_decode_step", "tkv_update_scores", "tkv_assign_tiers", "tkv_compact_workspace_bytes",
-    "tkv_compact", "tkv_quantize_t2", "tkv_gather_t1", "tkv_timing_enable", "tkv_timing_select",
-    "tkv_timing_reset", "tkv_timing_read",
+    "tkv_decode_step", "tkv_append_decode_step", "tkv_decode_step_t2",
+    "tkv_append_decode_step_t2", "tkv_update_scores", "tkv_assign_tiers",
+    "tkv_compact_workspace_bytes", "tkv_compact", "tkv_quantize_t2",
+    "tkv_t2_update_workspace_bytes", "tkv_t2_update", "tkv_gather_t1", "tkv_timing_enable",
+    "tkv_timing_select", "tkv_timing_reset", "tkv_timing_read",
 )
 
 
@@ -48,6 +50,13 @@ class tkv_policy(ctypes.Structure):
                 ("recent_window", ctypes.c_int32), ("frac_t1", ctypes.c_float),
                 ("frac_t2", ctypes.c_float), ("frac_t3", ctypes.c_float),
                 ("delta", ctypes.c_int32)]
+
+
+class tkv_t2_pool(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("t2_pos", ctypes.c_void_p), ("t2_len", ctypes.c_void_p),
+                ("cap2", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -81,6 +90,16 @@ def lib() -> ctypes.CDLL:
         "tkv_append_decode_step": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P,
                                         _I, _P, ctypes.c_size_t, _P]),
+        "tkv_decode_step_t2": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _P, _P, _P, _I,
+                                    _P, _P, _P, _I, ctypes.POINTER(tkv_t2_pool), _P, _P, _I,
+                                    _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
+        "tkv_append_decode_step_t2": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _I, _P, _P, _P, _I,
+                                           ctypes.POINTER(tkv_t2_pool), _P, _P, _I, _P, _P, _P,
+                                           _I, _P, ctypes.c_size_t, _P]),
+        "tkv_t2_update_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+        "tkv_t2_update": (_I, [ctypes.POINTER(tkv_model), _I, _P, _I, _P, _P, _P, _P, _P, _P,
+                               _P, _I, _P, _P, _P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]),
         "tkv_update_scores": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _I, _P, _P, _I,
                                    _P, _P, _I, _P, _I, _P]),
         "tkv_assign_tiers": (_I, [_I, _P, _I, _P, ctypes.POINTER(tkv_policy), _P, _P, _P, _P]),
@@ -215,6 +234,58 @@ def tkv_append_decode_step(model, batch, k_new, v_new, position, tier, q, k_t0, 
                                         _ptr(t1_pos), _ptr(scores), max_ctx, _ptr(workspace),
                                         workspace_bytes, _stream(stream)),
            "tkv_append_decode_step")
+
+
+class T2Pool:
+    """A tkv_t2_pool with the host length array it points to kept alive."""
+
+    def __init__(self, k_codes, v_codes, k_scale, v_scale, t2_pos, t2_len, cap2):
+        self._len = _HostInts(t2_len)
+        self.struct = tkv_t2_pool(_ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale),
+                                  _ptr(t2_pos), self._len.ptr, cap2)
+
+
+def tkv_decode_step_t2(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1,
+                       v_t1, t1_len, cap1, t2: Optional[T2Pool], out, alpha, alpha_stride,
+                       t0_pos=None, t1_pos=None, scores=None, max_ctx=0, workspace=None,
+                       workspace_bytes=0, stream=None) -> None:
+    a, b = _HostInts(t0_len), _HostInts(t1_len)
+    _check(lib().tkv_decode_step_t2(ctypes.byref(model), batch, layer_begin, layer_end, _ptr(q),
+                                    _ptr(k_t0), _ptr(v_t0), a.ptr, cap0, _ptr(k_t1), _ptr(v_t1),
+                                    b.ptr, cap1, None if t2 is None else ctypes.byref(t2.struct),
+                                    _ptr(out), _ptr(alpha), alpha_stride, _ptr(t0_pos),
+                                    _ptr(t1_pos), _ptr(scores), max_ctx, _ptr(workspace),
+                                    workspace_bytes, _stream(stream)), "tkv_decode_step_t2")
+
+
+def tkv_append_decode_step_t2(model, batch, k_new, v_new, position, tier, q, k_t0, v_t0, t0_len,
+                              cap0, k_t1, v_t1, t1_len, cap1, t2: Optional[T2Pool], out, alpha,
+                              alpha_stride, t0_pos, t1_pos=None, scores=None, max_ctx=0,
+                              workspace=None, workspace_bytes=0, stream=None) -> None:
+    a, b, p = _HostInts(t0_len), _HostInts(t1_len), _HostInts(position)
+    _check(lib().tkv_append_decode_step_t2(
+        ctypes.byref(model), batch, _ptr(k_new), _ptr(v_new), p.ptr, _ptr(tier), _ptr(q),
+        _ptr(k_t0), _ptr(v_t0), a.ptr, cap0, _ptr(k_t1), _ptr(v_t1), b.ptr, cap1,
+        None if t2 is None else ctypes.byref(t2.struct), _ptr(out), _ptr(alpha), alpha_stride,
+        _ptr(t0_pos), _ptr(t1_pos), _ptr(scores), max_ctx, _ptr(workspace), workspace_bytes,
+        _stream(stream)), "tkv_append_decode_step_t2")
+
+
+def tkv_t2_update_workspace_bytes(batch, cap2) -> int:
+    return lib().tkv_t2_update_workspace_bytes(batch, cap2)
+
+
+def tkv_t2_update(model, batch, ctx_len, max_ctx, tier_next, k_codes, v_codes, k_scale,
+                  v_scale, t2_pos, t2_len, cap2, new_pos, new_codes, new_scales, n_new,
+                  n_new_stride, max_rows, new_t2_len, workspace, workspace_bytes,
+                  stream=None) -> None:
+    a, b = _HostInts(ctx_len), _HostInts(t2_len)
+    _check(lib().tkv_t2_update(ctypes.byref(model), batch, a.ptr, max_ctx, _ptr(tier_next),
+                               _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale),
+                               _ptr(t2_pos), b.ptr, cap2, _ptr(new_pos), _ptr(new_codes),
+                               _ptr(new_scales), _ptr(n_new), n_new_stride, max_rows,
+                               _ptr(new_t2_len), _ptr(workspace), workspace_bytes,
+                               _stream(stream)), "tkv_t2_update")
 
 
 def tkv_update_scores(model, batch, layer_begin, layer_end, alpha, alpha_stride, t0_pos,
