@@ -35,6 +35,11 @@ def parse():
     p.add_argument("--no-pcie", action="store_true")
     p.add_argument("--no-flush-run", action="store_true",
                    help="skip the run that reads a 512 MB buffer before every step")
+    p.add_argument("--no-stream-leg", action="store_true",
+                   help="skip the run that streams T1 layer by layer from pinned host memory "
+                        "(reported under \"t1_streamed\", never in value)")
+    p.add_argument("--stream-chunk", type=int, default=1,
+                   help="layers per streamed chunk of T1 rows (two chunks are resident)")
     p.add_argument("--no-t2-leg", action="store_true",
                    help="skip the run that also attends the 8-bit T2 rows (reported under "
                         "\"attend_t2\", never in value)")
@@ -466,6 +471,37 @@ def main():
                 "mean_t2_rows": float(np.mean([t for _, t in att_t2])),
                 "note": "T0 u T1 u T2 attended, T2 as int8 code x float32 scale per row "
                         "(one run, attn_partial timed on every 8th step); not part of value"}
+    if not args.no_stream_leg:
+        # T1 streamed from pinned host memory every step, layer by layer through a
+        # two-buffer device window (the copy of layer l + 2 overlaps the attention of
+        # layer l + 1): the whole step as the pages describe it, host-link bound
+        from tiered_kv_cache_amd.driver import T1Stream
+        del cache
+        torch.cuda.empty_cache()
+        print("[bench] streamed-T1 run", file=sys.stderr, flush=True)
+        cache = dw.make_cache(contexts=contexts)
+        stream = T1Stream(cache, chunk_layers=args.stream_chunk)
+        for k in range(1, args.warmup + 1):
+            stream.step(*inputs[k - 1])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        link = 0
+        for k in range(args.warmup + 1, args.warmup + args.steps + 1):
+            link += stream.layer_bytes * wl.layers
+            stream.step(*inputs[k - 1])
+        torch.cuda.synchronize()
+        el_s = time.perf_counter() - t0
+        out["t1_streamed"] = {
+            "steps_per_s": args.steps / el_s, "ms_per_step": el_s / args.steps * 1e3,
+            "link_bytes_per_step": link / args.steps,
+            "link_gbps": link / el_s / 1e9,
+            "device_window_bytes": 2 * stream.chunk * stream.layer_bytes,
+            "chunk_layers": stream.chunk,
+            "note": "append, then per layer: wait for its T1 rows, attention (tkv_decode_step_"
+                    "window) over T0 and the two-buffer window; the host-to-device copy of layer "
+                    "l + 2 starts when layer l has read its buffer; every Delta steps the "
+                    "reassignment and a refresh of the pinned host copy; not part of value"}
+        del stream
     if not args.no_pcie:
         try:
             t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()   # window slot order

@@ -187,6 +187,55 @@ tkv_status tkv_append_decode_step(const tkv_model* model, int32_t batch, const v
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * tkv_decode_step_window -- tkv_decode_step with a T1 window that holds only
+ * the call's layers: k_t1_win, v_t1_win are device [B][Lr][Hkv][cap1][D] tiles
+ * (Lr = layer_end - layer_begin), window layer i holding layer layer_begin + i.
+ * q, out and alpha hold EVERY layer here ([B][L][Hq][D], [B][L][Hq][D],
+ * [B][L][Hq][alpha_stride]); the call reads and writes the rows of its layers.
+ * Methodologie section 1 brings T1 from host memory to the GPU before each
+ * attention step; with this call the T1 rows can be streamed layer by layer
+ * into a small double-buffered device window (copy layer l + 1 while layer l
+ * attends), so HBM holds T0 plus two layers of T1 instead of every layer.
+ * Other arguments, outputs, numerics and errors as for tkv_decode_step.
+ */
+tkv_status tkv_decode_step_window(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                                  int32_t layer_end, const void* q, const void* k_t0,
+                                  const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                                  const void* k_t1_win, const void* v_t1_win,
+                                  const int32_t* t1_len, int32_t cap1, float* out, float* alpha,
+                                  int32_t alpha_stride, const int32_t* t0_pos,
+                                  const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tkv_decode_step_streamed -- the decode step over all layers with the T1 rows
+ * streamed from pinned host memory (Methodologie section 1: T1 stays in host
+ * DDR at full precision and is brought to the GPU before each attention step).
+ * The layers run in chunks of chunk_layers; the host-to-device copy of chunk
+ * c + 2 goes on side_stream as soon as chunk c has read its buffer of the
+ * two-buffer device window, so copies overlap attention.  Each chunk is one
+ * tkv_decode_step_window call on `stream` (fused score update included).
+ *
+ * host_t1  : pinned host [2][B][L][Hkv][cap1][D] tiles: keys, then values, of
+ *            the T1 rows in the window-slot order of t1_pos
+ * win      : device [2][2][B][chunk_layers][Hkv][cap1][D] tiles (two buffers of
+ *            keys then values); a chunk is one 2-D copy of 2 * B rows
+ * events               : four caller-owned events (two "copied", two "read");
+ *                        their previous contents are overwritten
+ * q, out, alpha and the rest as for tkv_decode_step over layers [0, L).
+ * Every argument is checked before anything is queued.
+ */
+tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const void* q,
+                                    const void* k_t0, const void* v_t0, const int32_t* t0_len,
+                                    int32_t cap0, const void* host_t1, const int32_t* t1_len,
+                                    int32_t cap1, void* win, int32_t chunk_layers, float* out,
+                                    float* alpha,
+                                    int32_t alpha_stride, const int32_t* t0_pos,
+                                    const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    hipStream_t side_stream, hipEvent_t* events);
+
+/*
  * Attended T2 pool (optional variant of the decode step).  Methodologie
  * section 1 keeps T2 tokens at reduced precision (8-bit quantisation), and the
  * accuracy the pages report for offloading to T2 ("Resultats cles") is that of

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from oracle import Policy, TieredSequence, attention, assign_tiers, quantize_rows, widen
-from tiered_kv_cache_amd.driver import to_device, to_host_bits
+from tiered_kv_cache_amd.driver import T1Stream, to_device, to_host_bits
 from tiered_kv_cache_amd.synth import SequenceStream, Workload
 from tiered_kv_cache_amd.workload import DeviceWorkload
 
@@ -123,16 +123,18 @@ def step_inputs(cache, dw, q, kn, vn, fused_append: bool) -> None:
 
 def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
                  fused_scores: bool = True, fused_append: bool = True,
-                 attend_t2: bool = False) -> dict:
+                 attend_t2: bool = False, t1_streamed: int = 0) -> dict:
     """Every step compared; re-sync of the ranking at each reassignment.
     fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores;
     fused_append=False appends with tkv_append before tkv_decode_step instead of
     tkv_append_decode_step; attend_t2 attends the 8-bit T2 rows after T1 on both sides
-    (the _t2 entry points and the oracle's attend_t2 mode)."""
+    (the _t2 entry points and the oracle's attend_t2 mode); t1_streamed > 0 attends chunks
+    of that many layers with the T1 rows streamed from pinned host memory (T1Stream)."""
     n_steps = n_steps or wl.total_steps
     dw = DeviceWorkload(wl)
     cache = dw.make_cache(attend_t2=attend_t2)
     cache.fused_scores = fused_scores
+    streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
     pol = oracle_policy(wl)
     seqs = []
     for b in range(wl.batch):
@@ -141,8 +143,12 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
     stats = defaultdict(float)
     for k in range(1, n_steps + 1):
         q, kn, vn = dw.host_step(k)
-        step_inputs(cache, dw, q, kn, vn, fused_append)
-        cache.steps += 1
+        if streamer is not None:
+            streamer.step(to_device(q, dw.dtype, dw.device), to_device(kn, dw.dtype, dw.device),
+                          to_device(vn, dw.dtype, dw.device), reassign=False)
+        else:
+            step_inputs(cache, dw, q, kn, vn, fused_append)
+            cache.steps += 1
         torch.cuda.synchronize()
         out = cache.out.cpu().numpy()
         for b, seq in enumerate(seqs):
@@ -155,6 +161,8 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
             gpu_scores = cache.scores.cpu().numpy()
             prevs = [s.tier.copy() for s in seqs]
             cache.reassign()
+            if streamer is not None:
+                streamer.refresh()
             torch.cuda.synchronize()
             for b, seq in enumerate(seqs):
                 seq.reassign(scores=gpu_scores[b])

@@ -1,8 +1,11 @@
-"""Attended T2 rows on the GPU (tkv_decode_step_t2, tkv_append_decode_step_t2,
-tkv_t2_update) against the oracle's attend_t2 mode: every step compared in lock step
-(output, weights and scores within the tolerances of tests/parity.py; the T2 pool's
-positions, int8 codes and scales bit-exact after every reassignment), and the pool
-update called directly on adversarial transitions."""
+"""Variants of the decode step on the GPU, against the oracle:
+* attended T2 rows (tkv_decode_step_t2, tkv_append_decode_step_t2, tkv_t2_update) against
+  the oracle's attend_t2 mode, every step compared in lock step (output, weights and
+  scores within the tolerances of tests/parity.py; the T2 pool's positions, int8 codes and
+  scales bit-exact after every reassignment), and the pool update called directly on
+  adversarial transitions;
+* the T1 rows streamed layer by layer from pinned host memory into a two-buffer device
+  window (tkv_decode_step_window), in lock step with the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -158,3 +161,32 @@ def test_t2_update_adversarial():
         assert torch.equal(dev[k][b], before[k][b]), k
     say(f"[t2 update] {B - 1} sequences exact (lengths/moves {got_len[:-1].tolist()}), "
         f"inconsistent one rejected")
+
+
+# ---------------------------------------------------------------------------
+# T1 streamed layer by layer from pinned host memory (tkv_decode_step_window)
+# ---------------------------------------------------------------------------
+def test_small_t1_streamed_lockstep():
+    # batch 1: q, out and alpha rows of a layer are passed in place
+    wl = WORKLOADS["small"].scaled(warmup=8, steps=72)
+    st = run_lockstep(wl, t1_streamed=1, label="small_t1_streamed")
+    assert st["reassignments"] == 1
+
+
+def test_tiny_fp32_t1_streamed_lockstep():
+    # float32 path; one layer (a single buffer of the two is ever used)
+    st = run_lockstep(WORKLOADS["tiny"], t1_streamed=1, label="tiny_t1_streamed")
+    assert st["reassignments"] == 4
+
+
+@pytest.mark.parametrize("chunk", [1, 2], ids=["chunk1", "chunk2"])
+def test_ragged_batch_t1_streamed_lockstep(chunk):
+    # five sequences, three layers: both buffers alternate; rows of a chunk are strided
+    # over the batch in q / out / alpha; with chunks of two the last chunk is partial
+    base = WORKLOADS["small"]
+    wl = base.scaled(name=f"t1s_ragged5_L3_h8kv2_d64_c{chunk}", layers=3, head_dim=64,
+                     batch=5, ctx=(130, 700, 257, 1100, 12), warmup=8, steps=16, delta=8,
+                     prompt=16, recent=16, sinks=4, planted=(2, 8, 4, 10, 0), frac_t1=0.4,
+                     frac_t2=0.1, frac_t3=0.1)
+    st = run_lockstep(wl, t1_streamed=chunk)
+    assert st["reassignments"] == 3 * 5

@@ -268,7 +268,10 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
                               const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
                               int32_t max_ctx, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, const AppendInfo* app,
-                              const tkv_t2_pool* t2) {
+                              const tkv_t2_pool* t2, bool t1_window = false,
+                              bool validate_only = false) {
+  // t1_window: the T1 window holds only the call's layers, and q / out / alpha hold
+  // every layer (the call reads and writes the rows of its own layers)
   tkv_status st = check_model(model);
   if (st) return st;
   if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
@@ -323,6 +326,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
   // the group sums cover every attended slot: T2 slots follow T1
   if (workspace_bytes < tkv_decode_workspace_bytes(model, batch, Lr, cap0, cap1 + cap2))
     return fail(TKV_ERR_CAPACITY, "workspace too small");
+  if (validate_only) return TKV_OK;
 
   const int hq = model->num_q_heads;
   const int hkv = model->num_kv_heads;
@@ -385,6 +389,10 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     a.layer_begin = layer_begin;
     a.hq = hq;
     a.hkv = hkv;
+    a.t1_L = t1_window ? Lr : model->num_layers;
+    a.t1_l0 = t1_window ? 0 : layer_begin;
+    a.io_L = t1_window ? model->num_layers : Lr;
+    a.io_l0 = t1_window ? layer_begin : 0;
     // logits are kept in base 2: q.k * softmax_scale * log2(e)
     a.scale = (float)((double)scale_of(model) * 1.4426950408889634074);
     a.seq.nb = nb;
@@ -443,6 +451,8 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     m.Lr = Lr;
     m.hq = hq;
     m.hkv = hkv;
+    m.io_L = a.io_L;
+    m.io_l0 = a.io_l0;
     m.out_rows = nb * Lr * hq;
     m.out_blocks = merge_output_blocks(m.out_rows);
     m.seq = a.seq;
@@ -488,6 +498,92 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
   return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1,
                      v_t1, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
                      max_ctx, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+tkv_status tkv_decode_step_window(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                                  int32_t layer_end, const void* q, const void* k_t0,
+                                  const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                                  const void* k_t1_win, const void* v_t1_win,
+                                  const int32_t* t1_len, int32_t cap1, float* out, float* alpha,
+                                  int32_t alpha_stride, const int32_t* t0_pos,
+                                  const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1_win,
+                     v_t1_win, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
+                     max_ctx, workspace, workspace_bytes, stream, nullptr, nullptr, true);
+}
+
+tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const void* q,
+                                    const void* k_t0, const void* v_t0, const int32_t* t0_len,
+                                    int32_t cap0, const void* host_t1, const int32_t* t1_len,
+                                    int32_t cap1, void* win, int32_t chunk_layers, float* out,
+                                    float* alpha,
+                                    int32_t alpha_stride, const int32_t* t0_pos,
+                                    const int32_t* t1_pos, float* scores, int32_t max_ctx,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    hipStream_t side_stream, hipEvent_t* events) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (batch == 0) return TKV_OK;
+  if (!host_t1 || !win || !events || !t1_len) return fail(TKV_ERR_ARG, "null pointer");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(TKV_ERR_ARG, "null event");
+  const int L = model->num_layers;
+  if (chunk_layers < 1 || chunk_layers > L) return fail(TKV_ERR_ARG, "need 1 <= chunk_layers <= L");
+  if (cap1 < 0 || cap1 % 32) return fail(TKV_ERR_ARG, "cap1 must be a multiple of 32");
+  const size_t e = model->kv_dtype == TKV_BF16 ? 2 : 4;
+  const size_t layer_bytes = (size_t)model->num_kv_heads * cap1 * model->head_dim * e;
+  const size_t kv_bytes = (size_t)batch * chunk_layers * layer_bytes;  // K (or V) of a buffer
+  const int n_chunks = (L + chunk_layers - 1) / chunk_layers;
+  // every check of the per-chunk calls before anything is queued (the chunks differ
+  // only in their layer range)
+  if ((st = decode_step(model, batch, 0, chunk_layers, q, k_t0, v_t0, t0_len, cap0, win,
+                        (const char*)win + kv_bytes,
+                        t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores, max_ctx,
+                        workspace, workspace_bytes, stream, nullptr, nullptr, true, true)))
+    return st;
+  hipEvent_t* loaded = events;
+  hipEvent_t* read = events + 2;
+  // everything queued on `stream` before this call (the previous step's reads of the
+  // two buffers among it) happens before the first copies
+  if ((st = hip_check(hipEventRecord(read[0], stream), "event record"))) return st;
+  if ((st = hip_check(hipEventRecord(read[1], stream), "event record"))) return st;
+  auto copy_chunk = [&](int c) -> tkv_status {
+    const int buf = c & 1;
+    const int l0 = c * chunk_layers;
+    const int n = std::min(chunk_layers, L - l0);
+    tkv_status s2 = hip_check(hipStreamWaitEvent(side_stream, read[buf], 0), "stream wait");
+    if (s2) return s2;
+    // one copy: 2 * B rows (keys, then values, of each sequence) of n layers,
+    // [2][B][L][Hkv][cap1][D] host -> [2][B][n][Hkv][cap1][D] buffer
+    char* dst = (char*)win + (size_t)buf * 2 * kv_bytes;
+    const char* src = (const char*)host_t1 + (size_t)l0 * layer_bytes;
+    s2 = hip_check(hipMemcpy2DAsync(dst, n * layer_bytes, src, (size_t)L * layer_bytes,
+                                    n * layer_bytes, 2 * (size_t)batch, hipMemcpyHostToDevice,
+                                    side_stream),
+                   "T1 chunk copy");
+    if (s2) return s2;
+    return hip_check(hipEventRecord(loaded[buf], side_stream), "event record");
+  };
+  for (int c = 0; c < std::min(2, n_chunks); ++c)
+    if ((st = copy_chunk(c))) return st;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int buf = c & 1;
+    const int l0 = c * chunk_layers;
+    const int n = std::min(chunk_layers, L - l0);
+    if ((st = hip_check(hipStreamWaitEvent(stream, loaded[buf], 0), "stream wait"))) return st;
+    // a partial last chunk packs its rows with pitch n: keys at 0, values after B * n layers
+    const char* wk = (const char*)win + (size_t)buf * 2 * kv_bytes;
+    const char* wv = wk + (size_t)batch * n * layer_bytes;
+    if ((st = decode_step(model, batch, l0, l0 + n, q, k_t0, v_t0, t0_len, cap0, wk, wv, t1_len,
+                          cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores, max_ctx,
+                          workspace, workspace_bytes, stream, nullptr, nullptr, true)))
+      return st;
+    if ((st = hip_check(hipEventRecord(read[buf], stream), "event record"))) return st;
+    if (c + 2 < n_chunks && (st = copy_chunk(c + 2))) return st;
+  }
+  return TKV_OK;
 }
 
 tkv_status tkv_decode_step_t2(const tkv_model* model, int32_t batch, int32_t layer_begin,

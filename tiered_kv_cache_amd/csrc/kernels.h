@@ -55,6 +55,8 @@ struct AttnArgs {
   int unit;          // tokens per work unit
   int cap0, cap1, cap2;
   int L, Lr, layer_begin, hq, hkv;
+  int t1_L, t1_l0;   // T1 window: layers it holds per sequence, index of the call's first
+  int io_L, io_l0;   // q / out / alpha rows: layers they hold per sequence, the call's first
   float scale;       // softmax_scale * log2(e): logits are kept in base 2
   SeqTable seq;
   // append fused into the bf16 kernel (kn null: none).  The new row of sequence i
@@ -96,6 +98,7 @@ struct MergeArgs {
   long alpha_stride, gs_stride;
   long total_units, workers;  // as in the attention launch
   int Lr, hq, hkv;
+  int io_L, io_l0;            // out / alpha rows: layers they hold per sequence, the call's first
   int out_rows, out_blocks;   // O rows of the launch; workgroups merging them (first)
   SeqTable seq;               // base[] / units[] as in the attention launch
   int cbase[kMaxSeqPerLaunch + 1];  // alpha workgroups: prefix over sequences

@@ -140,7 +140,7 @@ __device__ void merge_output_row(const MergeArgs& a, int row_in_launch) {
       }
     }
   }
-  const long orow = (long)(a.seq.b_offset + bl) * rows + r;
+  const long orow = ((long)(a.seq.b_offset + bl) * a.io_L + a.io_l0 + lr) * a.hq + hd;
   const float inv = lam > 0.f ? 1.0f / lam : 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) a.out[orow * D + lane + kWave * i] = o[i] * inv;
@@ -177,7 +177,7 @@ __device__ void normalise_chunk(const MergeArgs& a, int cb) {
   const long b = a.seq.b_offset + bl;
   const int j0 = ch * kMergeChunk + 4 * (int)threadIdx.x;
   const bool full = j0 + 3 < natt;
-  float* arow = a.alpha + ((b * a.Lr + lr) * a.hq + (long)g * G) * a.alpha_stride + j0;
+  float* arow = a.alpha + ((b * a.io_L + a.io_l0 + lr) * a.hq + (long)g * G) * a.alpha_stride + j0;
 
   // 1. logits of the G heads for this thread's 4 slots (loads in flight during 2.)
   float4 x[GM];

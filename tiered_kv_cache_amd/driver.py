@@ -413,3 +413,71 @@ class TieredKVCache:
         r = self.t2_new[b]
         return (self.t2_pos[b, :r].cpu().numpy(), self.t2_codes[b, :r].cpu().numpy(),
                 self.t2_scales[b, :r].cpu().numpy())
+
+
+class T1Stream:
+    """Pipelined streaming of the T1 rows from pinned host memory, chunk of layers by
+    chunk of layers (tkv_decode_step_streamed).
+
+    Methodologie section 1 of the pages keeps T1 in host DDR at full precision and
+    brings it to the GPU before each attention step.  Here the T1 rows of every layer
+    sit in a pinned host copy [2][B][L][Hkv][cap1][D] (keys then values, tiles,
+    window-slot order); each
+    step the library runs the attention chunk by chunk over the resident T0 pool and
+    a two-buffer device window, the copy of chunk c + 2 starting on a side stream as
+    soon as chunk c has read its buffer.  HBM holds 2 x chunk_layers layers of T1
+    rows for this path instead of every layer.
+
+    The host copy is refreshed at each reassignment from the device window that the
+    in-place relocation keeps (the rows whose tier changed are placed there); the
+    step itself reads T1 only through the streamed buffers.
+    """
+
+    def __init__(self, cache: TieredKVCache, chunk_layers: int = 1):
+        if cache.attend_t2:
+            raise ValueError("the streamed T1 window is built for the T0 u T1 step")
+        self.cache = cache
+        sh = cache.shape
+        B, L, Hkv, D = cache.batch, sh.layers, sh.kv_heads, sh.head_dim
+        dt, dev = sh.torch_dtype, cache.device
+        self.chunk = max(1, min(chunk_layers, L))
+        self.host = torch.empty((2, B, L, Hkv, cache.cap1, D), dtype=dt).pin_memory()
+        self.win = torch.zeros((2, 2, B, self.chunk, Hkv, cache.cap1, D), dtype=dt, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
+        self.events = [torch.cuda.Event() for _ in range(4)]
+        main = torch.cuda.current_stream(dev)
+        for e in self.events:        # creates the underlying events
+            e.record(main)
+        self.layer_bytes = 2 * B * Hkv * cache.cap1 * D * self.host.element_size()
+        self.refresh()
+
+    def refresh(self) -> None:
+        """Host copy of the T1 rows of every layer (after a reassignment)."""
+        torch.cuda.synchronize(self.cache.device)
+        self.host[0].copy_(self.cache.k_t1)
+        self.host[1].copy_(self.cache.v_t1)
+
+    def attend(self, q: torch.Tensor) -> None:
+        """Attention of every layer over T0 and the streamed T1 rows, with the fused score
+        update; outputs land in the cache's `out` and `alpha` as with TieredKVCache.attend."""
+        c = self.cache
+        tkv.tkv_decode_step_streamed(c.model, c.batch, q, c.k_t0, c.v_t0, c.t0_len, c.cap0,
+                                     self.host, c.t1_len, c.cap1, self.win, self.chunk,
+                                     c.out, c.alpha, c.alpha_stride,
+                                     c.t0_pos, c.t1_pos, c.scores, c.max_ctx, c.ws, c.ws_bytes,
+                                     torch.cuda.current_stream(c.device), self.side,
+                                     self.events)
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             reassign: bool = True) -> bool:
+        """One decode step with streamed T1 rows; returns True when it ended with a
+        reassignment (after which the host copy is refreshed)."""
+        c = self.cache
+        c.append(k_new, v_new)
+        self.attend(q)
+        c.steps += 1
+        if reassign and c.steps % c.policy.delta == 0:
+            c.reassign()
+            self.refresh()
+            return True
+        return False
