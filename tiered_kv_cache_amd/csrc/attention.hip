@@ -111,25 +111,25 @@ struct Cursor {
   int n0, n1, n2;
 };
 
-// The cursor helpers take EXT (the extended kernel variant: the launch has T2
-// units, or its T1 window holds only the call's layers) as a template flag: the
-// plain launches keep the two-segment walk, whose scalar code the compiler
-// schedules around the key/value stream best (a three-way segment select there
-// measurably slowed the stream on chain-8K sizes).
-template <bool EXT>
+// Segment geometry of a unit whose format is known at compile time: Q8 units are
+// T2 units, the others T0 (seg 0) or T1 (seg 1) units.  Every loop over units
+// runs over units of one format, so no three-way segment select sits in the
+// loop (one there measurably slowed the key/value stream on chain-8K sizes).
+template <bool Q8>
 __device__ __forceinline__ int seg_len(const Cursor& c) {
-  if constexpr (EXT) return c.seg == 0 ? c.n0 : (c.seg == 1 ? c.n1 : c.n2);
+  if constexpr (Q8) return c.n2;
   else return c.seg ? c.n1 : c.n0;
 }
 
 // attended index of the unit's segment slot 0: T0, then T1, then T2
-template <bool EXT>
+template <bool Q8>
 __device__ __forceinline__ int seg_off(const Cursor& c) {
-  if constexpr (EXT) return c.seg == 0 ? 0 : (c.seg == 1 ? c.n0 : c.n0 + c.n1);
+  if constexpr (Q8) return c.n0 + c.n1;
   else return c.seg ? c.n0 : 0;
 }
 
-template <bool EXT>
+// T2: the launch has T2 units (three segments per group)
+template <bool T2>
 __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
   Cursor c;
   int bl = 0;
@@ -137,7 +137,7 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
   c.bl = bl;
   c.n0 = a.seq.t0_len[bl];
   c.n1 = a.seq.t1_len[bl];
-  c.n2 = EXT ? a.seq.t2_len[bl] : 0;
+  c.n2 = T2 ? a.seq.t2_len[bl] : 0;
   const long local = p - a.seq.base[bl];
   const int per = a.seq.units[bl];
   c.lgl = (int)(local / per);
@@ -145,7 +145,7 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
   c.lr = c.lgl / a.hkv;
   c.g = c.lgl - c.lr * a.hkv;
   const int nu0 = (c.n0 + kUnitMfma - 1) / kUnitMfma;
-  if constexpr (EXT) {
+  if constexpr (T2) {
     const int nu1 = (c.n1 + kUnitMfma - 1) / kUnitMfma;
     c.seg = q < nu0 ? 0 : (q < nu0 + nu1 ? 1 : 2);
     c.c0 = (q < nu0 ? q : (q < nu0 + nu1 ? q - nu0 : q - nu0 - nu1)) * kUnitMfma;
@@ -156,22 +156,15 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, long p) {
   return c;
 }
 
-// Next unit in the global order (T0 units, then T1 units, then T2 units,
-// group after group).
-template <bool EXT>
+// Next unit in the global order of a launch without T2 units (T0 units, then
+// T1 units, group after group).
 __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   c.c0 += kUnitMfma;
-  if (c.c0 < seg_len<EXT>(c)) return;
+  if (c.c0 < seg_len<false>(c)) return;
   c.c0 = 0;
   if (c.seg == 0 && c.n1 > 0) {
     c.seg = 1;
     return;
-  }
-  if constexpr (EXT) {
-    if (c.seg <= 1 && c.n2 > 0) {
-      c.seg = 2;
-      return;
-    }
   }
   if (++c.g == a.hkv) {
     c.g = 0;
@@ -186,11 +179,9 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
     if (c.bl < a.seq.nb) {
       c.n0 = a.seq.t0_len[c.bl];
       c.n1 = a.seq.t1_len[c.bl];
-      if constexpr (EXT) c.n2 = a.seq.t2_len[c.bl];
     }
   }
-  if constexpr (EXT) c.seg = c.n0 > 0 ? 0 : (c.n1 > 0 ? 1 : 2);
-  else c.seg = c.n0 > 0 ? 0 : 1;
+  c.seg = c.n0 > 0 ? 0 : 1;
 }
 
 // Operand registers of one unit.  T2 units hold 8 int8 codes per operand in
@@ -230,15 +221,15 @@ struct Stage {
   int cap;      // capacity in units for this group size
 };
 
-// EXT: q and alpha rows may belong to arrays of every layer (io_L, io_l0).
-template <int D, bool EXT>
+// GEO: q and alpha rows may belong to arrays of every layer (io_L, io_l0).
+template <int D, bool GEO>
 __device__ __forceinline__ void begin_group(const AttnArgs& a, const Cursor& c, int h, int grp,
                                             int G, WaveState<D>& st) {
   constexpr int KB = D / 32, NB = D / 16;
   const long b = a.seq.b_offset + c.bl;
   st.group = (long)c.bl * a.Lr * a.hkv + c.lgl;
   long row0;
-  if constexpr (EXT) row0 = (b * a.io_L + a.io_l0 + c.lr) * a.hq + (long)c.g * G;
+  if constexpr (GEO) row0 = (b * a.io_L + a.io_l0 + c.lr) * a.hq + (long)c.g * G;
   else row0 = (b * a.Lr + c.lr) * a.hq + (long)c.g * G;
   const uint16_t* qrow = (const uint16_t*)a.q + (row0 + h) * D;
 #pragma unroll
@@ -336,29 +327,30 @@ __device__ __forceinline__ long unit_row(const AttnArgs& a, const Cursor& c) {
 // The T1 window of a call may hold every layer of a sequence (t1_L = L,
 // t1_l0 = layer_begin) or only the call's layers (t1_L = Lr, t1_l0 = 0: a
 // window streamed layer by layer from host memory).
-template <int D, bool EXT>
+template <int D, bool Q8, bool GEO>
 __device__ __forceinline__ long unit_base(const AttnArgs& a, const Cursor& c) {
-  if constexpr (EXT) {
+  if constexpr (Q8) {
+    return unit_row(a, c) * (long)a.cap2 * D + (long)c.c0 * D;
+  } else if constexpr (GEO) {
     const long b = a.seq.b_offset + c.bl;
     if (c.seg == 1)
       return ((b * a.t1_L + a.t1_l0 + c.lr) * a.hkv + c.g) * (long)a.cap1 * D + (long)c.c0 * D;
-    return unit_row(a, c) * (long)(c.seg == 0 ? a.cap0 : a.cap2) * D + (long)c.c0 * D;
+    return unit_row(a, c) * (long)a.cap0 * D + (long)c.c0 * D;
   } else {
     const int cap = c.seg ? a.cap1 : a.cap0;
     return unit_row(a, c) * (long)cap * D + (long)c.c0 * D;
   }
 }
 
-// EXT: the extended variant (T2 units, or a T1 window of the call's layers).  A
-// separate instantiation, because loads of two formats into the same prefetch
-// registers behind a branch make the compiler wait for them early and the
-// key/value stream loses its overlap.
-template <int D, bool EXT>
+// Q8: the unit is a T2 unit.  The format is a compile-time property of every
+// load loop: loads of two formats into the same prefetch registers behind a
+// branch make the compiler wait for them early and the stream loses its overlap.
+template <int D, bool Q8, bool GEO>
 __device__ __forceinline__ void issue_k(const AttnArgs& a, const Cursor& c, int lane, int grp,
                                         UnitLoads<D>& L) {
   constexpr int KB = D / 32;
-  if (EXT && c.seg == 2) {  // int8 codes, and both scales of the lane's 8 tokens
-    const uint2* Ku = (const uint2*)(a.k2 + unit_base<D, EXT>(a, c));
+  if constexpr (Q8) {  // int8 codes, and both scales of the lane's 8 tokens
+    const uint2* Ku = (const uint2*)(a.k2 + unit_base<D, Q8, GEO>(a, c));
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -372,24 +364,24 @@ __device__ __forceinline__ void issue_k(const AttnArgs& a, const Cursor& c, int 
     L.vs[1] = vs[1];
     return;
   }
-  const uint4* Ku = (const uint4*)((const uint16_t*)(c.seg ? a.k1 : a.k0) + unit_base<D, EXT>(a, c));
+  const uint4* Ku = (const uint4*)((const uint16_t*)(c.seg ? a.k1 : a.k0) + unit_base<D, Q8, GEO>(a, c));
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) L.k[u][kb] = ld_stream(&Ku[u * 2 * D + kb * 64 + lane]);
 }
 
-template <int D, bool EXT>
+template <int D, bool Q8, bool GEO>
 __device__ __forceinline__ void issue_v(const AttnArgs& a, const Cursor& c, int lane,
                                         UnitLoads<D>& L) {
   constexpr int NB = D / 16;
-  if (EXT && c.seg == 2) {
-    const uint2* Vu = (const uint2*)(a.v2 + unit_base<D, EXT>(a, c));
+  if constexpr (Q8) {
+    const uint2* Vu = (const uint2*)(a.v2 + unit_base<D, Q8, GEO>(a, c));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) L.v[nb] = ld_stream8(&Vu[nb * 64 + lane]);
     return;
   }
-  const uint4* Vu = (const uint4*)((const uint16_t*)(c.seg ? a.v1 : a.v0) + unit_base<D, EXT>(a, c));
+  const uint4* Vu = (const uint4*)((const uint16_t*)(c.seg ? a.v1 : a.v0) + unit_base<D, Q8, GEO>(a, c));
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) L.v[nb] = ld_stream(&Vu[nb * 64 + lane]);
 }
@@ -412,12 +404,12 @@ struct AppendRow {
 
 // The appended row in this wave's unit range (a range holds at most one T0 tail
 // unit per group; the first one is taken, the others are written at once).
-template <int D, bool EXT>
+template <int D, bool T2>
 __device__ bool find_append(const AttnArgs& a, long p0, long p1, int lane, AppendRow& r,
                             long& pu_first) {
   const int per_seq = a.Lr * a.hkv;
-  const Cursor first = cursor_at<EXT>(a, p0);
-  const Cursor last = cursor_at<EXT>(a, p1 - 1);
+  const Cursor first = cursor_at<T2>(a, p0);
+  const Cursor last = cursor_at<T2>(a, p1 - 1);
   const long g0 = (long)first.bl * per_seq + first.lgl;
   const long g1 = (long)last.bl * per_seq + last.lgl;
   bool found = false;
@@ -476,11 +468,11 @@ __device__ __forceinline__ void store_append(const AttnArgs& a, const AppendRow&
   }
 }
 
-template <int D, bool EXT>
+template <int D, bool Q8, bool GEO>
 __device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, int lane, int grp,
                                             UnitLoads<D>& L) {
-  issue_k<D, EXT>(a, c, lane, grp, L);
-  issue_v<D, EXT>(a, c, lane, L);
+  issue_k<D, Q8, GEO>(a, c, lane, grp, L);
+  issue_v<D, Q8, GEO>(a, c, lane, L);
 }
 
 // Logits of one unit from its keys: S^T = K Q^T, staged in LDS, the online
@@ -489,13 +481,13 @@ __device__ __forceinline__ void issue_loads(const AttnArgs& a, const Cursor& c, 
 // product is q.code; the row's key scale turns it into q.(code x scale).  The
 // values are codes too: P enters P.V multiplied by each row's value scale,
 // while the softmax sum keeps the plain weights.
-template <int D, bool FULL, bool Q8, bool EXT>
+template <int D, bool FULL, bool Q8>
 __device__ __forceinline__ void unit_scores(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
                                             int h, int grp, int G, WaveState<D>& st, Stage& sg,
                                             bf16x8_t& phi, bf16x8_t& plo) {
   constexpr int KB = D / 32, NB = D / 16;
   constexpr float kLazy = 8.0f;  // rescale only when the max grows by more than 2^8
-  const int c1 = seg_len<EXT>(c);
+  const int c1 = seg_len<Q8>(c);
   const int tb = c.c0 + 8 * grp;  // first of this lane's 8 tokens
   // S^T = K Q^T: this lane gets tokens tb + e (e = 0..7) of head h
   f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -527,7 +519,7 @@ __device__ __forceinline__ void unit_scores(const AttnArgs& a, const Cursor& c, 
     dst[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
   }
   if ((threadIdx.x & 63) == 0) {
-    sg.dst[sg.n] = st.lrow0 + seg_off<EXT>(c) + c.c0;
+    sg.dst[sg.n] = st.lrow0 + seg_off<Q8>(c) + c.c0;
     sg.count[sg.n] = min(kUnitMfma, c1 - c.c0);
   }
   ++sg.n;
@@ -565,7 +557,7 @@ __device__ __forceinline__ void unit_scores(const AttnArgs& a, const Cursor& c, 
 
 // O += P V (high part, then the remainder).  Q8: the values are int8 codes,
 // widened exactly; P already carries the value scales.
-template <int D, bool FULL, bool Q8, bool EXT>
+template <int D, bool FULL, bool Q8>
 __device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, int grp,
                                             const bf16x8_t& phi, const bf16x8_t& plo,
                                             WaveState<D>& st) {
@@ -580,7 +572,7 @@ __device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, in
     return;
   }
   if (!FULL) {  // tail: zero the value slots past the end of the segment (they may hold NaN)
-    const int valid = seg_len<EXT>(c) - (c.c0 + 8 * grp);
+    const int valid = seg_len<Q8>(c) - (c.c0 + 8 * grp);
     if (valid < 8) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -603,42 +595,70 @@ __device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, in
 #define TKV_MFMA_MIN_BLOCKS 2
 #endif
 
-template <bool EXT>
+template <bool Q8>
 __device__ __forceinline__ bool unit_full(const Cursor& c) {
-  return c.c0 + kUnitMfma <= seg_len<EXT>(c);
+  return c.c0 + kUnitMfma <= seg_len<Q8>(c);
 }
 
-// One unit: group change, staging, Q.K, the next unit's keys, P.V, its values.
-template <int D, bool EXT>
+// One unit of format Q8: group change, staging, Q.K, the next unit's keys (the
+// next unit, when `more`, has the same format), P.V, its values.
+template <int D, bool Q8, bool GEO>
 __device__ __forceinline__ void process_unit(const AttnArgs& a, const Cursor& c, UnitLoads<D>& L,
                                              const Cursor& cn, bool more, long w, int lane,
                                              int h, int grp, int G, WaveState<D>& st, Stage& sg) {
   const long group = (long)c.bl * a.Lr * a.hkv + c.lgl;
   if (group != st.group) {
     flush_record<D>(a, w, h, grp, G, st);
-    begin_group<D, EXT>(a, c, h, grp, G, st);
+    begin_group<D, GEO>(a, c, h, grp, G, st);
   }
   if (sg.n == sg.cap) flush_stage(a, lane, G, sg);
   bf16x8_t phi, plo;
-  const bool full = unit_full<EXT>(c);
-  if (EXT && c.seg == 2) {  // 8-bit T2 rows
-    if (full) unit_scores<D, true, true, EXT>(a, c, L, h, grp, G, st, sg, phi, plo);
-    else unit_scores<D, false, true, EXT>(a, c, L, h, grp, G, st, sg, phi, plo);
-    if (more) issue_k<D, EXT>(a, cn, lane, grp, L);
-    unit_values<D, true, true, EXT>(c, L, grp, phi, plo, st);
-    if (more) issue_v<D, EXT>(a, cn, lane, L);
-    return;
+  const bool full = unit_full<Q8>(c);
+  if constexpr (Q8) {  // 8-bit T2 rows (codes are finite: no tail clearing of values)
+    if (full) unit_scores<D, true, true>(a, c, L, h, grp, G, st, sg, phi, plo);
+    else unit_scores<D, false, true>(a, c, L, h, grp, G, st, sg, phi, plo);
+    if (more) issue_k<D, Q8, GEO>(a, cn, lane, grp, L);
+    unit_values<D, true, true>(c, L, grp, phi, plo, st);
+    if (more) issue_v<D, Q8, GEO>(a, cn, lane, L);
+  } else {
+    if (full) unit_scores<D, true, false>(a, c, L, h, grp, G, st, sg, phi, plo);
+    else unit_scores<D, false, false>(a, c, L, h, grp, G, st, sg, phi, plo);
+    if (more) issue_k<D, Q8, GEO>(a, cn, lane, grp, L);
+    if (full) unit_values<D, true, false>(c, L, grp, phi, plo, st);
+    else unit_values<D, false, false>(c, L, grp, phi, plo, st);
+    if (more) issue_v<D, Q8, GEO>(a, cn, lane, L);
   }
-  if (full) unit_scores<D, true, false, EXT>(a, c, L, h, grp, G, st, sg, phi, plo);
-  else unit_scores<D, false, false, EXT>(a, c, L, h, grp, G, st, sg, phi, plo);
-  if (more) issue_k<D, EXT>(a, cn, lane, grp, L);
-  if (full) unit_values<D, true, false, EXT>(c, L, grp, phi, plo, st);
-  else unit_values<D, false, false, EXT>(c, L, grp, phi, plo, st);
-  if (more) issue_v<D, EXT>(a, cn, lane, L);
+}
+
+// A run of n units of one format inside one group, starting at c (left at the
+// run's last unit), with its own rolling prefetch.  Launches with T2 units walk
+// their work as such runs: a group's T0 and T1 units, then its T2 units.
+template <int D, bool Q8, bool GEO>
+__device__ __forceinline__ void run_units(const AttnArgs& a, Cursor& c, long n, long w, int lane,
+                                          int h, int grp, int G, WaveState<D>& st, Stage& sg) {
+  UnitLoads<D> L;
+  issue_loads<D, Q8, GEO>(a, c, lane, grp, L);
+  for (long i = 0; i < n; ++i) {
+    const bool more = i + 1 < n;
+    Cursor cn = c;
+    if (more) {  // the next unit of the run: same group, T0 -> T1 at most
+      cn.c0 += kUnitMfma;
+      if constexpr (!Q8) {
+        if (cn.c0 >= (cn.seg ? cn.n1 : cn.n0)) {
+          cn.seg = 1;
+          cn.c0 = 0;
+        }
+      }
+    }
+    process_unit<D, Q8, GEO>(a, c, L, cn, more, w, lane, h, grp, G, st, sg);
+    c = cn;
+  }
 }
 
 
-template <int D, bool EXT>
+// T2: the launch has T2 units (walked as runs of one format); GEO: the T1
+// window and the q / out / alpha rows use the geometry of a window call.
+template <int D, bool T2, bool GEO>
 __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_kernel(AttnArgs a) {
   __shared__ float stage_buf[4][kStageFloats];
   __shared__ long stage_dst[4][kStageUnits];
@@ -664,7 +684,7 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
   sg.cap = min(kStageUnits, kStageFloats / (32 * G));
   AppendRow ar;
   long pu = -1;
-  const bool app = a.kn && find_append<D, EXT>(a, p0, p1, lane, ar, pu);
+  const bool app = a.kn && find_append<D, T2>(a, p0, p1, lane, ar, pu);
   uint4 kx = make_uint4(0, 0, 0, 0);
   uint16_t vx[D / 64];
   if (app) {  // fetch the new rows
@@ -678,20 +698,42 @@ __global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_ke
     }
   }
   WaveState<D> st;
-  Cursor c = cursor_at<EXT>(a, p0);
-  begin_group<D, EXT>(a, c, h, grp, G, st);
-  // Rolling prefetch: the next unit's keys are requested as soon as Q.K of this
-  // unit has consumed the key registers, its values as soon as P.V has consumed
-  // the value registers, so a unit's worth of loads stays in flight.
-  UnitLoads<D> L;
-  issue_loads<D, EXT>(a, c, lane, grp, L);
-  if (app && pu != p0) store_append<D>(a, ar, lane, kx, vx);  // read back units later
-  for (long p = p0; p < p1; ++p) {
-    const bool more = p + 1 < p1;
-    Cursor cn = c;
-    if (more) cursor_next<EXT>(a, cn);
-    process_unit<D, EXT>(a, c, L, cn, more, w, lane, h, grp, G, st, sg);
-    c = cn;
+  Cursor c = cursor_at<T2>(a, p0);
+  begin_group<D, GEO>(a, c, h, grp, G, st);
+  if constexpr (!T2) {
+    // Rolling prefetch: the next unit's keys are requested as soon as Q.K of this
+    // unit has consumed the key registers, its values as soon as P.V has consumed
+    // the value registers, so a unit's worth of loads stays in flight.
+    UnitLoads<D> L;
+    issue_loads<D, false, GEO>(a, c, lane, grp, L);
+    if (app && pu != p0) store_append<D>(a, ar, lane, kx, vx);  // read back units later
+    for (long p = p0; p < p1; ++p) {
+      const bool more = p + 1 < p1;
+      Cursor cn = c;
+      if (more) cursor_next(a, cn);
+      process_unit<D, false, GEO>(a, c, L, cn, more, w, lane, h, grp, G, st, sg);
+      c = cn;
+    }
+  } else {
+    if (app && pu != p0) {  // before any unit is requested
+      store_append<D>(a, ar, lane, kx, vx);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    long p = p0;
+    for (;;) {
+      const int nu0 = (c.n0 + kUnitMfma - 1) / kUnitMfma;
+      const int nu1 = (c.n1 + kUnitMfma - 1) / kUnitMfma;
+      const int nu2 = (c.n2 + kUnitMfma - 1) / kUnitMfma;
+      const int u = c.c0 / kUnitMfma;
+      const int q = c.seg == 0 ? u : (c.seg == 1 ? nu0 + u : nu0 + nu1 + u);  // unit in group
+      const int end = c.seg == 2 ? nu0 + nu1 + nu2 : nu0 + nu1;              // end of the run
+      const long n = min((long)(end - q), p1 - p);
+      if (c.seg == 2) run_units<D, true, GEO>(a, c, n, w, lane, h, grp, G, st, sg);
+      else run_units<D, false, GEO>(a, c, n, w, lane, h, grp, G, st, sg);
+      p += n;
+      if (p >= p1) break;
+      c = cursor_at<true>(a, p);
+    }
   }
   flush_record<D>(a, w, h, grp, G, st);
   flush_stage(a, lane, G, sg);
@@ -927,20 +969,24 @@ void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int grou
   KernelTimer timer("attn_partial", s);
   if (kv_dtype == TKV_BF16) {
     dim3 grid((unsigned)((a.workers + 3) / 4));
-    // the extended variant: a T2 pool with rows in this launch, or a T1 window of
-    // the call's layers only
-    const bool t2 = a.k2 != nullptr || a.t1_L != a.L || a.t1_l0 != a.layer_begin ||
-                    a.io_L != a.Lr || a.io_l0 != 0;
-#define TKV_MFMA(DD, TT)                                                                 \
-  hipExtLaunchKernelGGL((attn_partial_mfma_kernel<DD, TT>), grid, dim3(256), 0, s,       \
+    // variants: a T2 pool with rows in this launch; a T1 window of the call's layers
+    // only (with q / out / alpha rows of every layer)
+    const bool t2 = a.k2 != nullptr;
+    const bool geo = a.t1_L != a.L || a.t1_l0 != a.layer_begin || a.io_L != a.Lr || a.io_l0 != 0;
+#define TKV_MFMA(DD, TT, GG)                                                             \
+  hipExtLaunchKernelGGL((attn_partial_mfma_kernel<DD, TT, GG>), grid, dim3(256), 0, s,   \
                         timer.start(), timer.stop(), 0, a)
+#define TKV_MFMA_D(DD)                     \
+  if (t2 && geo) TKV_MFMA(DD, true, true);  \
+  else if (t2) TKV_MFMA(DD, true, false);   \
+  else if (geo) TKV_MFMA(DD, false, true);  \
+  else TKV_MFMA(DD, false, false);
     if (head_dim == 128) {
-      if (t2) TKV_MFMA(128, true);
-      else TKV_MFMA(128, false);
+      TKV_MFMA_D(128)
     } else {
-      if (t2) TKV_MFMA(64, true);
-      else TKV_MFMA(64, false);
+      TKV_MFMA_D(64)
     }
+#undef TKV_MFMA_D
 #undef TKV_MFMA
   } else {
     dim3 grid((unsigned)a.workers);
