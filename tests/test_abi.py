@@ -197,6 +197,37 @@ def test_decode_step_t2_validation():
     assert status_of(call, None, fused_append=True) == tkv.TKV_ERR_ARG
 
 
+def test_window_and_streamed_validation():
+    m = model()
+    wargs = dict(batch=1, layer_begin=1, layer_end=2, q=FAKE, k_t0=FAKE, v_t0=FAKE, t0_len=[10],
+                 cap0=32, k_t1_win=FAKE, v_t1_win=FAKE, t1_len=[2], cap1=32, out=FAKE,
+                 alpha=FAKE, alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE, scores=FAKE, max_ctx=64,
+                 workspace=FAKE, workspace_bytes=1 << 30, stream=0)
+    assert status_of(tkv.tkv_decode_step_window, m, **{**wargs, "k_t1_win": NULL}) == \
+        tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_decode_step_window, m, **{**wargs, "layer_end": 3}) == \
+        tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_decode_step_window, m, **{**wargs, "t1_len": [40]}) == \
+        tkv.TKV_ERR_CAPACITY
+    sargs = dict(batch=1, q=FAKE, k_t0=FAKE, v_t0=FAKE, t0_len=[10], cap0=32, host_t1=FAKE,
+                 t1_len=[2], cap1=32, win=FAKE, chunk_layers=1, out=FAKE, alpha=FAKE,
+                 alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE, scores=FAKE, max_ctx=64,
+                 workspace=FAKE, workspace_bytes=1 << 30, stream=0, side_stream=0,
+                 events=[FAKE] * 4)
+    st = tkv.tkv_decode_step_streamed
+    assert status_of(st, m, **{**sargs, "host_t1": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(st, m, **{**sargs, "win": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(st, m, **{**sargs, "chunk_layers": 0}) == tkv.TKV_ERR_ARG
+    assert status_of(st, m, **{**sargs, "chunk_layers": 3}) == tkv.TKV_ERR_ARG     # > L
+    assert status_of(st, m, **{**sargs, "events": [FAKE, NULL, FAKE, FAKE]}) == tkv.TKV_ERR_ARG
+    assert status_of(st, m, **{**sargs, "cap1": 40}) == tkv.TKV_ERR_ARG
+    # the per-chunk checks run before any event is recorded or copy queued (the fake
+    # events would fail a HIP call with another status)
+    assert status_of(st, m, **{**sargs, "t0_len": [33]}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(st, m, **{**sargs, "alpha_stride": 8}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(st, m, **{**sargs, "workspace_bytes": 16}) == tkv.TKV_ERR_CAPACITY
+
+
 def test_t2_update_validation():
     m = model()
     ws = tkv.tkv_t2_update_workspace_bytes(2, 64)
