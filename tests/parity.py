@@ -195,18 +195,24 @@ class HostStore:
 
 
 def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=(),
-                label: str = "", byte_seqs=None) -> dict:
+                label: str = "", byte_seqs=None, attend_t2: bool = False,
+                t1_streamed: int = 0) -> dict:
     """Full-size run, checked on samples the oracle computes one at a time:
     * O and alpha of the sampled (layer, head) pairs over the GPU's attended set;
     * the whole score increment at `full_inc_steps` (all layers and heads);
     * total score mass == steps (any size);
     * at every reassignment: tiers from the oracle ranking of the GPU's scores, the
       counts and slot maps of every sequence; the T0/T1 row bytes and the int8 rows of
-      new T2 positions of the sequences in `byte_seqs` (default: all).
+      new T2 positions of the sequences in `byte_seqs` (default: all);
+    * with attend_t2, the attended T2 rows enter the oracle as code x scale of the int8
+      rows of the full-precision store (bit-exact codes, as the quantizer is), and the T2
+      pool's positions are checked at every reassignment; with t1_streamed > 0 the steps
+      run through T1Stream with chunks of that many layers.
     """
     byte_seqs = set(range(wl.batch)) if byte_seqs is None else set(byte_seqs)
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache()
+    cache = dw.make_cache(attend_t2=attend_t2)
+    streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
     store = HostStore(dw, cache.max_ctx)
     pol = oracle_policy(wl)
     scale = 1.0 / np.sqrt(wl.head_dim)
@@ -217,8 +223,12 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
         for b in range(wl.batch):
             store.put(b, cache.n[b], kn[b], vn[b])
         s_before = cache.scores.cpu().numpy() if k in full_inc_steps else None
-        step_inputs(cache, dw, q, kn, vn, True)
-        cache.steps += 1
+        if streamer is not None:
+            streamer.step(to_device(q, dw.dtype, dw.device), to_device(kn, dw.dtype, dw.device),
+                          to_device(vn, dw.dtype, dw.device), reassign=False)
+        else:
+            step_inputs(cache, dw, q, kn, vn, True)
+            cache.steps += 1
         if k in sample_steps or k in full_inc_steps:
             torch.cuda.synchronize()
             out = cache.out.cpu().numpy()
@@ -227,9 +237,16 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                 alpha_gpu = cache.alpha_of(b)
                 layers = range(wl.layers) if k in full_inc_steps else sorted({l for l, _ in heads})
                 inc = np.zeros(cache.n[b])
+                t2 = set(cache.t2_positions(b).tolist()) if attend_t2 else set()
+                t2_idx = np.array([j for j, p in enumerate(pos.tolist()) if p in t2], np.int64)
                 for l in layers:
                     Kl = store.K[b][l][:, pos]
                     Vl = store.V[b][l][:, pos]
+                    if len(t2_idx):  # attended T2 rows: code x scale, float64
+                        Kl, Vl = widen(Kl), widen(Vl)
+                        for X in (Kl, Vl):
+                            c_, s_ = quantize_rows(X[:, t2_idx].astype(np.float32))
+                            X[:, t2_idx] = c_.astype(np.float64) * s_.astype(np.float64)[..., None]
                     hs = range(wl.q_heads) if k in full_inc_steps else [h for ll, h in heads if ll == l]
                     for h in hs:
                         g = h // group
@@ -241,8 +258,11 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                     inc /= (wl.layers * wl.q_heads)
                     got = cache.scores[b, :cache.n[b]].cpu().numpy().astype(np.float64) - s_before[b, :cache.n[b]]
                     err = np.abs(got - inc)
-                    # the difference of two float32 sums carries their rounding (~1 ulp of s)
-                    lim = 1e-5 * inc + 2.0 ** -23 * np.abs(s_before[b, :cache.n[b]]) * 2 + 1e-12
+                    # the difference of two float32 sums carries their rounding (~1 ulp of s);
+                    # a streamed step adds each chunk's share of the layer sum separately,
+                    # one float32 rounding of s per chunk
+                    adds = -(-wl.layers // t1_streamed) if t1_streamed else 1
+                    lim = 1e-5 * inc + 2.0 ** -24 * (adds + 3) * np.abs(s_before[b, :cache.n[b]]) + 1e-12
                     assert (err <= lim).all(), f"score increment, step {k}, seq {b}: max {err.max():.3e}"
                     stats["inc_checked"] += 1
         if k % wl.delta == 0:
@@ -253,6 +273,8 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                 mass = float(gpu_scores[b, :cache.n[b]].astype(np.float64).sum())
                 assert abs(mass - k) <= 1e-4 * k, f"score mass {mass} after {k} steps"
             cache.reassign()
+            if streamer is not None:
+                streamer.refresh()
             torch.cuda.synchronize()
             for b in range(wl.batch):
                 n = cache.n[b]
@@ -264,6 +286,9 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                 t1 = np.nonzero(t_ref == 1)[0]
                 assert np.array_equal(cache.t0_positions(b), t0)
                 assert np.array_equal(cache.t1_positions(b), t1)
+                if attend_t2:
+                    assert np.array_equal(cache.t2_positions(b), np.nonzero(t_ref == 2)[0])
+                    stats["t2_pool_rows"] = max(stats["t2_pool_rows"], cache.t2_len[b])
                 stats["reassignments"] += 1
                 if b not in byte_seqs:
                     continue

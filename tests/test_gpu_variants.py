@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.parity import run_lockstep, say
+from tests.parity import run_lockstep, run_sampled, say
 from tiered_kv_cache_amd import tkv
 from tiered_kv_cache_amd.driver import (k_rows_to_tiles, k_tiles_to_rows, v_rows_to_tiles,
                                         v_tiles_to_rows)
@@ -190,3 +190,22 @@ def test_ragged_batch_t1_streamed_lockstep(chunk):
                      frac_t2=0.1, frac_t3=0.1)
     st = run_lockstep(wl, t1_streamed=chunk)
     assert st["reassignments"] == 3 * 5
+
+
+# ---------------------------------------------------------------------------
+# both variants at the size the bench times them (7B-class chain, 8K context)
+# ---------------------------------------------------------------------------
+def test_chain8k_attend_t2_full_size_sampled():
+    wl = WORKLOADS["chain8k"]
+    heads = [(0, 0), (0, 6), (13, 20), (27, 27)]
+    st = run_sampled(wl, n_steps=130, sample_steps={1, 64, 65, 100, 129}, heads=heads,
+                     full_inc_steps={66}, attend_t2=True, label="chain8k_attend_t2")
+    assert st["reassignments"] == 2 and st["t2_pool_rows"] > 1000
+
+
+def test_chain8k_t1_streamed_full_size_sampled():
+    wl = WORKLOADS["chain8k"]
+    heads = [(0, 0), (13, 20), (27, 27)]
+    st = run_sampled(wl, n_steps=130, sample_steps={1, 65, 100, 129}, heads=heads,
+                     full_inc_steps={66}, t1_streamed=1, label="chain8k_t1_streamed")
+    assert st["reassignments"] == 2

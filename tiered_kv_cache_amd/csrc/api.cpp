@@ -433,7 +433,11 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     if (units > (1L << 30)) return fail(TKV_ERR_CAPACITY, "too many attention work units");
     a.seq.base[nb] = (int)units;
     a.total_units = units;
-    a.workers = mfma ? resident : std::min<long>(units, kMaxWorkers);
+    // at least two units per wave: a small launch (one layer of a streamed step)
+    // spread over every SIMD leaves each group split into hundreds of records,
+    // which the merge then walks one output row at a time
+    a.workers = mfma ? std::min<long>(resident, std::max<long>(1, (units + 1) / 2))
+                     : std::min<long>(units, kMaxWorkers);
     if (units > 0) {
       launch_attn_partial(a, model->kv_dtype, D, G, stream);
       if ((st = hip_check(hipGetLastError(), "attn_partial launch"))) return st;
