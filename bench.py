@@ -241,7 +241,8 @@ def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
     For each share x of the context kept out of HBM, four policies run the same
     inputs as a full-attention run (every position in T0): eviction only (T3 = x),
     tiered (T1 = x, nothing evicted), T2 = x (8-bit rows, not attended, so at the
-    attention level the same as evicting them), and a fixed eviction with the rest
+    attention level the same as evicting them), T2 = x attended as code x scale (the
+    quantisation error alone), and a fixed eviction with the rest
     offloaded (T1 = x - 0.05, T3 = 0.05), which Proposition 1 of the pages says
     must match eviction only at 0.05.  Error of one step: max over (sequence,
     layer, head) rows of max|O - O_full| / max|O_full|."""
@@ -253,8 +254,9 @@ def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
     contexts = [st.context() for st in dw.streams]
     inputs = dw.preload(1, wl.total_steps)
 
-    def run(f1, f2, f3):
-        cache = DeviceWorkload(wl.with_fractions(f1, f2, f3)).make_cache(contexts=contexts)
+    def run(f1, f2, f3, attend_t2=False):
+        cache = DeviceWorkload(wl.with_fractions(f1, f2, f3)).make_cache(contexts=contexts,
+                                                                         attend_t2=attend_t2)
         outs = []
         for k in range(1, wl.total_steps + 1):
             cache.step(*inputs[k - 1])
@@ -278,7 +280,8 @@ def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
         row = {"off_hbm_share": x,
                "eviction_only": err(run(0.0, 0.0, x)),
                "tiered_t1": err(run(x, 0.0, 0.0)),
-               "t2_not_attended": err(run(0.0, x, 0.0))}
+               "t2_not_attended": err(run(0.0, x, 0.0)),
+               "t2_attended": err(run(0.0, x, 0.0, attend_t2=True))}
         if x > 0.05:
             row["t1_plus_fixed_eviction_0.05"] = err(run(x - 0.05, 0.0, 0.05))
         rows.append(row)
