@@ -500,10 +500,11 @@ def main():
             "link_gbps": link / el_s / 1e9,
             "device_window_bytes": 2 * stream.chunk * stream.layer_bytes,
             "chunk_layers": stream.chunk,
-            "note": "append, then per layer: wait for its T1 rows, attention (tkv_decode_step_"
-                    "window) over T0 and the two-buffer window; the host-to-device copy of layer "
-                    "l + 2 starts when layer l has read its buffer; every Delta steps the "
-                    "reassignment and a refresh of the pinned host copy; not part of value"}
+            "note": "append, then per chunk of layers: wait for its T1 rows, attention over T0 "
+                    "and the two-buffer window (tkv_decode_step_streamed); the host-to-device copy "
+                    "of chunk c + 2 starts when chunk c has read its buffer; no other T1 rows in "
+                    "HBM between reassignments; every Delta steps the pinned host copy goes to a "
+                    "transient device window for the relocation and back; not part of value"}
         del stream
     if not args.no_pcie:
         try:

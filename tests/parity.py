@@ -65,8 +65,10 @@ def check_scores(got, ref, stats):
     assert (err <= lim).all(), f"scores: {int((err > lim).sum())} positions off, max rel {rel:.3e}"
 
 
-def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, stats):
-    """After both sides reassigned from the same float32 scores: bit-exact state."""
+def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, stats,
+                       window=None):
+    """After both sides reassigned from the same float32 scores: bit-exact state.
+    `window` reads the T1 rows (default: the cache's device window)."""
     n = seq.n
     t_gpu = cache.tiers[b, :n].cpu().numpy()
     assert np.array_equal(t_gpu, seq.tier[:n]), \
@@ -77,7 +79,7 @@ def check_reassignment(cache, b, seq: TieredSequence, prev_tiers, gpu_scores, st
     assert cache.t0_len[b] == len(t0) and cache.t1_len[b] == len(seq.t1_positions)
     assert np.array_equal(cache.t0_positions(b), t0)
     assert np.array_equal(cache.t1_positions(b), seq.t1_positions)
-    k1, v1 = cache.t1_rows(b)
+    k1, v1 = (window or cache).t1_rows(b)
     assert k1.tobytes() == np.ascontiguousarray(seq.t1_K).tobytes(), "T1 window keys differ"
     assert v1.tobytes() == np.ascontiguousarray(seq.t1_V).tobytes(), "T1 window values differ"
     new_t2 = np.nonzero((seq.tier[:n] == 2) & (prev_tiers[:n] <= 1))[0]
@@ -160,13 +162,14 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
         if k % wl.delta == 0:
             gpu_scores = cache.scores.cpu().numpy()
             prevs = [s.tier.copy() for s in seqs]
-            cache.reassign()
             if streamer is not None:
-                streamer.refresh()
+                streamer.reassign()
+            else:
+                cache.reassign()
             torch.cuda.synchronize()
             for b, seq in enumerate(seqs):
                 seq.reassign(scores=gpu_scores[b])
-                check_reassignment(cache, b, seq, prevs[b], gpu_scores[b], stats)
+                check_reassignment(cache, b, seq, prevs[b], gpu_scores[b], stats, streamer)
     stats["steps"] = n_steps
     say(f"[{label or wl.name}] lockstep ok: " +
         ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))
@@ -272,9 +275,10 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
             for b in range(wl.batch):
                 mass = float(gpu_scores[b, :cache.n[b]].astype(np.float64).sum())
                 assert abs(mass - k) <= 1e-4 * k, f"score mass {mass} after {k} steps"
-            cache.reassign()
             if streamer is not None:
-                streamer.refresh()
+                streamer.reassign()
+            else:
+                cache.reassign()
             torch.cuda.synchronize()
             for b in range(wl.batch):
                 n = cache.n[b]
@@ -292,7 +296,7 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                 stats["reassignments"] += 1
                 if b not in byte_seqs:
                     continue
-                k1, v1 = cache.t1_rows(b)
+                k1, v1 = (streamer or cache).t1_rows(b)
                 assert k1.tobytes() == np.ascontiguousarray(store.K[b][:, :, t1]).tobytes()
                 assert v1.tobytes() == np.ascontiguousarray(store.V[b][:, :, t1]).tobytes()
                 k0, v0 = cache.t0_rows(b)

@@ -428,12 +428,14 @@ class T1Stream:
     soon as chunk c has read its buffer.  HBM holds 2 x chunk_layers layers of T1
     rows for this path instead of every layer.
 
-    The host copy is refreshed at each reassignment from the device window that the
-    in-place relocation keeps (the rows whose tier changed are placed there); the
-    step itself reads T1 only through the streamed buffers.
+    Between reassignments HBM holds no other T1 rows: the cache's persistent window is
+    released.  At a reassignment the host copy is brought into a transient device
+    window, the same in-place relocation (tkv_compact) runs on it, and the result goes
+    back to the host copy (two transfers of the window every Delta steps).  With
+    keep_window the persistent window stays and the host copy is refreshed from it.
     """
 
-    def __init__(self, cache: TieredKVCache, chunk_layers: int = 1):
+    def __init__(self, cache: TieredKVCache, chunk_layers: int = 1, keep_window: bool = False):
         if cache.attend_t2:
             raise ValueError("the streamed T1 window is built for the T0 u T1 step")
         self.cache = cache
@@ -449,13 +451,38 @@ class T1Stream:
         for e in self.events:        # creates the underlying events
             e.record(main)
         self.layer_bytes = 2 * B * Hkv * cache.cap1 * D * self.host.element_size()
+        self.keep_window = keep_window
         self.refresh()
+        if not keep_window:      # the window lives in host memory from here on
+            cache.k_t1 = cache.v_t1 = None
 
     def refresh(self) -> None:
-        """Host copy of the T1 rows of every layer (after a reassignment)."""
+        """Host copy of the T1 rows of every layer from the device window."""
         torch.cuda.synchronize(self.cache.device)
         self.host[0].copy_(self.cache.k_t1)
         self.host[1].copy_(self.cache.v_t1)
+
+    def reassign(self) -> None:
+        """Tier reassignment and relocation; the T1 rows end in the host copy."""
+        c = self.cache
+        if self.keep_window:
+            c.reassign()
+            self.refresh()
+            return
+        torch.cuda.synchronize(c.device)   # the step's copies have read the host copy
+        c.k_t1 = self.host[0].to(c.device)
+        c.v_t1 = self.host[1].to(c.device)
+        c.reassign()
+        self.refresh()
+        c.k_t1 = c.v_t1 = None
+
+    def t1_rows(self, b: int):
+        """Host copies of the T1 rows of sequence b in ascending position order."""
+        o1 = self.cache._order(b)[1]
+        n = self.cache.t1_len[b]
+        k = k_tiles_to_rows(self.host[0][b], n)
+        v = v_tiles_to_rows(self.host[1][b], n)
+        return to_host_bits(k)[:, :, o1], to_host_bits(v)[:, :, o1]
 
     def attend(self, q: torch.Tensor) -> None:
         """Attention of every layer over T0 and the streamed T1 rows, with the fused score
@@ -477,7 +504,6 @@ class T1Stream:
         self.attend(q)
         c.steps += 1
         if reassign and c.steps % c.policy.delta == 0:
-            c.reassign()
-            self.refresh()
+            self.reassign()
             return True
         return False
