@@ -6,15 +6,19 @@
   adversarial transitions;
 * the T1 rows streamed layer by layer from pinned host memory into a two-buffer device
   window (tkv_decode_step_window), in lock step with the oracle."""
+from collections import defaultdict
+
 import numpy as np
 import pytest
 import torch
 
-from tests.parity import run_lockstep, run_sampled, say
+from tests.parity import (check_alpha, check_output, check_scores, run_lockstep, run_sampled,
+                          say)
 from tiered_kv_cache_amd import tkv
-from tiered_kv_cache_amd.driver import (k_rows_to_tiles, k_tiles_to_rows, v_rows_to_tiles,
-                                        v_tiles_to_rows)
+from tiered_kv_cache_amd.driver import (k_rows_to_tiles, k_tiles_to_rows, to_device,
+                                        v_rows_to_tiles, v_tiles_to_rows)
 from tiered_kv_cache_amd.synth import WORKLOADS
+from tiered_kv_cache_amd.workload import DeviceWorkload
 
 pytestmark = pytest.mark.gpu
 
@@ -209,3 +213,50 @@ def test_chain8k_t1_streamed_full_size_sampled():
     st = run_sampled(wl, n_steps=130, sample_steps={1, 65, 100, 129}, heads=heads,
                      full_inc_steps={66}, t1_streamed=1, label="chain8k_t1_streamed")
     assert st["reassignments"] == 2
+
+
+def test_decode_step_window_matches_layer_subset_call():
+    # tkv_decode_step_window over layers [1, 3) of a 4-layer model, its T1 window holding
+    # only those layers and q / out / alpha holding every layer, against tkv_decode_step
+    # over the same layers with the full window: same work split, same outputs
+    wl = WORKLOADS["small"].scaled(name="window_L4_b3", batch=3, ctx=(700, 1300, 90),
+                                   planted=(4, 6, 0), warmup=0, steps=1, delta=1, frac_t1=0.4,
+                                   frac_t2=0.1, frac_t3=0.05)
+    dw = DeviceWorkload(wl)
+    cache = dw.make_cache()
+    cache.reassign()                      # populate the T1 window from the initial context
+    q, _, _ = dw.host_step(1)
+    qd = to_device(q, dw.dtype, dw.device)
+    B, L, Hq, D = wl.batch, wl.layers, wl.q_heads, wl.head_dim
+    lb, le = 1, 3
+    s0 = cache.scores.clone()
+    out_s = torch.zeros((B, le - lb, Hq, D), dtype=torch.float32, device="cuda")
+    alpha_s = torch.zeros((B, le - lb, Hq, cache.alpha_stride), dtype=torch.float32, device="cuda")
+    tkv.tkv_decode_step(cache.model, B, lb, le, qd[:, lb:le].contiguous(), cache.k_t0, cache.v_t0,
+                        cache.t0_len, cache.cap0, cache.k_t1, cache.v_t1, cache.t1_len,
+                        cache.cap1, out_s, alpha_s, cache.alpha_stride, cache.t0_pos,
+                        cache.t1_pos, cache.scores, cache.max_ctx, cache.ws, cache.ws_bytes)
+    torch.cuda.synchronize()
+    s_subset = cache.scores.clone()
+    cache.scores.copy_(s0)
+    win_k = cache.k_t1[:, lb:le].contiguous()
+    win_v = cache.v_t1[:, lb:le].contiguous()
+    out_w = torch.full((B, L, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    alpha_w = torch.zeros((B, L, Hq, cache.alpha_stride), dtype=torch.float32, device="cuda")
+    tkv.tkv_decode_step_window(cache.model, B, lb, le, qd, cache.k_t0, cache.v_t0, cache.t0_len,
+                               cache.cap0, win_k, win_v, cache.t1_len, cache.cap1, out_w,
+                               alpha_w, cache.alpha_stride, cache.t0_pos, cache.t1_pos,
+                               cache.scores, cache.max_ctx, cache.ws, cache.ws_bytes)
+    torch.cuda.synchronize()
+    stats = defaultdict(float)
+    ow, os_ = out_w.cpu().numpy(), out_s.cpu().numpy()
+    assert np.isnan(ow[:, 0]).all() and np.isnan(ow[:, 3]).all(), "rows of other layers written"
+    check_output(ow[:, lb:le], os_.astype(np.float64), stats)
+    for b in range(B):
+        m = cache.t0_len[b] + cache.t1_len[b]
+        a_w = alpha_w[b, lb:le, :, :m].cpu().numpy()
+        a_s = alpha_s[b, :, :, :m].cpu().numpy().astype(np.float64)
+        check_alpha(a_w, a_s, stats)
+        n = cache.n[b]
+        check_scores(cache.scores[b, :n].cpu().numpy(), s_subset[b, :n].cpu().numpy().astype(np.float64), stats)
+    say(f"[window call] " + ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))

@@ -1,4 +1,6 @@
-// Decode attention over T0 u T1 (with the append of the step's new token).
+// Decode attention over T0 u T1 (with the append of the step's new token), and
+// its two variants: the 8-bit T2 rows attended after T1, and a T1 window that
+// holds only the call's layers (streamed from host memory chunk by chunk).
 //
 // Method: "Not All Thoughts Need HBM" summary pages (gist.science, paper
 // 2605.09490).  Methodologie section 1: T1 rows reach the GPU before the
@@ -19,7 +21,9 @@
 // W + groups records).
 //
 // Kernels:
-//   attn_partial_mfma -- bf16 path; a worker is one wave, one wave per SIMD
+//   attn_partial_mfma<D, T2, GEO> -- bf16 path; T2: the launch has T2 units and
+//       walks its work as runs of one unit format; GEO: the window geometry.
+//       A worker is one wave, one wave per SIMD
 //       (the grid is resident at once).  Per 32-token unit:
 //       S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the group's query heads padded
 //       to 16 columns), an online softmax with lazy rescaling, and O += P V on
