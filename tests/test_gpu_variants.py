@@ -49,14 +49,15 @@ def test_head_groupings_attend_t2_lockstep(hq, hkv, d):
 
 
 def test_ragged_batch_attend_t2_lockstep():
-    # five sequences, one too short for any T2 row; T2 twice the T3 share
+    # six sequences: one too short for any T2 row, one starting empty (it grows from
+    # the appended tokens only); T2 twice the T3 share
     base = WORKLOADS["small"]
-    wl = base.scaled(name="t2_ragged5_L2_h8kv2_d64", layers=2, head_dim=64, batch=5,
-                     ctx=(130, 700, 257, 1100, 12), warmup=8, steps=16, delta=8, prompt=16,
-                     recent=16, sinks=4, planted=(2, 8, 4, 10, 0), frac_t1=0.3, frac_t2=0.2,
+    wl = base.scaled(name="t2_ragged6_L2_h8kv2_d64", layers=2, head_dim=64, batch=6,
+                     ctx=(130, 700, 257, 1100, 12, 0), warmup=8, steps=16, delta=8, prompt=16,
+                     recent=16, sinks=4, planted=(2, 8, 4, 10, 0, 0), frac_t1=0.3, frac_t2=0.2,
                      frac_t3=0.1)
     st = run_lockstep(wl, attend_t2=True)
-    assert st["reassignments"] == 3 * 5
+    assert st["reassignments"] == 3 * 6
 
 
 # ---------------------------------------------------------------------------
