@@ -37,14 +37,15 @@
  *            with r = slot%32, u = (r/4)%2, row = 4*(r/8) + r%4;
  *     values (V-tiles): (slot/32)*32*D + ((d/16)*4 + r/8)*128 + (d%16)*8 + r%8.
  *   With it every operand load of the attention kernel is one contiguous
- *   1 KB wave access.  Capacities (cap0, cap1) must be multiples of 32.
+ *   1 KB wave access.  The optional int8 T2 pool uses the same element order at
+ *   one byte per element.  Capacities (cap0, cap1, cap2) must be multiples of 32.
  *   Per sequence, the T0 pool holds the T0 positions in slots [0, t0_len) and
  *   the T1 window holds the T1 positions in slots [0, t1_len), in any order:
  *   the slot -> position maps t0_pos / t1_pos [B][cap] say which position a
  *   slot holds (an appended token takes slot t0_len; tkv_compact fills the
  *   holes a reassignment leaves).  The "attended index" j of a sequence runs
  *   over T0 slots then T1 slots: j < t0_len is T0 slot j, otherwise T1 slot
- *   j - t0_len.
+ *   j - t0_len; the _t2 calls continue with the T2 slots after T1.
  * - Query head h reads KV head h / (Hq / Hkv) (contiguous grouping).
  * - Supported shapes: head_dim 64 or 128; 1 <= Hq / Hkv <= 16.
  * - Calls on one stream are ordered; calls that write the same buffers on
