@@ -261,3 +261,23 @@ def test_decode_step_window_matches_layer_subset_call():
         n = cache.n[b]
         check_scores(cache.scores[b, :n].cpu().numpy(), s_subset[b, :n].cpu().numpy().astype(np.float64), stats)
     say(f"[window call] " + ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))
+
+
+def test_batch16_attend_t2_full_size_sampled():
+    # 16 ragged sequences (1K-8K), the 7B-class shape, T2 rows attended
+    wl = WORKLOADS["batch16"]
+    heads = [(0, 0), (27, 27)]
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={65, 128}, heads=heads,
+                     full_inc_steps={66}, byte_seqs={0, 15}, attend_t2=True,
+                     label="batch16_attend_t2")
+    assert st["reassignments"] == 2 * 16 and st["t2_pool_rows"] > 0
+
+
+def test_chain32k_attend_t2_full_size_sampled():
+    # 4 sequences of 32768 tokens, 32 layers, 32 query / 8 KV heads, T2 rows attended
+    wl = WORKLOADS["chain32k"]
+    heads = [(0, 3), (31, 31)]
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={65, 128}, heads=heads,
+                     full_inc_steps=set(), byte_seqs={1}, attend_t2=True,
+                     label="chain32k_attend_t2")
+    assert st["reassignments"] == 2 * 4 and st["t2_pool_rows"] > 4000
