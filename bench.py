@@ -95,6 +95,16 @@ def reassign_bytes(wl, n: int, n0: int, n1: int, r2: int, moved: int) -> int:
     return tiers + compact + quant
 
 
+def kernel_sum(kernels: dict, steps: int) -> dict:
+    """Per-step kernel time: the launches of every step plus the per-Delta launches
+    amortised over the timed steps (each kernel's total time / steps)."""
+    per = {name: k["total_ms"] * 1e3 / steps for name, k in kernels.items()}
+    every_step = ("attn_partial", "attn_merge", "score_update")
+    step = sum(v for n, v in per.items() if n in every_step)
+    reassign = sum(v for n, v in per.items() if n not in every_step)
+    return {"every_step": step, "reassignment_amortised": reassign, "total": step + reassign}
+
+
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_partial_{workload}_hbm_counters.md")
 
 
@@ -435,6 +445,7 @@ def main():
                              "plus the per-Delta terms amortised",
                      "mean_attended_tokens": float(np.mean(n_att_steps))},
         "kernels": kernels,
+        "kernels_sum_us_per_step": kernel_sum(kernels, args.steps),
         "kernels_note": ("per-kernel averages from a second identical run with every kernel "
                          "timed (events between launches slow that run to "
                          f"{args.steps / elapsed_bd:.0f} steps/s); value and roofline come "
