@@ -305,9 +305,10 @@ def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the tiered "
-              "path shards by sequence or KV head and needs no collective per step, but no "
-              "multi-GPU run is part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the tiered "
+              "path would shard by sequence or by KV head (one all-reduce of the partial "
+              "scores every Delta steps), and this program measures one GPU's share",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
