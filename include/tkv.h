@@ -221,6 +221,9 @@ tkv_status tkv_decode_step_window(const tkv_model* model, int32_t batch, int32_t
  *            the T1 rows in the window-slot order of t1_pos
  * win      : device [2][2][B][chunk_layers][Hkv][cap1][D] tiles (two buffers of
  *            keys then values); a chunk is one 2-D copy of 2 * B rows
+ * side_stream2         : optional (may be null) second copy stream: chunks then
+ *                        alternate between the two, so two copy engines overlap
+ *                        each other's per-copy set-up
  * events               : four caller-owned events (two "copied", two "read");
  *                        their previous contents are overwritten
  * q, out, alpha and the rest as for tkv_decode_step over layers [0, L).
@@ -234,7 +237,8 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
                                     int32_t alpha_stride, const int32_t* t0_pos,
                                     const int32_t* t1_pos, float* scores, int32_t max_ctx,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                    hipStream_t side_stream, hipEvent_t* events);
+                                    hipStream_t side_stream, hipStream_t side_stream2,
+                                    hipEvent_t* events);
 
 /*
  * Attended T2 pool (optional variant of the decode step).  Methodologie

@@ -213,7 +213,7 @@ def test_window_and_streamed_validation():
                  t1_len=[2], cap1=32, win=FAKE, chunk_layers=1, out=FAKE, alpha=FAKE,
                  alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE, scores=FAKE, max_ctx=64,
                  workspace=FAKE, workspace_bytes=1 << 30, stream=0, side_stream=0,
-                 events=[FAKE] * 4)
+                 events=[FAKE] * 4, side_stream2=None)
     st = tkv.tkv_decode_step_streamed
     assert status_of(st, m, **{**sargs, "host_t1": NULL}) == tkv.TKV_ERR_ARG
     assert status_of(st, m, **{**sargs, "win": NULL}) == tkv.TKV_ERR_ARG

@@ -525,7 +525,8 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
                                     int32_t alpha_stride, const int32_t* t0_pos,
                                     const int32_t* t1_pos, float* scores, int32_t max_ctx,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                    hipStream_t side_stream, hipEvent_t* events) {
+                                    hipStream_t side_stream, hipStream_t side_stream2,
+                                    hipEvent_t* events) {
   tkv_status st = check_model(model);
   if (st) return st;
   if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
@@ -553,11 +554,14 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
   // two buffers among it) happens before the first copies
   if ((st = hip_check(hipEventRecord(read[0], stream), "event record"))) return st;
   if ((st = hip_check(hipEventRecord(read[1], stream), "event record"))) return st;
+  // chunk c goes on side stream c % 2 when two are given: two copy engines overlap
+  // each other's per-copy set-up (each buffer is always filled from the same stream)
   auto copy_chunk = [&](int c) -> tkv_status {
     const int buf = c & 1;
     const int l0 = c * chunk_layers;
     const int n = std::min(chunk_layers, L - l0);
-    tkv_status s2 = hip_check(hipStreamWaitEvent(side_stream, read[buf], 0), "stream wait");
+    hipStream_t ss = (side_stream2 && buf) ? side_stream2 : side_stream;
+    tkv_status s2 = hip_check(hipStreamWaitEvent(ss, read[buf], 0), "stream wait");
     if (s2) return s2;
     // one copy: 2 * B rows (keys, then values, of each sequence) of n layers,
     // [2][B][L][Hkv][cap1][D] host -> [2][B][n][Hkv][cap1][D] buffer
@@ -565,10 +569,10 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
     const char* src = (const char*)host_t1 + (size_t)l0 * layer_bytes;
     s2 = hip_check(hipMemcpy2DAsync(dst, n * layer_bytes, src, (size_t)L * layer_bytes,
                                     n * layer_bytes, 2 * (size_t)batch, hipMemcpyHostToDevice,
-                                    side_stream),
+                                    ss),
                    "T1 chunk copy");
     if (s2) return s2;
-    return hip_check(hipEventRecord(loaded[buf], side_stream), "event record");
+    return hip_check(hipEventRecord(loaded[buf], ss), "event record");
   };
   for (int c = 0; c < std::min(2, n_chunks); ++c)
     if ((st = copy_chunk(c))) return st;

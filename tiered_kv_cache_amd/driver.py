@@ -446,6 +446,7 @@ class T1Stream:
         self.host = torch.empty((2, B, L, Hkv, cache.cap1, D), dtype=dt).pin_memory()
         self.win = torch.zeros((2, 2, B, self.chunk, Hkv, cache.cap1, D), dtype=dt, device=dev)
         self.side = torch.cuda.Stream(device=dev)
+        self.side2 = torch.cuda.Stream(device=dev)   # chunks alternate between the two
         self.events = [torch.cuda.Event() for _ in range(4)]
         main = torch.cuda.current_stream(dev)
         for e in self.events:        # creates the underlying events
@@ -493,7 +494,7 @@ class T1Stream:
                                      c.out, c.alpha, c.alpha_stride,
                                      c.t0_pos, c.t1_pos, c.scores, c.max_ctx, c.ws, c.ws_bytes,
                                      torch.cuda.current_stream(c.device), self.side,
-                                     self.events)
+                                     self.events, side_stream2=self.side2)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              reassign: bool = True) -> bool:

@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_size_t, _P]),
         "tkv_decode_step_streamed": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _P, _P, _I,
                                           _P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P, _I, _P,
-                                          ctypes.c_size_t, _P, _P, _P]),
+                                          ctypes.c_size_t, _P, _P, _P, _P]),
         "tkv_decode_step_t2": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _P, _P, _P, _I,
                                     _P, _P, _P, _I, ctypes.POINTER(tkv_t2_pool), _P, _P, _I,
                                     _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
@@ -259,7 +259,7 @@ def tkv_decode_step_window(model, batch, layer_begin, layer_end, q, k_t0, v_t0, 
 def tkv_decode_step_streamed(model, batch, q, k_t0, v_t0, t0_len, cap0, host_t1, t1_len, cap1,
                              win, chunk_layers, out, alpha, alpha_stride, t0_pos, t1_pos,
                              scores, max_ctx, workspace, workspace_bytes, stream, side_stream,
-                             events) -> None:
+                             events, side_stream2=None) -> None:
     a, b = _HostInts(t0_len), _HostInts(t1_len)
     ev = (ctypes.c_void_p * 4)(*[_event(e) for e in events])
     _check(lib().tkv_decode_step_streamed(ctypes.byref(model), batch, _ptr(q), _ptr(k_t0),
@@ -268,7 +268,9 @@ def tkv_decode_step_streamed(model, batch, q, k_t0, v_t0, t0_len, cap0, host_t1,
                                           alpha_stride, _ptr(t0_pos), _ptr(t1_pos),
                                           _ptr(scores), max_ctx, _ptr(workspace),
                                           workspace_bytes, _stream(stream),
-                                          _stream(side_stream), ev),
+                                          _stream(side_stream),
+                                          None if side_stream2 is None else _stream(side_stream2),
+                                          ev),
            "tkv_decode_step_streamed")
 
 
