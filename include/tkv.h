@@ -222,8 +222,8 @@ tkv_status tkv_decode_step_window(const tkv_model* model, int32_t batch, int32_t
  * win      : device [2][2][B][chunk_layers][Hkv][cap1][D] tiles (two buffers of
  *            keys then values); a chunk is one 2-D copy of 2 * B rows
  * side_stream2         : optional (may be null) second copy stream: chunks then
- *                        alternate between the two, so two copy engines overlap
- *                        each other's per-copy set-up
+ *                        alternate between the two, so the next copy is queued
+ *                        when the running one ends (shorter idle gaps on the link)
  * events               : four caller-owned events (two "copied", two "read");
  *                        their previous contents are overwritten
  * q, out, alpha and the rest as for tkv_decode_step over layers [0, L).

@@ -554,8 +554,9 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
   // two buffers among it) happens before the first copies
   if ((st = hip_check(hipEventRecord(read[0], stream), "event record"))) return st;
   if ((st = hip_check(hipEventRecord(read[1], stream), "event record"))) return st;
-  // chunk c goes on side stream c % 2 when two are given: two copy engines overlap
-  // each other's per-copy set-up (each buffer is always filled from the same stream)
+  // chunk c goes on side stream c % 2 when two are given: the next copy is then
+  // already queued when the running one ends (each buffer is always filled from
+  // the same stream)
   auto copy_chunk = [&](int c) -> tkv_status {
     const int buf = c & 1;
     const int l0 = c * chunk_layers;
