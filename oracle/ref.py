@@ -109,13 +109,6 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
     return O, alpha
 
 
-def full_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
-                   ) -> Tuple[np.ndarray, np.ndarray]:
-    """Attention of every layer over a whole cache: q [L][Hq][D], K/V [L][Hkv][n][D]."""
-    outs, alphas = zip(*(attention(q[l], K[l], V[l], scale) for l in range(q.shape[0])))
-    return np.stack(outs), np.stack(alphas)
-
-
 # --------------------------------------------------------------------------
 # importance score  (Methodologie section 2, score equation)
 # --------------------------------------------------------------------------

@@ -274,7 +274,7 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
             prev = cache.tiers.cpu().numpy()
             for b in range(wl.batch):
                 mass = float(gpu_scores[b, :cache.n[b]].astype(np.float64).sum())
-                assert abs(mass - k) <= 1e-4 * k, f"score mass {mass} after {k} steps"
+                assert abs(mass - k) <= 1e-5 * k, f"score mass {mass} after {k} steps"
             if streamer is not None:
                 streamer.reassign()
             else:

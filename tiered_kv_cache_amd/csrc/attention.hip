@@ -595,10 +595,6 @@ __device__ __forceinline__ void unit_values(const Cursor& c, UnitLoads<D>& L, in
   }
 }
 
-// Minimum workgroups per CU the compiler must fit (register budget).
-#ifndef TKV_MFMA_MIN_BLOCKS
-#define TKV_MFMA_MIN_BLOCKS 2
-#endif
 
 template <bool Q8>
 __device__ __forceinline__ bool unit_full(const Cursor& c) {
@@ -663,8 +659,9 @@ __device__ __forceinline__ void run_units(const AttnArgs& a, Cursor& c, long n, 
 
 // T2: the launch has T2 units (walked as runs of one format); GEO: the T1
 // window and the q / out / alpha rows use the geometry of a window call.
+// One workgroup per CU: the logit stage takes 147 KB of the CU's 160 KB of LDS.
 template <int D, bool T2, bool GEO>
-__global__ __launch_bounds__(256, TKV_MFMA_MIN_BLOCKS) void attn_partial_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 1) void attn_partial_mfma_kernel(AttnArgs a) {
   __shared__ float stage_buf[4][kStageFloats];
   __shared__ long stage_dst[4][kStageUnits];
   __shared__ int stage_cnt[4][kStageUnits];
