@@ -8,6 +8,13 @@ tokens.  Inputs are resident in HBM before the timed region starts; the T1
 rows are in their device window (the host-link transfer is measured on its own
 and reported under "pcie", never in `value`).
 
+The timed steps always start from the tiered state: the warm-up runs at least
+Delta steps, so the first reassignment (every position in T0 until then) is
+behind it.  When the K timed steps hold no reassignment (K < Delta), the
+untimed steps continue to the next multiple of Delta and that reassignment is
+timed on its own; K / Delta of its cost is added to the timed interval, so
+`value` always pays for the tier work at the method's cadence.
+
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 from __future__ import annotations
@@ -95,22 +102,39 @@ def reassign_bytes(wl, n: int, n0: int, n1: int, r2: int, moved: int) -> int:
     return tiers + compact + quant
 
 
-def kernel_sum(kernels: dict, steps: int) -> dict:
+EVERY_STEP_KERNELS = ("append", "attn_partial", "attn_merge", "score_update")
+
+
+def kernel_sum(kernels: dict, steps: int, reassignments: int = None, delta: int = None) -> dict:
     """Per-step kernel time: the launches of every step plus the per-Delta launches
-    amortised over the timed steps (each kernel's total time / steps)."""
-    per = {name: k["total_ms"] * 1e3 / steps for name, k in kernels.items()}
-    every_step = ("attn_partial", "attn_merge", "score_update")
-    step = sum(v for n, v in per.items() if n in every_step)
-    reassign = sum(v for n, v in per.items() if n not in every_step)
+    amortised.  With `reassignments` and `delta`, the per-Delta launches were timed over
+    that many reassignments and each costs 1/delta of it per step; otherwise they ran
+    inside the `steps` timed steps (each kernel's total time / steps)."""
+    step = sum(k["total_ms"] * 1e3 / steps for n, k in kernels.items() if n in EVERY_STEP_KERNELS)
+    re_total = sum(k["total_ms"] * 1e3 for n, k in kernels.items() if n not in EVERY_STEP_KERNELS)
+    if reassignments:
+        reassign = re_total / reassignments / delta
+    else:
+        reassign = re_total / steps
     return {"every_step": step, "reassignment_amortised": reassign, "total": step + reassign}
+
+
+def budget_counts(wl, n: int):
+    """Tier counts the stated split gives at length n (T1..T3 = floor(f * n) of the
+    float32 fractions, T0 the rest)."""
+    import numpy as np
+    n1, n2, n3 = (int(math.floor(float(np.float32(f)) * n)) for f in wl.fractions())
+    return [n - n1 - n2 - n3, n1, n2, n3]
 
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_partial_{workload}_hbm_counters.md")
 
 
-def counter_traffic(workload: str):
+def counter_traffic(workload: str, attended_rows: float):
     """HBM bytes per attn_partial launch from the committed counter summary, or None when
-    there is none for this workload or the kernel sources changed since it was taken."""
+    there is none for this workload, the kernel sources changed since it was taken, or
+    its launches attended another mean number of rows than this run's (more than 0.5%
+    apart): counter bytes of one state are not the traffic of another."""
     import hashlib
     path = COUNTERS_FILE.format(workload=workload)
     if not os.path.exists(path):
@@ -126,6 +150,9 @@ def counter_traffic(workload: str):
             with open(os.path.join(ROOT, f), "rb") as fh:
                 h.update(fh.read())
         if h.hexdigest() != fields["source_sha256"]:
+            return None
+        rows = float(fields["attended_rows_per_launch"])
+        if abs(rows - attended_rows) > 0.005 * attended_rows:
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
@@ -199,12 +226,10 @@ def cpu_baseline(wl, seconds: float) -> dict:
 
 
 def pcie_leg(wl, cache, positions, device_step_s: float) -> dict:
-    """Host-link path of T1: host pack into pinned staging + H2D on a side stream.
-
-    Also the end-to-end rate if T1 were streamed from host memory every step (the pack
-    redone at each reassignment only, since T1 membership changes only then), next to
-    the link bytes of the persistent device window, which moves changed rows on the
-    device and sends nothing over the link."""
+    """Host-link path of a full T1 gather (tkv_gather_t1): host pack of every T1 row into
+    pinned staging, then one 2-D copy to a device window on a side stream.  This is what
+    a T1 set moved wholesale would cost; the host-resident mode (the t1_streamed leg)
+    moves only the rows that change tier at a reassignment and streams the window."""
     import numpy as np
     import torch
     from tiered_kv_cache_amd import tkv
@@ -215,34 +240,26 @@ def pcie_leg(wl, cache, positions, device_step_s: float) -> dict:
     r = np.random.default_rng(0)
     host_k = torch.from_numpy(r.integers(0, 1 << 15, size=(L, Hkv, max_ctx, D), dtype=np.int16)).view(dt)
     host_v = host_k.clone()
-    stg_k = torch.empty((L, Hkv, cap1, D), dtype=dt).pin_memory()
-    stg_v = torch.empty((L, Hkv, cap1, D), dtype=dt).pin_memory()
-    dev_k = torch.empty((L, Hkv, cap1, D), dtype=dt, device="cuda")
-    dev_v = torch.empty((L, Hkv, cap1, D), dtype=dt, device="cuda")
+    stg = torch.empty((L, Hkv, 2, cap1, D), dtype=dt, pin_memory=True)
+    dev = torch.empty((L, Hkv, 2, cap1, D), dtype=dt, device="cuda")
     side = torch.cuda.Stream()
     n1 = len(positions)
-    bytes_t1 = 2 * L * Hkv * n1 * D * dev_k.element_size()
+    bytes_t1 = 2 * L * Hkv * n1 * D * dev.element_size()
     t0 = time.perf_counter()
-    tkv.tkv_gather_t1(cache.model, host_k, host_v, max_ctx, positions, n1, stg_k, stg_v, cap1,
-                      None, None, side, None)
+    tkv.tkv_gather_t1(cache.model, host_k, host_v, max_ctx, positions, n1, stg, cap1, None,
+                      side, None)
     t_pack = time.perf_counter() - t0
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
     ev0.record(side)
     for _ in range(reps):
-        tkv.tkv_gather_t1(cache.model, None, None, max_ctx, None, n1, stg_k, stg_v, cap1,
-                          dev_k, dev_v, side, None)
+        tkv.tkv_gather_t1(cache.model, None, None, max_ctx, None, n1, stg, cap1, dev, side, None)
     ev1.record(side)
     ev1.synchronize()
     t_h2d = ev0.elapsed_time(ev1) / 1e3 / reps
-    streamed_step_s = max(t_h2d + t_pack / wl.delta, device_step_s)
     return {"t1_rows": n1, "t1_bytes": bytes_t1, "pack_ms": t_pack * 1e3,
-            "pack_gbps": bytes_t1 / t_pack / 1e9, "h2d_ms": t_h2d * 1e3,
-            "h2d_gbps": bytes_t1 / t_h2d / 1e9,
-            "link_bytes_per_step_streamed": bytes_t1,
-            "link_bytes_per_step_device_window": 0,
-            "streamed_steps_per_s": 1.0 / streamed_step_s,
-            "streamed_bound": "host link" if t_h2d + t_pack / wl.delta > device_step_s else "device"}
+            "pack_gbps": bytes_t1 / t_pack / 1e9 if t_pack > 0 else None,
+            "h2d_ms": t_h2d * 1e3, "h2d_gbps": bytes_t1 / t_h2d / 1e9 if t_h2d > 0 else None}
 
 
 def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
@@ -324,43 +341,62 @@ def main():
         torch.neg(src, out=dst)       # reads 256 MiB, writes 256 MiB
         torch.cuda.synchronize()
         del src, dst
-    wl = WORKLOADS[args.workload].scaled(steps=args.steps, warmup=args.warmup)
+    base = WORKLOADS[args.workload]
+    delta = base.delta
+    K = args.steps
+    # the timed steps start from the tiered state: the first reassignment (after step
+    # Delta) lies inside the warm-up
+    W = max(args.warmup, delta)
+    # untimed steps after the timed ones, up to the next reassignment, when the timed
+    # steps hold none: that reassignment is timed on its own and amortised
+    extra = 0 if K >= delta else (-(W + K)) % delta
+    wl = base.scaled(steps=K + extra, warmup=W)
     if args.eviction_curve:
-        print(json.dumps(eviction_curve(wl)), flush=True)
+        print(json.dumps(eviction_curve(base.scaled(steps=K, warmup=W))), flush=True)
         return
     print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
     dw = DeviceWorkload(wl)
     contexts = [st.context() for st in dw.streams]
-    inputs = dw.preload(1, wl.total_steps)
+    inputs = dw.preload(1, W + K + extra)
 
     flush_buf = None
+    re_kernels = "assign_tiers,reloc_scan,quantize_t2,reloc_stage,reloc_to_t1,reloc_to_t0,t2_scan,t2_move"
 
     def run(timed_kernels, every=1, flush=False, attend_t2=False):
-        """Fresh cache, W warm-up steps, then exactly K steps between two syncs with the
-        kernel timers on for `timed_kernels` (None = all) on every `every`-th step (each
-        pair of events adds a few microseconds around the launch it brackets).  With
-        `flush`, a 512 MB buffer is read before every step (outside the kernel timers).
-        With `attend_t2`, the 8-bit T2 rows are attended too; the attended counts are
-        then (full-precision rows, T2 rows) pairs."""
-        cache = dw.make_cache(contexts=contexts, attend_t2=attend_t2)
+        """Fresh cache, W warm-up steps (at least Delta: the first reassignment is behind
+        them), then exactly K steps between two syncs with the kernel timers on for
+        `timed_kernels` (None = all) on every `every`-th step (each pair of events adds a
+        few microseconds around the launch it brackets).  With `flush`, a 512 MB buffer is
+        read before every step (outside the kernel timers).  With `attend_t2`, the 8-bit
+        T2 rows are attended too; the attended counts are then (full-precision rows, T2
+        rows) pairs.  When the K steps hold no reassignment, the steps continue untimed to
+        the next multiple of Delta and that reassignment alone is timed (wall clock
+        between two syncs, its kernels under the timers when `timed_kernels` is None)."""
+        cache = dw.make_cache(contexts=contexts, attend_t2=attend_t2, t0_budget=True)
         torch.cuda.synchronize()
-        for k in range(1, args.warmup + 1):
+        for k in range(1, W + 1):
             cache.step(*inputs[k - 1])
         torch.cuda.synchronize()
+        state = {"n": [int(x) for x in cache.n],
+                 "counts": cache.counts.cpu().numpy().astype(int).tolist(),
+                 "n_at_reassignment": [int(x) - (W % delta) for x in cache.n],
+                 "resident_kv_bytes": cache.resident_kv_bytes(),
+                 "full_cache_kv_bytes": cache.full_cache_bytes(), "cap0": cache.cap0,
+                 "cap1": cache.cap1}
         n_att, n_all, re, sampled = [], [], [], []
         tkv.tkv_timing_select(timed_kernels)
         tkv.tkv_timing_reset()
         tkv.tkv_timing_enable(True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for k in range(args.warmup + 1, args.warmup + args.steps + 1):
+        for k in range(W + 1, W + K + 1):
             full_rows = sum(cache.t0_len) + sum(cache.t1_len) + wl.batch
             n_att.append((full_rows, sum(cache.t2_len)) if attend_t2 else full_rows)
             n_all.append(sum(cache.n) + wl.batch)
             if flush:
                 flush_buf.sum()
             if every > 1:
-                on = (k - args.warmup - 1) % every == 0
+                on = (k - W - 1) % every == 0
                 tkv.tkv_timing_enable(on)
                 if on:
                     sampled.append(n_att[-1])
@@ -370,6 +406,22 @@ def main():
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         tkv.tkv_timing_enable(False)
+        re_alone = None
+        if not re:
+            for k in range(W + K + 1, W + K + extra + 1):
+                cache.step(*inputs[k - 1], reassign=False)
+            assert cache.steps % delta == 0
+            tkv.tkv_timing_enable(timed_kernels is None)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            cache.reassign()
+            torch.cuda.synchronize()
+            re_alone = time.perf_counter() - t1
+            tkv.tkv_timing_enable(False)
+            re_alone_info = (sum(cache.n), sum(cache.t0_len), sum(cache.t1_len),
+                             sum(cache.t2_new), sum(cache.moved))
+        else:
+            re_alone_info = None
         kernels = {}
         for name in ("append", "attn_partial", "attn_merge", "alpha_score", "score_update",
                      "assign_tiers", "reloc_scan", "quantize_t2", "reloc_stage", "reloc_to_t1",
@@ -378,63 +430,106 @@ def main():
             if cnt:
                 kernels[name] = {"launches": cnt, "avg_us": ms * 1e3 / cnt, "total_ms": ms}
         tkv.tkv_timing_select(None)
-        return cache, elapsed, n_att, n_all, re, kernels, (sampled or n_att)
+        return {"cache": cache, "elapsed": elapsed, "n_att": n_att, "n_all": n_all, "re": re,
+                "kernels": kernels, "sampled": sampled or n_att, "re_alone": re_alone,
+                "re_alone_info": re_alone_info, "state": state}
+
+    def amortised_elapsed(r):
+        """Timed interval plus K / Delta of a reassignment timed on its own, when the K
+        timed steps held none."""
+        return r["elapsed"] + (K / delta * r["re_alone"] if r["re_alone"] is not None else 0.0)
+
+    def check_split(r):
+        """The tier counts left by the last reassignment before the timed steps must be
+        those of the stated split at that length (refuse to report a mislabelled state)."""
+        st = r["state"]
+        for b in range(wl.batch):
+            want = budget_counts(wl, st["n_at_reassignment"][b])
+            if st["counts"][b] != want:
+                print(f"[bench] sequence {b}: tier counts {st['counts'][b]} at n = "
+                      f"{st['n_at_reassignment'][b]} differ from the split {want}; no line "
+                      "printed", file=sys.stderr, flush=True)
+                sys.exit(3)
 
     # the measured run: only the reported kernel carries timers
-    print(f"[bench] warm-up {args.warmup} steps, {args.steps} timed steps", file=sys.stderr,
-          flush=True)
+    print(f"[bench] warm-up {W} steps, {K} timed steps", file=sys.stderr, flush=True)
     # repeated: the reported figures are the medians over the repetitions
     reps = []
     for _ in range(max(1, args.repeats)):
-        cache, elapsed, n_att_steps, n_steps, re_info, timed, n_att_timed = run(["attn_partial"],
-                                                                                 every=8)
-        reps.append((elapsed, timed.get("attn_partial", {}).get("avg_us", float("nan"))))
-        del cache
+        r = run(["attn_partial"], every=8)
+        check_split(r)
+        reps.append((amortised_elapsed(r), r["kernels"].get("attn_partial", {}).get("avg_us", float("nan")),
+                     r["elapsed"], r["re_alone"]))
+        last = r
+        del r["cache"]
         torch.cuda.empty_cache()
-    elapsed = float(np.median([r[0] for r in reps]))
-    attn_med = float(np.median([r[1] for r in reps]))
+    elapsed = float(np.median([x[0] for x in reps]))
+    attn_med = float(np.median([x[1] for x in reps]))
+    n_att_steps, n_steps, re_info, n_att_timed = last["n_att"], last["n_all"], last["re"], last["sampled"]
     # a second, identical run with every kernel timed (the per-kernel breakdown only)
     print("[bench] breakdown run", file=sys.stderr, flush=True)
-    cache, elapsed_bd, _, _, _, kernels, _ = run(None)
+    bd = run(None)
+    cache = bd["cache"]
+    kernels = bd["kernels"]
 
-    steps_per_s = args.steps / elapsed
+    steps_per_s = K / elapsed
     step_b = [step_bytes(wl, n_att, n) for n_att, n in zip(n_att_steps, n_steps)]
-    re_b = sum(reassign_bytes(wl, *r) for r in re_info)
-    alg_bytes = (sum(x["total"] for x in step_b) + re_b) / args.steps
-    min_bytes = (sum(x["minimal"] for x in step_b) + re_b) / args.steps
-    attn = dict(timed.get("attn_partial", {"launches": 1, "avg_us": float("nan"),
-                                           "total_ms": float("nan")}))
+    if re_info:
+        re_b = sum(reassign_bytes(wl, *x) for x in re_info)
+    else:
+        re_b = K / delta * reassign_bytes(wl, *last["re_alone_info"])
+    alg_bytes = (sum(x["total"] for x in step_b) + re_b) / K
+    min_bytes = (sum(x["minimal"] for x in step_b) + re_b) / K
+    attn = dict(last["kernels"].get("attn_partial", {"launches": 1, "avg_us": float("nan"),
+                                                     "total_ms": float("nan")}))
     attn["avg_us"] = attn_med
     attn_bytes = float(np.mean([attn_partial_bytes(wl, n) for n in n_att_timed]))
+    attn_rows = float(np.mean(n_att_timed))
     achieved = attn_bytes / (attn["avg_us"] * 1e-6) / 1e9
+    st = last["state"]
+    counts = np.array(st["counts"]).sum(axis=0).tolist()
+    traffic = counter_traffic(args.workload, attn_rows)
 
     out = {
         "metric": "decode steps/sec (attn+score+tier) at 8K ctx; achieved HBM GB/s vs peak",
         "value": steps_per_s,
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": elapsed / args.steps * 1e3,
+        "ms_per_step": elapsed / K * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded generator: sinks, planted resurfacing keys, N(0,1) K/V)",
-        "config": {"workload": f"{wl.name}: {wl.description}", "batch": wl.batch,
+        "config": {"workload": f"{base.name}: {base.description}", "batch": wl.batch,
                    "context": list(wl.ctx) if wl.batch > 1 else wl.ctx[0],
                    "layers": wl.layers, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
                    "head_dim": wl.head_dim,
                    "tiers_t0_t1_t2_t3": [round(1 - wl.frac_t1 - wl.frac_t2 - wl.frac_t3, 4),
                                          wl.frac_t1, wl.frac_t2, wl.frac_t3],
-                   "delta": wl.delta, "reassignments_timed": len(re_info),
-                   "rows_copied_per_reassignment": [r[4] for r in re_info]},
+                   "delta": delta, "warmup_steps_run": W,
+                   "tier_counts_before_timed_steps": counts,
+                   "context_at_that_reassignment": int(sum(st["n_at_reassignment"])),
+                   "mean_attended_rows": float(np.mean(n_att_steps)),
+                   "reassignments_timed": len(re_info),
+                   "reassignment_timed_alone_ms": (float(np.median([x[3] for x in reps])) * 1e3
+                                                   if not re_info else None),
+                   "rows_copied_per_reassignment": ([x[4] for x in re_info] if re_info
+                                                    else [last["re_alone_info"][4]]),
+                   "value_basis": ("timed steps as measured (they hold the reassignments)"
+                                   if re_info else
+                                   f"timed steps plus {K}/{delta} of one reassignment timed "
+                                   "alone at the next multiple of delta")},
         "repetitions": {"count": len(reps),
-                        "steps_per_s": [args.steps / r[0] for r in reps],
-                        "attn_partial_avg_us": [r[1] for r in reps]},
+                        "steps_per_s": [K / x[0] for x in reps],
+                        "timed_interval_steps_per_s": [K / x[2] for x in reps],
+                        "attn_partial_avg_us": [x[1] for x in reps]},
         "roofline": {"bound": "hbm", "kernel": "attn_partial", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": counter_traffic(args.workload), "bytes_per_launch": attn_bytes,
+                     "traffic": traffic, "bytes_per_launch": attn_bytes,
+                     "attended_rows_per_launch": attn_rows,
                      "avg_launch_us": attn["avg_us"]},
         "step_hbm": {"algorithmic_bytes_per_step": alg_bytes,
                      "achieved_gbps": alg_bytes * steps_per_s / 1e9,
@@ -445,47 +540,57 @@ def main():
                              "update) and minimal bytes (K/V, q, O, score RMW, append), "
                              "plus the per-Delta terms amortised",
                      "mean_attended_tokens": float(np.mean(n_att_steps))},
+        "hbm_resident": {"kv_bytes": st["resident_kv_bytes"],
+                         "full_cache_kv_bytes": st["full_cache_kv_bytes"],
+                         "ratio": st["resident_kv_bytes"] / st["full_cache_kv_bytes"],
+                         "t0_capacity": st["cap0"], "t1_window_capacity": st["cap1"],
+                         "note": "device bytes holding K/V rows after the first "
+                                 "reassignment (T0 pool at its budget, T1 window) against "
+                                 "every row of the context at full precision"},
         "kernels": kernels,
-        "kernels_sum_us_per_step": kernel_sum(kernels, args.steps),
+        "kernels_sum_us_per_step": (kernel_sum(kernels, K) if bd["re"] else
+                                    kernel_sum(kernels, K, 1, delta)),
         "kernels_note": ("per-kernel averages from a second identical run with every kernel "
                          "timed (events between launches slow that run to "
-                         f"{args.steps / elapsed_bd:.0f} steps/s); value and roofline come "
+                         f"{K / amortised_elapsed(bd):.0f} steps/s); value and roofline come "
                          "from the run that times attn_partial only, on every 8th step"),
     }
     if not args.no_flush_run:
         # a real decode streams the model weights between two visits of a layer, which
         # evicts the memory-side cache: the same steps with 512 MB read before each one
-        del cache
+        del cache, bd
         torch.cuda.empty_cache()
         print("[bench] cache-flushed run", file=sys.stderr, flush=True)
         flush_buf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-        cache, elapsed_fl, _, _, _, fl_kernels, fl_att = run(["attn_partial"], flush=True)
-        fa = fl_kernels.get("attn_partial")
+        fr = run(["attn_partial"], flush=True)
+        cache = fr["cache"]
+        fa = fr["kernels"].get("attn_partial")
         if fa:
-            fb = float(np.mean([attn_partial_bytes(wl, n) for n in fl_att]))
+            fb = float(np.mean([attn_partial_bytes(wl, n) for n in fr["sampled"]]))
             out["flushed"] = {"attn_partial_avg_us": fa["avg_us"],
                               "achieved_gbps": fb / (fa["avg_us"] * 1e-6) / 1e9,
                               "frac": fb / (fa["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
                               "note": "512 MB read before every step (memory-side cache "
                                       "cold, as after a model's weight stream)"}
-        del flush_buf
+        del flush_buf, fr
     if not args.no_t2_leg:
         # the variant that attends the 8-bit T2 rows after T1: same inputs and policy
         del cache
         torch.cuda.empty_cache()
         print("[bench] attended-T2 run", file=sys.stderr, flush=True)
-        cache, el_t2, att_t2, _, re_t2, k_t2, smp_t2 = run(["attn_partial"], every=8,
-                                                           attend_t2=True)
-        a2 = k_t2.get("attn_partial")
+        tr = run(["attn_partial"], every=8, attend_t2=True)
+        cache = tr["cache"]
+        a2 = tr["kernels"].get("attn_partial")
         if a2:
-            b2 = float(np.mean([attn_partial_bytes(wl, f, t) for f, t in smp_t2]))
+            b2 = float(np.mean([attn_partial_bytes(wl, f, t) for f, t in tr["sampled"]]))
             out["attend_t2"] = {
-                "steps_per_s": args.steps / el_t2, "attn_partial_avg_us": a2["avg_us"],
+                "steps_per_s": K / amortised_elapsed(tr), "attn_partial_avg_us": a2["avg_us"],
                 "bytes_per_launch": b2, "achieved_gbps": b2 / (a2["avg_us"] * 1e-6) / 1e9,
                 "frac": b2 / (a2["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                "mean_t2_rows": float(np.mean([t for _, t in att_t2])),
+                "mean_t2_rows": float(np.mean([t for _, t in tr["n_att"]])),
                 "note": "T0 u T1 u T2 attended, T2 as int8 code x float32 scale per row "
                         "(one run, attn_partial timed on every 8th step); not part of value"}
+        del tr
     if not args.no_stream_leg:
         # T1 streamed from pinned host memory every step, layer by layer through a
         # two-buffer device window (the copy of layer l + 2 overlaps the attention of
@@ -494,41 +599,64 @@ def main():
         del cache
         torch.cuda.empty_cache()
         print("[bench] streamed-T1 run", file=sys.stderr, flush=True)
-        cache = dw.make_cache(contexts=contexts)
+        cache = dw.make_cache(contexts=contexts, t0_budget=True)
         stream = T1Stream(cache, chunk_layers=args.stream_chunk)
-        for k in range(1, args.warmup + 1):
+        for k in range(1, W + 1):
             stream.step(*inputs[k - 1])
         torch.cuda.synchronize()
+        first_re = list(stream.link_reassign)
         t0 = time.perf_counter()
         link = 0
-        for k in range(args.warmup + 1, args.warmup + args.steps + 1):
-            link += stream.layer_bytes * wl.layers
+        t1_rows = []
+        for k in range(W + 1, W + K + 1):
+            t1_rows.append(sum(cache.t1_len))
             stream.step(*inputs[k - 1])
+            link += stream.link_bytes_per_step()
         torch.cuda.synchronize()
         el_s = time.perf_counter() - t0
+        re_s = None
+        if len(stream.link_reassign) == len(first_re):      # none in the timed steps
+            for k in range(W + K + 1, W + K + extra + 1):
+                stream.step(*inputs[k - 1], reassign=False)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            stream.reassign()
+            re_s = time.perf_counter() - t1
+        el_amort = el_s + (K / delta * re_s if re_s is not None else 0.0)
+        sh = cache.shape
+        row = sh.layers * sh.kv_heads * 2 * sh.head_dim * (2 if sh.dtype == "bf16" else 4)
         out["t1_streamed"] = {
-            "steps_per_s": args.steps / el_s, "ms_per_step": el_s / args.steps * 1e3,
-            "link_bytes_per_step": link / args.steps,
+            "steps_per_s": K / el_amort, "ms_per_step": el_amort / K * 1e3,
+            "link_bytes_per_step": link / K,
             "link_gbps": link / el_s / 1e9,
-            "device_window_bytes": 2 * stream.chunk * stream.layer_bytes,
+            "mean_t1_rows": float(np.mean(t1_rows)),
+            "t1_row_bytes_per_step": float(np.mean(t1_rows)) * row,
+            "link_bytes_per_reassignment": {"first": first_re[0] if first_re else None,
+                                            "later": stream.link_reassign[len(first_re):]},
+            "resident_kv_bytes": stream.resident_kv_bytes(),
+            "full_cache_kv_bytes": cache.full_cache_bytes(),
+            "resident_over_full": stream.resident_kv_bytes() / cache.full_cache_bytes(),
+            "device_window_bytes": stream.window_bytes(),
+            "t0_capacity": cache.cap0,
             "chunk_layers": stream.chunk,
-            "note": "append, then per chunk of layers: wait for its T1 rows, attention over T0 "
-                    "and the two-buffer window (tkv_decode_step_streamed); the host-to-device copy "
-                    "of chunk c + 2 starts when chunk c has read its buffer; no other T1 rows in "
-                    "HBM between reassignments; every Delta steps the pinned host copy goes to a "
-                    "transient device window for the relocation and back; not part of value"}
+            "note": "T1 rows in host memory (pinned window, full-precision store by position); "
+                    "every step: append, then per chunk of layers the live T1 blocks cross the "
+                    "link while the previous chunk attends (tkv_decode_step_streamed); every "
+                    "Delta steps only the rows that enter T1 from T0 go to the host and only the "
+                    "rows that leave T1 come back (tkv_compact_host_t1); HBM holds the T0 pool "
+                    "at its budget and a two-chunk window; not part of value"}
         del stream
     if not args.no_pcie:
         try:
             t1 = cache.t1_pos[0, :cache.t1_len[0]].cpu().numpy().tolist()   # window slot order
             out["pcie"] = pcie_leg(wl, cache, t1, 1.0 / steps_per_s)
-            out["pcie"]["note"] = ("host-link path of T1, not part of value: host pack into "
-                                   "pinned staging, then hipMemcpy2DAsync on a side stream")
+            out["pcie"]["note"] = ("a whole T1 set through tkv_gather_t1 (host pack into pinned "
+                                   "staging, one 2-D copy on a side stream); not part of value")
         except Exception as e:  # reported, never fatal for the device number
             out["pcie"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(base.scaled(steps=K, warmup=W), args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -74,7 +74,7 @@ typedef int32_t tkv_status;
 #define TKV_BF16 0
 #define TKV_F32 1
 
-#define TKV_ABI_VERSION 1
+#define TKV_ABI_VERSION 2
 
 /* Model shape.  softmax_scale <= 0 selects 1/sqrt(head_dim). */
 typedef struct {
@@ -189,24 +189,27 @@ tkv_status tkv_append_decode_step(const tkv_model* model, int32_t batch, const v
 
 /*
  * tkv_decode_step_window -- tkv_decode_step with a T1 window that holds only
- * the call's layers: k_t1_win, v_t1_win are device [B][Lr][Hkv][cap1][D] tiles
- * (Lr = layer_end - layer_begin), window layer i holding layer layer_begin + i.
- * q, out and alpha hold EVERY layer here ([B][L][Hq][D], [B][L][Hq][D],
- * [B][L][Hq][alpha_stride]); the call reads and writes the rows of its layers.
- * Methodologie section 1 brings T1 from host memory to the GPU before each
- * attention step; with this call the T1 rows can be streamed layer by layer
- * into a small double-buffered device window (copy layer l + 1 while layer l
- * attends), so HBM holds T0 plus two layers of T1 instead of every layer.
- * Other arguments, outputs, numerics and errors as for tkv_decode_step.
+ * the call's layers: t1_win is device [B][Lr][Hkv][2][cap1][D] tiles
+ * (Lr = layer_end - layer_begin), window layer i holding layer layer_begin + i,
+ * and each (sequence, layer, KV head) row holding its cap1 key slots followed
+ * by its cap1 value slots (the layout of the streamed host copy, so one 2-D copy
+ * per sequence fills a window).  q, out and alpha hold EVERY layer here
+ * ([B][L][Hq][D], [B][L][Hq][D], [B][L][Hq][alpha_stride]); the call reads and
+ * writes the rows of its layers.  Methodologie section 1 brings T1 from host
+ * memory to the GPU before each attention step; with this call the T1 rows can
+ * be streamed layer by layer into a small double-buffered device window (copy
+ * layer l + 1 while layer l attends), so HBM holds T0 plus two layers of T1
+ * instead of every layer.  Other arguments, outputs, numerics and errors as for
+ * tkv_decode_step.
  */
 tkv_status tkv_decode_step_window(const tkv_model* model, int32_t batch, int32_t layer_begin,
                                   int32_t layer_end, const void* q, const void* k_t0,
                                   const void* v_t0, const int32_t* t0_len, int32_t cap0,
-                                  const void* k_t1_win, const void* v_t1_win,
-                                  const int32_t* t1_len, int32_t cap1, float* out, float* alpha,
-                                  int32_t alpha_stride, const int32_t* t0_pos,
-                                  const int32_t* t1_pos, float* scores, int32_t max_ctx,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                  const void* t1_win, const int32_t* t1_len, int32_t cap1,
+                                  float* out, float* alpha, int32_t alpha_stride,
+                                  const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
+                                  int32_t max_ctx, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * tkv_decode_step_streamed -- the decode step over all layers with the T1 rows
@@ -214,18 +217,25 @@ tkv_status tkv_decode_step_window(const tkv_model* model, int32_t batch, int32_t
  * DDR at full precision and is brought to the GPU before each attention step).
  * The layers run in chunks of chunk_layers; the host-to-device copy of chunk
  * c + 2 goes on side_stream as soon as chunk c has read its buffer of the
- * two-buffer device window, so copies overlap attention.  Each chunk is one
- * tkv_decode_step_window call on `stream` (fused score update included).
+ * two-buffer device window, so copies overlap attention.  Only the 32-slot
+ * blocks that hold live T1 rows cross the link: per chunk, one 2-D copy per
+ * sequence of ceil32(t1_len[b]) slots of each of its chunk_layers * Hkv * 2 rows.
+ * The score update runs once, after the last chunk, over the group sums of
+ * every layer (the same summation as a single tkv_decode_step over all layers),
+ * so each score takes one float32 rounding per step.
  *
- * host_t1  : pinned host [2][B][L][Hkv][cap1][D] tiles: keys, then values, of
- *            the T1 rows in the window-slot order of t1_pos
- * win      : device [2][2][B][chunk_layers][Hkv][cap1][D] tiles (two buffers of
- *            keys then values); a chunk is one 2-D copy of 2 * B rows
- * side_stream2         : optional (may be null) second copy stream: chunks then
- *                        alternate between the two, so the next copy is queued
- *                        when the running one ends (shorter idle gaps on the link)
- * events               : four caller-owned events (two "copied", two "read");
- *                        their previous contents are overwritten
+ * host_t1  : pinned host [B][L][Hkv][2][cap1][D] tiles: per (sequence, layer,
+ *            KV head), the keys then the values of the T1 rows in the
+ *            window-slot order of t1_pos
+ * win      : device [2][B][chunk_layers][Hkv][2][cap1][D] tiles (two buffers)
+ * side_stream2 : optional (may be null) second copy stream: chunks then
+ *                alternate between the two, so the next copy is queued when the
+ *                running one ends (shorter idle gaps on the link)
+ * events   : four caller-owned events (two "copied", two "read"); their
+ *            previous contents are overwritten
+ * link_bytes : optional host out: bytes queued host -> device by this call
+ * workspace: tkv_decode_workspace_bytes(model, batch, L, cap0, cap1) bytes
+ * batch    : at most 64 (TKV_ERR_CAPACITY above)
  * q, out, alpha and the rest as for tkv_decode_step over layers [0, L).
  * Every argument is checked before anything is queued.
  */
@@ -233,12 +243,11 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
                                     const void* k_t0, const void* v_t0, const int32_t* t0_len,
                                     int32_t cap0, const void* host_t1, const int32_t* t1_len,
                                     int32_t cap1, void* win, int32_t chunk_layers, float* out,
-                                    float* alpha,
-                                    int32_t alpha_stride, const int32_t* t0_pos,
+                                    float* alpha, int32_t alpha_stride, const int32_t* t0_pos,
                                     const int32_t* t1_pos, float* scores, int32_t max_ctx,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
                                     hipStream_t side_stream, hipStream_t side_stream2,
-                                    hipEvent_t* events);
+                                    hipEvent_t* events, int64_t* link_bytes);
 
 /*
  * Attended T2 pool (optional variant of the decode step).  Methodologie
@@ -399,6 +408,72 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * tkv_t0_capacity -- a T0 pool capacity that no reassignment at a length in
+ * [n_from, n_to] can exceed, Delta appended rows included (Methodologie sections
+ * 1 and 4: T0 keeps the protected rows and the most important rest; the tier
+ * budgets are fractions of the current length).  After a reassignment at length
+ * n, T0 holds at most max(N0(n), |protected(n)|) rows, N0(n) = n - N1 - N2 - N3;
+ * the result is that bound's maximum over [n_from, n_to] plus delta, rounded up
+ * to a multiple of 32.  A caller can shrink its T0 pool to it after the first
+ * reassignment.  Returns -1 on a bad policy or range.
+ */
+int32_t tkv_t0_capacity(const tkv_policy* policy, int32_t n_from, int32_t n_to);
+
+/* Bytes of device workspace and of pinned host scratch tkv_compact_host_t1
+ * needs (0 for an invalid model or a negative size).  The device workspace is
+ * tkv_compact's without its row staging: the rows that cross the link are staged
+ * in the host scratch. */
+size_t tkv_compact_host_t1_workspace_bytes(const tkv_model* model, int32_t batch, int32_t max_ctx,
+                                           int32_t cap0, int32_t cap1);
+size_t tkv_compact_host_t1_scratch_bytes(const tkv_model* model, int32_t batch, int32_t max_ctx,
+                                         int32_t cap1);
+
+/*
+ * tkv_compact_host_t1 -- tkv_compact for T1 rows that live in host memory
+ * (Methodologie section 1: T1 in host DDR at full precision; section 4: at a
+ * reassignment only the tokens whose tier changed move, and only newly
+ * promoted tokens go from host memory to the GPU).  The device holds the T0
+ * pool and the T1 slot -> position map; the host holds a store of full-precision
+ * rows by position and the streamed T1 window in window-slot order.  Only these
+ * rows cross the host link:
+ *   device -> host : rows that enter T1 from T0 (into the store);
+ *   host -> device : rows that leave T1 for T0 (promoted) or for T2 (to be
+ *                    quantised on the device);
+ * plus the tier and slot maps the host reads (2 max_ctx + 16 cap1 + 32 bytes per
+ * sequence: both tier maps, the T1 slot map before and after, the list of rows
+ * entering T1, the new lengths and list counts).  Rows that stay in T1 never move; the window slots whose
+ * position changed are rewritten on the host from the store.  Results are those
+ * of tkv_compact on the same state (same holes, same slot maps, same int8 rows).
+ * The call is host-synchronous: it returns when every queued operation is done.
+ *
+ * Arguments as for tkv_compact, without the device T1 window, and:
+ * workspace        : device, tkv_compact_host_t1_workspace_bytes() bytes
+ * store_k, store_v : host [B][L][Hkv][max_ctx][D] full-precision rows by
+ *                    position (read and written by host threads)
+ * t1_host          : pinned host [B][L][Hkv][2][cap1][D] tiles: the window that
+ *                    tkv_decode_step_streamed streams, updated in place
+ * new_lens_host    : host [B][4], a copy of new_lens
+ * host_scratch     : pinned, device-mapped host memory of
+ *                    tkv_compact_host_t1_scratch_bytes() bytes; the device reads
+ *                    and writes its row staging directly (TKV_ERR_HIP if the
+ *                    memory is not device-mapped)
+ * link_bytes       : optional host out: bytes that crossed the link
+ * A sequence whose maps disagree with tier_prev gets new_lens {-1,-1,-1,-1} as
+ * with tkv_compact; its T1 window is then left as it was.
+ */
+tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
+                               int32_t max_ctx, const uint8_t* tier_prev,
+                               const uint8_t* tier_next, void* k_t0, void* v_t0,
+                               int32_t* t0_pos, const int32_t* t0_len, int32_t cap0,
+                               int32_t* t1_pos, const int32_t* t1_len, int32_t cap1,
+                               void* store_k, void* store_v, void* t1_host, int32_t* t2_src,
+                               int32_t* t2_pos, int32_t t2_cap, int8_t* t2_codes,
+                               float* t2_scales, int32_t* new_lens, int32_t* new_lens_host,
+                               void* workspace, size_t workspace_bytes, void* host_scratch,
+                               size_t host_scratch_bytes, int64_t* link_bytes,
+                               hipStream_t stream);
+
+/*
  * tkv_quantize_t2 -- 8-bit rows of the tokens that enter T2 (Methodologie
  * section 1, T2 holds low-importance tokens at reduced precision, 8-bit
  * quantisation being the example).  Per (row, layer, KV head, K or V) row of D
@@ -465,28 +540,31 @@ tkv_status tkv_t2_update(const tkv_model* model, int32_t batch, const int32_t* c
  * tkv_gather_t1 -- bring one sequence's T1 rows to the GPU (Methodologie
  * section 1: T1 stays in host DDR at full precision and is brought to the GPU
  * before each attention step).  Packs the rows of the host store at the given
- * positions, in the given order, into contiguous pinned staging
- * with host threads, then queues the host-to-device copy of the staging on
- * side_stream and records `ready` there.  The attention stream must wait on
- * `ready` before reading the window.
+ * positions, in the given order, into contiguous pinned staging with host
+ * threads, then queues the host-to-device copy of the staging on side_stream
+ * and records `ready` there.  The attention stream must wait on `ready` before
+ * reading the window.
  *
- * host_k, host_v   : host [L][Hkv][max_ctx][D] full-precision store
- * positions        : host [n_t1], distinct, each < max_ctx: window slot i
- *                    receives positions[i] (pass the window's slot ->
- *                    position map); null re-sends the staging as it is
- *                    (no pack)
- * staging_k/v      : pinned host [L][Hkv][cap1][D] tiles (n_t1 <= cap1), written in
- *                    the device window's storage order (value slots past n_t1
- *                    in the last panel are zeroed), so the copy is a plain
- *                    strided transfer of whole 32-slot blocks
- * dev_k_t1/dev_v_t1: device window [L][Hkv][cap1][D] tiles; null packs only
- * ready            : event recorded on side_stream after the copies; may be null
- * The pack is synchronous on the calling thread; only the copies are queued.
+ * host_k, host_v : host [L][Hkv][max_ctx][D] full-precision store
+ * positions      : host [n_t1], distinct, each < max_ctx: window slot i
+ *                  receives positions[i] (pass the window's slot -> position
+ *                  map); null re-sends the staging as it is (no pack)
+ * staging        : pinned host [L][Hkv][2][cap1][D] tiles (n_t1 <= cap1): per
+ *                  (layer, KV head) the key slots, then the value slots, in the
+ *                  device window's storage order (slots past n_t1 in the last
+ *                  32-slot block are zeroed)
+ * dev_t1         : device window of the same layout ([L][Hkv][2][cap1][D], the
+ *                  layout of tkv_decode_step_window); null packs only.  Only the
+ *                  ceil32(n_t1) leading slots of each row are copied.
+ * ready          : event recorded on side_stream after the copy; may be null
+ * Before packing, a call with dev_t1 waits for the work already queued on
+ * side_stream (an earlier copy may still be reading the staging); a pack-only
+ * call (dev_t1 null) leaves that ordering to its caller.  The pack is
+ * synchronous on the calling thread; only the copy is queued.
  */
 tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k, const void* host_v,
-                         int32_t max_ctx, const int32_t* positions, int32_t n_t1,
-                         void* staging_k, void* staging_v, int32_t cap1, void* dev_k_t1,
-                         void* dev_v_t1, hipStream_t side_stream, hipEvent_t ready);
+                         int32_t max_ctx, const int32_t* positions, int32_t n_t1, void* staging,
+                         int32_t cap1, void* dev_t1, hipStream_t side_stream, hipEvent_t ready);
 
 /*
  * Kernel timers for benchmarks.  While enabled, every kernel the library

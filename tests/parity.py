@@ -123,19 +123,54 @@ def step_inputs(cache, dw, q, kn, vn, fused_append: bool) -> None:
         cache.attend(qd)
 
 
+def streamed_step_link(cache) -> int:
+    """Bytes a streamed step must send: the live 32-slot blocks of every sequence's T1
+    rows, keys and values of every (layer, KV head)."""
+    sh = cache.shape
+    e = 2 if sh.dtype == "bf16" else 4
+    return sum(-(-n // 32) * 32 for n in cache.t1_len) * sh.head_dim * e * sh.layers * sh.kv_heads * 2
+
+
+def reassign_link_rows(prev_tiers, new_tiers) -> int:
+    """Rows a reassignment with host-resident T1 must move over the link: those that
+    enter T1 from T0 (device -> host) and those that leave T1 for T0 or T2 (host ->
+    device).  Rows that stay, and every other transition, move no row."""
+    rows = 0
+    for p, w in zip(prev_tiers, new_tiers):
+        rows += int(((p == 0) & (w == 1)).sum() + ((p == 1) & ((w == 0) | (w == 2))).sum())
+    return rows
+
+
+def check_reassign_link(streamer, prevs, news, stats):
+    """The link bytes of the last reassignment: the rows that changed side, plus the tier
+    maps and T1 slot maps the host reads (2 max_ctx + 16 cap1 + 32 bytes per sequence)."""
+    c = streamer.cache
+    sh = c.shape
+    e = 2 if sh.dtype == "bf16" else 4
+    row = sh.layers * sh.kv_heads * 2 * sh.head_dim * e
+    maps = c.batch * (2 * c.max_ctx + 16 * c.cap1 + 32)
+    rows = reassign_link_rows(prevs, news)
+    got = streamer.link_reassign[-1]
+    assert got == rows * row + maps, f"reassignment link bytes {got} != {rows} rows + maps"
+    stats["link_rows"] += rows
+
+
 def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
                  fused_scores: bool = True, fused_append: bool = True,
-                 attend_t2: bool = False, t1_streamed: int = 0) -> dict:
+                 attend_t2: bool = False, t1_streamed: int = 0, t0_budget: bool = False) -> dict:
     """Every step compared; re-sync of the ranking at each reassignment.
     fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores;
     fused_append=False appends with tkv_append before tkv_decode_step instead of
     tkv_append_decode_step; attend_t2 attends the 8-bit T2 rows after T1 on both sides
-    (the _t2 entry points and the oracle's attend_t2 mode); t1_streamed > 0 attends chunks
-    of that many layers with the T1 rows streamed from pinned host memory (T1Stream)."""
+    (the _t2 entry points and the oracle's attend_t2 mode); t1_streamed > 0 keeps the T1
+    rows in host memory and attends chunks of that many layers with them streamed from
+    pinned memory (T1Stream), checking the link bytes of every step and reassignment;
+    t0_budget shrinks the T0 pool to its budget after the first reassignment."""
     n_steps = n_steps or wl.total_steps
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache(attend_t2=attend_t2)
+    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget)
     cache.fused_scores = fused_scores
+    cap0_start = cache.cap0
     streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
     pol = oracle_policy(wl)
     seqs = []
@@ -148,6 +183,7 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
         if streamer is not None:
             streamer.step(to_device(q, dw.dtype, dw.device), to_device(kn, dw.dtype, dw.device),
                           to_device(vn, dw.dtype, dw.device), reassign=False)
+            assert streamer.link_step == streamed_step_link(cache), f"step link bytes, step {k}"
         else:
             step_inputs(cache, dw, q, kn, vn, fused_append)
             cache.steps += 1
@@ -170,6 +206,12 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
             for b, seq in enumerate(seqs):
                 seq.reassign(scores=gpu_scores[b])
                 check_reassignment(cache, b, seq, prevs[b], gpu_scores[b], stats, streamer)
+            if streamer is not None:
+                check_reassign_link(streamer, [p[:s.n] for p, s in zip(prevs, seqs)],
+                                    [s.tier[:s.n] for s in seqs], stats)
+            if t0_budget and cache.reassignments == 1:
+                assert cache.cap0 <= cap0_start
+                stats["cap0"] = cache.cap0
     stats["steps"] = n_steps
     say(f"[{label or wl.name}] lockstep ok: " +
         ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))
@@ -199,7 +241,7 @@ class HostStore:
 
 def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=(),
                 label: str = "", byte_seqs=None, attend_t2: bool = False,
-                t1_streamed: int = 0) -> dict:
+                t1_streamed: int = 0, t0_budget: bool = False) -> dict:
     """Full-size run, checked on samples the oracle computes one at a time:
     * O and alpha of the sampled (layer, head) pairs over the GPU's attended set;
     * the whole score increment at `full_inc_steps` (all layers and heads);
@@ -209,12 +251,14 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
       new T2 positions of the sequences in `byte_seqs` (default: all);
     * with attend_t2, the attended T2 rows enter the oracle as code x scale of the int8
       rows of the full-precision store (bit-exact codes, as the quantizer is), and the T2
-      pool's positions are checked at every reassignment; with t1_streamed > 0 the steps
-      run through T1Stream with chunks of that many layers.
+      pool's positions are checked at every reassignment; with t1_streamed > 0 the T1
+      rows live in host memory and the steps run through T1Stream with chunks of that
+      many layers (link bytes of every step and reassignment checked); t0_budget shrinks
+      the T0 pool after the first reassignment.
     """
     byte_seqs = set(range(wl.batch)) if byte_seqs is None else set(byte_seqs)
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache(attend_t2=attend_t2)
+    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget)
     streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
     store = HostStore(dw, cache.max_ctx)
     pol = oracle_policy(wl)
@@ -229,6 +273,7 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
         if streamer is not None:
             streamer.step(to_device(q, dw.dtype, dw.device), to_device(kn, dw.dtype, dw.device),
                           to_device(vn, dw.dtype, dw.device), reassign=False)
+            assert streamer.link_step == streamed_step_link(cache), f"step link bytes, step {k}"
         else:
             step_inputs(cache, dw, q, kn, vn, True)
             cache.steps += 1
@@ -261,11 +306,9 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                     inc /= (wl.layers * wl.q_heads)
                     got = cache.scores[b, :cache.n[b]].cpu().numpy().astype(np.float64) - s_before[b, :cache.n[b]]
                     err = np.abs(got - inc)
-                    # the difference of two float32 sums carries their rounding (~1 ulp of s);
-                    # a streamed step adds each chunk's share of the layer sum separately,
-                    # one float32 rounding of s per chunk
-                    adds = -(-wl.layers // t1_streamed) if t1_streamed else 1
-                    lim = 1e-5 * inc + 2.0 ** -24 * (adds + 3) * np.abs(s_before[b, :cache.n[b]]) + 1e-12
+                    # the difference of two float32 values carries their rounding (a few
+                    # ulp of s); every path adds the step's increment to s once
+                    lim = 1e-5 * inc + 2.0 ** -24 * 4 * np.abs(s_before[b, :cache.n[b]]) + 1e-12
                     assert (err <= lim).all(), f"score increment, step {k}, seq {b}: max {err.max():.3e}"
                     stats["inc_checked"] += 1
         if k % wl.delta == 0:
@@ -280,6 +323,10 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
             else:
                 cache.reassign()
             torch.cuda.synchronize()
+            if streamer is not None:
+                news = [cache.tiers[b, :cache.n[b]].cpu().numpy() for b in range(wl.batch)]
+                check_reassign_link(streamer, [prev[b, :cache.n[b]] for b in range(wl.batch)],
+                                    news, stats)
             for b in range(wl.batch):
                 n = cache.n[b]
                 t_ref, counts = assign_tiers(gpu_scores[b, :n].astype(np.float64), prev[b, :n], n, pol)

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(tkv.EXPORTED)
-    assert tkv.tkv_abi_version() == 1
+    assert tkv.tkv_abi_version() == 2
 
 
 def model(**kw):
@@ -200,10 +200,12 @@ def test_decode_step_t2_validation():
 def test_window_and_streamed_validation():
     m = model()
     wargs = dict(batch=1, layer_begin=1, layer_end=2, q=FAKE, k_t0=FAKE, v_t0=FAKE, t0_len=[10],
-                 cap0=32, k_t1_win=FAKE, v_t1_win=FAKE, t1_len=[2], cap1=32, out=FAKE,
+                 cap0=32, t1_win=FAKE, t1_len=[2], cap1=32, out=FAKE,
                  alpha=FAKE, alpha_stride=24, t0_pos=FAKE, t1_pos=FAKE, scores=FAKE, max_ctx=64,
                  workspace=FAKE, workspace_bytes=1 << 30, stream=0)
-    assert status_of(tkv.tkv_decode_step_window, m, **{**wargs, "k_t1_win": NULL}) == \
+    assert status_of(tkv.tkv_decode_step_window, m, **{**wargs, "t1_win": NULL}) == \
+        tkv.TKV_ERR_ARG
+    assert status_of(tkv.tkv_decode_step_window, m, **{**wargs, "cap1": 48}) == \
         tkv.TKV_ERR_ARG
     assert status_of(tkv.tkv_decode_step_window, m, **{**wargs, "layer_end": 3}) == \
         tkv.TKV_ERR_ARG
@@ -226,6 +228,68 @@ def test_window_and_streamed_validation():
     assert status_of(st, m, **{**sargs, "t0_len": [33]}) == tkv.TKV_ERR_CAPACITY
     assert status_of(st, m, **{**sargs, "alpha_stride": 8}) == tkv.TKV_ERR_CAPACITY
     assert status_of(st, m, **{**sargs, "workspace_bytes": 16}) == tkv.TKV_ERR_CAPACITY
+    # the score update covers every layer after the last chunk: its group sums need the
+    # workspace of a whole-step call
+    ws_chunk = tkv.tkv_decode_workspace_bytes(m, 1, 1, 32, 32)
+    assert ws_chunk < tkv.tkv_decode_workspace_bytes(m, 1, 2, 32, 32)
+    assert status_of(st, m, **{**sargs, "workspace_bytes": ws_chunk}) == tkv.TKV_ERR_CAPACITY
+    big = {**sargs, "batch": 65, "t0_len": [10] * 65, "t1_len": [2] * 65}
+    assert status_of(st, m, **big) == tkv.TKV_ERR_CAPACITY                         # > 64
+
+
+def test_t0_capacity_bounds_the_oracle_assignment():
+    # after any reassignment the T0 count stays within tkv_t0_capacity - delta, whatever
+    # the scores and the tier history (T2/T3 absorbing), including policies whose
+    # protected set exceeds the T0 budget
+    from oracle import Policy, assign_tiers
+    r = np.random.default_rng(5)
+    for case in range(300):
+        n = int(r.integers(1, 400))
+        pol = Policy(int(r.integers(0, 40)), int(r.integers(0, 8)), int(r.integers(0, 40)),
+                     *r.dirichlet([1, 1, 1, 1])[1:].astype(np.float32).tolist(),
+                     int(r.integers(1, 9)))
+        if sum(np.float32(f) for f in (pol.frac_t1, pol.frac_t2, pol.frac_t3)) > 1:
+            continue
+        prev = r.choice(4, size=n, p=[0.5, 0.2, 0.2, 0.1]).astype(np.uint8) if case % 2 else \
+            np.zeros(n, np.uint8)
+        scores = r.choice([0.0, 0.5, 1.0], size=n) if case % 3 == 0 else r.random(n)
+        tier, counts = assign_tiers(scores, prev, n, pol)
+        tp = tkv.make_policy(pol.prompt, pol.sinks, pol.recent, pol.frac_t1, pol.frac_t2,
+                             pol.frac_t3, pol.delta)
+        cap = tkv.tkv_t0_capacity(tp, n, n)
+        assert cap % 32 == 0 and counts[0] + pol.delta <= cap, (case, counts, cap)
+        assert tkv.tkv_t0_capacity(tp, max(0, n - 5), n + 5) >= cap      # a range: the maximum
+    # the 7B-class chain after its first reassignment: N0 = n - N1 - N2 - N3 bounds T0
+    tp = tkv.make_policy(256, 4, 128, 0.3, 0.15, 0.05, 64)
+    n0 = [n - int(np.floor(np.float64(np.float32(0.3)) * n)) - int(np.floor(np.float64(np.float32(0.15)) * n))
+          - int(np.floor(np.float64(np.float32(0.05)) * n)) for n in range(8256, 8513)]
+    assert tkv.tkv_t0_capacity(tp, 8256, 8512) == -(-(max(n0) + 64) // 32) * 32
+    assert tkv.lib().tkv_t0_capacity(ctypes.byref(tp), 10, 5) == -1
+
+
+def test_compact_host_t1_validation():
+    m = model()
+    ws = tkv.tkv_compact_host_t1_workspace_bytes(m, 1, 64, 32, 32)
+    assert 0 < ws < tkv.tkv_compact_workspace_bytes(m, 1, 64, 32, 32)   # no device row staging
+    hs = tkv.tkv_compact_host_t1_scratch_bytes(m, 1, 64, 32)
+    # the row staging of the host scratch holds cap1 rows of every (layer, KV head)
+    assert hs >= 32 * 2 * 2 * 2 * 128 * 2
+    args = dict(model=m, batch=1, ctx_len=[60], max_ctx=64, tier_prev=FAKE, tier_next=FAKE + 64,
+                k_t0=FAKE, v_t0=FAKE, t0_pos=FAKE, t0_len=[40], cap0=64, t1_pos=FAKE,
+                t1_len=[10], cap1=32, store_k=FAKE, store_v=FAKE, t1_host=FAKE, t2_src=FAKE,
+                t2_pos=FAKE, t2_cap=16, t2_codes=FAKE, t2_scales=FAKE, new_lens=FAKE,
+                workspace=FAKE, workspace_bytes=ws, host_scratch=FAKE, host_scratch_bytes=hs,
+                stream=0)
+    call = tkv.tkv_compact_host_t1
+    assert status_of(call, **{**args, "store_k": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(call, **{**args, "t1_host": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(call, **{**args, "host_scratch": NULL}) == tkv.TKV_ERR_ARG
+    assert status_of(call, **{**args, "tier_next": FAKE}) == tkv.TKV_ERR_ARG     # distinct maps
+    assert status_of(call, **{**args, "cap1": 40}) == tkv.TKV_ERR_ARG
+    assert status_of(call, **{**args, "t1_len": [33]}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(call, **{**args, "t0_len": [55]}) == tkv.TKV_ERR_STATE      # > ctx_len
+    assert status_of(call, **{**args, "workspace_bytes": ws - 1}) == tkv.TKV_ERR_CAPACITY
+    assert status_of(call, **{**args, "host_scratch_bytes": hs - 1}) == tkv.TKV_ERR_CAPACITY
 
 
 def test_t2_update_validation():
@@ -261,33 +325,34 @@ def test_append_validation():
 
 def test_gather_host_pack_without_device():
     # position checks (repeats, range, capacity), then a pack-only call (no device
-    # pointers -> no HIP call) with positions in window-slot order, not sorted
+    # pointer -> no HIP call) with positions in window-slot order, not sorted
     m = model(layers=2, kv_heads=2, q_heads=2, head_dim=64)
     r = np.random.default_rng(0)
     max_ctx, cap1 = 40, 32
     hk = r.integers(0, 65535, size=(2, 2, max_ctx, 64)).astype(np.uint16)
     hv = r.integers(0, 65535, size=(2, 2, max_ctx, 64)).astype(np.uint16)
-    sk = np.zeros((2, 2, cap1, 64), np.uint16)
-    sv = np.zeros((2, 2, cap1, 64), np.uint16)
-    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 2, 3], 3, sk, sv, cap1) == \
+    stg = np.zeros((2, 2, 2, cap1, 64), np.uint16)        # per row: key slots, value slots
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 2, 3], 3, stg, cap1) == \
         tkv.TKV_ERR_ARG
-    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 40], 2, sk, sv, cap1) == \
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, [3, 40], 2, stg, cap1) == \
         tkv.TKV_ERR_ARG
-    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, list(range(33)), 33, sk, sv, cap1) == \
+    assert status_of(tkv.tkv_gather_t1, m, hk, hv, max_ctx, list(range(33)), 33, stg, cap1) == \
         tkv.TKV_ERR_CAPACITY
     pos = [17, 5, 39, 1, 6]
-    tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), sk, sv, cap1)
+    tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), stg, cap1)
+    sk = stg[:, :, 0].reshape(2, 2, -1)
+    sv = stg[:, :, 1].reshape(2, 2, -1)
     # storage order of 32-slot blocks: K-tiles and V-tiles (element-wise definition)
     for r in range(len(pos)):
         for d in range(64):
             jj, u, i = (r % 32) // 8, (r % 32) // 4 % 2, r % 4
             ko = (r // 32) * 32 * 64 + u * 16 * 64 + ((d // 8) * 16 + 4 * jj + i) * 8 + d % 8
             vo = (r // 32) * 32 * 64 + ((d // 16) * 4 + (r % 32) // 8) * 128 + (d % 16) * 8 + r % 8
-            assert sk.reshape(2, 2, -1)[:, :, ko].tolist() == hk[:, :, pos[r], d].tolist()
-            assert sv.reshape(2, 2, -1)[:, :, vo].tolist() == hv[:, :, pos[r], d].tolist()
+            assert sk[:, :, ko].tolist() == hk[:, :, pos[r], d].tolist()
+            assert sv[:, :, vo].tolist() == hv[:, :, pos[r], d].tolist()
     for r in range(len(pos), 8):                 # the rest of the last value panel is cleared
         vo = [((d // 16) * 4 + r // 8) * 128 + (d % 16) * 8 + r % 8 for d in range(64)]
-        assert not sv.reshape(2, 2, -1)[:, :, vo].any()
+        assert not sv[:, :, vo].any()
 
 
 def test_gather_host_pack_blocks_d128():
@@ -298,10 +363,9 @@ def test_gather_host_pack_blocks_d128():
     max_ctx, cap1, D = 300, 96, 128
     hk = r.integers(0, 65535, size=(3, 2, max_ctx, D)).astype(np.uint16)
     hv = r.integers(0, 65535, size=(3, 2, max_ctx, D)).astype(np.uint16)
-    sk = np.full((3, 2, cap1, D), 7, np.uint16)
-    sv = np.full((3, 2, cap1, D), 7, np.uint16)
+    stg = np.full((3, 2, 2, cap1, D), 7, np.uint16)
     pos = sorted(r.choice(max_ctx, 77, replace=False).tolist())
-    tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), sk, sv, cap1)
+    tkv.tkv_gather_t1(m, hk, hv, max_ctx, pos, len(pos), stg, cap1)
     n = len(pos)
     slots = np.arange(96)[:, None]
     d = np.arange(D)[None, :]
@@ -312,7 +376,7 @@ def test_gather_host_pack_blocks_d128():
     exp_v = np.zeros((3, 2, 96, D), np.uint16)
     exp_k[:, :, :n] = hk[:, :, pos]
     exp_v[:, :, :n] = hv[:, :, pos]
-    got_k = sk.reshape(3, 2, -1)[:, :, ko]
-    got_v = sv.reshape(3, 2, -1)[:, :, vo]
-    assert np.array_equal(got_k, exp_k)
+    got_k = stg[:, :, 0].reshape(3, 2, -1)[:, :, ko]
+    got_v = stg[:, :, 1].reshape(3, 2, -1)[:, :, vo]
+    assert np.array_equal(got_k, exp_k)          # slots past n of the last block cleared
     assert np.array_equal(got_v, exp_v)

@@ -127,11 +127,20 @@ def test_empty_sequence_in_batch():
     say(f"[empty sequence] ok: " + ", ".join(f"{k}={v:.3g}" for k, v in sorted(stats.items())))
 
 
+def test_small_t0_budget_lockstep():
+    # the T0 pool moved into one sized by the tier budget after the first reassignment:
+    # the same results, step by step
+    wl = WORKLOADS["small"]
+    st = run_lockstep(wl, t0_budget=True, label="small_t0_budget")
+    assert st["reassignments"] == 3 and st["cap0"] < 2048
+
+
 def test_chain8k_full_size_sampled():
+    # the bench's configuration: the T0 pool at its budget after the first reassignment
     wl = WORKLOADS["chain8k"]
     heads = [(0, 0), (0, 6), (13, 20), (27, 27)]
     st = run_sampled(wl, n_steps=130, sample_steps={1, 63, 64, 65, 100, 128, 129},
-                     heads=heads, full_inc_steps={2, 66})
+                     heads=heads, full_inc_steps={2, 66}, t0_budget=True)
     assert st["reassignments"] == 2
 
 

@@ -209,11 +209,32 @@ def test_chain8k_attend_t2_full_size_sampled():
 
 
 def test_chain8k_t1_streamed_full_size_sampled():
+    # T1 in host memory, the T0 pool shrunk to its budget after the first reassignment:
+    # the HBM of this mode holds the T0 pool and a two-layer window only
     wl = WORKLOADS["chain8k"]
     heads = [(0, 0), (13, 20), (27, 27)]
     st = run_sampled(wl, n_steps=130, sample_steps={1, 65, 100, 129}, heads=heads,
-                     full_inc_steps={66}, t1_streamed=1, label="chain8k_t1_streamed")
-    assert st["reassignments"] == 2
+                     full_inc_steps={66}, t1_streamed=1, t0_budget=True,
+                     label="chain8k_t1_streamed")
+    assert st["reassignments"] == 2 and st["link_rows"] > 0
+
+
+def test_chain32k_t1_streamed_full_size_sampled():
+    # 4 sequences of 32768 tokens with T1 (50% of the context) in host memory, streamed
+    # every step in two-layer chunks
+    wl = WORKLOADS["chain32k"]
+    heads = [(0, 3), (31, 31)]
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={65, 128}, heads=heads,
+                     full_inc_steps={66}, byte_seqs={2}, t1_streamed=2, t0_budget=True,
+                     label="chain32k_t1_streamed")
+    assert st["reassignments"] == 2 * 4
+
+
+def test_small_t1_streamed_t0_budget_lockstep():
+    # host-resident T1 with the T0 pool moved to its budget after the first reassignment
+    wl = WORKLOADS["small"]
+    st = run_lockstep(wl, t1_streamed=2, t0_budget=True, label="small_t1_streamed_budget")
+    assert st["reassignments"] == 3 and st["cap0"] < 2048
 
 
 def test_decode_step_window_matches_layer_subset_call():
@@ -240,12 +261,12 @@ def test_decode_step_window_matches_layer_subset_call():
     torch.cuda.synchronize()
     s_subset = cache.scores.clone()
     cache.scores.copy_(s0)
-    win_k = cache.k_t1[:, lb:le].contiguous()
-    win_v = cache.v_t1[:, lb:le].contiguous()
+    # the window layout: per (sequence, layer, KV head) the key slots, then the value slots
+    win = torch.stack([cache.k_t1[:, lb:le], cache.v_t1[:, lb:le]], dim=3).contiguous()
     out_w = torch.full((B, L, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     alpha_w = torch.zeros((B, L, Hq, cache.alpha_stride), dtype=torch.float32, device="cuda")
     tkv.tkv_decode_step_window(cache.model, B, lb, le, qd, cache.k_t0, cache.v_t0, cache.t0_len,
-                               cache.cap0, win_k, win_v, cache.t1_len, cache.cap1, out_w,
+                               cache.cap0, win, cache.t1_len, cache.cap1, out_w,
                                alpha_w, cache.alpha_stride, cache.t0_pos, cache.t1_pos,
                                cache.scores, cache.max_ctx, cache.ws, cache.ws_bytes)
     torch.cuda.synchronize()

@@ -257,6 +257,14 @@ struct AppendInfo {
   uint8_t* tier;
 };
 
+// The per-slot group sums of a call that covers only some layers of a step,
+// written into a region that covers every layer; the score launch is left to the
+// caller, which adds the whole step's increment once (tkv_decode_step_streamed).
+struct DeferredScore {
+  float* gsum;      // [nb][L * Hkv][gs_stride]
+  int row0;         // first (layer, KV head) row of the call
+};
+
 // tkv_decode_step; with `app`, t0_len are the lengths before the append and the
 // attention kernel performs the append (bf16; the float32 path appends first);
 // with `t2`, the 8-bit T2 rows are attended after T1.
@@ -269,9 +277,11 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
                               int32_t max_ctx, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, const AppendInfo* app,
                               const tkv_t2_pool* t2, bool t1_window = false,
-                              bool validate_only = false) {
+                              bool validate_only = false, long t1_rs = 0,
+                              const DeferredScore* deferred = nullptr) {
   // t1_window: the T1 window holds only the call's layers, and q / out / alpha hold
-  // every layer (the call reads and writes the rows of its own layers)
+  // every layer (the call reads and writes the rows of its own layers); t1_rs: the
+  // elements between consecutive rows of the window (0: cap1 * head_dim)
   tkv_status st = check_model(model);
   if (st) return st;
   if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
@@ -323,8 +333,10 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     return fail(TKV_ERR_ARG,
                 "alpha_stride must be a multiple of 4, alpha 16-byte and workspace 256-byte aligned");
   const int Lr = layer_end - layer_begin;
-  // the group sums cover every attended slot: T2 slots follow T1
-  if (workspace_bytes < tkv_decode_workspace_bytes(model, batch, Lr, cap0, cap1 + cap2))
+  // the group sums cover every attended slot: T2 slots follow T1 (a deferred score
+  // keeps the group sums of every layer)
+  if (workspace_bytes < tkv_decode_workspace_bytes(model, batch, deferred ? model->num_layers : Lr,
+                                                   cap0, cap1 + cap2))
     return fail(TKV_ERR_CAPACITY, "workspace too small");
   if (validate_only) return TKV_OK;
 
@@ -346,7 +358,8 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
   }
   const int32_t* att_len = app ? len_after.data() : t0_len;  // attended T0 rows
   const int unit = mfma ? kUnitMfma : kUnitValu;
-  const DecodeWorkspace wl = decode_workspace(model, batch, Lr, cap0, cap1 + cap2);
+  const DecodeWorkspace wl =
+      decode_workspace(model, batch, deferred ? model->num_layers : Lr, cap0, cap1 + cap2);
   float* part = (float*)workspace + wl.part;
   float* ml = (float*)workspace + wl.ml;
   float* gsum = (float*)workspace + wl.gsum;
@@ -391,6 +404,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     a.hkv = hkv;
     a.t1_L = t1_window ? Lr : model->num_layers;
     a.t1_l0 = t1_window ? 0 : layer_begin;
+    a.t1_rs = t1_rs > 0 ? t1_rs : (long)cap1 * D;
     a.io_L = t1_window ? model->num_layers : Lr;
     a.io_l0 = t1_window ? layer_begin : 0;
     // logits are kept in base 2: q.k * softmax_scale * log2(e)
@@ -447,9 +461,11 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     m.ml = ml;
     m.out = out;
     m.alpha = alpha;
-    m.gsum = scores ? gsum : nullptr;
+    m.gsum = deferred ? deferred->gsum : (scores ? gsum : nullptr);
     m.alpha_stride = alpha_stride;
     m.gs_stride = (long)wl.gs_stride;
+    m.gs_seq_rows = (long)(deferred ? model->num_layers : Lr) * hkv;
+    m.gs_row0 = deferred ? deferred->row0 : 0;
     m.total_units = a.total_units;
     m.workers = a.workers > 0 ? a.workers : 1;
     m.Lr = Lr;
@@ -464,7 +480,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     launch_attn_merge(m, D, m.out_blocks + cblocks, stream);
     if ((st = hip_check(hipGetLastError(), "attn_merge launch"))) return st;
 
-    if (scores && sblocks > 0) {
+    if (scores && sblocks > 0 && !deferred) {
       sa.src = gsum;
       sa.row_stride = (long)wl.gs_stride;
       sa.seq_stride = (long)Lr * hkv * (long)wl.gs_stride;
@@ -507,56 +523,74 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
 tkv_status tkv_decode_step_window(const tkv_model* model, int32_t batch, int32_t layer_begin,
                                   int32_t layer_end, const void* q, const void* k_t0,
                                   const void* v_t0, const int32_t* t0_len, int32_t cap0,
-                                  const void* k_t1_win, const void* v_t1_win,
-                                  const int32_t* t1_len, int32_t cap1, float* out, float* alpha,
-                                  int32_t alpha_stride, const int32_t* t0_pos,
-                                  const int32_t* t1_pos, float* scores, int32_t max_ctx,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1_win,
-                     v_t1_win, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
-                     max_ctx, workspace, workspace_bytes, stream, nullptr, nullptr, true);
+                                  const void* t1_win, const int32_t* t1_len, int32_t cap1,
+                                  float* out, float* alpha, int32_t alpha_stride,
+                                  const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
+                                  int32_t max_ctx, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (!model) return fail(TKV_ERR_ARG, "model is null");
+  if (cap1 < 0 || cap1 % 32) return fail(TKV_ERR_ARG, "cap1 must be a multiple of 32");
+  // each (sequence, layer, KV head) row of the window: cap1 key slots, then cap1 value slots
+  const size_t e = model->kv_dtype == TKV_BF16 ? 2 : 4;
+  const void* v_win = t1_win ? (const char*)t1_win + (size_t)cap1 * model->head_dim * e : nullptr;
+  return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, t1_win,
+                     v_win, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
+                     max_ctx, workspace, workspace_bytes, stream, nullptr, nullptr, true, false,
+                     2L * cap1 * model->head_dim);
 }
 
 tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const void* q,
                                     const void* k_t0, const void* v_t0, const int32_t* t0_len,
                                     int32_t cap0, const void* host_t1, const int32_t* t1_len,
                                     int32_t cap1, void* win, int32_t chunk_layers, float* out,
-                                    float* alpha,
-                                    int32_t alpha_stride, const int32_t* t0_pos,
+                                    float* alpha, int32_t alpha_stride, const int32_t* t0_pos,
                                     const int32_t* t1_pos, float* scores, int32_t max_ctx,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
                                     hipStream_t side_stream, hipStream_t side_stream2,
-                                    hipEvent_t* events) {
+                                    hipEvent_t* events, int64_t* link_bytes) {
   tkv_status st = check_model(model);
   if (st) return st;
   if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
   if (batch == 0) return TKV_OK;
+  if (batch > kMaxSeqPerLaunch)
+    return fail(TKV_ERR_CAPACITY, "the streamed step takes at most 64 sequences per call");
   if (!host_t1 || !win || !events || !t1_len) return fail(TKV_ERR_ARG, "null pointer");
   for (int i = 0; i < 4; ++i)
     if (!events[i]) return fail(TKV_ERR_ARG, "null event");
   const int L = model->num_layers;
   if (chunk_layers < 1 || chunk_layers > L) return fail(TKV_ERR_ARG, "need 1 <= chunk_layers <= L");
   if (cap1 < 0 || cap1 % 32) return fail(TKV_ERR_ARG, "cap1 must be a multiple of 32");
+  const int hkv = model->num_kv_heads, D = model->head_dim;
   const size_t e = model->kv_dtype == TKV_BF16 ? 2 : 4;
-  const size_t layer_bytes = (size_t)model->num_kv_heads * cap1 * model->head_dim * e;
-  const size_t kv_bytes = (size_t)batch * chunk_layers * layer_bytes;  // K (or V) of a buffer
+  const size_t slot_bytes = (size_t)D * e;
+  const size_t row_bytes = 2 * (size_t)cap1 * slot_bytes;        // keys then values of one row
+  const size_t layer_bytes = (size_t)hkv * row_bytes;             // one layer of one sequence
+  const size_t buf_bytes = (size_t)batch * chunk_layers * layer_bytes;
   const int n_chunks = (L + chunk_layers - 1) / chunk_layers;
+  const long t1_rs = 2L * cap1 * D;
   // every check of the per-chunk calls before anything is queued (the chunks differ
   // only in their layer range)
+  const DecodeWorkspace wfull = decode_workspace(model, batch, L, cap0, cap1);
+  float* gsum = (float*)workspace + wfull.gsum;
+  DeferredScore ds{gsum, 0};
   if ((st = decode_step(model, batch, 0, chunk_layers, q, k_t0, v_t0, t0_len, cap0, win,
-                        (const char*)win + kv_bytes,
-                        t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores, max_ctx,
-                        workspace, workspace_bytes, stream, nullptr, nullptr, true, true)))
+                        (const char*)win + cap1 * slot_bytes, t1_len, cap1, out, alpha,
+                        alpha_stride, t0_pos, t1_pos, scores, max_ctx, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, true, true, t1_rs,
+                        scores ? &ds : nullptr)))
     return st;
   hipEvent_t* loaded = events;
   hipEvent_t* read = events + 2;
+  int64_t link = 0;
   // everything queued on `stream` before this call (the previous step's reads of the
   // two buffers among it) happens before the first copies
   if ((st = hip_check(hipEventRecord(read[0], stream), "event record"))) return st;
   if ((st = hip_check(hipEventRecord(read[1], stream), "event record"))) return st;
   // chunk c goes on side stream c % 2 when two are given: the next copy is then
   // already queued when the running one ends (each buffer is always filled from
-  // the same stream)
+  // the same stream).  Only whole 32-slot blocks holding live T1 rows move: one
+  // 2-D copy per sequence of its n * Hkv * 2 rows (keys, values), each
+  // ceil32(t1_len) slots wide.
   auto copy_chunk = [&](int c) -> tkv_status {
     const int buf = c & 1;
     const int l0 = c * chunk_layers;
@@ -564,15 +598,18 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
     hipStream_t ss = (side_stream2 && buf) ? side_stream2 : side_stream;
     tkv_status s2 = hip_check(hipStreamWaitEvent(ss, read[buf], 0), "stream wait");
     if (s2) return s2;
-    // one copy: 2 * B rows (keys, then values, of each sequence) of n layers,
-    // [2][B][L][Hkv][cap1][D] host -> [2][B][n][Hkv][cap1][D] buffer
-    char* dst = (char*)win + (size_t)buf * 2 * kv_bytes;
-    const char* src = (const char*)host_t1 + (size_t)l0 * layer_bytes;
-    s2 = hip_check(hipMemcpy2DAsync(dst, n * layer_bytes, src, (size_t)L * layer_bytes,
-                                    n * layer_bytes, 2 * (size_t)batch, hipMemcpyHostToDevice,
-                                    ss),
-                   "T1 chunk copy");
-    if (s2) return s2;
+    char* dbuf = (char*)win + (size_t)buf * buf_bytes;
+    for (int b = 0; b < batch; ++b) {
+      const size_t live = (size_t)((t1_len[b] + 31) / 32 * 32) * slot_bytes;
+      if (live == 0) continue;
+      const char* src = (const char*)host_t1 + ((size_t)b * L + l0) * layer_bytes;
+      char* dst = dbuf + (size_t)b * n * layer_bytes;     // a partial last chunk packs with pitch n
+      s2 = hip_check(hipMemcpy2DAsync(dst, cap1 * slot_bytes, src, cap1 * slot_bytes, live,
+                                      (size_t)n * hkv * 2, hipMemcpyHostToDevice, ss),
+                     "T1 chunk copy");
+      if (s2) return s2;
+      link += (int64_t)(live * n * hkv * 2);
+    }
     return hip_check(hipEventRecord(loaded[buf], ss), "event record");
   };
   for (int c = 0; c < std::min(2, n_chunks); ++c)
@@ -582,16 +619,47 @@ tkv_status tkv_decode_step_streamed(const tkv_model* model, int32_t batch, const
     const int l0 = c * chunk_layers;
     const int n = std::min(chunk_layers, L - l0);
     if ((st = hip_check(hipStreamWaitEvent(stream, loaded[buf], 0), "stream wait"))) return st;
-    // a partial last chunk packs its rows with pitch n: keys at 0, values after B * n layers
-    const char* wk = (const char*)win + (size_t)buf * 2 * kv_bytes;
-    const char* wv = wk + (size_t)batch * n * layer_bytes;
-    if ((st = decode_step(model, batch, l0, l0 + n, q, k_t0, v_t0, t0_len, cap0, wk, wv, t1_len,
-                          cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores, max_ctx,
-                          workspace, workspace_bytes, stream, nullptr, nullptr, true)))
+    const char* wk = (const char*)win + (size_t)buf * buf_bytes;
+    ds.row0 = l0 * hkv;
+    if ((st = decode_step(model, batch, l0, l0 + n, q, k_t0, v_t0, t0_len, cap0, wk,
+                          wk + cap1 * slot_bytes, t1_len, cap1, out, alpha, alpha_stride,
+                          t0_pos, t1_pos, scores, max_ctx, workspace, workspace_bytes, stream,
+                          nullptr, nullptr, true, false, t1_rs, scores ? &ds : nullptr)))
       return st;
     if ((st = hip_check(hipEventRecord(read[buf], stream), "event record"))) return st;
     if (c + 2 < n_chunks && (st = copy_chunk(c + 2))) return st;
   }
+  // the whole step's score increment, added once: the group sums of every layer in
+  // the order of a single-call step
+  if (scores) {
+    ScoreArgs sa{};
+    int sblocks = 0;
+    for (int i = 0; i < batch; ++i) {
+      sa.seq.t0_len[i] = t0_len[i];
+      sa.seq.t1_len[i] = t1_len[i];
+      sa.seq.base[i] = sblocks;
+      sblocks += ceil_div(t0_len[i] + t1_len[i], kScoreSlots);
+    }
+    sa.seq.nb = batch;
+    sa.seq.b_offset = 0;
+    sa.seq.base[batch] = sblocks;
+    sa.src = gsum;
+    sa.row_stride = (long)wfull.gs_stride;
+    sa.seq_stride = (long)L * hkv * (long)wfull.gs_stride;
+    sa.rows = L * hkv;
+    sa.t0_pos = t0_pos;
+    sa.t1_pos = t1_pos;
+    sa.scores = scores;
+    sa.cap0 = cap0;
+    sa.cap1 = cap1;
+    sa.max_ctx = max_ctx;
+    sa.weight = 1.0 / ((double)L * model->num_q_heads);
+    if (sblocks > 0) {
+      launch_score_rows(sa, sblocks, "score_update", stream);
+      if ((st = hip_check(hipGetLastError(), "score_update launch"))) return st;
+    }
+  }
+  if (link_bytes) *link_bytes = link;
   return TKV_OK;
 }
 
@@ -833,6 +901,7 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
     a.cap1 = cap1;
     a.t2_cap = t2_cap;
     a.b_offset = b0;
+    a.host_t1 = 0;
     for (int i = 0; i < nb; ++i) {
       a.n[i] = ctx_len[b0 + i];
       a.len0[i] = t0_len[b0 + i];
@@ -847,6 +916,8 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
       q.v0 = v_t0;
       q.k1 = k_t1;
       q.v1 = v_t1;
+      q.staging = nullptr;
+      q.only = 0;
       q.src = t2_src;
       q.n_rows = new_lens + 2;
       q.codes = t2_codes;
@@ -892,6 +963,337 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
   return TKV_OK;
 }
 
+// Pinned host scratch of tkv_compact_host_t1, every region 256-byte aligned:
+//   rows [B][cap1][L*Hkv][2][D] | tier_prev, tier_next [B][max_ctx] u8 |
+//   pos1 before, after [B][cap1] | to_t1 [B][cap1] int2 | lens, cnt [B][4]
+struct HostT1Scratch {
+  size_t rows, tprev, tnext, pos_old, pos_new, to_t1, lens, cnt, total;
+};
+
+static HostT1Scratch host_t1_scratch(const tkv_model* m, int batch, int max_ctx, int cap1) {
+  const size_t B = (size_t)batch;
+  const size_t elem = m->kv_dtype == TKV_BF16 ? 2 : 4;
+  HostT1Scratch h;
+  h.rows = 0;
+  h.tprev = round_up(B * cap1 * (size_t)m->num_layers * m->num_kv_heads * 2 * m->head_dim * elem, 256);
+  h.tnext = round_up(h.tprev + B * max_ctx, 256);
+  h.pos_old = round_up(h.tnext + B * max_ctx, 256);
+  h.pos_new = round_up(h.pos_old + B * cap1 * 4, 256);
+  h.to_t1 = round_up(h.pos_new + B * cap1 * 4, 256);
+  h.lens = round_up(h.to_t1 + B * cap1 * 8, 256);
+  h.cnt = round_up(h.lens + B * 16, 256);
+  h.total = round_up(h.cnt + B * 16, 256);
+  return h;
+}
+
+size_t tkv_compact_host_t1_workspace_bytes(const tkv_model* model, int32_t batch, int32_t max_ctx,
+                                           int32_t cap0, int32_t cap1) {
+  if (check_model(model) || batch < 0 || max_ctx < 0 || cap0 < 0 || cap1 < 0) return 0;
+  return reloc_workspace(model, batch, max_ctx, cap0, cap1).staging;  // no device staging
+}
+
+size_t tkv_compact_host_t1_scratch_bytes(const tkv_model* model, int32_t batch, int32_t max_ctx,
+                                         int32_t cap1) {
+  if (check_model(model) || batch < 0 || max_ctx < 0 || cap1 < 0) return 0;
+  return host_t1_scratch(model, batch, max_ctx, cap1).total;
+}
+
+int32_t tkv_t0_capacity(const tkv_policy* policy, int32_t n_from, int32_t n_to) {
+  if (!policy || n_from < 0 || n_to < n_from || policy->delta < 1) return -1;
+  const float f1 = policy->frac_t1, f2 = policy->frac_t2, f3 = policy->frac_t3;
+  if (!(f1 >= 0.f && f2 >= 0.f && f3 >= 0.f) || (double)f1 + f2 + f3 > 1.0) return -1;
+  if (policy->prompt_len < 0 || policy->num_sinks < 0 || policy->recent_window < 0) return -1;
+  // after a reassignment at length n, T0 holds at most max(N0(n), |protected(n)|) rows:
+  // either every budget of T1..T3 is met (T0 = N0 or fewer, T2/T3 being absorbing), or
+  // the non-protected candidates ran out (T0 = the protected T0/T1 rows); then Delta
+  // appended rows before the next reassignment
+  long best = 0;
+  const long lo = std::max(policy->prompt_len, policy->num_sinks);
+  for (long n = n_from; n <= n_to; ++n) {
+    const long n0 = n - (long)floor((double)f1 * n) - (long)floor((double)f2 * n) -
+                    (long)floor((double)f3 * n);
+    const long head = std::min(n, lo);
+    const long tail = std::max(head, std::max(0L, n - (long)policy->recent_window));
+    const long prot = head + (n - tail);
+    best = std::max(best, std::max(n0, prot));
+  }
+  const long cap = (best + policy->delta + 31) / 32 * 32;
+  return cap > INT32_MAX ? -1 : (int32_t)cap;
+}
+
+tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int32_t* ctx_len,
+                               int32_t max_ctx, const uint8_t* tier_prev,
+                               const uint8_t* tier_next, void* k_t0, void* v_t0,
+                               int32_t* t0_pos, const int32_t* t0_len, int32_t cap0,
+                               int32_t* t1_pos, const int32_t* t1_len, int32_t cap1,
+                               void* store_k, void* store_v, void* t1_host, int32_t* t2_src,
+                               int32_t* t2_pos, int32_t t2_cap, int8_t* t2_codes,
+                               float* t2_scales, int32_t* new_lens, int32_t* new_lens_host,
+                               void* workspace, size_t workspace_bytes, void* host_scratch,
+                               size_t host_scratch_bytes, int64_t* link_bytes,
+                               hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0) return fail(TKV_ERR_ARG, "batch < 0");
+  if (batch == 0) return TKV_OK;
+  if (!ctx_len || !tier_prev || !tier_next || !k_t0 || !v_t0 || !t0_pos || !t0_len || !t1_pos ||
+      !t1_len || !store_k || !store_v || !t1_host || !t2_src || !t2_pos || !new_lens ||
+      !new_lens_host || !workspace || !host_scratch)
+    return fail(TKV_ERR_ARG, "null pointer");
+  if (t2_cap > 0 && (!t2_codes || !t2_scales))
+    return fail(TKV_ERR_ARG, "null T2 codes or scales with t2_cap > 0");
+  if (cap0 < 1 || cap1 < 0 || t2_cap < 0 || max_ctx < 1 || cap0 % 32 || cap1 % 32)
+    return fail(TKV_ERR_ARG, "bad capacity (cap0, cap1 multiples of 32)");
+  if (t2_cap > 65535) return fail(TKV_ERR_CAPACITY, "t2_cap above 65535");
+  if (tier_prev == tier_next) return fail(TKV_ERR_ARG, "tier_prev and tier_next must differ");
+  for (int b = 0; b < batch; ++b) {
+    if (ctx_len[b] < 0 || t0_len[b] < 0 || t1_len[b] < 0)
+      return fail(TKV_ERR_ARG, "negative length");
+    if (ctx_len[b] > max_ctx) return fail(TKV_ERR_CAPACITY, "ctx_len > max_ctx");
+    if (t0_len[b] > cap0 || t1_len[b] > cap1) return fail(TKV_ERR_CAPACITY, "length > capacity");
+    if ((long)t0_len[b] + t1_len[b] > ctx_len[b])
+      return fail(TKV_ERR_STATE, "t0_len + t1_len > ctx_len");
+  }
+  const RelocWorkspace w = reloc_workspace(model, batch, max_ctx, cap0, cap1);
+  if (workspace_bytes < w.staging) return fail(TKV_ERR_CAPACITY, "workspace too small");
+  const HostT1Scratch hs = host_t1_scratch(model, batch, max_ctx, cap1);
+  if (host_scratch_bytes < hs.total) return fail(TKV_ERR_CAPACITY, "host scratch too small");
+  char* hb = (char*)host_scratch;
+  // the row staging is read and written by the kernels in place (pinned host memory)
+  void* rows_dev = nullptr;
+  if ((st = hip_check(hipHostGetDevicePointer(&rows_dev, hb + hs.rows, 0),
+                      "host scratch is not pinned, device-mapped memory")))
+    return st;
+  char* base = (char*)workspace;
+  const int L = model->num_layers, hkv = model->num_kv_heads, D = model->head_dim;
+  const int lgs = L * hkv;
+  const size_t elem = model->kv_dtype == TKV_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)lgs * 2 * D * elem;  // one position: K and V of every (l, g)
+  int32_t* pos_old = (int32_t*)(hb + hs.pos_old);
+  int32_t* pos_new = (int32_t*)(hb + hs.pos_new);
+  uint8_t* tp_h = (uint8_t*)(hb + hs.tprev);
+  uint8_t* tn_h = (uint8_t*)(hb + hs.tnext);
+  int2* to1_h = (int2*)(hb + hs.to_t1);
+  int32_t* lens_h = (int32_t*)(hb + hs.lens);
+  int32_t* cnt_h = (int32_t*)(hb + hs.cnt);
+  const size_t B = (size_t)batch;
+  int64_t link = 0;
+  // 1. the slot -> position map of the T1 window before the relocation
+  if ((st = hip_check(hipMemcpyAsync(pos_old, t1_pos, B * cap1 * 4, hipMemcpyDeviceToHost, stream),
+                      "T1 map copy")))
+    return st;
+  link += (int64_t)(B * cap1 * 4);
+  // 2. the scan, the new T2 rows that leave T0, and the rows that enter T1 from T0
+  //    written to host memory (the only rows that go device -> host)
+  RelocArgs a{};
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    a = RelocArgs{};
+    a.tprev = tier_prev;
+    a.tnext = tier_next;
+    a.t0_pos = t0_pos;
+    a.t1_pos = t1_pos;
+    a.inv = (int*)(base + w.inv);
+    a.holes0 = (int*)(base + w.holes0);
+    a.holes1 = (int*)(base + w.holes1);
+    a.to_t0 = (int2*)(base + w.to_t0);
+    a.to_t1 = (int2*)(base + w.to_t1);
+    a.staged = (int2*)(base + w.staged);
+    a.cnt = (int*)(base + w.cnt);
+    a.t2_src = t2_src;
+    a.t2_pos = t2_pos;
+    a.new_lens = new_lens;
+    a.max_ctx = max_ctx;
+    a.cap0 = cap0;
+    a.cap1 = cap1;
+    a.t2_cap = t2_cap;
+    a.b_offset = b0;
+    a.host_t1 = 1;
+    for (int i = 0; i < nb; ++i) {
+      a.n[i] = ctx_len[b0 + i];
+      a.len0[i] = t0_len[b0 + i];
+      a.len1[i] = t1_len[b0 + i];
+    }
+    launch_reloc_scan(a, nb, stream);
+    if ((st = hip_check(hipGetLastError(), "reloc_scan launch"))) return st;
+    if (t2_cap > 0) {
+      QuantArgs q{};
+      q.k0 = k_t0;
+      q.v0 = v_t0;
+      q.staging = rows_dev;
+      q.only = 1;
+      q.src = t2_src;
+      q.n_rows = new_lens + 2;
+      q.codes = t2_codes;
+      q.scales = t2_scales;
+      q.n_rows_stride = 4;
+      q.max_rows = t2_cap;
+      q.cap0 = cap0;
+      q.cap1 = cap1;
+      q.L = L;
+      q.hkv = hkv;
+      q.b_offset = b0;
+      launch_quantize(q, model->kv_dtype, D, nb, stream);
+      if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
+    }
+    if (cap1 > 0) {
+      MoveArgs mv{};
+      mv.k0 = k_t0;
+      mv.v0 = v_t0;
+      mv.staging = rows_dev;
+      mv.cnt = a.cnt;
+      mv.cap0 = cap0;
+      mv.cap1 = cap1;
+      mv.lgs = lgs;
+      mv.b_offset = b0;
+      mv.nb = nb;
+      mv.which = kMoveDown;
+      mv.list = a.to_t1;
+      mv.list_stride = cap1;
+      launch_reloc_move(mv, model->kv_dtype, D, stream);
+      if ((st = hip_check(hipGetLastError(), "reloc_move launch"))) return st;
+    }
+  }
+  // 3. the maps the host side needs, then one sync
+  struct Cp {
+    void* dst;
+    const void* src;
+    size_t bytes;
+  } cps[] = {{tp_h, tier_prev, B * max_ctx},           {tn_h, tier_next, B * max_ctx},
+             {pos_new, t1_pos, B * cap1 * 4},          {to1_h, base + w.to_t1, B * cap1 * 8},
+             {lens_h, new_lens, B * 16},               {cnt_h, base + w.cnt, B * 16}};
+  for (const Cp& c : cps) {
+    if ((st = hip_check(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToHost, stream),
+                        "map copy")))
+      return st;
+    link += (int64_t)c.bytes;
+  }
+  if ((st = hip_check(hipStreamSynchronize(stream), "stream sync"))) return st;
+  // 4. host: rows that entered T1 from T0 into the store; the rows that leave T1 for
+  //    T0 (promoted, ascending position) and for T2 (after them) into the staging rows
+  const size_t store_rs = (size_t)max_ctx * D * elem;  // one (l, g) row of the store
+  char* rows_h = hb + hs.rows;
+  std::vector<int> ok(batch, 1);
+  std::vector<std::vector<int32_t>> up(batch);
+  std::vector<std::vector<std::pair<int32_t, int32_t>>> down(batch);  // (staging row, position)
+  for (int b = 0; b < batch; ++b) {
+    memcpy(new_lens_host + 4 * b, lens_h + 4 * b, 16);
+    if (lens_h[4 * b] < 0) {
+      ok[b] = 0;
+      continue;
+    }
+    const int n = ctx_len[b];
+    const uint8_t* tp = tp_h + (size_t)b * max_ctx;
+    const uint8_t* tn = tn_h + (size_t)b * max_ctx;
+    for (int p = 0; p < n; ++p)
+      if (tp[p] == 1 && tn[p] == 0) up[b].push_back(p);
+    const int mp = (int)up[b].size();
+    for (int p = 0; p < n; ++p)
+      if (tp[p] == 1 && tn[p] == 2) up[b].push_back(p);
+    if (mp != cnt_h[4 * b + kMoveStage] || (long)up[b].size() > cap1)
+      return fail(TKV_ERR_STATE, "promoted rows disagree with the device relocation lists");
+    const int m1 = cnt_h[4 * b + kMoveToT1];
+    const int2* l1 = to1_h + (size_t)b * cap1;
+    for (int i = 0; i < m1; ++i)
+      if (l1[i].x >= 0) down[b].push_back({i, pos_new[(size_t)b * cap1 + l1[i].y]});
+  }
+  std::vector<std::pair<int, int>> jobs;  // (sequence, index) over down then up rows
+  for (int b = 0; b < batch; ++b)
+    for (int i = 0; i < (int)down[b].size(); ++i) jobs.push_back({b, i});
+  const size_t n_down = jobs.size();
+  parallel_ranges((long)n_down, std::min<long>(host_threads(), 1 + (long)n_down / 64),
+                  [&](long lo, long hi) {
+    for (long j = lo; j < hi; ++j) {
+      const int b = jobs[j].first;
+      const auto& d = down[b][jobs[j].second];
+      const char* src = rows_h + ((size_t)b * cap1 + d.first) * row_bytes;
+      for (int lg = 0; lg < lgs; ++lg) {
+        const size_t so = ((size_t)b * lgs + lg) * store_rs + (size_t)d.second * D * elem;
+        memcpy((char*)store_k + so, src + (size_t)lg * 2 * D * elem, D * elem);
+        memcpy((char*)store_v + so, src + ((size_t)lg * 2 + 1) * D * elem, D * elem);
+      }
+    }
+  });
+  jobs.clear();
+  for (int b = 0; b < batch; ++b)
+    for (int i = 0; i < (int)up[b].size(); ++i) jobs.push_back({b, i});
+  parallel_ranges((long)jobs.size(), std::min<long>(host_threads(), 1 + (long)jobs.size() / 64),
+                  [&](long lo, long hi) {
+    for (long j = lo; j < hi; ++j) {
+      const int b = jobs[j].first, i = jobs[j].second;
+      const int p = up[b][i];
+      char* dst = rows_h + ((size_t)b * cap1 + i) * row_bytes;
+      for (int lg = 0; lg < lgs; ++lg) {
+        const size_t so = ((size_t)b * lgs + lg) * store_rs + (size_t)p * D * elem;
+        memcpy(dst + (size_t)lg * 2 * D * elem, (const char*)store_k + so, D * elem);
+        memcpy(dst + ((size_t)lg * 2 + 1) * D * elem, (const char*)store_v + so, D * elem);
+      }
+    }
+  });
+  link += (int64_t)((n_down + jobs.size()) * row_bytes);
+  // 5. device: the new T2 rows that left T1, then every row into the T0 pool (the
+  //    promoted rows straight from the staging rows)
+  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
+    if (t2_cap > 0) {
+      QuantArgs q{};
+      q.k0 = k_t0;
+      q.v0 = v_t0;
+      q.staging = rows_dev;
+      q.only = 2;
+      q.src = t2_src;
+      q.n_rows = new_lens + 2;
+      q.codes = t2_codes;
+      q.scales = t2_scales;
+      q.n_rows_stride = 4;
+      q.max_rows = t2_cap;
+      q.cap0 = cap0;
+      q.cap1 = cap1;
+      q.L = L;
+      q.hkv = hkv;
+      q.b_offset = b0;
+      launch_quantize(q, model->kv_dtype, D, nb, stream);
+      if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
+    }
+    MoveArgs mv{};
+    mv.k0 = k_t0;
+    mv.v0 = v_t0;
+    mv.staging = rows_dev;
+    mv.cnt = (int*)(base + w.cnt);
+    mv.cap0 = cap0;
+    mv.cap1 = cap1;
+    mv.lgs = lgs;
+    mv.b_offset = b0;
+    mv.nb = nb;
+    mv.which = kMoveToT0;
+    mv.list = (int2*)(base + w.to_t0);
+    mv.list_stride = cap0;
+    launch_reloc_move(mv, model->kv_dtype, D, stream);
+    if ((st = hip_check(hipGetLastError(), "reloc_move launch"))) return st;
+  }
+  // 6. host, while the device moves rows: the streamed T1 window takes the rows of the
+  //    slots whose position changed (holes refilled), from the store
+  const size_t seq_t1 = (size_t)lgs * 2 * cap1 * D * elem;
+  for (int b = 0; b < batch; ++b) {
+    if (!ok[b]) continue;
+    const int n1 = lens_h[4 * b + 1];
+    std::vector<int32_t> slots, poss;
+    for (int s2 = 0; s2 < n1; ++s2) {
+      const int32_t pn = pos_new[(size_t)b * cap1 + s2];
+      if (s2 >= t1_len[b] || pn != pos_old[(size_t)b * cap1 + s2]) {
+        slots.push_back(s2);
+        poss.push_back(pn);
+      }
+    }
+    pack_t1_slots(model, (const char*)store_k + (size_t)b * lgs * store_rs,
+                  (const char*)store_v + (size_t)b * lgs * store_rs, max_ctx, slots.data(),
+                  poss.data(), (int)slots.size(), (char*)t1_host + b * seq_t1, cap1);
+  }
+  if ((st = hip_check(hipStreamSynchronize(stream), "stream sync"))) return st;
+  if (link_bytes) *link_bytes = link;
+  return TKV_OK;
+}
+
 tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_t0,
                            const void* v_t0, int32_t cap0, const void* k_t1, const void* v_t1,
                            int32_t cap1, const int32_t* src, const int32_t* n_rows,
@@ -914,6 +1316,8 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
     a.v0 = v_t0;
     a.k1 = k_t1;
     a.v1 = v_t1;
+    a.staging = nullptr;
+    a.only = 0;
     a.src = src;
     a.n_rows = n_rows;
     a.codes = codes;

@@ -331,7 +331,10 @@ __device__ __forceinline__ long unit_row(const AttnArgs& a, const Cursor& c) {
 
 // The T1 window of a call may hold every layer of a sequence (t1_L = L,
 // t1_l0 = layer_begin) or only the call's layers (t1_L = Lr, t1_l0 = 0: a
-// window streamed layer by layer from host memory).
+// window streamed layer by layer from host memory).  Consecutive (sequence,
+// layer, KV head) rows of the window lie t1_rs elements apart (cap1 * D for
+// separate key and value arrays; 2 * cap1 * D when each row's keys are followed
+// by its values, the layout of a streamed window).
 template <int D, bool Q8, bool GEO>
 __device__ __forceinline__ long unit_base(const AttnArgs& a, const Cursor& c) {
   if constexpr (Q8) {
@@ -339,7 +342,7 @@ __device__ __forceinline__ long unit_base(const AttnArgs& a, const Cursor& c) {
   } else if constexpr (GEO) {
     const long b = a.seq.b_offset + c.bl;
     if (c.seg == 1)
-      return ((b * a.t1_L + a.t1_l0 + c.lr) * a.hkv + c.g) * (long)a.cap1 * D + (long)c.c0 * D;
+      return ((b * a.t1_L + a.t1_l0 + c.lr) * a.hkv + c.g) * a.t1_rs + (long)c.c0 * D;
     return unit_row(a, c) * (long)a.cap0 * D + (long)c.c0 * D;
   } else {
     const int cap = c.seg ? a.cap1 : a.cap0;
@@ -803,8 +806,8 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
     const int cap = u.seg == 0 ? a.cap0 : (u.seg == 1 ? a.cap1 : a.cap2);
     const long lg = (u.b * a.L + a.layer_begin + u.lr) * a.hkv + u.g;
     const long lg1 = (u.b * a.t1_L + a.t1_l0 + u.lr) * a.hkv + u.g;  // T1 window row
-    const float* Kb = u.seg ? (const float*)a.k1 + lg1 * cap * D : (const float*)a.k0 + lg * cap * D;
-    const float* Vb = u.seg ? (const float*)a.v1 + lg1 * cap * D : (const float*)a.v0 + lg * cap * D;
+    const float* Kb = u.seg ? (const float*)a.k1 + lg1 * a.t1_rs : (const float*)a.k0 + lg * cap * D;
+    const float* Vb = u.seg ? (const float*)a.v1 + lg1 * a.t1_rs : (const float*)a.v0 + lg * cap * D;
     const int8_t* Kc = a.k2 + lg * cap * D;
     const int8_t* Vc = a.v2 + lg * cap * D;
     const int t = u.c0 + tid;
@@ -974,7 +977,8 @@ void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int grou
     // variants: a T2 pool with rows in this launch; a T1 window of the call's layers
     // only (with q / out / alpha rows of every layer)
     const bool t2 = a.k2 != nullptr;
-    const bool geo = a.t1_L != a.L || a.t1_l0 != a.layer_begin || a.io_L != a.Lr || a.io_l0 != 0;
+    const bool geo = a.t1_L != a.L || a.t1_l0 != a.layer_begin || a.io_L != a.Lr || a.io_l0 != 0 ||
+                     a.t1_rs != (long)a.cap1 * head_dim;
 #define TKV_MFMA(DD, TT, GG)                                                             \
   hipExtLaunchKernelGGL((attn_partial_mfma_kernel<DD, TT, GG>), grid, dim3(256), 0, s,   \
                         timer.start(), timer.stop(), 0, a)

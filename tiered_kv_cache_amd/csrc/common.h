@@ -5,7 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <string>
+#include <thread>
+#include <vector>
 
 #include "../../include/tkv.h"
 
@@ -104,5 +107,25 @@ struct KernelTimer {
 };
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Host threads for the library's host-side copies: the process's CPU affinity,
+// at most 16.
+int host_threads();
+
+// Runs f(lo, hi) over [0, total) split into at most `nt` contiguous ranges, on
+// the calling thread and nt - 1 helpers.
+template <class F>
+void parallel_ranges(long total, int nt, F f) {
+  nt = (int)std::max<long>(1, std::min<long>(nt, total));
+  if (nt == 1) {
+    if (total > 0) f(0L, total);
+    return;
+  }
+  std::vector<std::thread> pool;
+  pool.reserve(nt - 1);
+  for (int t = 1; t < nt; ++t) pool.emplace_back([&, t] { f(total * t / nt, total * (t + 1) / nt); });
+  f(0L, total / nt);
+  for (auto& th : pool) th.join();
+}
 
 }  // namespace tkv

@@ -56,6 +56,7 @@ struct AttnArgs {
   int cap0, cap1, cap2;
   int L, Lr, layer_begin, hq, hkv;
   int t1_L, t1_l0;   // T1 window: layers it holds per sequence, index of the call's first
+  long t1_rs;        // T1 window: elements between consecutive (sequence, layer, KV head) rows
   int io_L, io_l0;   // q / out / alpha rows: layers they hold per sequence, the call's first
   float scale;       // softmax_scale * log2(e): logits are kept in base 2
   SeqTable seq;
@@ -94,8 +95,10 @@ struct MergeArgs {
   const float* ml;
   float* out;
   float* alpha;
-  float* gsum;  // [nb][Lr * Hkv][gs_stride] sums of alpha over a group's heads, or null
+  float* gsum;  // [nb][gs_seq_rows][gs_stride] sums of alpha over a group's heads, or null
   long alpha_stride, gs_stride;
+  long gs_seq_rows;           // gsum rows per sequence (Lr * Hkv, or L * Hkv for a whole step)
+  int gs_row0;                // gsum row of the launch's first (layer, KV head)
   long total_units, workers;  // as in the attention launch
   int Lr, hq, hkv;
   int io_L, io_l0;            // out / alpha rows: layers they hold per sequence, the call's first
@@ -150,12 +153,18 @@ struct RelocArgs {
   int* t2_pos;
   int* new_lens;
   int max_ctx, cap0, cap1, t2_cap, b_offset;
+  // T1 rows live in host memory: new T2 rows that leave T1 are listed by a
+  // staging row after the promoted rows (t2_src = -(row) - 1) instead of by
+  // their T1 slot; the T1 side of the moves is the host's
+  int host_t1;
   int n[kMaxSeqPerLaunch];
   int len0[kMaxSeqPerLaunch];
   int len1[kMaxSeqPerLaunch];
 };
 
-enum MoveList { kMoveStage = 0, kMoveToT1 = 1, kMoveToT0 = 2 };
+// kMoveDown (T1 rows in host memory): the rows of the T1-destination list that
+// come from the T0 pool go to staging row = their list index.
+enum MoveList { kMoveStage = 0, kMoveToT1 = 1, kMoveToT0 = 2, kMoveDown = 3 };
 
 struct MoveArgs {
   void* k0;
@@ -173,6 +182,11 @@ struct QuantArgs {
   const void* v0;
   const void* k1;
   const void* v1;
+  // with staging set, a source s < 0 is staging row -s-1 ([B][cap1][L * Hkv][2][D]
+  // plain rows) rather than T1 slot -s-1; `only` = 1 takes only the T0 sources,
+  // 2 only the negative ones, 0 every row
+  const void* staging;
+  int only;
   const int* src;
   const int* n_rows;
   int8_t* codes;
@@ -210,6 +224,16 @@ struct T2MoveArgs {
   const int* cnt;
   int cap2, max_rows, lgs, b_offset, nb;
 };
+
+// Host-side T1 packers (gather.cpp): every slot [0, n) of a window of one
+// sequence from its positions, or only the listed (slot, position) pairs.  The
+// store is [L][Hkv][max_ctx][D] rows by position; the staging [L][Hkv][2][cap1][D]
+// tiles (each row's key slots, then its value slots).
+void pack_t1_blocks(const tkv_model* m, const void* store_k, const void* store_v, int max_ctx,
+                    const int32_t* positions, int n, void* staging, int cap1);
+void pack_t1_slots(const tkv_model* m, const void* store_k, const void* store_v, int max_ctx,
+                   const int32_t* slots, const int32_t* positions, int n, void* staging,
+                   int cap1);
 
 bool attn_group_supported(int group);
 int mfma_resident_waves(int head_dim);

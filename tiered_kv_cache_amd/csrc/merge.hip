@@ -234,7 +234,7 @@ __device__ void normalise_chunk(const MergeArgs& a, int cb) {
     }
   }
   if (!a.gsum) return;
-  float* gp = a.gsum + ((long)bl * a.Lr * a.hkv + gi) * a.gs_stride + j0;
+  float* gp = a.gsum + ((long)bl * a.gs_seq_rows + a.gs_row0 + gi) * a.gs_stride + j0;
   if (full) {
     *reinterpret_cast<float4*>(gp) = sum;
   } else {

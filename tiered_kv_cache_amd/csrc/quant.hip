@@ -30,18 +30,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int kv = combo & 1;
   const long lg = combo >> 1;
   const int s = a.src[b * a.max_rows + r];
-  const int cap = s >= 0 ? a.cap0 : a.cap1;
-  const long slot = s >= 0 ? s : -s - 1;
-  const T* blk = (const T*)(kv ? (s >= 0 ? a.v0 : a.v1) : (s >= 0 ? a.k0 : a.k1)) +
-                 (b * lgs + lg) * cap * D;
+  if ((a.only == 1 && s < 0) || (a.only == 2 && s >= 0)) return;
   float v[PER];
   float am = 0.f;
+  if (s < 0 && a.staging) {  // a plain staging row: D keys, then D values
+    const T* row = (const T*)a.staging + (((b * a.cap1 + (-s - 1)) * lgs + lg) * 2 + kv) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = lane * PER + i;
-    const long off = kv ? v_off(slot, d, D) : k_off(slot, d, D);  // tile storage order
-    v[i] = to_f32(blk[off]);
-    am = fmaxf(am, fabsf(v[i]));
+    for (int i = 0; i < PER; ++i) {
+      v[i] = to_f32(row[lane * PER + i]);
+      am = fmaxf(am, fabsf(v[i]));
+    }
+  } else {
+    const int cap = s >= 0 ? a.cap0 : a.cap1;
+    const long slot = s >= 0 ? s : -s - 1;
+    const T* blk = (const T*)(kv ? (s >= 0 ? a.v0 : a.v1) : (s >= 0 ? a.k0 : a.k1)) +
+                   (b * lgs + lg) * cap * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int d = lane * PER + i;
+      const long off = kv ? v_off(slot, d, D) : k_off(slot, d, D);  // tile storage order
+      v[i] = to_f32(blk[off]);
+      am = fmaxf(am, fabsf(v[i]));
+    }
   }
   am = wave_max(am);
   const float scale = am / 127.0f;

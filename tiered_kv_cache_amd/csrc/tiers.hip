@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
   const int seg = (n + kTierThreads - 1) / kTierThreads;
   const int lo = min(n, tid * seg);
   const int hi = min(n, lo + seg);
-  int cp0 = 0, cp1 = 0, cn0 = 0, cn1 = 0, ct2 = 0;
+  int cp0 = 0, cp1 = 0, cn0 = 0, cn1 = 0, ct2 = 0, ct2h = 0;
   for_segment(lo, hi, tp, tn, inv, [&](int, int o, int w, int v) {
     bad += o > 3 || w > 3 || (w <= 1 && o > 1);  // T2/T3 never return to full precision
     bad += o == 0 && v < 0;
@@ -406,6 +406,7 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
     cn0 += w == 0;
     cn1 += w == 1;
     ct2 += w == 2 && o <= 1;
+    ct2h += w == 2 && o == 1;  // new T2 rows that leave T1
   });
   bad = block_sum_i(bad, tmp);
   cp0 = block_sum_i(cp0, tmp);
@@ -451,11 +452,12 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
     m1 += w == 1 && (o == 0 || (o == 1 && -v - 1 >= n1));
     mp += w == 0 && o == 1;
   });
-  int M0, M1, MP, T2;
+  int M0, M1, MP, T2, T2H;
   int i0 = block_excl_scan(m0, tmp, &M0);
   int i1 = block_excl_scan(m1, tmp, &M1);
   int ip = block_excl_scan(mp, tmp, &MP);
   int it2 = block_excl_scan(ct2, tmp, &T2);
+  int ih = block_excl_scan(ct2h, tmp, &T2H);
   if (M0 != h0 || M1 != h1) {  // cannot happen once the checks above hold
     if (tid < 4) lens[tid] = -1;
     if (tid < 4) cnt[tid] = 0;
@@ -483,7 +485,9 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
       to1[i1++] = make_int2(v, d);
       pos1[d] = p;
     } else if (w == 2 && o <= 1) {
-      t2s[it2] = v;
+      // host-resident T1: the row reaches the device in staging row MP + (its rank
+      // among the new T2 rows that leave T1), after the promoted rows
+      t2s[it2] = (a.host_t1 && o == 1) ? -(MP + ih++) - 1 : v;
       t2p[it2++] = p;
     }
   });
@@ -530,7 +534,7 @@ struct RowRef {
 
 // Source and destination rows of one move of one (layer, KV head).
 template <typename T, int D>
-__device__ __forceinline__ void move_rows(const MoveArgs& m, long b, int lg, int2 mv,
+__device__ __forceinline__ void move_rows(const MoveArgs& m, long b, int lg, int2 mv, long idx,
                                           RowRef<T>& src, RowRef<T>& dst) {
   const long g = b * m.lgs + lg;
   T* p0k = (T*)m.k0 + g * m.cap0 * D;
@@ -540,6 +544,10 @@ __device__ __forceinline__ void move_rows(const MoveArgs& m, long b, int lg, int
   if (m.which == kMoveStage) {  // T1 slot -> staging row
     src = {p1k, p1v, (long)(-mv.x - 1)};
     T* r = (T*)m.staging + ((b * m.cap1 + mv.y) * m.lgs + lg) * 2 * D;
+    dst = {r, r + D, -1};
+  } else if (m.which == kMoveDown) {  // T0 slot -> staging row (the entry's list index)
+    src = {p0k, p0v, (long)mv.x};
+    T* r = (T*)m.staging + ((b * m.cap1 + idx) * m.lgs + lg) * 2 * D;
     dst = {r, r + D, -1};
   } else if (m.which == kMoveToT1) {  // T0 or T1 slot -> T1 slot
     src = mv.x >= 0 ? RowRef<T>{p0k, p0v, (long)mv.x} : RowRef<T>{p1k, p1v, (long)(-mv.x - 1)};
@@ -569,29 +577,37 @@ __global__ __launch_bounds__(256) void reloc_move_kernel(MoveArgs m) {
   const long nw = (long)gridDim.x * (256 / kWave);
   for (int bl = 0; bl < m.nb; ++bl) {
     const long b = m.b_offset + bl;
-    const int cnt = m.cnt[b * 4 + m.which];
+    // the down list is the T1-destination list; it moves only the entries whose
+    // source is a T0 slot
+    const bool down = m.which == kMoveDown;
+    const int cnt = m.cnt[b * 4 + (down ? kMoveToT1 : m.which)];
     const long items = (long)cnt * m.lgs;
     const int2* list = m.list + b * m.list_stride;
     for (long it0 = gw; it0 < items; it0 += nw * kMoveBatch) {
       int2 mv[kMoveBatch];
       int lg[kMoveBatch];
+      long li[kMoveBatch];
+      bool on[kMoveBatch];
 #pragma unroll
       for (int k = 0; k < kMoveBatch; ++k) {
         const long it = it0 + k * nw;
         lg[k] = 0;
+        li[k] = 0;
         mv[k] = make_int2(0, 0);
         if (it < items) {
           lg[k] = (int)(it / cnt);
-          mv[k] = list[it - (long)lg[k] * cnt];
+          li[k] = it - (long)lg[k] * cnt;
+          mv[k] = list[li[k]];
         }
+        on[k] = it < items && !(down && mv[k].x < 0);
       }
       RowRef<T> src[kMoveBatch], dst[kMoveBatch];
       Vec8<T> kv[kMoveBatch];
       T x[kMoveBatch][VE];
 #pragma unroll
       for (int k = 0; k < kMoveBatch; ++k) {
-        if (it0 + k * nw >= items) continue;
-        move_rows<T, D>(m, b, lg[k], mv[k], src[k], dst[k]);
+        if (!on[k]) continue;
+        move_rows<T, D>(m, b, lg[k], mv[k], li[k], src[k], dst[k]);
         if (lane < D / 8) {
           const int d = 8 * lane;
           kv[k] = load8(src[k].slot >= 0 ? src[k].k + k_off(src[k].slot, d, D) : src[k].k + d);
@@ -604,7 +620,7 @@ __global__ __launch_bounds__(256) void reloc_move_kernel(MoveArgs m) {
       }
 #pragma unroll
       for (int k = 0; k < kMoveBatch; ++k) {
-        if (it0 + k * nw >= items) continue;
+        if (!on[k]) continue;
         if (lane < D / 8) {
           const int d = 8 * lane;
           store8(dst[k].slot >= 0 ? dst[k].k + k_off(dst[k].slot, d, D) : dst[k].k + d, kv[k]);
@@ -627,7 +643,7 @@ void launch_reloc_scan(const RelocArgs& a, int nb, hipStream_t s) {
 }
 
 void launch_reloc_move(const MoveArgs& m, int kv_dtype, int head_dim, hipStream_t s) {
-  static const char* names[3] = {"reloc_stage", "reloc_to_t1", "reloc_to_t0"};
+  static const char* names[4] = {"reloc_stage", "reloc_to_t1", "reloc_to_t0", "reloc_down"};
   KernelTimer timer(names[m.which], s);
   const dim3 grid(2048);
   if (kv_dtype == TKV_BF16) {

@@ -124,8 +124,13 @@ class TieredKVCache:
 
     def __init__(self, shape: Shape, policy: PolicyCfg, batch: int, max_ctx: int,
                  device: str = "cuda", cap0: Optional[int] = None, cap1: Optional[int] = None,
-                 t2_cap: Optional[int] = None, attend_t2: bool = False):
+                 t2_cap: Optional[int] = None, attend_t2: bool = False, t0_budget: bool = False):
+        """t0_budget: after the first reassignment, move the T0 pool into one sized by the
+        tier budget (tkv_t0_capacity) instead of the whole context."""
         self.shape = shape
+        self.t0_budget = t0_budget
+        self.host_t1 = False       # set by T1Stream: T1 rows live in host memory
+        self.reassignments = 0
         self.policy = policy
         self.batch = batch
         self.device = torch.device(device)
@@ -312,6 +317,8 @@ class TieredKVCache:
 
     def reassign(self, stream=None) -> None:
         """Rank, quantise the new T2 rows, relocate in place; one host sync for the new lengths."""
+        if self.host_t1:
+            raise RuntimeError("T1 rows live in host memory: reassign through T1Stream")
         tnx = 1 - self.tcur
         B = self.batch
         tkv.tkv_assign_tiers(B, self.n, self.max_ctx, self.scores, self.tpolicy,
@@ -334,6 +341,10 @@ class TieredKVCache:
             self.t2_len = t2l[:, 0].tolist()
         else:
             lens = self.new_lens.cpu().numpy()      # the one sync per reassignment
+        self.finish_reassign(lens, tnx)
+
+    def finish_reassign(self, lens: np.ndarray, tnx: int) -> None:
+        """New lengths of a reassignment; the T0 pool moves to its budget after the first."""
         if (lens < 0).any():
             raise RuntimeError(f"tier state error reported by the device: {lens.tolist()}")
         self.t0_len = lens[:, 0].tolist()
@@ -341,6 +352,61 @@ class TieredKVCache:
         self.t2_new = lens[:, 2].tolist()
         self.moved = lens[:, 3].tolist()
         self.tcur = tnx
+        self.reassignments += 1
+        if self.t0_budget and self.reassignments == 1:
+            cap = tkv.tkv_t0_capacity(self.tpolicy, min(self.n), self.max_ctx)
+            if cap < self.cap0:
+                self.resize_t0(cap)
+
+    def resize_t0(self, cap0: int) -> None:
+        """Move the T0 pool into one of capacity cap0 (a multiple of 32 that holds every
+        current row): slots [0, t0_len) keep their rows; the weights, the decode and the
+        relocation workspaces follow the new capacity."""
+        if cap0 % 32 or cap0 < _round_up(max(self.t0_len), 32):
+            raise ValueError("the new T0 capacity must be a multiple of 32 holding every row")
+        m = min(self.cap0, _round_up(max(self.t0_len), 32))     # whole 32-slot blocks
+        torch.cuda.synchronize(self.device)
+        B, L, Hkv, D = self.batch, self.shape.layers, self.shape.kv_heads, self.shape.head_dim
+        dt = self.shape.torch_dtype
+        k = torch.empty((B, L, Hkv, cap0, D), dtype=dt, device=self.device)
+        v = torch.empty_like(k)
+        k[:, :, :, :m] = self.k_t0[:, :, :, :m]
+        v[:, :, :, :m] = self.v_t0[:, :, :, :m]
+        pos = torch.zeros((B, cap0), dtype=torch.int32, device=self.device)
+        pos[:, :m] = self.t0_pos[:, :m]
+        self.k_t0, self.v_t0, self.t0_pos = k, v, pos
+        self.cap0 = cap0
+        self.alpha_stride = _round_up(self.cap0 + self.cap1 + self.cap2, 64)
+        self.alpha = torch.zeros((B, L, self.shape.q_heads, self.alpha_stride),
+                                 dtype=torch.float32, device=self.device)
+        self.ws_bytes = tkv.tkv_decode_workspace_bytes(self.model, B, L, self.cap0,
+                                                       self.cap1 + self.cap2)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.alloc_compact_workspace()
+        torch.cuda.synchronize(self.device)
+
+    def alloc_compact_workspace(self) -> None:
+        if self.host_t1:
+            self.cws_bytes = tkv.tkv_compact_host_t1_workspace_bytes(
+                self.model, self.batch, self.max_ctx, self.cap0, self.cap1)
+        else:
+            self.cws_bytes = tkv.tkv_compact_workspace_bytes(self.model, self.batch, self.max_ctx,
+                                                             self.cap0, self.cap1)
+        self.cws = torch.zeros(self.cws_bytes, dtype=torch.uint8, device=self.device)
+
+    def resident_kv_bytes(self) -> int:
+        """Device bytes that hold key/value rows: the T0 pool, the T1 window (when it is
+        on the device) and the attended int8 T2 pool."""
+        t = [self.k_t0, self.v_t0, self.k_t1, self.v_t1]
+        if self.attend_t2:
+            t += [self.k_t2, self.v_t2, self.ks_t2, self.vs_t2]
+        return sum(x.numel() * x.element_size() for x in t if x is not None)
+
+    def full_cache_bytes(self) -> int:
+        """Bytes of every sequence's K/V rows at its current length (a full cache)."""
+        sh = self.shape
+        e = 2 if sh.dtype == "bf16" else 4
+        return sum(self.n) * sh.layers * sh.kv_heads * sh.head_dim * e * 2
 
     # ---- read-back helpers (tests, tools): ascending position order -------------
     def _order(self, b: int):
@@ -416,90 +482,103 @@ class TieredKVCache:
 
 
 class T1Stream:
-    """Pipelined streaming of the T1 rows from pinned host memory, chunk of layers by
-    chunk of layers (tkv_decode_step_streamed).
+    """T1 rows in host memory, streamed to the device chunk of layers by chunk of layers
+    (Methodologie section 1 of the pages: T1 stays in host DDR at full precision and is
+    brought to the GPU before each attention step; section 4: tiers change every Delta
+    steps and only the newly promoted tokens go from host memory to the GPU).
 
-    Methodologie section 1 of the pages keeps T1 in host DDR at full precision and
-    brings it to the GPU before each attention step.  Here the T1 rows of every layer
-    sit in a pinned host copy [2][B][L][Hkv][cap1][D] (keys then values, tiles,
-    window-slot order); each
-    step the library runs the attention chunk by chunk over the resident T0 pool and
-    a two-buffer device window, the copy of chunk c + 2 starting on a side stream as
-    soon as chunk c has read its buffer.  HBM holds 2 x chunk_layers layers of T1
-    rows for this path instead of every layer.
+    Host memory holds a store of full-precision rows by position [B][L][Hkv][max_ctx][D]
+    and the streamed window [B][L][Hkv][2][cap1][D] (pinned, tiles, window-slot order).
+    The device holds the T0 pool and a two-buffer window of chunk_layers layers
+    [2][B][chunk][Hkv][2][cap1][D]; the cache's own T1 window is released.
 
-    Between reassignments HBM holds no other T1 rows: the cache's persistent window is
-    released.  At a reassignment the host copy is brought into a transient device
-    window, the same in-place relocation (tkv_compact) runs on it, and the result goes
-    back to the host copy (two transfers of the window every Delta steps).  With
-    keep_window the persistent window stays and the host copy is refreshed from it.
+    Every step (tkv_decode_step_streamed): the live 32-slot blocks of every layer's T1
+    rows cross the link while the previous chunk attends.  Every Delta steps
+    (tkv_assign_tiers, tkv_compact_host_t1): only the rows that enter T1 from T0 go to the
+    host store and only the rows that leave T1 (for T0 or T2) come back; the window slots
+    whose position changed are rewritten on the host.  `link_step` / `link_reassign` count
+    the bytes that crossed the link.
     """
 
-    def __init__(self, cache: TieredKVCache, chunk_layers: int = 1, keep_window: bool = False):
+    def __init__(self, cache: TieredKVCache, chunk_layers: int = 1):
         if cache.attend_t2:
             raise ValueError("the streamed T1 window is built for the T0 u T1 step")
+        if any(cache.t1_len):
+            raise ValueError("T1 must be empty when its rows move to host memory")
         self.cache = cache
         sh = cache.shape
         B, L, Hkv, D = cache.batch, sh.layers, sh.kv_heads, sh.head_dim
         dt, dev = sh.torch_dtype, cache.device
         self.chunk = max(1, min(chunk_layers, L))
-        self.host = torch.empty((2, B, L, Hkv, cache.cap1, D), dtype=dt).pin_memory()
-        self.win = torch.zeros((2, 2, B, self.chunk, Hkv, cache.cap1, D), dtype=dt, device=dev)
+        self.store_k = torch.empty((B, L, Hkv, cache.max_ctx, D), dtype=dt)
+        self.store_v = torch.empty((B, L, Hkv, cache.max_ctx, D), dtype=dt)
+        self.t1_host = torch.empty((B, L, Hkv, 2, cache.cap1, D), dtype=dt, pin_memory=True)
+        self.t1_host.zero_()
+        self.win = torch.zeros((2, B, self.chunk, Hkv, 2, cache.cap1, D), dtype=dt, device=dev)
+        self.scratch_bytes = tkv.tkv_compact_host_t1_scratch_bytes(cache.model, B, cache.max_ctx,
+                                                                   cache.cap1)
+        self.scratch = torch.empty(self.scratch_bytes, dtype=torch.uint8, pin_memory=True)
         self.side = torch.cuda.Stream(device=dev)
         self.side2 = torch.cuda.Stream(device=dev)   # chunks alternate between the two
         self.events = [torch.cuda.Event() for _ in range(4)]
         main = torch.cuda.current_stream(dev)
         for e in self.events:        # creates the underlying events
             e.record(main)
-        self.layer_bytes = 2 * B * Hkv * cache.cap1 * D * self.host.element_size()
-        self.keep_window = keep_window
-        self.refresh()
-        if not keep_window:      # the window lives in host memory from here on
-            cache.k_t1 = cache.v_t1 = None
+        # the device no longer holds T1 rows, nor a staging area for them
+        cache.host_t1 = True
+        cache.k_t1 = cache.v_t1 = None
+        cache.alloc_compact_workspace()
+        self.link_step = 0
+        self.link_reassign: List[int] = []
 
-    def refresh(self) -> None:
-        """Host copy of the T1 rows of every layer from the device window."""
-        torch.cuda.synchronize(self.cache.device)
-        self.host[0].copy_(self.cache.k_t1)
-        self.host[1].copy_(self.cache.v_t1)
+    def window_bytes(self) -> int:
+        """Device bytes of the two-buffer chunk window."""
+        return self.win.numel() * self.win.element_size()
+
+    def resident_kv_bytes(self) -> int:
+        """Device bytes that hold key/value rows: the T0 pool and the chunk window."""
+        return self.cache.resident_kv_bytes() + self.window_bytes()
+
+    def link_bytes_per_step(self) -> int:
+        """Bytes the last step sent over the host link."""
+        return self.link_step
 
     def reassign(self) -> None:
-        """Tier reassignment and relocation; the T1 rows end in the host copy."""
+        """Tier reassignment with the T1 rows in host memory (one host-synchronous call)."""
         c = self.cache
-        if self.keep_window:
-            c.reassign()
-            self.refresh()
-            return
-        torch.cuda.synchronize(c.device)   # the step's copies have read the host copy
-        c.k_t1 = self.host[0].to(c.device)
-        c.v_t1 = self.host[1].to(c.device)
-        c.reassign()
-        self.refresh()
-        c.k_t1 = c.v_t1 = None
+        tnx = 1 - c.tcur
+        tkv.tkv_assign_tiers(c.batch, c.n, c.max_ctx, c.scores, c.tpolicy, c.tier[c.tcur],
+                             c.tier[tnx], c.counts)
+        lens, link = tkv.tkv_compact_host_t1(
+            c.model, c.batch, c.n, c.max_ctx, c.tier[c.tcur], c.tier[tnx], c.k_t0, c.v_t0,
+            c.t0_pos, c.t0_len, c.cap0, c.t1_pos, c.t1_len, c.cap1, self.store_k, self.store_v,
+            self.t1_host, c.t2_src, c.t2_pos, c.t2_cap, c.t2_codes, c.t2_scales, c.new_lens,
+            c.cws, c.cws_bytes, self.scratch, self.scratch_bytes)
+        self.link_reassign.append(link)
+        c.finish_reassign(lens, tnx)
 
     def t1_rows(self, b: int):
         """Host copies of the T1 rows of sequence b in ascending position order."""
         o1 = self.cache._order(b)[1]
         n = self.cache.t1_len[b]
-        k = k_tiles_to_rows(self.host[0][b], n)
-        v = v_tiles_to_rows(self.host[1][b], n)
+        k = k_tiles_to_rows(self.t1_host[b, :, :, 0], n)
+        v = v_tiles_to_rows(self.t1_host[b, :, :, 1], n)
         return to_host_bits(k)[:, :, o1], to_host_bits(v)[:, :, o1]
 
     def attend(self, q: torch.Tensor) -> None:
-        """Attention of every layer over T0 and the streamed T1 rows, with the fused score
-        update; outputs land in the cache's `out` and `alpha` as with TieredKVCache.attend."""
+        """Attention of every layer over T0 and the streamed T1 rows, with the score update;
+        outputs land in the cache's `out` and `alpha` as with TieredKVCache.attend."""
         c = self.cache
-        tkv.tkv_decode_step_streamed(c.model, c.batch, q, c.k_t0, c.v_t0, c.t0_len, c.cap0,
-                                     self.host, c.t1_len, c.cap1, self.win, self.chunk,
-                                     c.out, c.alpha, c.alpha_stride,
-                                     c.t0_pos, c.t1_pos, c.scores, c.max_ctx, c.ws, c.ws_bytes,
-                                     torch.cuda.current_stream(c.device), self.side,
-                                     self.events, side_stream2=self.side2)
+        self.link_step = tkv.tkv_decode_step_streamed(
+            c.model, c.batch, q, c.k_t0, c.v_t0, c.t0_len, c.cap0, self.t1_host, c.t1_len,
+            c.cap1, self.win, self.chunk, c.out, c.alpha, c.alpha_stride, c.t0_pos, c.t1_pos,
+            c.scores, c.max_ctx, c.ws, c.ws_bytes, torch.cuda.current_stream(c.device), self.side,
+            self.events, side_stream2=self.side2)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              reassign: bool = True) -> bool:
         """One decode step with streamed T1 rows; returns True when it ended with a
-        reassignment (after which the host copy is refreshed)."""
+        reassignment."""
         c = self.cache
         c.append(k_new, v_new)
         self.attend(q)

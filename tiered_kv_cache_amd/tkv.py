@@ -29,7 +29,9 @@ EXPORTED = (
     "tkv_decode_step_streamed", "tkv_decode_step_t2",
     "tkv_append_decode_step_t2", "tkv_update_scores", "tkv_assign_tiers",
     "tkv_compact_workspace_bytes", "tkv_compact", "tkv_quantize_t2",
-    "tkv_t2_update_workspace_bytes", "tkv_t2_update", "tkv_gather_t1", "tkv_timing_enable",
+    "tkv_t2_update_workspace_bytes", "tkv_t2_update", "tkv_gather_t1", "tkv_t0_capacity",
+    "tkv_compact_host_t1_workspace_bytes", "tkv_compact_host_t1_scratch_bytes",
+    "tkv_compact_host_t1", "tkv_timing_enable",
     "tkv_timing_select", "tkv_timing_reset", "tkv_timing_read",
 )
 
@@ -92,11 +94,12 @@ def lib() -> ctypes.CDLL:
                                         _P, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P,
                                         _I, _P, ctypes.c_size_t, _P]),
         "tkv_decode_step_window": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _P, _P, _P,
-                                        _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _I, _P,
+                                        _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _I, _P,
                                         ctypes.c_size_t, _P]),
         "tkv_decode_step_streamed": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _P, _P, _I,
                                           _P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P, _I, _P,
-                                          ctypes.c_size_t, _P, _P, _P, _P]),
+                                          ctypes.c_size_t, _P, _P, _P, _P,
+                                          ctypes.POINTER(ctypes.c_int64)]),
         "tkv_decode_step_t2": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _P, _P, _P, _I,
                                     _P, _P, _P, _I, ctypes.POINTER(tkv_t2_pool), _P, _P, _I,
                                     _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
@@ -117,8 +120,17 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_size_t, _P]),
         "tkv_quantize_t2": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _I, _P, _P, _I, _P,
                                  _P, _I, _I, _P, _P, _P]),
-        "tkv_gather_t1": (_I, [ctypes.POINTER(tkv_model), _P, _P, _I, _P, _I, _P, _P, _I, _P,
-                               _P, _P, _P]),
+        "tkv_gather_t1": (_I, [ctypes.POINTER(tkv_model), _P, _P, _I, _P, _I, _P, _I, _P, _P,
+                               _P]),
+        "tkv_t0_capacity": (_I, [ctypes.POINTER(tkv_policy), _I, _I]),
+        "tkv_compact_host_t1_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(tkv_model),
+                                                                  _I, _I, _I, _I]),
+        "tkv_compact_host_t1_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(tkv_model), _I,
+                                                                _I, _I]),
+        "tkv_compact_host_t1": (_I, [ctypes.POINTER(tkv_model), _I, _P, _I, _P, _P, _P, _P, _P,
+                                     _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P,
+                                     _P, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
+                                     ctypes.POINTER(ctypes.c_int64), _P]),
         "tkv_timing_enable": (_I, [_I]),
         "tkv_timing_select": (_I, [ctypes.c_char_p]),
         "tkv_timing_reset": (_I, []),
@@ -244,24 +256,26 @@ def tkv_append_decode_step(model, batch, k_new, v_new, position, tier, q, k_t0, 
 
 
 def tkv_decode_step_window(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0,
-                           k_t1_win, v_t1_win, t1_len, cap1, out, alpha, alpha_stride,
-                           t0_pos=None, t1_pos=None, scores=None, max_ctx=0, workspace=None,
+                           t1_win, t1_len, cap1, out, alpha, alpha_stride, t0_pos=None,
+                           t1_pos=None, scores=None, max_ctx=0, workspace=None,
                            workspace_bytes=0, stream=None) -> None:
     a, b = _HostInts(t0_len), _HostInts(t1_len)
     _check(lib().tkv_decode_step_window(ctypes.byref(model), batch, layer_begin, layer_end,
                                         _ptr(q), _ptr(k_t0), _ptr(v_t0), a.ptr, cap0,
-                                        _ptr(k_t1_win), _ptr(v_t1_win), b.ptr, cap1, _ptr(out),
-                                        _ptr(alpha), alpha_stride, _ptr(t0_pos), _ptr(t1_pos),
-                                        _ptr(scores), max_ctx, _ptr(workspace), workspace_bytes,
+                                        _ptr(t1_win), b.ptr, cap1, _ptr(out), _ptr(alpha),
+                                        alpha_stride, _ptr(t0_pos), _ptr(t1_pos), _ptr(scores),
+                                        max_ctx, _ptr(workspace), workspace_bytes,
                                         _stream(stream)), "tkv_decode_step_window")
 
 
 def tkv_decode_step_streamed(model, batch, q, k_t0, v_t0, t0_len, cap0, host_t1, t1_len, cap1,
                              win, chunk_layers, out, alpha, alpha_stride, t0_pos, t1_pos,
                              scores, max_ctx, workspace, workspace_bytes, stream, side_stream,
-                             events, side_stream2=None) -> None:
+                             events, side_stream2=None) -> int:
+    """Returns the bytes queued host -> device."""
     a, b = _HostInts(t0_len), _HostInts(t1_len)
     ev = (ctypes.c_void_p * 4)(*[_event(e) for e in events])
+    link = ctypes.c_int64()
     _check(lib().tkv_decode_step_streamed(ctypes.byref(model), batch, _ptr(q), _ptr(k_t0),
                                           _ptr(v_t0), a.ptr, cap0, _ptr(host_t1), b.ptr, cap1,
                                           _ptr(win), chunk_layers, _ptr(out), _ptr(alpha),
@@ -270,8 +284,9 @@ def tkv_decode_step_streamed(model, batch, q, k_t0, v_t0, t0_len, cap0, host_t1,
                                           workspace_bytes, _stream(stream),
                                           _stream(side_stream),
                                           None if side_stream2 is None else _stream(side_stream2),
-                                          ev),
+                                          ev, ctypes.byref(link)),
            "tkv_decode_step_streamed")
+    return link.value
 
 
 class T2Pool:
@@ -367,13 +382,47 @@ def tkv_quantize_t2(model, batch, k_t0, v_t0, cap0, k_t1, v_t1, cap1, src, n_row
                                  _stream(stream)), "tkv_quantize_t2")
 
 
-def tkv_gather_t1(model, host_k, host_v, max_ctx, positions, n_t1, staging_k, staging_v,
-                  cap1, dev_k_t1=None, dev_v_t1=None, side_stream=None, ready=None) -> None:
+def tkv_gather_t1(model, host_k, host_v, max_ctx, positions, n_t1, staging, cap1, dev_t1=None,
+                  side_stream=None, ready=None) -> None:
     p = _HostInts(positions)
     _check(lib().tkv_gather_t1(ctypes.byref(model), _ptr(host_k), _ptr(host_v), max_ctx, p.ptr,
-                               n_t1, _ptr(staging_k), _ptr(staging_v), cap1, _ptr(dev_k_t1),
-                               _ptr(dev_v_t1), _stream(side_stream), _event(ready)),
-           "tkv_gather_t1")
+                               n_t1, _ptr(staging), cap1, _ptr(dev_t1), _stream(side_stream),
+                               _event(ready)), "tkv_gather_t1")
+
+
+def tkv_t0_capacity(policy, n_from, n_to) -> int:
+    cap = lib().tkv_t0_capacity(ctypes.byref(policy), n_from, n_to)
+    if cap < 0:
+        raise TkvError(cap, "tkv_t0_capacity", "bad policy or range")
+    return cap
+
+
+def tkv_compact_host_t1_workspace_bytes(model, batch, max_ctx, cap0, cap1) -> int:
+    return lib().tkv_compact_host_t1_workspace_bytes(ctypes.byref(model), batch, max_ctx, cap0,
+                                                     cap1)
+
+
+def tkv_compact_host_t1_scratch_bytes(model, batch, max_ctx, cap1) -> int:
+    return lib().tkv_compact_host_t1_scratch_bytes(ctypes.byref(model), batch, max_ctx, cap1)
+
+
+def tkv_compact_host_t1(model, batch, ctx_len, max_ctx, tier_prev, tier_next, k_t0, v_t0, t0_pos,
+                        t0_len, cap0, t1_pos, t1_len, cap1, store_k, store_v, t1_host, t2_src,
+                        t2_pos, t2_cap, t2_codes, t2_scales, new_lens, workspace,
+                        workspace_bytes, host_scratch, host_scratch_bytes, stream=None):
+    """Returns (new lengths [B][4] as a NumPy array, bytes that crossed the host link)."""
+    a, b, c = _HostInts(ctx_len), _HostInts(t0_len), _HostInts(t1_len)
+    lens = np.zeros((batch, 4), dtype=np.int32)
+    link = ctypes.c_int64()
+    _check(lib().tkv_compact_host_t1(ctypes.byref(model), batch, a.ptr, max_ctx, _ptr(tier_prev),
+                                     _ptr(tier_next), _ptr(k_t0), _ptr(v_t0), _ptr(t0_pos), b.ptr,
+                                     cap0, _ptr(t1_pos), c.ptr, cap1, _ptr(store_k),
+                                     _ptr(store_v), _ptr(t1_host), _ptr(t2_src), _ptr(t2_pos),
+                                     t2_cap, _ptr(t2_codes), _ptr(t2_scales), _ptr(new_lens),
+                                     lens.ctypes.data, _ptr(workspace), workspace_bytes,
+                                     _ptr(host_scratch), host_scratch_bytes, ctypes.byref(link),
+                                     _stream(stream)), "tkv_compact_host_t1")
+    return lens, link.value
 
 
 def tkv_timing_enable(enable: bool) -> None:
