@@ -165,6 +165,29 @@ tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_
                            hipStream_t stream);
 
 /*
+ * tkv_decode_step_noalloc -- tkv_decode_step for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a 64 MiB array
+ * inside the library, one per GPU, held until the process ends; its device
+ * address is looked up on the first call made with that GPU current (the only
+ * global state of the library besides the benchmark timers; the lookup is
+ * mutex-guarded).  The call allocates nothing.
+ * Arguments, outputs, numerics and errors as for tkv_decode_step without the
+ * workspace; a call whose tkv_decode_workspace_bytes(model, batch, Lr, cap0,
+ * cap1) exceeds 64 MiB is rejected with TKV_ERR_CAPACITY before anything is
+ * queued.  Every call on one GPU uses the same array: calls that overlap on that
+ * GPU (on different streams, or from different threads) race.  The workspace
+ * needs no initial contents, so nothing is cleared between calls.
+ */
+tkv_status tkv_decode_step_noalloc(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                                   int32_t layer_end, const void* q, const void* k_t0,
+                                   const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                                   const void* k_t1, const void* v_t1, const int32_t* t1_len,
+                                   int32_t cap1, float* out, float* alpha, int32_t alpha_stride,
+                                   const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
+                                   int32_t max_ctx, hipStream_t stream);
+
+/*
  * tkv_append_decode_step -- tkv_append followed by tkv_decode_step over all
  * layers, as one pass over the key/value rows: each generated token adds one
  * key/value pair (Enonce du probleme), which enters T0 and is attended in the

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <set>
 #include <string>
 #include <vector>
@@ -506,7 +507,65 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
 
 }  // namespace tkv
 
+namespace tkv {
+
+// Workspace of tkv_decode_step_noalloc: one array per GPU, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device memory:
+// its device address is looked up once per device and used from then on.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device ordinal
+
+// The device address of `scratch` on the current device (looked up on the first call
+// made with that device current).
+static tkv_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  tkv_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(TKV_ERR_HIP, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((st = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address")))
+      return st;
+    if (!p) return fail(TKV_ERR_HIP, "scratch address is null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TKV_OK;
+}
+
+}  // namespace tkv
+
 extern "C" {
+
+tkv_status tkv_decode_step_noalloc(const tkv_model* model, int32_t batch, int32_t layer_begin,
+                                   int32_t layer_end, const void* q, const void* k_t0,
+                                   const void* v_t0, const int32_t* t0_len, int32_t cap0,
+                                   const void* k_t1, const void* v_t1, const int32_t* t1_len,
+                                   int32_t cap1, float* out, float* alpha, int32_t alpha_stride,
+                                   const int32_t* t0_pos, const int32_t* t1_pos, float* scores,
+                                   int32_t max_ctx, hipStream_t stream) {
+  tkv_status st = check_model(model);
+  if (st) return st;
+  if (batch < 0 || layer_begin < 0 || layer_end > model->num_layers || layer_begin >= layer_end ||
+      cap0 < 0 || cap1 < 0)
+    return fail(TKV_ERR_ARG, "bad batch, layer range or capacity");
+  const size_t need = tkv_decode_workspace_bytes(model, batch, layer_end - layer_begin, cap0, cap1);
+  if (need > kNoAllocScratchBytes)
+    return fail(TKV_ERR_CAPACITY, "the call needs " + std::to_string(need) +
+                                      " bytes of workspace; tkv_decode_step_noalloc holds " +
+                                      std::to_string(kNoAllocScratchBytes));
+  if (batch == 0) return TKV_OK;
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws))) return st;
+  return decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0, k_t1,
+                     v_t1, t1_len, cap1, out, alpha, alpha_stride, t0_pos, t1_pos, scores,
+                     max_ctx, ws, kNoAllocScratchBytes, stream, nullptr, nullptr);
+}
 
 tkv_status tkv_decode_step(const tkv_model* model, int32_t batch, int32_t layer_begin,
                            int32_t layer_end, const void* q, const void* k_t0, const void* v_t0,

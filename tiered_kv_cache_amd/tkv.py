@@ -25,7 +25,8 @@ TKV_F32 = 1
 
 EXPORTED = (
     "tkv_abi_version", "tkv_last_error", "tkv_append", "tkv_decode_workspace_bytes",
-    "tkv_decode_step", "tkv_append_decode_step", "tkv_decode_step_window",
+    "tkv_decode_step", "tkv_decode_step_noalloc", "tkv_append_decode_step",
+    "tkv_decode_step_window",
     "tkv_decode_step_streamed", "tkv_decode_step_t2",
     "tkv_append_decode_step_t2", "tkv_update_scores", "tkv_assign_tiers",
     "tkv_compact_workspace_bytes", "tkv_compact", "tkv_quantize_t2",
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         "tkv_decode_step": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _P, _P, _P, _I,
                                  _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _I, _P,
                                  ctypes.c_size_t, _P]),
+        "tkv_decode_step_noalloc": (_I, [ctypes.POINTER(tkv_model), _I, _I, _I, _P, _P, _P, _P,
+                                         _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _I, _P]),
         "tkv_append_decode_step": (_I, [ctypes.POINTER(tkv_model), _I, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P,
                                         _I, _P, ctypes.c_size_t, _P]),
@@ -239,6 +242,18 @@ def tkv_decode_step(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len,
                                  _ptr(t0_pos), _ptr(t1_pos), _ptr(scores), max_ctx,
                                  _ptr(workspace), workspace_bytes, _stream(stream)),
            "tkv_decode_step")
+
+
+def tkv_decode_step_noalloc(model, batch, layer_begin, layer_end, q, k_t0, v_t0, t0_len, cap0,
+                            k_t1, v_t1, t1_len, cap1, out, alpha, alpha_stride, t0_pos=None,
+                            t1_pos=None, scores=None, max_ctx=0, stream=None) -> None:
+    a, b = _HostInts(t0_len), _HostInts(t1_len)
+    _check(lib().tkv_decode_step_noalloc(ctypes.byref(model), batch, layer_begin, layer_end,
+                                         _ptr(q), _ptr(k_t0), _ptr(v_t0), a.ptr, cap0,
+                                         _ptr(k_t1), _ptr(v_t1), b.ptr, cap1, _ptr(out),
+                                         _ptr(alpha), alpha_stride, _ptr(t0_pos), _ptr(t1_pos),
+                                         _ptr(scores), max_ctx, _stream(stream)),
+           "tkv_decode_step_noalloc")
 
 
 def tkv_append_decode_step(model, batch, k_new, v_new, position, tier, q, k_t0, v_t0, t0_len,
