@@ -58,6 +58,11 @@ def parse():
                    help="instead of the bench line: output error against full attention, per "
                         "step, for eviction-only policies and tiered policies that keep the same "
                         "share of the context in HBM (one JSON line)")
+    p.add_argument("--read-ceiling", action="store_true",
+                   help="instead of the bench line: the read bandwidth of the attention kernel's "
+                        "access pattern without its arithmetic (tkv_read_probe) on the bytes of "
+                        "one attention launch of the workload, 512 MB read before each repetition "
+                        "(one JSON line)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one plain 256 MiB read + 256 MiB write elementwise kernel first "
                         "(scale reference for HBM byte counters)")
@@ -262,6 +267,43 @@ def pcie_leg(wl, cache, positions, device_step_s: float) -> dict:
             "h2d_ms": t_h2d * 1e3, "h2d_gbps": bytes_t1 / t_h2d / 1e9 if t_h2d > 0 else None}
 
 
+def read_ceiling(wl, n_att: int, repeats: int = 20) -> dict:
+    """The attention kernel's access pattern without its arithmetic: one wave per SIMD,
+    contiguous per-wave ranges, 16 KB units of 1 KB non-temporal wave loads, over the
+    bytes one attention launch of the workload reads (K/V of n_att rows per layer and
+    KV head, and the logits it writes, counted as reads), 512 MB read before every
+    repetition so the memory-side cache is cold."""
+    import numpy as np
+    import torch
+    from tiered_kv_cache_amd import tkv
+
+    nbytes = attn_partial_bytes(wl, n_att)
+    nbytes = (nbytes + (16 << 10) - 1) // (16 << 10) * (16 << 10)
+    buf = torch.randint(0, 1 << 30, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = 4 * cus
+    sink = torch.zeros(waves, dtype=torch.int32, device="cuda")
+    times = []
+    for _ in range(repeats):
+        flush.sum()
+        tkv.tkv_timing_select(["read_probe"])
+        tkv.tkv_timing_reset()
+        tkv.tkv_timing_enable(True)
+        tkv.tkv_read_probe(buf, nbytes, waves, sink)
+        tkv.tkv_timing_enable(False)
+        torch.cuda.synchronize()
+        ms, _ = tkv.tkv_timing_read("read_probe")
+        times.append(ms * 1e3)
+    tkv.tkv_timing_select(None)
+    us = float(np.median(times))
+    return {"read_ceiling": {"bytes": nbytes, "waves": waves, "median_us": us,
+                             "min_us": float(min(times)), "gbps": nbytes / (us * 1e-6) / 1e9,
+                             "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                             "attended_rows": n_att, "repeats": repeats,
+                             "workload": f"{wl.name}: {wl.description}"}}
+
+
 def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
     """Mechanism-level accuracy of the tiers on synthetic inputs.
 
@@ -354,6 +396,11 @@ def main():
     if args.eviction_curve:
         print(json.dumps(eviction_curve(base.scaled(steps=K, warmup=W))), flush=True)
         return
+    if args.read_ceiling:
+        # attended rows of the tiered 8K chain right after a reassignment (T0 + T1 of 8 256)
+        n_att = sum(budget_counts(base, base.ctx[0] + delta)[:2]) + 1
+        print(json.dumps(read_ceiling(base, n_att)), flush=True)
+        return
     print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
     dw = DeviceWorkload(wl)
     contexts = [st.context() for st in dw.streams]
@@ -384,9 +431,10 @@ def main():
                  "full_cache_kv_bytes": cache.full_cache_bytes(), "cap0": cache.cap0,
                  "cap1": cache.cap1}
         n_att, n_all, re, sampled = [], [], [], []
+        timed = timed_kernels is None or len(timed_kernels) > 0
         tkv.tkv_timing_select(timed_kernels)
         tkv.tkv_timing_reset()
-        tkv.tkv_timing_enable(True)
+        tkv.tkv_timing_enable(timed)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(W + 1, W + K + 1):
@@ -395,7 +443,7 @@ def main():
             n_all.append(sum(cache.n) + wl.batch)
             if flush:
                 flush_buf.sum()
-            if every > 1:
+            if timed and every > 1:
                 on = (k - W - 1) % every == 0
                 tkv.tkv_timing_enable(on)
                 if on:
@@ -451,21 +499,29 @@ def main():
                       "printed", file=sys.stderr, flush=True)
                 sys.exit(3)
 
-    # the measured run: only the reported kernel carries timers
+    # the measured runs carry no kernel timer at all (value); the roofline runs time the
+    # attention kernel on every timed step with events the kernel records itself
     print(f"[bench] warm-up {W} steps, {K} timed steps", file=sys.stderr, flush=True)
     # repeated: the reported figures are the medians over the repetitions
     reps = []
     for _ in range(max(1, args.repeats)):
-        r = run(["attn_partial"], every=8)
+        r = run([])
         check_split(r)
-        reps.append((amortised_elapsed(r), r["kernels"].get("attn_partial", {}).get("avg_us", float("nan")),
-                     r["elapsed"], r["re_alone"]))
+        reps.append((amortised_elapsed(r), r["elapsed"], r["re_alone"]))
         last = r
         del r["cache"]
         torch.cuda.empty_cache()
+    att_reps = []
+    for _ in range(max(1, (args.repeats + 1) // 2)):
+        r = run(["attn_partial"])
+        att_reps.append(r["kernels"].get("attn_partial", {}).get("avg_us", float("nan")))
+        last_att = r
+        del r["cache"]
+        torch.cuda.empty_cache()
     elapsed = float(np.median([x[0] for x in reps]))
-    attn_med = float(np.median([x[1] for x in reps]))
-    n_att_steps, n_steps, re_info, n_att_timed = last["n_att"], last["n_all"], last["re"], last["sampled"]
+    attn_med = float(np.median(att_reps))
+    n_att_steps, n_steps, re_info = last["n_att"], last["n_all"], last["re"]
+    n_att_timed = last_att["sampled"]
     # a second, identical run with every kernel timed (the per-kernel breakdown only)
     print("[bench] breakdown run", file=sys.stderr, flush=True)
     bd = run(None)
@@ -480,9 +536,7 @@ def main():
         re_b = K / delta * reassign_bytes(wl, *last["re_alone_info"])
     alg_bytes = (sum(x["total"] for x in step_b) + re_b) / K
     min_bytes = (sum(x["minimal"] for x in step_b) + re_b) / K
-    attn = dict(last["kernels"].get("attn_partial", {"launches": 1, "avg_us": float("nan"),
-                                                     "total_ms": float("nan")}))
-    attn["avg_us"] = attn_med
+    attn = {"avg_us": attn_med}
     attn_bytes = float(np.mean([attn_partial_bytes(wl, n) for n in n_att_timed]))
     attn_rows = float(np.mean(n_att_timed))
     achieved = attn_bytes / (attn["avg_us"] * 1e-6) / 1e9
@@ -514,7 +568,7 @@ def main():
                    "context_at_that_reassignment": int(sum(st["n_at_reassignment"])),
                    "mean_attended_rows": float(np.mean(n_att_steps)),
                    "reassignments_timed": len(re_info),
-                   "reassignment_timed_alone_ms": (float(np.median([x[3] for x in reps])) * 1e3
+                   "reassignment_timed_alone_ms": (float(np.median([x[2] for x in reps])) * 1e3
                                                    if not re_info else None),
                    "rows_copied_per_reassignment": ([x[4] for x in re_info] if re_info
                                                     else [last["re_alone_info"][4]]),
@@ -524,8 +578,10 @@ def main():
                                    "alone at the next multiple of delta")},
         "repetitions": {"count": len(reps),
                         "steps_per_s": [K / x[0] for x in reps],
-                        "timed_interval_steps_per_s": [K / x[2] for x in reps],
-                        "attn_partial_avg_us": [x[1] for x in reps]},
+                        "timed_interval_steps_per_s": [K / x[1] for x in reps],
+                        "attn_partial_avg_us": att_reps,
+                        "note": "steps_per_s: runs without kernel timers; attn_partial_avg_us: "
+                                "separate runs timing that kernel on every timed step"},
         "roofline": {"bound": "hbm", "kernel": "attn_partial", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic, "bytes_per_launch": attn_bytes,
@@ -550,10 +606,10 @@ def main():
         "kernels": kernels,
         "kernels_sum_us_per_step": (kernel_sum(kernels, K) if bd["re"] else
                                     kernel_sum(kernels, K, 1, delta)),
-        "kernels_note": ("per-kernel averages from a second identical run with every kernel "
+        "kernels_note": ("per-kernel averages from another identical run with every kernel "
                          "timed (events between launches slow that run to "
-                         f"{K / amortised_elapsed(bd):.0f} steps/s); value and roofline come "
-                         "from the run that times attn_partial only, on every 8th step"),
+                         f"{K / amortised_elapsed(bd):.0f} steps/s); value comes from runs with "
+                         "no timers, the roofline from runs timing attn_partial alone"),
     }
     if not args.no_flush_run:
         # a real decode streams the model weights between two visits of a layer, which
@@ -578,7 +634,7 @@ def main():
         del cache
         torch.cuda.empty_cache()
         print("[bench] attended-T2 run", file=sys.stderr, flush=True)
-        tr = run(["attn_partial"], every=8, attend_t2=True)
+        tr = run(["attn_partial"], attend_t2=True)
         cache = tr["cache"]
         a2 = tr["kernels"].get("attn_partial")
         if a2:
@@ -589,7 +645,7 @@ def main():
                 "frac": b2 / (a2["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
                 "mean_t2_rows": float(np.mean([t for _, t in tr["n_att"]])),
                 "note": "T0 u T1 u T2 attended, T2 as int8 code x float32 scale per row "
-                        "(one run, attn_partial timed on every 8th step); not part of value"}
+                        "(one run, attn_partial timed on every timed step); not part of value"}
         del tr
     if not args.no_stream_leg:
         # T1 streamed from pinned host memory every step, layer by layer through a

@@ -590,6 +590,17 @@ tkv_status tkv_gather_t1(const tkv_model* model, const void* host_k, const void*
                          int32_t cap1, void* dev_t1, hipStream_t side_stream, hipEvent_t ready);
 
 /*
+ * tkv_read_probe -- benchmark aid: streams `bytes` of device memory (a multiple of
+ * 16 KB, 16-byte aligned) with the access pattern of the decode-attention kernel
+ * (`waves` waves, one per SIMD when waves = 4 x CUs, each reading one contiguous
+ * range in 16 KB units of 1 KB wave loads, non-temporal) and stores one word per
+ * wave into sink (device, `waves` words).  Timed by the kernel timers as
+ * "read_probe": the read ceiling the attention kernel is measured against.
+ */
+tkv_status tkv_read_probe(const void* buf, size_t bytes, int32_t waves, uint32_t* sink,
+                          hipStream_t stream);
+
+/*
  * Kernel timers for benchmarks.  While enabled, every kernel the library
  * launches is bracketed by HIP events on its own stream; tkv_timing_read
  * synchronises those events and returns the summed milliseconds and launch

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtkv.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["api.cpp", "gather.cpp", "attention.hip", "merge.hip", "tiers.hip", "quant.hip",
-           "t2pool.hip"]
+           "t2pool.hip", "probe.hip"]
 
 ARCH = os.environ.get("TKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -32,7 +32,7 @@ EXPORTED = (
     "tkv_compact_workspace_bytes", "tkv_compact", "tkv_quantize_t2",
     "tkv_t2_update_workspace_bytes", "tkv_t2_update", "tkv_gather_t1", "tkv_t0_capacity",
     "tkv_compact_host_t1_workspace_bytes", "tkv_compact_host_t1_scratch_bytes",
-    "tkv_compact_host_t1", "tkv_timing_enable",
+    "tkv_compact_host_t1", "tkv_read_probe", "tkv_timing_enable",
     "tkv_timing_select", "tkv_timing_reset", "tkv_timing_read",
 )
 
@@ -134,6 +134,7 @@ def lib() -> ctypes.CDLL:
                                      _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P,
                                      _P, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
                                      ctypes.POINTER(ctypes.c_int64), _P]),
+        "tkv_read_probe": (_I, [_P, ctypes.c_size_t, _I, _P, _P]),
         "tkv_timing_enable": (_I, [_I]),
         "tkv_timing_select": (_I, [ctypes.c_char_p]),
         "tkv_timing_reset": (_I, []),
@@ -438,6 +439,11 @@ def tkv_compact_host_t1(model, batch, ctx_len, max_ctx, tier_prev, tier_next, k_
                                      _ptr(host_scratch), host_scratch_bytes, ctypes.byref(link),
                                      _stream(stream)), "tkv_compact_host_t1")
     return lens, link.value
+
+
+def tkv_read_probe(buf, nbytes, waves, sink, stream=None) -> None:
+    _check(lib().tkv_read_probe(_ptr(buf), nbytes, waves, _ptr(sink), _stream(stream)),
+           "tkv_read_probe")
 
 
 def tkv_timing_enable(enable: bool) -> None:
