@@ -1,7 +1,10 @@
 """GPU tier classifier (tkv_assign_tiers) against the oracle's ranking on score arrays built
 to stress it: continuous scores, few distinct values (long runs of ties), all-equal scores,
-signed zeros and subnormals, earlier tier maps with T2/T3 history, lengths from 0 to 33000
-in one ragged batch.  The tier maps and counts must be bit-identical."""
+signed zeros and subnormals, earlier tier maps with T2/T3 history, ragged batches with lengths
+from 0 to 70000.  The kernel keeps a sequence's keys in registers when the launch's longest
+sequence has at most 1024 * {8, 16, 32, 48} positions and streams them from memory above that,
+so each batch below tops out in another of those ranges (at its edge).  The tier maps and counts
+must be bit-identical."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +15,13 @@ from tiered_kv_cache_amd import tkv
 
 pytestmark = pytest.mark.gpu
 
-LENGTHS = [0, 1, 5, 37, 1000, 4097, 8448, 16500, 33000]
+BATCHES = {
+    "le8k": [0, 1, 5, 37, 1000, 4097, 8192],
+    "le16k": [8193, 37, 16384],
+    "le32k": [16385, 1000, 32768],
+    "le48k": [32769, 5, 49152],
+    "streamed": [49153, 0, 70000],
+}
 
 
 def make_scores(rng, n, kind):
@@ -43,15 +52,17 @@ def history(rng, n, pol):
     Policy(32, 64, 16, 0.00, 0.60, 0.30, 8),
     Policy(8, 2, 4000, 0.25, 0.25, 0.25, 8),
 ], ids=["chain", "unprotected", "sinks_gt_prompt", "recent_dominates"])
-def test_assign_tiers_bit_exact(pol):
+@pytest.mark.parametrize("batch", list(BATCHES))
+def test_assign_tiers_bit_exact(pol, batch):
     rng = np.random.default_rng(20261298)
-    B = len(LENGTHS)
-    max_ctx = (max(LENGTHS) + 63) // 64 * 64
+    lengths = [n for n in BATCHES[batch] for _ in range(4)]   # every length with every kind
+    B = len(lengths)
+    max_ctx = (max(lengths) + 63) // 64 * 64
     scores = np.zeros((B, max_ctx), np.float32)
     prev = np.zeros((B, max_ctx), np.uint8)
-    for b, n in enumerate(LENGTHS):
+    for b, n in enumerate(lengths):
         scores[b, :n] = make_scores(rng, n, b % 4)
-        if b % 2:
+        if (b // 4) % 2 == 0 or b % 4 == 1:
             prev[b, :n] = history(rng, n, pol)
     dev = torch.device("cuda")
     s_d = torch.from_numpy(scores).to(dev)
@@ -60,13 +71,13 @@ def test_assign_tiers_bit_exact(pol):
     c_d = torch.zeros((B, 4), dtype=torch.int32, device=dev)
     policy = tkv.make_policy(pol.prompt, pol.sinks, pol.recent, pol.frac_t1, pol.frac_t2,
                              pol.frac_t3, pol.delta)
-    tkv.tkv_assign_tiers(B, LENGTHS, max_ctx, s_d, policy, p_d, n_d, c_d)
+    tkv.tkv_assign_tiers(B, lengths, max_ctx, s_d, policy, p_d, n_d, c_d)
     torch.cuda.synchronize()
     got = n_d.cpu().numpy()
     counts = c_d.cpu().numpy()
-    for b, n in enumerate(LENGTHS):
+    for b, n in enumerate(lengths):
         ref, ref_counts = assign_tiers(scores[b].astype(np.float64), prev[b], n, pol)
         bad = np.nonzero(got[b, :n] != ref[:n])[0]
         assert bad.size == 0, f"n={n} kind={b % 4}: tiers differ at {bad[:8]}"
         assert counts[b].tolist() == list(ref_counts), f"n={n}: counts"
-    say(f"[assign_tiers] {len(LENGTHS)} sequences bit-exact")
+    say(f"[assign_tiers {batch}] {B} sequences bit-exact")

@@ -48,10 +48,28 @@ __device__ __forceinline__ bool in_sel(const Sel& s, uint32_t key, int p) {
   return key < s.T || (key == s.T && p >= s.cut);
 }
 
-// hist[bin] += 1 for every active lane: one LDS atomic per lane.  (Aggregating
-// equal bins of a wave first with ballots costs a serial round per distinct bin,
-// and after the leading digit the candidates spread over many bins.)
+// hist[bin] += 1 for every active lane.  Lanes that share the bin of the first
+// active lane add their count with one atomic (up to kHistPeel such rounds, while
+// a round takes at least a quarter of the wave); the others add one each.  Keys
+// of similar scores share their leading byte, and 64 same-address LDS atomics of
+// one instruction would be serialised; after the leading digit the candidates
+// spread over many bins and the plain atomics do not collide.
+constexpr int kHistPeel = 3;
+
 __device__ __forceinline__ void hist_add(unsigned* hist, unsigned bin, bool active) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int r = 0; r < kHistPeel; ++r) {
+    const uint64_t act = __ballot(active);
+    if (act == 0) return;
+    const int leader = __ffsll((unsigned long long)act) - 1;
+    const unsigned lb = (unsigned)__builtin_amdgcn_readlane((int)bin, leader);
+    const uint64_t same = __ballot(active && bin == lb);
+    const int c = __popcll(same);
+    if (lane == leader) atomicAdd(&hist[lb], (unsigned)c);
+    active = active && bin != lb;
+    if (c < kWave / 4) break;
+  }
   if (active) atomicAdd(&hist[bin], 1u);
 }
 
@@ -281,10 +299,218 @@ __global__ __launch_bounds__(kTierThreads) void assign_tiers_kernel(TierArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// the same selection with every key in registers (n <= 1024 * PPT)
+// ---------------------------------------------------------------------------
+// The positions are cut into chunks of PPT from position 0 and thread t owns chunk
+// ceil(n / PPT) - 1 - t (positions >= n absent): thread 0 holds the highest
+// positions, so a block scan over threads counts what lies above a thread's chunk.  The scores and previous tiers
+// are read once; the keys stay in registers and every per-position condition is a
+// bit mask over the owned positions (bit i: position base + i), so the radix passes
+// touch no memory but the LDS histogram.
+template <int PPT>
+struct Owned {
+  uint32_t key[PPT];
+  int base;  // position of key[0]
+};
+
+// Bit i set for the owned positions that are candidates (mask), have key == T and
+// lie at or above cut: the ties a selection (T, cut) takes.
+template <int PPT>
+__device__ __forceinline__ uint64_t sel_mask(const Owned<PPT>& o, uint64_t cand, const Sel& s) {
+  uint64_t m = 0;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+    m |= (uint64_t)((cand >> i & 1) && in_sel(s, o.key[i], o.base + i)) << i;
+  return m;
+}
+
+// k (block-uniform) least important positions among the owned candidates (bits of
+// cand).  The same digits, counts and tie rule as radix_select.
+template <int PPT>
+__device__ __forceinline__ Sel radix_select_owned(int k, const Owned<PPT>& o, uint64_t cand,
+                                                  unsigned* hist, int* tmp, int* sh) {
+  Sel r;
+  r.T = 0u;
+  r.cut = INT_MAX;
+  if (k <= 0) return r;
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u;
+  int kk = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kTierThreads) hist[i] = 0u;
+    __syncthreads();
+    const uint32_t himask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      hist_add(hist, (o.key[i] >> shift) & 255u, (cand >> i & 1) && (o.key[i] & himask) == prefix);
+    __syncthreads();
+    pick_digit(hist, kk, tmp, sh);
+    prefix |= (uint32_t)sh[0] << shift;
+    kk = sh[1];
+    __syncthreads();
+  }
+  const int ties = (int)hist[prefix & 255u];
+  __syncthreads();
+  if (kk == ties) {  // every candidate with key == prefix is taken
+    r.T = prefix;
+    r.cut = 0;
+    return r;
+  }
+  // kk of the ties are taken: the highest positions
+  uint64_t tie = 0;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) tie |= (uint64_t)((cand >> i & 1) && o.key[i] == prefix) << i;
+  const int cnt = __popcll(tie);
+  int total;
+  const int excl = block_excl_scan(cnt, tmp, &total);
+  if (excl < kk && kk <= excl + cnt) {
+    // the (kk - excl)-th tie counted from the top of this chunk
+    for (int need = kk - excl; need > 1; --need) tie &= ~(1ull << (63 - __clzll(tie)));
+    sh[2] = o.base + 63 - __clzll(tie);
+  }
+  __syncthreads();
+  r.T = prefix;
+  r.cut = sh[2];
+  __syncthreads();
+  return r;
+}
+
+template <int PPT>
+__global__ __launch_bounds__(kTierThreads) void assign_tiers_reg_kernel(TierArgs a) {
+  static_assert(PPT <= 64 && PPT % 16 == 0, "one bit per owned position in a 64-bit mask");
+  __shared__ unsigned hist[256];
+  __shared__ int tmp[kTierThreads / kWave + 1];
+  __shared__ int sh[4];
+  const int tid = threadIdx.x;
+  const int bl = blockIdx.x;
+  const long b = a.b_offset + bl;
+  const int n = a.n[bl];
+  const float* sc = a.scores + b * a.max_ctx;
+  const uint8_t* tp = a.tprev + b * a.max_ctx;
+  uint8_t* tn = a.tnext + b * a.max_ctx;
+  int* counts = a.counts + b * 4;
+  const int prot_lo = a.prot_lo;
+  const int prot_hi = n - a.recent;  // positions >= prot_hi are the recent window
+
+  Owned<PPT> o;
+  const int chunks = (n + PPT - 1) / PPT;
+  o.base = (chunks - 1 - tid) * PPT;  // chunk-aligned: thread 0 owns the top chunk
+  uint32_t tw[PPT / 4];               // previous tiers, four per word
+  const bool aligned = (((uintptr_t)(sc + o.base) | (uintptr_t)(tp + o.base)) & 15) == 0;
+  if (o.base >= 0 && o.base + PPT <= n && aligned) {  // whole chunk: vector loads
+    const uint4* s4 = reinterpret_cast<const uint4*>(sc + o.base);
+    const uint4* t4 = reinterpret_cast<const uint4*>(tp + o.base);
+#pragma unroll
+    for (int i = 0; i < PPT / 4; ++i) {
+      const uint4 v = s4[i];
+      o.key[4 * i] = v.x;
+      o.key[4 * i + 1] = v.y;
+      o.key[4 * i + 2] = v.z;
+      o.key[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < PPT / 16; ++i) {
+      const uint4 v = t4[i];
+      tw[4 * i] = v.x;
+      tw[4 * i + 1] = v.y;
+      tw[4 * i + 2] = v.z;
+      tw[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PPT / 4; ++i) tw[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = o.base + i;
+      const bool in = p >= 0 && p < n;
+      o.key[i] = in ? __float_as_uint(sc[p]) : 0u;
+      tw[i / 4] |= (in ? (uint32_t)tp[p] : 0u) << (8 * (i % 4));
+    }
+  }
+  // masks over the owned positions
+  uint64_t valid = 0, m3 = 0, m2 = 0, m01 = 0, bad = 0, np = 0;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = o.base + i;
+    const uint32_t t = (tw[i / 4] >> (8 * (i % 4))) & 0xFFu;
+    o.key[i] = score_key(__uint_as_float(o.key[i]));
+    const uint64_t bit = 1ull << i;
+    if (p >= 0 && p < n) {
+      valid |= bit;
+      if (t > 3) bad |= bit;
+      if (t == 3) m3 |= bit;
+      if (t == 2) m2 |= bit;
+      if (t <= 1) m01 |= bit;
+      if (p >= prot_lo && p < prot_hi) np |= bit;
+    }
+  }
+  const int cBad = block_sum_i(__popcll(bad), tmp);
+  if (cBad) {
+    if (tid < 4) counts[tid] = -1;
+    return;
+  }
+  const uint64_t pool = np & (m2 | m01);  // non-protected T0/T1/T2
+  const int cE = block_sum_i(__popcll(m3), tmp);
+  const int cT2 = block_sum_i(__popcll(m2), tmp);
+  const int cPool = block_sum_i(__popcll(pool), tmp);
+
+  // 1. eviction from the pool
+  const int e = min(max(a.n3[bl] - cE, 0), cPool);
+  const Sel s1 = radix_select_owned(e, o, pool, hist, tmp, sh);
+  const uint64_t ev = sel_mask(o, pool, s1);
+  const uint64_t live = pool & m01 & ~ev;  // non-protected T0/T1 not just evicted
+  const int cEvT2 = block_sum_i(__popcll(ev & m2), tmp);
+  const int cLive = block_sum_i(__popcll(live), tmp);
+
+  // 2. T2 from live
+  const int survivors = cT2 - cEvT2;
+  const int q = min(max(a.n2[bl] - survivors, 0), cLive);
+  const Sel s2 = radix_select_owned(q, o, live, hist, tmp, sh);
+  const uint64_t to2 = sel_mask(o, live, s2);
+
+  // 3. T1 from what is left of live
+  const int r1 = min(a.n1[bl], cLive - q);
+  const Sel s3 = radix_select_owned(r1, o, live & ~to2, hist, tmp, sh);
+  const uint64_t to1 = sel_mask(o, live & ~to2, s3);
+
+  const uint64_t n3 = (m3 | ev) & valid;
+  const uint64_t n2 = (m2 & ~ev) | to2;
+  const uint64_t n1 = to1;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    if (valid >> i & 1)
+      tn[o.base + i] = (uint8_t)((n3 >> i & 1) ? 3 : (n2 >> i & 1) ? 2 : (n1 >> i & 1) ? 1 : 0);
+  }
+  const int c3 = block_sum_i(__popcll(n3), tmp);
+  const int c2 = block_sum_i(__popcll(n2), tmp);
+  const int c1 = block_sum_i(__popcll(n1), tmp);
+  const int c0 = block_sum_i(__popcll(valid), tmp) - c1 - c2 - c3;
+  if (tid == 0) {
+    counts[0] = c0;
+    counts[1] = c1;
+    counts[2] = c2;
+    counts[3] = c3;
+  }
+}
+
+// Keys in registers when the longest sequence of the launch fits; the kernel that
+// streams them from memory on every pass otherwise.
 void launch_assign_tiers(const TierArgs& a, int nb, hipStream_t s) {
   KernelTimer timer("assign_tiers", s);
-  hipExtLaunchKernelGGL(assign_tiers_kernel, dim3(nb), dim3(kTierThreads), 0, s,
-                        timer.start(), timer.stop(), 0, a);
+  int nmax = 0;
+  for (int i = 0; i < nb; ++i) nmax = max(nmax, a.n[i]);
+  const dim3 grid(nb), block(kTierThreads);
+  if (nmax <= kTierThreads * 16)
+    hipExtLaunchKernelGGL(assign_tiers_reg_kernel<16>, grid, block, 0, s, timer.start(), timer.stop(), 0, a);
+  else if (nmax <= kTierThreads * 32)
+    hipExtLaunchKernelGGL(assign_tiers_reg_kernel<32>, grid, block, 0, s, timer.start(), timer.stop(), 0, a);
+  else if (nmax <= kTierThreads * 48)
+    hipExtLaunchKernelGGL(assign_tiers_reg_kernel<48>, grid, block, 0, s, timer.start(), timer.stop(), 0, a);
+  else if (nmax <= kTierThreads * 64)
+    hipExtLaunchKernelGGL(assign_tiers_reg_kernel<64>, grid, block, 0, s, timer.start(), timer.stop(), 0, a);
+  else
+    hipExtLaunchKernelGGL(assign_tiers_kernel, grid, block, 0, s, timer.start(), timer.stop(), 0, a);
 }
 
 // ---------------------------------------------------------------------------
