@@ -419,7 +419,8 @@ def main():
         rows) pairs.  When the K steps hold no reassignment, the steps continue untimed to
         the next multiple of Delta and that reassignment alone is timed (wall clock
         between two syncs, its kernels under the timers when `timed_kernels` is None)."""
-        cache = dw.make_cache(contexts=contexts, attend_t2=attend_t2, t0_budget=True)
+        cache = dw.make_cache(contexts=contexts, attend_t2=attend_t2, t0_budget=True,
+                              alpha_scratch=True)
         torch.cuda.synchronize()
         for k in range(1, W + 1):
             cache.step(*inputs[k - 1])
@@ -655,7 +656,7 @@ def main():
         del cache
         torch.cuda.empty_cache()
         print("[bench] streamed-T1 run", file=sys.stderr, flush=True)
-        cache = dw.make_cache(contexts=contexts, t0_budget=True)
+        cache = dw.make_cache(contexts=contexts, t0_budget=True, alpha_scratch=True)
         stream = T1Stream(cache, chunk_layers=args.stream_chunk)
         for k in range(1, W + 1):
             stream.step(*inputs[k - 1])

@@ -74,9 +74,15 @@ typedef int32_t tkv_status;
 #define TKV_BF16 0
 #define TKV_F32 1
 
-#define TKV_ABI_VERSION 2
+#define TKV_ABI_VERSION 3
 
-/* Model shape.  softmax_scale <= 0 selects 1/sqrt(head_dim). */
+/* Model shape.  softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * alpha_scratch (0 or 1): with 1 the decode calls use their alpha buffer as
+ * scratch only -- it is left holding the raw base-2 logits, the normalised
+ * weights are never stored -- for callers that need the weights only through the
+ * importance score (Methodologie section 2 consumes them as a per-position sum
+ * over heads and layers, which the fused score update still adds exactly as with
+ * 0).  Each step then writes the weights once (the logits) instead of twice. */
 typedef struct {
   int32_t num_layers;
   int32_t num_q_heads;
@@ -84,6 +90,7 @@ typedef struct {
   int32_t head_dim;
   int32_t kv_dtype; /* TKV_BF16 or TKV_F32 */
   float softmax_scale;
+  int32_t alpha_scratch;
 } tkv_model;
 
 /* Tier policy (Methodologie sections 1 and 4).  The fractions are of the
@@ -142,7 +149,9 @@ size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t
  *              may be null when every t1_len is 0
  * out        : device [B][Lr][Hq][D] float32
  * alpha      : device [B][Lr][Hq][alpha_stride] float32; entry j is the weight
- *              of attended index j (alpha_stride >= t0_len + t1_len)
+ *              of attended index j (alpha_stride >= t0_len + t1_len); with
+ *              model->alpha_scratch = 1 its contents after the call are
+ *              unspecified (scratch)
  * Fused score update (optional: pass scores = null to skip): with t0_pos
  *   [B][cap0], t1_pos [B][cap1] (device slot -> position maps) and scores
  *   device [B][max_ctx] float32, adds to scores[b][pos(j)] the sum over the

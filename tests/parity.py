@@ -157,7 +157,8 @@ def check_reassign_link(streamer, prevs, news, stats):
 
 def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
                  fused_scores: bool = True, fused_append: bool = True,
-                 attend_t2: bool = False, t1_streamed: int = 0, t0_budget: bool = False) -> dict:
+                 attend_t2: bool = False, t1_streamed: int = 0, t0_budget: bool = False,
+                 alpha_scratch: bool = False) -> dict:
     """Every step compared; re-sync of the ranking at each reassignment.
     fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores;
     fused_append=False appends with tkv_append before tkv_decode_step instead of
@@ -165,10 +166,12 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
     (the _t2 entry points and the oracle's attend_t2 mode); t1_streamed > 0 keeps the T1
     rows in host memory and attends chunks of that many layers with them streamed from
     pinned memory (T1Stream), checking the link bytes of every step and reassignment;
-    t0_budget shrinks the T0 pool to its budget after the first reassignment."""
+    t0_budget shrinks the T0 pool to its budget after the first reassignment;
+    alpha_scratch runs the calls that store no weights (alpha is then checked through
+    the scores, which every step compares)."""
     n_steps = n_steps or wl.total_steps
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget)
+    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget, alpha_scratch=alpha_scratch)
     cache.fused_scores = fused_scores
     cap0_start = cache.cap0
     streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
@@ -193,7 +196,8 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
             O, alpha, pos = seq.step(q[b], kn[b], vn[b], reassign=False)
             assert np.array_equal(cache.attended_positions(b), pos), f"attended set, step {k}"
             check_output(out[b], O, stats)
-            check_alpha(cache.alpha_of(b), alpha, stats)
+            if not alpha_scratch:
+                check_alpha(cache.alpha_of(b), alpha, stats)
             check_scores(cache.scores[b, :seq.n].cpu().numpy(), seq.s[:seq.n], stats)
         if k % wl.delta == 0:
             gpu_scores = cache.scores.cpu().numpy()
@@ -241,7 +245,7 @@ class HostStore:
 
 def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=(),
                 label: str = "", byte_seqs=None, attend_t2: bool = False,
-                t1_streamed: int = 0, t0_budget: bool = False) -> dict:
+                t1_streamed: int = 0, t0_budget: bool = False, alpha_scratch: bool = False) -> dict:
     """Full-size run, checked on samples the oracle computes one at a time:
     * O and alpha of the sampled (layer, head) pairs over the GPU's attended set;
     * the whole score increment at `full_inc_steps` (all layers and heads);
@@ -258,7 +262,7 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
     """
     byte_seqs = set(range(wl.batch)) if byte_seqs is None else set(byte_seqs)
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget)
+    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget, alpha_scratch=alpha_scratch)
     streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
     store = HostStore(dw, cache.max_ctx)
     pol = oracle_policy(wl)
@@ -282,7 +286,7 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
             out = cache.out.cpu().numpy()
             for b in range(wl.batch):
                 pos = cache.attended_positions(b)
-                alpha_gpu = cache.alpha_of(b)
+                alpha_gpu = None if alpha_scratch else cache.alpha_of(b)
                 layers = range(wl.layers) if k in full_inc_steps else sorted({l for l, _ in heads})
                 inc = np.zeros(cache.n[b])
                 t2 = set(cache.t2_positions(b).tolist()) if attend_t2 else set()
@@ -300,7 +304,8 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
                         g = h // group
                         O, a = attention(q[b][l][h:h + 1], Kl[g:g + 1], Vl[g:g + 1], scale)
                         check_output(out[b, l, h][None], O, stats)
-                        check_alpha(alpha_gpu[l, h][None], a, stats)
+                        if alpha_gpu is not None:
+                            check_alpha(alpha_gpu[l, h][None], a, stats)
                         inc[pos] += a[0]
                 if k in full_inc_steps:
                     inc /= (wl.layers * wl.q_heads)

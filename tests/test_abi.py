@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(tkv.EXPORTED)
-    assert tkv.tkv_abi_version() == 2
+    assert tkv.tkv_abi_version() == 3
 
 
 def model(**kw):
@@ -70,6 +70,9 @@ def test_model_validation():
     assert status_of(decode, model(kv_dtype=7)) == tkv.TKV_ERR_ARG
     assert status_of(decode, model(q_heads=24, kv_heads=2)) == tkv.TKV_ERR_ARG  # group 12
     assert status_of(decode, model(layers=0)) == tkv.TKV_ERR_ARG
+    bad = model()
+    bad.alpha_scratch = 2
+    assert status_of(decode, bad) == tkv.TKV_ERR_ARG
 
 
 def test_decode_step_validation():

@@ -135,13 +135,23 @@ def test_small_t0_budget_lockstep():
     assert st["reassignments"] == 3 and st["cap0"] < 2048
 
 
+def test_small_alpha_scratch_lockstep():
+    # the calls that keep the weights only for the score update (the alpha buffer is
+    # scratch): output and scores every step, tiers and rows at every reassignment
+    wl = WORKLOADS["small"]
+    st = run_lockstep(wl, t0_budget=True, alpha_scratch=True, label="small_alpha_scratch")
+    assert st["reassignments"] == 3
+
+
 def test_chain8k_full_size_sampled():
-    # the bench's configuration: the T0 pool at its budget after the first reassignment
+    # the bench's configuration: the T0 pool at its budget after the first reassignment,
+    # the weights kept only for the score update (checked as the whole score increment)
     wl = WORKLOADS["chain8k"]
     heads = [(0, 0), (0, 6), (13, 20), (27, 27)]
     st = run_sampled(wl, n_steps=130, sample_steps={1, 63, 64, 65, 100, 128, 129},
-                     heads=heads, full_inc_steps={2, 66}, t0_budget=True)
-    assert st["reassignments"] == 2
+                     heads=heads, full_inc_steps={2, 66, 100, 129}, t0_budget=True,
+                     alpha_scratch=True)
+    assert st["reassignments"] == 2 and st["inc_checked"] == 4
 
 
 def test_batch16_ragged_full_size_sampled():

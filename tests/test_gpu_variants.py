@@ -231,9 +231,11 @@ def test_chain32k_t1_streamed_full_size_sampled():
 
 
 def test_small_t1_streamed_t0_budget_lockstep():
-    # host-resident T1 with the T0 pool moved to its budget after the first reassignment
+    # host-resident T1 with the T0 pool moved to its budget after the first reassignment,
+    # the weights kept only for the score update
     wl = WORKLOADS["small"]
-    st = run_lockstep(wl, t1_streamed=2, t0_budget=True, label="small_t1_streamed_budget")
+    st = run_lockstep(wl, t1_streamed=2, t0_budget=True, alpha_scratch=True,
+                      label="small_t1_streamed_budget")
     assert st["reassignments"] == 3 and st["cap0"] < 2048
 
 

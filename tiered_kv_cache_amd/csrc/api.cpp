@@ -111,6 +111,7 @@ static tkv_status check_model(const tkv_model* m) {
   if (m->kv_dtype != TKV_BF16 && m->kv_dtype != TKV_F32) return fail(TKV_ERR_ARG, "bad kv_dtype");
   if (!(m->softmax_scale == m->softmax_scale) || isinf(m->softmax_scale))
     return fail(TKV_ERR_ARG, "softmax_scale must be finite");
+  if (m->alpha_scratch != 0 && m->alpha_scratch != 1) return fail(TKV_ERR_ARG, "alpha_scratch must be 0 or 1");
   return TKV_OK;
 }
 
@@ -462,6 +463,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     m.ml = ml;
     m.out = out;
     m.alpha = alpha;
+    m.alpha_out = !model->alpha_scratch;
     m.gsum = deferred ? deferred->gsum : (scores ? gsum : nullptr);
     m.alpha_stride = alpha_stride;
     m.gs_stride = (long)wl.gs_stride;

@@ -95,6 +95,7 @@ struct MergeArgs {
   const float* ml;
   float* out;
   float* alpha;
+  int alpha_out;  // 0: alpha holds the logits only, the normalised weights are not stored
   float* gsum;  // [nb][gs_seq_rows][gs_stride] sums of alpha over a group's heads, or null
   long alpha_stride, gs_stride;
   long gs_seq_rows;           // gsum rows per sequence (Lr * Hkv, or L * Hkv for a whole step)

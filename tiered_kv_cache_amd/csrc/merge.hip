@@ -25,8 +25,9 @@
 //       a time.  Every other workgroup owns 1024 consecutive attended slots of
 //       one group: it issues the loads of the G logit rows first, works out
 //       (M, Lambda) of its G heads from the records while those loads are in
-//       flight, then writes alpha and, if scores are kept, the per-slot sum of
-//       alpha over the G heads into a [group][slot] array.
+//       flight, then writes alpha (unless the caller keeps the alpha buffer as
+//       scratch) and, if scores are kept, the per-slot sum of alpha over the G
+//       heads into a [group][slot] array.
 //   score_rows -- per 64 attended slots: the float64 sum over the rows of such
 //       an array (the group sums of the fused step, or a caller's normalised
 //       alpha rows for tkv_update_scores), weighted 1/(num_layers * Hq) and
@@ -219,13 +220,15 @@ __device__ void normalise_chunk(const MergeArgs& a, int cb) {
       y.y = __builtin_amdgcn_exp2f(x[h].y - m) * inv;
       y.z = __builtin_amdgcn_exp2f(x[h].z - m) * inv;
       y.w = __builtin_amdgcn_exp2f(x[h].w - m) * inv;
-      float* p = arow + (long)h * a.alpha_stride;
-      if (full) {
-        st_stream4(p, y);
-      } else {
-        p[0] = y.x;
-        if (j0 + 1 < natt) p[1] = y.y;
-        if (j0 + 2 < natt) p[2] = y.z;
+      if (a.alpha_out) {
+        float* p = arow + (long)h * a.alpha_stride;
+        if (full) {
+          st_stream4(p, y);
+        } else {
+          p[0] = y.x;
+          if (j0 + 1 < natt) p[1] = y.y;
+          if (j0 + 2 < natt) p[2] = y.z;
+        }
       }
       sum.x += y.x;
       sum.y += y.y;

@@ -124,9 +124,12 @@ class TieredKVCache:
 
     def __init__(self, shape: Shape, policy: PolicyCfg, batch: int, max_ctx: int,
                  device: str = "cuda", cap0: Optional[int] = None, cap1: Optional[int] = None,
-                 t2_cap: Optional[int] = None, attend_t2: bool = False, t0_budget: bool = False):
+                 t2_cap: Optional[int] = None, attend_t2: bool = False, t0_budget: bool = False,
+                 alpha_scratch: bool = False):
         """t0_budget: after the first reassignment, move the T0 pool into one sized by the
-        tier budget (tkv_t0_capacity) instead of the whole context."""
+        tier budget (tkv_t0_capacity) instead of the whole context.  alpha_scratch: the
+        decode calls keep the weights only as the score update's input (alpha holds the
+        raw logits afterwards; alpha_of is unavailable)."""
         self.shape = shape
         self.t0_budget = t0_budget
         self.host_t1 = False       # set by T1Stream: T1 rows live in host memory
@@ -144,8 +147,9 @@ class TieredKVCache:
         # the attended T2 pool holds at most as many rows as one reassignment can quantise
         self.cap2 = self.t2_cap if attend_t2 else 0
         self.alpha_stride = _round_up(self.cap0 + self.cap1 + self.cap2, 64)
+        self.alpha_scratch = alpha_scratch
         self.model = tkv.make_model(shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim,
-                                    shape.kv_code)
+                                    shape.kv_code, alpha_scratch=alpha_scratch)
         self.tpolicy = tkv.make_policy(policy.prompt, policy.sinks, policy.recent,
                                        policy.frac_t1, policy.frac_t2, policy.frac_t3,
                                        policy.delta)
@@ -457,6 +461,8 @@ class TieredKVCache:
 
     def alpha_of(self, b: int) -> np.ndarray:
         """alpha [L][Hq][n_att] in attended_positions() order."""
+        if self.alpha_scratch:
+            raise RuntimeError("alpha_scratch: the decode calls store no weights")
         o0, o1, _, _ = self._order(b)
         o2, _ = self.t2_order(b)
         n01 = self.t0_len[b] + self.t1_len[b]

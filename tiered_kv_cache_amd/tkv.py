@@ -46,7 +46,8 @@ class TkvError(RuntimeError):
 class tkv_model(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("kv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("alpha_scratch", ctypes.c_int32)]
 
 
 class tkv_policy(ctypes.Structure):
@@ -204,8 +205,9 @@ def _check(status: int, where: str) -> None:
 
 
 def make_model(layers: int, q_heads: int, kv_heads: int, head_dim: int, kv_dtype: int,
-               softmax_scale: float = 0.0) -> tkv_model:
-    return tkv_model(layers, q_heads, kv_heads, head_dim, kv_dtype, softmax_scale)
+               softmax_scale: float = 0.0, alpha_scratch: bool = False) -> tkv_model:
+    return tkv_model(layers, q_heads, kv_heads, head_dim, kv_dtype, softmax_scale,
+                     1 if alpha_scratch else 0)
 
 
 def make_policy(prompt: int, sinks: int, recent: int, f1: float, f2: float, f3: float,
