@@ -452,6 +452,7 @@ def main():
             if cache.step(*inputs[k - 1]):
                 re.append((sum(cache.n), sum(cache.t0_len), sum(cache.t1_len), sum(cache.t2_new),
                            sum(cache.moved)))
+        issued = time.perf_counter() - t0  # host time to queue the K steps
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         tkv.tkv_timing_enable(False)
@@ -479,7 +480,8 @@ def main():
             if cnt:
                 kernels[name] = {"launches": cnt, "avg_us": ms * 1e3 / cnt, "total_ms": ms}
         tkv.tkv_timing_select(None)
-        return {"cache": cache, "elapsed": elapsed, "n_att": n_att, "n_all": n_all, "re": re,
+        return {"cache": cache, "elapsed": elapsed, "issued": issued, "n_att": n_att,
+                "n_all": n_all, "re": re,
                 "kernels": kernels, "sampled": sampled or n_att, "re_alone": re_alone,
                 "re_alone_info": re_alone_info, "state": state}
 
@@ -508,7 +510,7 @@ def main():
     for _ in range(max(1, args.repeats)):
         r = run([])
         check_split(r)
-        reps.append((amortised_elapsed(r), r["elapsed"], r["re_alone"]))
+        reps.append((amortised_elapsed(r), r["elapsed"], r["re_alone"], r["issued"]))
         last = r
         del r["cache"]
         torch.cuda.empty_cache()
@@ -580,9 +582,12 @@ def main():
         "repetitions": {"count": len(reps),
                         "steps_per_s": [K / x[0] for x in reps],
                         "timed_interval_steps_per_s": [K / x[1] for x in reps],
+                        "host_issue_us_per_step": [x[3] / K * 1e6 for x in reps],
                         "attn_partial_avg_us": att_reps,
                         "note": "steps_per_s: runs without kernel timers; attn_partial_avg_us: "
-                                "separate runs timing that kernel on every timed step"},
+                                "separate runs timing that kernel on every timed step; "
+                                "host_issue_us_per_step: host time to queue a timed step (the "
+                                "GPU is the bound while it stays below the step time)"},
         "roofline": {"bound": "hbm", "kernel": "attn_partial", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic, "bytes_per_launch": attn_bytes,

@@ -44,8 +44,8 @@
 //   attn_partial_valu -- float32 path (plain FMAs); a worker is a workgroup.
 // The records are merged, and the logits normalised into alpha, by the merge
 // kernels (merge.hip).
+#include "attn_args.h"
 #include "common.h"
-#include "kernels.h"
 #include "layout.h"
 
 namespace tkv {
