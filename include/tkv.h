@@ -74,7 +74,7 @@ typedef int32_t tkv_status;
 #define TKV_BF16 0
 #define TKV_F32 1
 
-#define TKV_ABI_VERSION 3
+#define TKV_ABI_VERSION 4
 
 /* Model shape.  softmax_scale <= 0 selects 1/sqrt(head_dim).
  * alpha_scratch (0 or 1): with 1 the decode calls use their alpha buffer as
@@ -82,7 +82,21 @@ typedef int32_t tkv_status;
  * weights are never stored -- for callers that need the weights only through the
  * importance score (Methodologie section 2 consumes them as a per-position sum
  * over heads and layers, which the fused score update still adds exactly as with
- * 0).  Each step then writes the weights once (the logits) instead of twice. */
+ * 0).  Each step then writes the weights once (the logits) instead of twice.
+ *
+ * t0_caps, t1_caps (optional host arrays over the batch of every call, or null):
+ * per-sequence capacities of the T0 pool and of the device T1 window, so that a
+ * batch of sequences of different lengths does not pad every sequence to the
+ * longest one's budget (Importance et revendications section 1: HBM holds only
+ * what the tiers need).  With t0_caps, sequence b's T0 block holds t0_caps[b]
+ * slots per (layer, KV head) (a multiple of 32, at most cap0) and the blocks are
+ * packed in sequence order: sequence b's block starts L * Hkv * (t0_caps[0] + ...
+ * + t0_caps[b-1]) slots of D elements after the start of k_t0 / v_t0, laid out
+ * [L][Hkv][t0_caps[b]][D] tiles.  t1_caps likewise for k_t1 / v_t1 (the device T1
+ * window; not the host-resident T1 of tkv_compact_host_t1 / the streamed calls).
+ * Null: cap0 (cap1) slots for every sequence, [B][L][Hkv][cap][D].  The calls' cap0
+ * / cap1 arguments stay the strides of the slot -> position maps and of the
+ * workspaces; lengths are checked against the per-sequence capacities. */
 typedef struct {
   int32_t num_layers;
   int32_t num_q_heads;
@@ -91,6 +105,8 @@ typedef struct {
   int32_t kv_dtype; /* TKV_BF16 or TKV_F32 */
   float softmax_scale;
   int32_t alpha_scratch;
+  const int32_t* t0_caps;
+  const int32_t* t1_caps;
 } tkv_model;
 
 /* Tier policy (Methodologie sections 1 and 4).  The fractions are of the
@@ -116,7 +132,8 @@ const char* tkv_last_error(void);
  * (Enonce du probleme; Methodologie section 1: the recent window is in T0).
  *
  * k_new, v_new : device [B][L][Hkv][D]
- * k_t0, v_t0   : device T0 pools [B][L][Hkv][cap0][D] tiles; slot t0_len[b]
+ * k_t0, v_t0   : device T0 pools [B][L][Hkv][cap0][D] tiles (or per-sequence
+ *                capacities, tkv_model.t0_caps); slot t0_len[b]
  *                of sequence b is written
  * t0_len       : host [B], current T0 length (the slot written); < cap0
  * t0_pos       : device [B][cap0] slot -> position map; t0_pos[b][t0_len[b]]
@@ -144,7 +161,8 @@ size_t tkv_decode_workspace_bytes(const tkv_model* model, int32_t batch, int32_t
  * score sums (Methodologie section 2).
  *
  * q          : device [B][Lr][Hq][D], Lr = layer_end - layer_begin
- * k_t0, v_t0 : device [B][L][Hkv][cap0][D] tiles; t0_len host [B] (<= cap0)
+ * k_t0, v_t0 : device [B][L][Hkv][cap0][D] tiles (or per-sequence capacities,
+ *              tkv_model.t0_caps); t0_len host [B] (<= the sequence's capacity)
  * k_t1, v_t1 : device [B][L][Hkv][cap1][D] tiles; t1_len host [B] (<= cap1);
  *              may be null when every t1_len is 0
  * out        : device [B][Lr][Hq][D] float32

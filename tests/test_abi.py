@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(tkv.EXPORTED)
-    assert tkv.tkv_abi_version() == 3
+    assert tkv.tkv_abi_version() == 4
 
 
 def model(**kw):

@@ -115,6 +115,54 @@ static tkv_status check_model(const tkv_model* m) {
   return TKV_OK;
 }
 
+// Per-sequence pool capacities (tkv_model.t0_caps / t1_caps, or the call's cap for
+// every sequence).
+static int cap0_of(const tkv_model* m, int b, int cap0) { return m->t0_caps ? m->t0_caps[b] : cap0; }
+static int cap1_of(const tkv_model* m, int b, int cap1) { return m->t1_caps ? m->t1_caps[b] : cap1; }
+
+// The per-sequence capacities of a call over `batch` sequences: multiples of 32, at
+// most the call's cap0 / cap1, and pools of fewer than 2^31 32-slot blocks (t1: the
+// call addresses a device T1 pool through t1_caps).
+static tkv_status check_caps(const tkv_model* m, int batch, int cap0, int cap1, bool t1) {
+  const long per = (long)m->num_layers * m->num_kv_heads;
+  long blk0 = 0, blk1 = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int c0 = cap0_of(m, b, cap0), c1 = t1 ? cap1_of(m, b, cap1) : 0;
+    if (c0 < 0 || c0 % 32 || c0 > cap0 || c1 < 0 || c1 % 32 || c1 > cap1)
+      return fail(TKV_ERR_ARG, "per-sequence capacities must be multiples of 32 within cap0 / cap1");
+    blk0 += per * (c0 / 32);
+    blk1 += per * (c1 / 32);
+  }
+  if (blk0 >= (1L << 31) || blk1 >= (1L << 31))
+    return fail(TKV_ERR_CAPACITY, "a pool of 2^31 or more 32-slot blocks");
+  return TKV_OK;
+}
+
+// Pool table of sequences [b0, b0 + nb): their capacities and the first block of
+// each (the blocks of the sequences before b0 come first).
+static void fill_pool(PoolTable& t, const tkv_model* m, int b0, int nb, int cap0, int cap1) {
+  const long per = (long)m->num_layers * m->num_kv_heads;
+  long s0 = 0, s1 = 0;
+  if (m->t0_caps || m->t1_caps) {
+    for (int b = 0; b < b0; ++b) {
+      s0 += per * (cap0_of(m, b, cap0) / 32);
+      s1 += per * (cap1_of(m, b, cap1) / 32);
+    }
+  } else {
+    s0 = per * (long)b0 * (cap0 / 32);
+    s1 = per * (long)b0 * (cap1 / 32);
+  }
+  for (int i = 0; i < nb; ++i) {
+    const int c0 = cap0_of(m, b0 + i, cap0), c1 = cap1_of(m, b0 + i, cap1);
+    t.blk0[i] = (int)s0;
+    t.cap0[i] = c0;
+    t.blk1[i] = (int)s1;
+    t.cap1[i] = c1;
+    s0 += per * (c0 / 32);
+    s1 += per * (c1 / 32);
+  }
+}
+
 static float scale_of(const tkv_model* m) {
   return m->softmax_scale > 0.f ? m->softmax_scale : 1.0f / sqrtf((float)m->head_dim);
 }
@@ -207,9 +255,11 @@ tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new, 
   if (!k_new || !v_new || !k_t0 || !v_t0 || !t0_len || !t0_pos || !position)
     return fail(TKV_ERR_ARG, "null pointer");
   if (cap0 < 1 || cap0 % 32) return fail(TKV_ERR_ARG, "cap0 must be a positive multiple of 32");
+  if ((st = check_caps(model, batch, cap0, 0, false))) return st;
   for (int b = 0; b < batch; ++b) {
     if (t0_len[b] < 0 || position[b] < 0) return fail(TKV_ERR_ARG, "negative length or position");
-    if (t0_len[b] >= cap0) return fail(TKV_ERR_CAPACITY, "T0 pool full (t0_len >= cap0)");
+    if (t0_len[b] >= cap0_of(model, b, cap0))
+      return fail(TKV_ERR_CAPACITY, "T0 pool full (t0_len >= its capacity)");
     if ((scores || tier) && position[b] >= max_ctx)
       return fail(TKV_ERR_CAPACITY, "position >= max_ctx");
   }
@@ -232,6 +282,7 @@ tkv_status tkv_append(const tkv_model* model, int32_t batch, const void* k_new, 
       a.slot[i] = t0_len[b0 + i];
       a.pos[i] = position[b0 + i];
     }
+    fill_pool(a.pool, model, b0, nb, cap0, 0);
     launch_append(a, model->kv_dtype, model->head_dim, nb, stream);
     if ((st = hip_check(hipGetLastError(), "append launch"))) return st;
   }
@@ -299,10 +350,12 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     return fail(TKV_ERR_ARG, "T2 pool: t2_len is null or cap2 is not a multiple of 32");
   bool any_t1 = false, any_t2 = false;
   const int grow = app ? 1 : 0;  // T0 rows added by the append
+  if ((st = check_caps(model, batch, cap0, cap1, !t1_window))) return st;
   for (int b = 0; b < batch; ++b) {
     const int n2 = t2 ? t2->t2_len[b] : 0;
     if (t0_len[b] < 0 || t1_len[b] < 0 || n2 < 0) return fail(TKV_ERR_ARG, "negative length");
-    if (t0_len[b] + grow > cap0 || t1_len[b] > cap1 || n2 > cap2)
+    if (t0_len[b] + grow > cap0_of(model, b, cap0) ||
+        t1_len[b] > (t1_window ? cap1 : cap1_of(model, b, cap1)) || n2 > cap2)
       return fail(TKV_ERR_CAPACITY, "length > capacity");
     if ((long)t0_len[b] + grow + t1_len[b] + n2 > alpha_stride)
       return fail(TKV_ERR_CAPACITY, "alpha_stride < t0_len + t1_len + t2_len");
@@ -413,6 +466,7 @@ static tkv_status decode_step(const tkv_model* model, int32_t batch, int32_t lay
     a.scale = (float)((double)scale_of(model) * 1.4426950408889634074);
     a.seq.nb = nb;
     a.seq.b_offset = b0;
+    fill_pool(a.pool, model, b0, nb, cap0, cap1);
     MergeArgs m{};
     ScoreArgs sa{};
     long units = 0;
@@ -931,11 +985,12 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
     if (ctx_len[b] < 0 || t0_len[b] < 0 || t1_len[b] < 0)
       return fail(TKV_ERR_ARG, "negative length");
     if (ctx_len[b] > max_ctx) return fail(TKV_ERR_CAPACITY, "ctx_len > max_ctx");
-    if (t0_len[b] > cap0 || t1_len[b] > cap1)
+    if (t0_len[b] > cap0_of(model, b, cap0) || t1_len[b] > cap1_of(model, b, cap1))
       return fail(TKV_ERR_CAPACITY, "length > capacity");
     if ((long)t0_len[b] + t1_len[b] > ctx_len[b])
       return fail(TKV_ERR_STATE, "t0_len + t1_len > ctx_len");
   }
+  if ((st = check_caps(model, batch, cap0, cap1, true))) return st;
   const RelocWorkspace w = reloc_workspace(model, batch, max_ctx, cap0, cap1);
   if (workspace_bytes < w.total) return fail(TKV_ERR_CAPACITY, "workspace too small");
   char* base = (char*)workspace;
@@ -967,6 +1022,8 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
       a.n[i] = ctx_len[b0 + i];
       a.len0[i] = t0_len[b0 + i];
       a.len1[i] = t1_len[b0 + i];
+      a.lim0[i] = cap0_of(model, b0 + i, cap0);
+      a.lim1[i] = cap1_of(model, b0 + i, cap1);
     }
     launch_reloc_scan(a, nb, stream);
     if ((st = hip_check(hipGetLastError(), "reloc_scan launch"))) return st;
@@ -990,6 +1047,7 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
       q.L = model->num_layers;
       q.hkv = model->num_kv_heads;
       q.b_offset = b0;
+      fill_pool(q.pool, model, b0, nb, cap0, cap1);
       launch_quantize(q, model->kv_dtype, model->head_dim, nb, stream);
       if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
     }
@@ -1009,6 +1067,7 @@ tkv_status tkv_compact(const tkv_model* model, int32_t batch, const int32_t* ctx
     mv.lgs = lgs;
     mv.b_offset = b0;
     mv.nb = nb;
+    fill_pool(mv.pool, model, b0, nb, cap0, cap1);
     const int2* lists[3] = {a.staged, a.to_t1, a.to_t0};
     const int strides[3] = {cap1, cap1, cap0};
     const int order[3] = {kMoveStage, kMoveToT1, kMoveToT0};
@@ -1111,10 +1170,12 @@ tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int3
     if (ctx_len[b] < 0 || t0_len[b] < 0 || t1_len[b] < 0)
       return fail(TKV_ERR_ARG, "negative length");
     if (ctx_len[b] > max_ctx) return fail(TKV_ERR_CAPACITY, "ctx_len > max_ctx");
-    if (t0_len[b] > cap0 || t1_len[b] > cap1) return fail(TKV_ERR_CAPACITY, "length > capacity");
+    if (t0_len[b] > cap0_of(model, b, cap0) || t1_len[b] > cap1)
+      return fail(TKV_ERR_CAPACITY, "length > capacity");
     if ((long)t0_len[b] + t1_len[b] > ctx_len[b])
       return fail(TKV_ERR_STATE, "t0_len + t1_len > ctx_len");
   }
+  if ((st = check_caps(model, batch, cap0, cap1, false))) return st;
   const RelocWorkspace w = reloc_workspace(model, batch, max_ctx, cap0, cap1);
   if (workspace_bytes < w.staging) return fail(TKV_ERR_CAPACITY, "workspace too small");
   const HostT1Scratch hs = host_t1_scratch(model, batch, max_ctx, cap1);
@@ -1174,6 +1235,8 @@ tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int3
       a.n[i] = ctx_len[b0 + i];
       a.len0[i] = t0_len[b0 + i];
       a.len1[i] = t1_len[b0 + i];
+      a.lim0[i] = cap0_of(model, b0 + i, cap0);
+      a.lim1[i] = cap1;  // the host window
     }
     launch_reloc_scan(a, nb, stream);
     if ((st = hip_check(hipGetLastError(), "reloc_scan launch"))) return st;
@@ -1194,6 +1257,7 @@ tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int3
       q.L = L;
       q.hkv = hkv;
       q.b_offset = b0;
+      fill_pool(q.pool, model, b0, nb, cap0, 0);
       launch_quantize(q, model->kv_dtype, D, nb, stream);
       if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
     }
@@ -1208,6 +1272,7 @@ tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int3
       mv.lgs = lgs;
       mv.b_offset = b0;
       mv.nb = nb;
+      fill_pool(mv.pool, model, b0, nb, cap0, 0);
       mv.which = kMoveDown;
       mv.list = a.to_t1;
       mv.list_stride = cap1;
@@ -1313,6 +1378,7 @@ tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int3
       q.L = L;
       q.hkv = hkv;
       q.b_offset = b0;
+      fill_pool(q.pool, model, b0, nb, cap0, 0);
       launch_quantize(q, model->kv_dtype, D, nb, stream);
       if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
     }
@@ -1326,6 +1392,7 @@ tkv_status tkv_compact_host_t1(const tkv_model* model, int32_t batch, const int3
     mv.lgs = lgs;
     mv.b_offset = b0;
     mv.nb = nb;
+    fill_pool(mv.pool, model, b0, nb, cap0, 0);
     mv.which = kMoveToT0;
     mv.list = (int2*)(base + w.to_t0);
     mv.list_stride = cap0;
@@ -1370,6 +1437,7 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
   if (n_rows_stride < 1 || cap0 < 0 || cap1 < 0 || cap0 % 32 || cap1 % 32)
     return fail(TKV_ERR_ARG, "bad stride or capacity (cap0, cap1 multiples of 32)");
   if (max_rows > 65535) return fail(TKV_ERR_CAPACITY, "max_rows above 65535");
+  if ((st = check_caps(model, batch, cap0, cap1, true))) return st;
   for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, batch - b0);
     QuantArgs a{};
@@ -1390,6 +1458,7 @@ tkv_status tkv_quantize_t2(const tkv_model* model, int32_t batch, const void* k_
     a.L = model->num_layers;
     a.hkv = model->num_kv_heads;
     a.b_offset = b0;
+    fill_pool(a.pool, model, b0, nb, cap0, cap1);
     launch_quantize(a, model->kv_dtype, model->head_dim, nb, stream);
     if ((st = hip_check(hipGetLastError(), "quantize launch"))) return st;
   }

@@ -322,11 +322,14 @@ __device__ __forceinline__ bf16x8_t widen_codes(const uint4& x) {
                               bf16_pair_of_codes(x.y, 0), bf16_pair_of_codes(x.y, 16)));
 }
 
-// Row index (sequence, layer, KV head) of the unit's group, and its first slot
-// as an element offset inside the segment's storage.
+// Row index (sequence, layer, KV head) of the unit's group in a uniform pool (the
+// T2 pool), and its pool row inside the sequence (layer * Hkv + KV head).
 __device__ __forceinline__ long unit_row(const AttnArgs& a, const Cursor& c) {
   const long b = a.seq.b_offset + c.bl;
   return (b * a.L + a.layer_begin + c.lr) * a.hkv + c.g;
+}
+__device__ __forceinline__ long unit_lg(const AttnArgs& a, const Cursor& c) {
+  return (long)(a.layer_begin + c.lr) * a.hkv + c.g;
 }
 
 // The T1 window of a call may hold every layer of a sequence (t1_L = L,
@@ -343,10 +346,11 @@ __device__ __forceinline__ long unit_base(const AttnArgs& a, const Cursor& c) {
     const long b = a.seq.b_offset + c.bl;
     if (c.seg == 1)
       return ((b * a.t1_L + a.t1_l0 + c.lr) * a.hkv + c.g) * a.t1_rs + (long)c.c0 * D;
-    return unit_row(a, c) * (long)a.cap0 * D + (long)c.c0 * D;
+    return pool_row(a.pool.blk0, a.pool.cap0, c.bl, unit_lg(a, c), D) + (long)c.c0 * D;
   } else {
-    const int cap = c.seg ? a.cap1 : a.cap0;
-    return unit_row(a, c) * (long)cap * D + (long)c.c0 * D;
+    return (c.seg ? pool_row(a.pool.blk1, a.pool.cap1, c.bl, unit_lg(a, c), D)
+                  : pool_row(a.pool.blk0, a.pool.cap0, c.bl, unit_lg(a, c), D)) +
+           (long)c.c0 * D;
   }
 }
 
@@ -433,7 +437,8 @@ __device__ bool find_append(const AttnArgs& a, long p0, long p1, int lane, Appen
     const int lr = lgl / a.hkv, gk = lgl - lr * a.hkv;
     AppendRow x;
     x.row = ((b * a.L + a.layer_begin + lr) * a.hkv + gk) * (long)D;
-    x.blk = x.row * a.cap0 + (long)(slot & ~(kUnitMfma - 1)) * D;
+    x.blk = pool_row(a.pool.blk0, a.pool.cap0, bl, (long)(a.layer_begin + lr) * a.hkv + gk, D) +
+            (long)(slot & ~(kUnitMfma - 1)) * D;
     x.rn = slot & (kUnitMfma - 1);
     x.bl = bl;
     x.lgl = lgl;
@@ -803,13 +808,18 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
       __syncthreads();
     }
     const bool q8 = u.seg == 2;  // 8-bit T2 rows: code x scale
-    const int cap = u.seg == 0 ? a.cap0 : (u.seg == 1 ? a.cap1 : a.cap2);
-    const long lg = (u.b * a.L + a.layer_begin + u.lr) * a.hkv + u.g;
-    const long lg1 = (u.b * a.t1_L + a.t1_l0 + u.lr) * a.hkv + u.g;  // T1 window row
-    const float* Kb = u.seg ? (const float*)a.k1 + lg1 * a.t1_rs : (const float*)a.k0 + lg * cap * D;
-    const float* Vb = u.seg ? (const float*)a.v1 + lg1 * a.t1_rs : (const float*)a.v0 + lg * cap * D;
-    const int8_t* Kc = a.k2 + lg * cap * D;
-    const int8_t* Vc = a.v2 + lg * cap * D;
+    const long lg = (u.b * a.L + a.layer_begin + u.lr) * a.hkv + u.g;  // T2 pool row
+    const long lgs = (long)(a.layer_begin + u.lr) * a.hkv + u.g;       // row in the sequence
+    const int bl = (int)(u.b - a.seq.b_offset);
+    // T1: a window of the call's layers (t1_rs apart), or the T1 pool
+    const long t1o = a.t1_L != a.L || a.t1_l0 != a.layer_begin || a.t1_rs != (long)a.cap1 * D
+                         ? ((u.b * a.t1_L + a.t1_l0 + u.lr) * a.hkv + u.g) * a.t1_rs
+                         : pool_row(a.pool.blk1, a.pool.cap1, bl, lgs, D);
+    const long t0o = pool_row(a.pool.blk0, a.pool.cap0, bl, lgs, D);
+    const float* Kb = u.seg ? (const float*)a.k1 + t1o : (const float*)a.k0 + t0o;
+    const float* Vb = u.seg ? (const float*)a.v1 + t1o : (const float*)a.v0 + t0o;
+    const int8_t* Kc = a.k2 + lg * a.cap2 * D;
+    const int8_t* Vc = a.v2 + lg * a.cap2 * D;
     const int t = u.c0 + tid;
     const bool valid = t < u.c1;
     float s[G];
@@ -838,7 +848,7 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
         }
       }
       if (q8) {  // q.code x key scale
-        const float ksc = a.ks2[lg * cap + t];
+        const float ksc = a.ks2[lg * a.cap2 + t];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) s[hh] *= ksc;
       }
@@ -885,7 +895,7 @@ __global__ __launch_bounds__(256) void attn_partial_valu_kernel(AttnArgs a) {
       const long slot = u.c0 + tt;
       float v0, v1;
       if (q8) {  // code x value scale
-        const float vsc = a.vs2[lg * cap + slot];
+        const float vsc = a.vs2[lg * a.cap2 + slot];
         v0 = (float)Vc[v_off(slot, 2 * dp, D)] * vsc;
         v1 = (float)Vc[v_off(slot, 2 * dp + 1, D)] * vsc;
       } else {

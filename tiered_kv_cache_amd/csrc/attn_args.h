@@ -23,6 +23,23 @@ struct SeqTable {
   int units[kMaxSeqPerLaunch];     // attention: work units per (layer, KV head) group
 };
 
+// Where the T0 pool and T1 window blocks of the sequences of one launch start, in
+// 32-slot blocks of 32 * D elements from the start of the pool, and how many slots
+// each (layer, KV head) row of a sequence holds.  Uniform pools: blk = b * L * Hkv *
+// cap / 32 and cap the same for every sequence; per-sequence capacities pack the
+// sequences' blocks one after the other.
+struct PoolTable {
+  int blk0[kMaxSeqPerLaunch];
+  int cap0[kMaxSeqPerLaunch];
+  int blk1[kMaxSeqPerLaunch];
+  int cap1[kMaxSeqPerLaunch];
+};
+
+// Element offset of slot 0 of pool row lg (= layer * Hkv + KV head) of sequence bl.
+__host__ __device__ inline long pool_row(const int* blk, const int* cap, int bl, long lg, int D) {
+  return ((long)blk[bl] * 32 + lg * (long)cap[bl]) * D;
+}
+
 // Split records of the partial P.V: per record (worker + group) the G heads'
 // D values, stored in the order the matrix-core kernel holds them, so that its
 // stores are whole 64-byte (G <= 4), 128-byte (G <= 8) or 256-byte rows:
@@ -62,6 +79,7 @@ struct AttnArgs {
   int io_L, io_l0;   // q / out / alpha rows: layers they hold per sequence, the call's first
   float scale;       // softmax_scale * log2(e): logits are kept in base 2
   SeqTable seq;
+  PoolTable pool;    // the T0 pool and (unless a window call) the T1 pool rows
   // append fused into the bf16 kernel (kn null: none).  The new row of sequence i
   // sits at T0 slot app_slot[i] (< seq.t0_len[i]); the kernel reads it from kn/vn
   // ([B][L][Hkv][D]), writes it into the pool, and records its position.

@@ -54,6 +54,7 @@ struct AppendArgs {
   int cap0, max_ctx, L, hkv, b_offset;
   int slot[kMaxSeqPerLaunch];
   int pos[kMaxSeqPerLaunch];
+  PoolTable pool;  // T0 rows of the launch's sequences
 };
 
 struct TierArgs {
@@ -96,6 +97,8 @@ struct RelocArgs {
   int n[kMaxSeqPerLaunch];
   int len0[kMaxSeqPerLaunch];
   int len1[kMaxSeqPerLaunch];
+  int lim0[kMaxSeqPerLaunch];  // the sequence's T0 pool capacity (<= cap0)
+  int lim1[kMaxSeqPerLaunch];  // its T1 window capacity (<= cap1)
 };
 
 // kMoveDown (T1 rows in host memory): the rows of the T1-destination list that
@@ -111,6 +114,7 @@ struct MoveArgs {
   const int2* list;   // [B][list_stride]
   const int* cnt;     // [B][4]
   int list_stride, which, cap0, cap1, lgs, b_offset, nb;
+  PoolTable pool;     // T0 pool and T1 window rows of the launch's sequences
 };
 
 struct QuantArgs {
@@ -128,6 +132,7 @@ struct QuantArgs {
   int8_t* codes;
   float* scales;
   int n_rows_stride, max_rows, cap0, cap1, L, hkv, b_offset;
+  PoolTable pool;  // T0 pool and T1 window rows of the launch's sequences
 };
 
 // In-place update of the attended T2 pool after a reassignment: rows whose

@@ -41,10 +41,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
       am = fmaxf(am, fabsf(v[i]));
     }
   } else {
-    const int cap = s >= 0 ? a.cap0 : a.cap1;
     const long slot = s >= 0 ? s : -s - 1;
+    const int bl = blockIdx.z;
     const T* blk = (const T*)(kv ? (s >= 0 ? a.v0 : a.v1) : (s >= 0 ? a.k0 : a.k1)) +
-                   (b * lgs + lg) * cap * D;
+                   (s >= 0 ? pool_row(a.pool.blk0, a.pool.cap0, bl, lg, D)
+                           : pool_row(a.pool.blk1, a.pool.cap1, bl, lg, D));
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int d = lane * PER + i;

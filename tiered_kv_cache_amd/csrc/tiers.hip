@@ -640,7 +640,7 @@ __global__ __launch_bounds__(kTierThreads) void reloc_scan_kernel(RelocArgs a) {
   const int n0 = block_sum_i(cn0, tmp);
   const int n1 = block_sum_i(cn1, tmp);
   const int nt2 = block_sum_i(ct2, tmp);
-  if (bad || cp0 != len0 || cp1 != len1 || n0 > a.cap0 || n1 > a.cap1 || nt2 > a.t2_cap) {
+  if (bad || cp0 != len0 || cp1 != len1 || n0 > a.lim0[bl] || n1 > a.lim1[bl] || nt2 > a.t2_cap) {
     if (tid < 4) lens[tid] = -1;
     if (tid < 4) cnt[tid] = 0;
     return;
@@ -762,11 +762,13 @@ struct RowRef {
 template <typename T, int D>
 __device__ __forceinline__ void move_rows(const MoveArgs& m, long b, int lg, int2 mv, long idx,
                                           RowRef<T>& src, RowRef<T>& dst) {
-  const long g = b * m.lgs + lg;
-  T* p0k = (T*)m.k0 + g * m.cap0 * D;
-  T* p0v = (T*)m.v0 + g * m.cap0 * D;
-  T* p1k = (T*)m.k1 + g * m.cap1 * D;
-  T* p1v = (T*)m.v1 + g * m.cap1 * D;
+  const int bl = (int)(b - m.b_offset);
+  const long o0 = pool_row(m.pool.blk0, m.pool.cap0, bl, lg, D);
+  const long o1 = pool_row(m.pool.blk1, m.pool.cap1, bl, lg, D);
+  T* p0k = (T*)m.k0 + o0;
+  T* p0v = (T*)m.v0 + o0;
+  T* p1k = (T*)m.k1 + o1;
+  T* p1v = (T*)m.v1 + o1;
   if (m.which == kMoveStage) {  // T1 slot -> staging row
     src = {p1k, p1v, (long)(-mv.x - 1)};
     T* r = (T*)m.staging + ((b * m.cap1 + mv.y) * m.lgs + lg) * 2 * D;
@@ -898,8 +900,9 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int pos = a.pos[bl];
   const T* ks = (const T*)a.kn + (b * lgs + lg) * D;
   const T* vs = (const T*)a.vn + (b * lgs + lg) * D;
-  T* kd = (T*)a.k0 + (b * lgs + lg) * a.cap0 * D;
-  T* vd = (T*)a.v0 + (b * lgs + lg) * a.cap0 * D;
+  const long o0 = pool_row(a.pool.blk0, a.pool.cap0, (int)(b - a.b_offset), lg, D);
+  T* kd = (T*)a.k0 + o0;
+  T* vd = (T*)a.v0 + o0;
   for (int d = threadIdx.x; d < D; d += 64) {  // K-tiles / V-tiles storage order
     kd[k_off(slot, d, D)] = ks[d];
     vd[v_off(slot, d, D)] = vs[d];

@@ -47,7 +47,8 @@ class tkv_model(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("alpha_scratch", ctypes.c_int32)]
+                ("alpha_scratch", ctypes.c_int32),
+                ("t0_caps", ctypes.c_void_p), ("t1_caps", ctypes.c_void_p)]
 
 
 class tkv_policy(ctypes.Structure):
@@ -205,9 +206,22 @@ def _check(status: int, where: str) -> None:
 
 
 def make_model(layers: int, q_heads: int, kv_heads: int, head_dim: int, kv_dtype: int,
-               softmax_scale: float = 0.0, alpha_scratch: bool = False) -> tkv_model:
-    return tkv_model(layers, q_heads, kv_heads, head_dim, kv_dtype, softmax_scale,
-                     1 if alpha_scratch else 0)
+               softmax_scale: float = 0.0, alpha_scratch: bool = False,
+               t0_caps=None, t1_caps=None) -> tkv_model:
+    """t0_caps / t1_caps: per-sequence pool capacities (sequences of int, or None); the
+    model keeps its own int32 copies alive (set_caps replaces them)."""
+    m = tkv_model(layers, q_heads, kv_heads, head_dim, kv_dtype, softmax_scale,
+                  1 if alpha_scratch else 0, None, None)
+    set_caps(m, t0_caps, t1_caps)
+    return m
+
+
+def set_caps(m: tkv_model, t0_caps=None, t1_caps=None) -> None:
+    """Per-sequence pool capacities of a model (None: the calls' cap0 / cap1 for all)."""
+    m._caps = [None if c is None else np.ascontiguousarray(np.asarray(c, dtype=np.int32))
+               for c in (t0_caps, t1_caps)]
+    m.t0_caps = None if m._caps[0] is None else m._caps[0].ctypes.data
+    m.t1_caps = None if m._caps[1] is None else m._caps[1].ctypes.data
 
 
 def make_policy(prompt: int, sinks: int, recent: int, f1: float, f2: float, f3: float,
