@@ -253,10 +253,13 @@ def pcie_leg(wl, cache, positions, device_step_s: float) -> dict:
     side = torch.cuda.Stream()
     n1 = len(positions)
     bytes_t1 = 2 * L * Hkv * n1 * D * dev.element_size()
-    t0 = time.perf_counter()
-    tkv.tkv_gather_t1(cache.model, host_k, host_v, max_ctx, positions, n1, stg, cap1, None,
-                      side, None)
-    t_pack = time.perf_counter() - t0
+    packs = []
+    for _ in range(3):  # the first call also starts the host threads and touches the staging
+        t0 = time.perf_counter()
+        tkv.tkv_gather_t1(cache.model, host_k, host_v, max_ctx, positions, n1, stg, cap1, None,
+                          side, None)
+        packs.append(time.perf_counter() - t0)
+    t_pack = float(np.median(packs))
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
     ev0.record(side)
@@ -266,6 +269,7 @@ def pcie_leg(wl, cache, positions, device_step_s: float) -> dict:
     ev1.synchronize()
     t_h2d = ev0.elapsed_time(ev1) / 1e3 / reps
     return {"t1_rows": n1, "t1_bytes": bytes_t1, "pack_ms": t_pack * 1e3,
+            "pack_ms_each": [x * 1e3 for x in packs],
             "pack_gbps": bytes_t1 / t_pack / 1e9 if t_pack > 0 else None,
             "h2d_ms": t_h2d * 1e3, "h2d_gbps": bytes_t1 / t_h2d / 1e9 if t_h2d > 0 else None}
 
@@ -423,7 +427,7 @@ def main():
         the next multiple of Delta and that reassignment alone is timed (wall clock
         between two syncs, its kernels under the timers when `timed_kernels` is None)."""
         cache = dw.make_cache(contexts=contexts, attend_t2=attend_t2, t0_budget=True,
-                              alpha_scratch=True)
+                              alpha_scratch=True, per_sequence=True)
         torch.cuda.synchronize()
         for k in range(1, W + 1):
             cache.step(*inputs[k - 1])
@@ -433,6 +437,8 @@ def main():
                  "n_at_reassignment": [int(x) - (W % delta) for x in cache.n],
                  "resident_kv_bytes": cache.resident_kv_bytes(),
                  "full_cache_kv_bytes": cache.full_cache_bytes(), "cap0": cache.cap0,
+                 "caps0": list(cache.caps0), "caps1": list(cache.caps1),
+                 "alpha_bytes": cache.alpha.numel() * cache.alpha.element_size(),
                  "cap1": cache.cap1}
         n_att, n_all, re, sampled = [], [], [], []
         timed = timed_kernels is None or len(timed_kernels) > 0
@@ -609,9 +615,13 @@ def main():
                          "full_cache_kv_bytes": st["full_cache_kv_bytes"],
                          "ratio": st["resident_kv_bytes"] / st["full_cache_kv_bytes"],
                          "t0_capacity": st["cap0"], "t1_window_capacity": st["cap1"],
+                         "t0_capacity_sum": sum(st["caps0"]),
+                         "t1_window_capacity_sum": sum(st["caps1"]),
+                         "alpha_scratch_bytes": st["alpha_bytes"],
                          "note": "device bytes holding K/V rows after the first "
-                                 "reassignment (T0 pool at its budget, T1 window) against "
-                                 "every row of the context at full precision"},
+                                 "reassignment (each sequence's T0 pool at its budget, its T1 "
+                                 "window) against every row of the context at full precision; "
+                                 "capacities: the largest, and the sum over the sequences"},
         "kernels": kernels,
         "kernels_sum_us_per_step": (kernel_sum(kernels, K) if bd["re"] else
                                     kernel_sum(kernels, K, 1, delta)),
@@ -664,7 +674,8 @@ def main():
         del cache
         torch.cuda.empty_cache()
         print("[bench] streamed-T1 run", file=sys.stderr, flush=True)
-        cache = dw.make_cache(contexts=contexts, t0_budget=True, alpha_scratch=True)
+        cache = dw.make_cache(contexts=contexts, t0_budget=True, alpha_scratch=True,
+                              per_sequence=True)
         stream = T1Stream(cache, chunk_layers=args.stream_chunk)
         for k in range(1, W + 1):
             stream.step(*inputs[k - 1])

@@ -158,7 +158,7 @@ def check_reassign_link(streamer, prevs, news, stats):
 def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
                  fused_scores: bool = True, fused_append: bool = True,
                  attend_t2: bool = False, t1_streamed: int = 0, t0_budget: bool = False,
-                 alpha_scratch: bool = False) -> dict:
+                 alpha_scratch: bool = False, per_sequence: bool = False) -> dict:
     """Every step compared; re-sync of the ranking at each reassignment.
     fused_scores=False adds alpha to the scores with the stand-alone tkv_update_scores;
     fused_append=False appends with tkv_append before tkv_decode_step instead of
@@ -168,10 +168,12 @@ def run_lockstep(wl: Workload, n_steps: int = None, label: str = "",
     pinned memory (T1Stream), checking the link bytes of every step and reassignment;
     t0_budget shrinks the T0 pool to its budget after the first reassignment;
     alpha_scratch runs the calls that store no weights (alpha is then checked through
-    the scores, which every step compares)."""
+    the scores, which every step compares); per_sequence gives every sequence pools of
+    its own capacity (packed one after the other)."""
     n_steps = n_steps or wl.total_steps
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget, alpha_scratch=alpha_scratch)
+    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget, alpha_scratch=alpha_scratch,
+                          per_sequence=per_sequence)
     cache.fused_scores = fused_scores
     cap0_start = cache.cap0
     streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
@@ -245,7 +247,8 @@ class HostStore:
 
 def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=(),
                 label: str = "", byte_seqs=None, attend_t2: bool = False,
-                t1_streamed: int = 0, t0_budget: bool = False, alpha_scratch: bool = False) -> dict:
+                t1_streamed: int = 0, t0_budget: bool = False, alpha_scratch: bool = False,
+                per_sequence: bool = False) -> dict:
     """Full-size run, checked on samples the oracle computes one at a time:
     * O and alpha of the sampled (layer, head) pairs over the GPU's attended set;
     * the whole score increment at `full_inc_steps` (all layers and heads);
@@ -262,7 +265,8 @@ def run_sampled(wl: Workload, n_steps: int, sample_steps, heads, full_inc_steps=
     """
     byte_seqs = set(range(wl.batch)) if byte_seqs is None else set(byte_seqs)
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget, alpha_scratch=alpha_scratch)
+    cache = dw.make_cache(attend_t2=attend_t2, t0_budget=t0_budget, alpha_scratch=alpha_scratch,
+                          per_sequence=per_sequence)
     streamer = T1Stream(cache, chunk_layers=t1_streamed) if t1_streamed else None
     store = HostStore(dw, cache.max_ctx)
     pol = oracle_policy(wl)

@@ -92,6 +92,24 @@ def test_decode_step_validation():
     assert "negative" in msg
 
 
+def test_per_sequence_capacity_validation():
+    # tkv_model.t0_caps / t1_caps: multiples of 32 within cap0 / cap1, and each sequence's
+    # lengths within its own capacities
+    def caps_model(t0, t1):
+        return model(t0_caps=t0, t1_caps=t1)
+    two = dict(batch=2, t0_len=[10, 40], t1_len=[2, 3], cap0=64, cap1=32, alpha_stride=128)
+    assert status_of(decode, caps_model([48, 64], None), **two) == tkv.TKV_ERR_ARG
+    assert status_of(decode, caps_model([32, 96], None), **two) == tkv.TKV_ERR_ARG
+    assert status_of(decode, caps_model(None, [32, 16]), **two) == tkv.TKV_ERR_ARG
+    assert status_of(decode, caps_model([32, 32], None), **two) == tkv.TKV_ERR_CAPACITY  # 40 > 32
+    assert status_of(decode, caps_model([64, 64], [0, 32]), **two) == tkv.TKV_ERR_CAPACITY
+    # the same layout with fitting capacities gets past the checks to the workspace one
+    assert status_of(decode, caps_model([32, 64], [32, 32]), workspace_bytes=16,
+                     **two) == tkv.TKV_ERR_CAPACITY
+    msg = tkv.lib().tkv_last_error().decode()
+    assert "workspace" in msg
+
+
 def append_decode(m, **kw):
     args = dict(batch=1, k_new=FAKE, v_new=FAKE, position=[10], tier=FAKE, q=FAKE, k_t0=FAKE,
                 v_t0=FAKE, t0_len=[10], cap0=32, k_t1=FAKE, v_t1=FAKE, t1_len=[2], cap1=32,

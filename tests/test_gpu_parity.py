@@ -93,6 +93,37 @@ def test_batch70_crosses_the_per_launch_sequence_limit():
     assert st["reassignments"] == 3 * 70
 
 
+@pytest.mark.parametrize("batch", [5, 70], ids=["ragged5", "batch70_two_launches"])
+def test_per_sequence_pools_lockstep(batch):
+    # every sequence's T0 pool and T1 window sized for its own length (tkv_model.t0_caps /
+    # t1_caps, blocks packed sequence after sequence), the T0 pools shrunk to each
+    # sequence's budget after the first reassignment; with 70 sequences the second
+    # launch's sequences start after the first launch's blocks
+    base = WORKLOADS["small"]
+    if batch == 5:
+        wl = base.scaled(name="percap_ragged5_L2_h8kv2_d64", layers=2, head_dim=64, batch=5,
+                         ctx=(130, 700, 257, 1100, 64), warmup=8, steps=16, delta=8, prompt=16,
+                         recent=16, sinks=4, planted=(2, 8, 4, 10, 0), frac_t1=0.4,
+                         frac_t2=0.15, frac_t3=0.05)
+    else:
+        ctx = tuple(int(c) for c in np.random.default_rng(11).integers(33, 400, size=70))
+        wl = base.scaled(name="percap_batch70_L1_h4kv2_d64", layers=1, q_heads=4, kv_heads=2,
+                         head_dim=64, batch=70, ctx=ctx, warmup=4, steps=8, delta=4, prompt=8,
+                         recent=8, sinks=2, planted=(0,) * 70, frac_t1=0.3, frac_t2=0.1,
+                         frac_t3=0.1)
+    st = run_lockstep(wl, per_sequence=True, t0_budget=True, alpha_scratch=batch == 70,
+                      label=wl.name)
+    assert st["reassignments"] == (3 if batch == 5 else 3) * batch
+
+
+def test_per_sequence_pools_fp32():
+    # the float32 path (vector-ALU attention, separate append) with per-sequence pools
+    wl = WORKLOADS["tiny"].scaled(name="percap_tiny3_fp32", batch=3, ctx=(256, 100, 33),
+                                  planted=(0, 0, 0))
+    st = run_lockstep(wl, per_sequence=True, t0_budget=True, label=wl.name)
+    assert st["reassignments"] == 4 * 3
+
+
 def test_empty_sequence_in_batch():
     # one sequence of the batch has no attended token: its output rows are zero and the
     # other sequences are unaffected (one attention call, no append)
@@ -160,6 +191,17 @@ def test_batch16_ragged_full_size_sampled():
     heads = [(0, 0), (11, 13), (27, 27)]
     st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 64, 65, 97, 128},
                      heads=heads, full_inc_steps={2, 70}, byte_seqs={0, 7, 15})
+    assert st["reassignments"] == 2 * 16
+
+
+def test_batch16_per_sequence_pools_full_size_sampled():
+    # the bench's batch configuration: per-sequence pools, T0 at each sequence's budget,
+    # the weights kept only for the score update
+    wl = WORKLOADS["batch16"]
+    heads = [(0, 0), (11, 13), (27, 27)]
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 64, 65, 97, 128},
+                     heads=heads, full_inc_steps={2, 70, 128}, byte_seqs={0, 7, 15},
+                     per_sequence=True, t0_budget=True, alpha_scratch=True)
     assert st["reassignments"] == 2 * 16
 
 

@@ -56,7 +56,7 @@ def test_ragged_batch_attend_t2_lockstep():
                      ctx=(130, 700, 257, 1100, 12, 0), warmup=8, steps=16, delta=8, prompt=16,
                      recent=16, sinks=4, planted=(2, 8, 4, 10, 0, 0), frac_t1=0.3, frac_t2=0.2,
                      frac_t3=0.1)
-    st = run_lockstep(wl, attend_t2=True)
+    st = run_lockstep(wl, attend_t2=True, per_sequence=True)
     assert st["reassignments"] == 3 * 6
 
 
@@ -193,7 +193,7 @@ def test_ragged_batch_t1_streamed_lockstep(chunk):
                      batch=5, ctx=(130, 700, 257, 1100, 12), warmup=8, steps=16, delta=8,
                      prompt=16, recent=16, sinks=4, planted=(2, 8, 4, 10, 0), frac_t1=0.4,
                      frac_t2=0.1, frac_t3=0.1)
-    st = run_lockstep(wl, t1_streamed=chunk)
+    st = run_lockstep(wl, t1_streamed=chunk, per_sequence=chunk == 2, t0_budget=chunk == 2)
     assert st["reassignments"] == 3 * 5
 
 

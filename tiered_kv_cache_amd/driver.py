@@ -125,11 +125,14 @@ class TieredKVCache:
     def __init__(self, shape: Shape, policy: PolicyCfg, batch: int, max_ctx: int,
                  device: str = "cuda", cap0: Optional[int] = None, cap1: Optional[int] = None,
                  t2_cap: Optional[int] = None, attend_t2: bool = False, t0_budget: bool = False,
-                 alpha_scratch: bool = False):
+                 alpha_scratch: bool = False, seq_max_ctx: Optional[List[int]] = None):
         """t0_budget: after the first reassignment, move the T0 pool into one sized by the
         tier budget (tkv_t0_capacity) instead of the whole context.  alpha_scratch: the
         decode calls keep the weights only as the score update's input (alpha holds the
-        raw logits afterwards; alpha_of is unavailable)."""
+        raw logits afterwards; alpha_of is unavailable).  seq_max_ctx: the longest each
+        sequence gets; the T0 pool and the T1 window then give every sequence its own
+        capacity (tkv_model.t0_caps / t1_caps, blocks packed sequence after sequence)
+        instead of the longest sequence's."""
         self.shape = shape
         self.t0_budget = t0_budget
         self.host_t1 = False       # set by T1Stream: T1 rows live in host memory
@@ -144,23 +147,36 @@ class TieredKVCache:
         self.t2_cap = _round_up(t2_cap if t2_cap is not None
                                 else int(math.floor(float(np.float32(policy.frac_t2)) * self.max_ctx)) + 64, 64)
         self.attend_t2 = attend_t2
+        # per-sequence capacities: each sequence's own context bound, and the T1 budget at it
+        self.ragged = seq_max_ctx is not None
+        if self.ragged:
+            if len(seq_max_ctx) != batch:
+                raise ValueError("seq_max_ctx needs one bound per sequence")
+            f1 = float(np.float32(policy.frac_t1))
+            self.seq_max = [_round_up(min(int(x), self.max_ctx), 64) for x in seq_max_ctx]
+            self.caps0 = list(self.seq_max)
+            self.caps1 = [_round_up(int(math.floor(f1 * x)) + 64, 64) for x in self.seq_max]
+            self.cap0 = max(self.caps0)
+            self.cap1 = max(self.caps1)
+        else:
+            self.seq_max = [self.max_ctx] * batch
+            self.caps0 = [self.cap0] * batch
+            self.caps1 = [self.cap1] * batch
         # the attended T2 pool holds at most as many rows as one reassignment can quantise
         self.cap2 = self.t2_cap if attend_t2 else 0
         self.alpha_stride = _round_up(self.cap0 + self.cap1 + self.cap2, 64)
         self.alpha_scratch = alpha_scratch
         self.model = tkv.make_model(shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim,
-                                    shape.kv_code, alpha_scratch=alpha_scratch)
+                                    shape.kv_code, alpha_scratch=alpha_scratch,
+                                    t0_caps=self.caps0 if self.ragged else None,
+                                    t1_caps=self.caps1 if self.ragged else None)
         self.tpolicy = tkv.make_policy(policy.prompt, policy.sinks, policy.recent,
                                        policy.frac_t1, policy.frac_t2, policy.frac_t3,
                                        policy.delta)
         L, Hq, Hkv, D = shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim
         dt, dev, B = shape.torch_dtype, self.device, batch
-        pool0 = (B, L, Hkv, self.cap0, D)
-        pool1 = (B, L, Hkv, self.cap1, D)
-        self.k_t0 = torch.zeros(pool0, dtype=dt, device=dev)
-        self.v_t0 = torch.zeros(pool0, dtype=dt, device=dev)
-        self.k_t1 = torch.zeros(pool1, dtype=dt, device=dev)
-        self.v_t1 = torch.zeros(pool1, dtype=dt, device=dev)
+        self.k_t0, self.v_t0 = self._pool(self.caps0), self._pool(self.caps0)
+        self.k_t1, self.v_t1 = self._pool(self.caps1), self._pool(self.caps1)
         self.t0_pos = torch.zeros((B, self.cap0), dtype=torch.int32, device=dev)
         self.t1_pos = torch.zeros((B, self.cap1), dtype=torch.int32, device=dev)
         self.tier = [torch.zeros((B, self.max_ctx), dtype=torch.uint8, device=dev) for _ in range(2)]
@@ -200,6 +216,26 @@ class TieredKVCache:
         self.fused_scores = True
         self.fused_append = True   # step(): tkv_append_decode_step rather than the two calls
 
+    # ---- pools ---------------------------------------------------------------
+    def _pool(self, caps: List[int]) -> torch.Tensor:
+        """A pool of K or V rows: [B][L][Hkv][cap][D] tiles, or with per-sequence
+        capacities one flat buffer of the sequences' [L][Hkv][cap_b][D] blocks in order."""
+        sh = self.shape
+        L, Hkv, D = sh.layers, sh.kv_heads, sh.head_dim
+        if not self.ragged:
+            return torch.zeros((self.batch, L, Hkv, caps[0], D), dtype=sh.torch_dtype,
+                               device=self.device)
+        return torch.zeros(sum(caps) * L * Hkv * D, dtype=sh.torch_dtype, device=self.device)
+
+    def block(self, pool: torch.Tensor, caps: List[int], b: int) -> torch.Tensor:
+        """Sequence b's [L][Hkv][cap_b][D] block of a pool."""
+        if not self.ragged:
+            return pool[b]
+        sh = self.shape
+        per = sh.layers * sh.kv_heads * sh.head_dim
+        o = sum(caps[:b]) * per
+        return pool[o:o + caps[b] * per].view(sh.layers, sh.kv_heads, caps[b], sh.head_dim)
+
     # ---- views -------------------------------------------------------------
     @property
     def tiers(self):
@@ -216,18 +252,16 @@ class TieredKVCache:
     def load_context(self, b: int, K: np.ndarray, V: np.ndarray) -> None:
         """Initial context of sequence b (all in T0, scores 0): K, V [L][Hkv][n0][D]."""
         n0 = K.shape[2]
-        if n0 > self.cap0:
-            raise ValueError("context longer than the T0 pool")
         n0p = (n0 + 31) // 32 * 32
-        if n0p > self.cap0:
+        if n0p > self.caps0[b]:
             raise ValueError("context longer than the T0 pool")
         shape = (K.shape[0], K.shape[1], n0p, K.shape[3])
         kpad = torch.zeros(shape, dtype=self.shape.torch_dtype, device=self.device)
         vpad = torch.zeros(shape, dtype=self.shape.torch_dtype, device=self.device)
         kpad[:, :, :n0] = to_device(K, self.shape.torch_dtype, self.device)
         vpad[:, :, :n0] = to_device(V, self.shape.torch_dtype, self.device)
-        self.k_t0[b, :, :, :n0p] = k_rows_to_tiles(kpad)
-        self.v_t0[b, :, :, :n0p] = v_rows_to_tiles(vpad)
+        self.block(self.k_t0, self.caps0, b)[:, :, :n0p] = k_rows_to_tiles(kpad)
+        self.block(self.v_t0, self.caps0, b)[:, :, :n0p] = v_rows_to_tiles(vpad)
         self.t0_pos[b, :n0] = torch.arange(n0, dtype=torch.int32, device=self.device)
         self.tier[self.tcur][b].zero_()
         self.scores[b].zero_()
@@ -358,28 +392,43 @@ class TieredKVCache:
         self.tcur = tnx
         self.reassignments += 1
         if self.t0_budget and self.reassignments == 1:
-            cap = tkv.tkv_t0_capacity(self.tpolicy, min(self.n), self.max_ctx)
-            if cap < self.cap0:
-                self.resize_t0(cap)
+            if self.ragged:
+                caps = [min(c, tkv.tkv_t0_capacity(self.tpolicy, n, m))
+                        for c, n, m in zip(self.caps0, self.n, self.seq_max)]
+                if caps != self.caps0:
+                    self.resize_t0(caps)
+            else:
+                cap = tkv.tkv_t0_capacity(self.tpolicy, min(self.n), self.max_ctx)
+                if cap < self.cap0:
+                    self.resize_t0([cap] * self.batch)
 
-    def resize_t0(self, cap0: int) -> None:
-        """Move the T0 pool into one of capacity cap0 (a multiple of 32 that holds every
-        current row): slots [0, t0_len) keep their rows; the weights, the decode and the
-        relocation workspaces follow the new capacity."""
-        if cap0 % 32 or cap0 < _round_up(max(self.t0_len), 32):
-            raise ValueError("the new T0 capacity must be a multiple of 32 holding every row")
-        m = min(self.cap0, _round_up(max(self.t0_len), 32))     # whole 32-slot blocks
+    def resize_t0(self, caps0: List[int]) -> None:
+        """Move the T0 pool into one of per-sequence capacities caps0 (multiples of 32
+        that hold every current row; one value for every sequence unless the cache has
+        per-sequence capacities): slots [0, t0_len) keep their rows; the weights, the
+        decode and the relocation workspaces follow the new capacity."""
+        if not self.ragged and len(set(caps0)) != 1:
+            raise ValueError("one T0 capacity for every sequence")
+        for c, n in zip(caps0, self.t0_len):
+            if c % 32 or c < _round_up(n, 32):
+                raise ValueError("each new T0 capacity must be a multiple of 32 holding its rows")
         torch.cuda.synchronize(self.device)
-        B, L, Hkv, D = self.batch, self.shape.layers, self.shape.kv_heads, self.shape.head_dim
-        dt = self.shape.torch_dtype
-        k = torch.empty((B, L, Hkv, cap0, D), dtype=dt, device=self.device)
-        v = torch.empty_like(k)
-        k[:, :, :, :m] = self.k_t0[:, :, :, :m]
-        v[:, :, :, :m] = self.v_t0[:, :, :, :m]
+        B, L = self.batch, self.shape.layers
+        old_k, old_v, old_caps = self.k_t0, self.v_t0, self.caps0
+        self.caps0 = list(caps0)
+        k, v = self._pool(self.caps0), self._pool(self.caps0)
+        cap0 = max(self.caps0)
         pos = torch.zeros((B, cap0), dtype=torch.int32, device=self.device)
-        pos[:, :m] = self.t0_pos[:, :m]
+        for b in range(B):
+            m = min(old_caps[b], _round_up(self.t0_len[b], 32))   # whole 32-slot blocks
+            self.block(k, self.caps0, b)[:, :, :m] = self.block(old_k, old_caps, b)[:, :, :m]
+            self.block(v, self.caps0, b)[:, :, :m] = self.block(old_v, old_caps, b)[:, :, :m]
+            pos[b, :m] = self.t0_pos[b, :m]
+        del old_k, old_v
         self.k_t0, self.v_t0, self.t0_pos = k, v, pos
         self.cap0 = cap0
+        tkv.set_caps(self.model, self.caps0 if self.ragged else None,
+                     self.caps1 if self.ragged else None)
         self.alpha_stride = _round_up(self.cap0 + self.cap1 + self.cap2, 64)
         self.alpha = torch.zeros((B, L, self.shape.q_heads, self.alpha_stride),
                                  dtype=torch.float32, device=self.device)
@@ -449,15 +498,15 @@ class TieredKVCache:
         position order: K, V [L][Hkv][n][D]."""
         o0 = self._order(b)[0]
         n = self.t0_len[b]
-        return (to_host_bits(k_tiles_to_rows(self.k_t0[b], n))[:, :, o0],
-                to_host_bits(v_tiles_to_rows(self.v_t0[b], n))[:, :, o0])
+        return (to_host_bits(k_tiles_to_rows(self.block(self.k_t0, self.caps0, b), n))[:, :, o0],
+                to_host_bits(v_tiles_to_rows(self.block(self.v_t0, self.caps0, b), n))[:, :, o0])
 
     def t1_rows(self, b: int):
         """Host copies of the T1 rows of sequence b in ascending position order."""
         o1 = self._order(b)[1]
         n = self.t1_len[b]
-        return (to_host_bits(k_tiles_to_rows(self.k_t1[b], n))[:, :, o1],
-                to_host_bits(v_tiles_to_rows(self.v_t1[b], n))[:, :, o1])
+        return (to_host_bits(k_tiles_to_rows(self.block(self.k_t1, self.caps1, b), n))[:, :, o1],
+                to_host_bits(v_tiles_to_rows(self.block(self.v_t1, self.caps1, b), n))[:, :, o1])
 
     def alpha_of(self, b: int) -> np.ndarray:
         """alpha [L][Hq][n_att] in attended_positions() order."""

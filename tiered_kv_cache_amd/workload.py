@@ -29,10 +29,14 @@ class DeviceWorkload:
         self.streams = [SequenceStream(wl, b) for b in range(wl.batch)]
         self.dtype = shape_of(wl).torch_dtype
 
-    def make_cache(self, contexts=None, **kw) -> TieredKVCache:
+    def make_cache(self, contexts=None, per_sequence: bool = False, **kw) -> TieredKVCache:
         """A cache holding every sequence's initial context (regenerated unless
-        `contexts`, a list of (K, V) host arrays per sequence, is given)."""
+        `contexts`, a list of (K, V) host arrays per sequence, is given).  per_sequence:
+        pools sized for each sequence's own longest length (its context plus the
+        workload's steps) rather than the longest sequence's."""
         wl = self.wl
+        if per_sequence:
+            kw["seq_max_ctx"] = [st.n0 + wl.total_steps + 1 for st in self.streams]
         cache = TieredKVCache(shape_of(wl), policy_of(wl), wl.batch, wl.max_ctx,
                               device=str(self.device), **kw)
         for b, st in enumerate(self.streams):
