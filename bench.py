@@ -416,18 +416,20 @@ def main():
     flush_buf = None
     re_kernels = "assign_tiers,reloc_scan,quantize_t2,reloc_stage,reloc_to_t1,reloc_to_t0,t2_scan,t2_move"
 
-    def run(timed_kernels, every=1, flush=False, attend_t2=False):
+    def run(timed_kernels, every=1, flush=False, attend_t2=False, alpha_scratch=False):
         """Fresh cache, W warm-up steps (at least Delta: the first reassignment is behind
         them), then exactly K steps between two syncs with the kernel timers on for
         `timed_kernels` (None = all) on every `every`-th step (each pair of events adds a
         few microseconds around the launch it brackets).  With `flush`, a 512 MB buffer is
         read before every step (outside the kernel timers).  With `attend_t2`, the 8-bit
         T2 rows are attended too; the attended counts are then (full-precision rows, T2
-        rows) pairs.  When the K steps hold no reassignment, the steps continue untimed to
-        the next multiple of Delta and that reassignment alone is timed (wall clock
-        between two syncs, its kernels under the timers when `timed_kernels` is None)."""
+        rows) pairs.  With `alpha_scratch`, the decode calls store no normalised weights
+        (they still enter the scores).  When the K steps hold no reassignment, the steps
+        continue untimed to the next multiple of Delta and that reassignment alone is timed
+        (wall clock between two syncs, its kernels under the timers when `timed_kernels`
+        is None)."""
         cache = dw.make_cache(contexts=contexts, attend_t2=attend_t2, t0_budget=True,
-                              alpha_scratch=True, per_sequence=True)
+                              alpha_scratch=alpha_scratch, per_sequence=True)
         torch.cuda.synchronize()
         for k in range(1, W + 1):
             cache.step(*inputs[k - 1])
@@ -648,6 +650,18 @@ def main():
                               "note": "512 MB read before every step (memory-side cache "
                                       "cold, as after a model's weight stream)"}
         del flush_buf, fr
+    # the same steps with the weights kept only for the score update (tkv_model.alpha_scratch):
+    # what a caller that never reads alpha saves; not the headline, which stores alpha
+    print("[bench] weights-as-scratch run", file=sys.stderr, flush=True)
+    sr = [run([], alpha_scratch=True) for _ in range(max(1, (args.repeats + 1) // 2))]
+    out["alpha_scratch"] = {
+        "steps_per_s": float(np.median([K / amortised_elapsed(r) for r in sr])),
+        "note": "normalised weights not stored (tkv_model.alpha_scratch = 1); the scores, "
+                "outputs and tiers are the same; not part of value"}
+    for r in sr:
+        del r["cache"]
+    del sr
+    torch.cuda.empty_cache()
     if not args.no_t2_leg:
         # the variant that attends the 8-bit T2 rows after T1: same inputs and policy
         del cache
@@ -674,8 +688,7 @@ def main():
         del cache
         torch.cuda.empty_cache()
         print("[bench] streamed-T1 run", file=sys.stderr, flush=True)
-        cache = dw.make_cache(contexts=contexts, t0_budget=True, alpha_scratch=True,
-                              per_sequence=True)
+        cache = dw.make_cache(contexts=contexts, t0_budget=True, per_sequence=True)
         stream = T1Stream(cache, chunk_layers=args.stream_chunk)
         for k in range(1, W + 1):
             stream.step(*inputs[k - 1])

@@ -175,14 +175,24 @@ def test_small_alpha_scratch_lockstep():
 
 
 def test_chain8k_full_size_sampled():
-    # the bench's configuration: the T0 pool at its budget after the first reassignment,
-    # the weights kept only for the score update (checked as the whole score increment)
+    # the bench's configuration: per-sequence pools, the T0 pool at its budget after the
+    # first reassignment, the normalised weights stored
     wl = WORKLOADS["chain8k"]
     heads = [(0, 0), (0, 6), (13, 20), (27, 27)]
     st = run_sampled(wl, n_steps=130, sample_steps={1, 63, 64, 65, 100, 128, 129},
                      heads=heads, full_inc_steps={2, 66, 100, 129}, t0_budget=True,
-                     alpha_scratch=True)
+                     per_sequence=True)
     assert st["reassignments"] == 2 and st["inc_checked"] == 4
+
+
+def test_chain8k_alpha_scratch_full_size_sampled():
+    # the same with the weights kept only for the score update (the bench's
+    # alpha_scratch leg): outputs and the whole score increment at full size
+    wl = WORKLOADS["chain8k"]
+    st = run_sampled(wl, n_steps=70, sample_steps={1, 65, 70}, heads=[(0, 0), (27, 27)],
+                     full_inc_steps={66, 70}, t0_budget=True, per_sequence=True,
+                     alpha_scratch=True)
+    assert st["reassignments"] == 1 and st["inc_checked"] == 2
 
 
 def test_batch16_ragged_full_size_sampled():
@@ -195,13 +205,12 @@ def test_batch16_ragged_full_size_sampled():
 
 
 def test_batch16_per_sequence_pools_full_size_sampled():
-    # the bench's batch configuration: per-sequence pools, T0 at each sequence's budget,
-    # the weights kept only for the score update
+    # the bench's batch configuration: per-sequence pools, T0 at each sequence's budget
     wl = WORKLOADS["batch16"]
     heads = [(0, 0), (11, 13), (27, 27)]
     st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 64, 65, 97, 128},
                      heads=heads, full_inc_steps={2, 70, 128}, byte_seqs={0, 7, 15},
-                     per_sequence=True, t0_budget=True, alpha_scratch=True)
+                     per_sequence=True, t0_budget=True)
     assert st["reassignments"] == 2 * 16
 
 
