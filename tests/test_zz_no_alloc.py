@@ -3,7 +3,8 @@ allocate) against tkv_decode_step with a caller workspace, through the C ABI: th
 kernels on the same inputs give the same bits (output, weights, scores).  Two calls in a
 row, the second with a smaller input, so the second runs on the scratch contents the
 first left behind; then a call whose workspace would exceed the library's array is
-rejected before anything is queued."""
+rejected before anything is queued.  The first call's two sequences have pools of their
+own capacities (tkv_model.t0_caps / t1_caps)."""
 import pytest
 import torch
 
@@ -15,9 +16,9 @@ from tiered_kv_cache_amd.workload import DeviceWorkload
 pytestmark = pytest.mark.gpu
 
 
-def one_call(wl):
+def one_call(wl, per_sequence=False):
     dw = DeviceWorkload(wl)
-    cache = dw.make_cache()
+    cache = dw.make_cache(per_sequence=per_sequence)
     cache.reassign()                       # T0 and T1 both populated
     qd, _, _ = dw.device_step(1)
     B = wl.batch
@@ -49,7 +50,7 @@ def test_noalloc_matches_the_workspace_call_twice():
                                     planted=(8, 6), warmup=0, steps=1, delta=1)
     small = WORKLOADS["small"].scaled(name="noalloc_small", layers=2, batch=1, ctx=(300,),
                                       planted=(2,), warmup=0, steps=1, delta=1)
-    n1 = one_call(big)
+    n1 = one_call(big, per_sequence=True)
     n2 = one_call(small)
     assert n2 < n1
     say(f"[noalloc] identical bits on two calls ({n1} then {n2} attended rows)")
