@@ -31,7 +31,10 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(tkv.EXPORTED)
-    assert tkv.tkv_abi_version() == 4
+    assert tkv.tkv_abi_version() == 4 == tkv.ABI_VERSION
+    with open(os.path.join(ROOT, "include", "tkv.h")) as f:
+        header = re.search(r"#define TKV_ABI_VERSION (\d+)", f.read())
+    assert header and int(header.group(1)) == tkv.ABI_VERSION
 
 
 def model(**kw):

@@ -22,6 +22,8 @@ TKV_ERR_STATE = -3
 TKV_ERR_HIP = -4
 TKV_BF16 = 0
 TKV_F32 = 1
+# the TKV_ABI_VERSION of include/tkv.h these structures and signatures follow
+ABI_VERSION = 4
 
 EXPORTED = (
     "tkv_abi_version", "tkv_last_error", "tkv_append", "tkv_decode_workspace_bytes",
@@ -147,6 +149,10 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.restype = res
         f.argtypes = args
+    found = L.tkv_abi_version()
+    if found != ABI_VERSION:
+        raise ImportError(f"{_LIB_PATH} has ABI version {found}, this binding expects "
+                          f"{ABI_VERSION}: rebuild it with `python -m tiered_kv_cache_amd.build`")
     _lib = L
     return L
 
