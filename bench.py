@@ -63,6 +63,9 @@ def parse():
                         "access pattern without its arithmetic (tkv_read_probe) on the bytes of "
                         "one attention launch of the workload, 512 MB read before each repetition "
                         "(one JSON line)")
+    p.add_argument("--read-ceiling-sweep", action="store_true",
+                   help="with --read-ceiling (implied): also the read probe at 0.5 to 8 waves "
+                        "per SIMD over the launch's bytes and four times them (a second JSON line)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one plain 256 MiB read + 256 MiB write elementwise kernel first "
                         "(scale reference for HBM byte counters)")
@@ -311,6 +314,48 @@ def read_ceiling(wl, n_att: int, repeats: int = 20) -> dict:
                              "workload": f"{wl.name}: {wl.description}"}}
 
 
+def read_ceiling_sweep(wl, n_att: int, repeats: int = 10) -> dict:
+    """The read probe over the launch's bytes and four times them, with 0.5 to 8 waves per
+    SIMD: whether the one-wave-per-SIMD figure is the chip's streaming rate or an artefact of
+    the geometry, and what a launch's fixed ramp and tail cost at this size."""
+    import numpy as np
+    import torch
+    from tiered_kv_cache_amd import tkv
+
+    base = attn_partial_bytes(wl, n_att)
+    base = (base + (16 << 10) - 1) // (16 << 10) * (16 << 10)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = []
+    for scale in (1, 4):
+        nbytes = base * scale
+        buf = torch.randint(0, 1 << 30, (nbytes // 4,), dtype=torch.int32, device="cuda")
+        for per_simd in (0.5, 1, 2, 4, 8):
+            waves = int(4 * cus * per_simd)
+            sink = torch.zeros(waves, dtype=torch.int32, device="cuda")
+            times = []
+            for _ in range(repeats):
+                flush.sum()
+                tkv.tkv_timing_select(["read_probe"])
+                tkv.tkv_timing_reset()
+                tkv.tkv_timing_enable(True)
+                tkv.tkv_read_probe(buf, nbytes, waves, sink)
+                tkv.tkv_timing_enable(False)
+                torch.cuda.synchronize()
+                ms, _ = tkv.tkv_timing_read("read_probe")
+                times.append(ms * 1e3)
+            us = float(np.median(times))
+            rows.append({"bytes": nbytes, "waves": waves, "waves_per_simd": per_simd,
+                         "median_us": us, "gbps": nbytes / (us * 1e-6) / 1e9,
+                         "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS})
+            print(f"[bench] read probe {nbytes / 1e6:.1f} MB, {waves} waves: {us:.1f} us",
+                  file=sys.stderr, flush=True)
+        del buf
+    tkv.tkv_timing_select(None)
+    return {"read_ceiling_sweep": {"rows": rows, "repeats": repeats, "attended_rows": n_att,
+                                   "workload": f"{wl.name}: {wl.description}"}}
+
+
 def eviction_curve(wl, shares=(0.05, 0.10, 0.20, 0.30, 0.50)) -> dict:
     """Mechanism-level accuracy of the tiers on synthetic inputs.
 
@@ -403,10 +448,12 @@ def main():
     if args.eviction_curve:
         print(json.dumps(eviction_curve(base.scaled(steps=K, warmup=W))), flush=True)
         return
-    if args.read_ceiling:
+    if args.read_ceiling or args.read_ceiling_sweep:
         # attended rows of the tiered 8K chain right after a reassignment (T0 + T1 of 8 256)
         n_att = sum(budget_counts(base, base.ctx[0] + delta)[:2]) + 1
         print(json.dumps(read_ceiling(base, n_att)), flush=True)
+        if args.read_ceiling_sweep:
+            print(json.dumps(read_ceiling_sweep(base, n_att)), flush=True)
         return
     print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
     dw = DeviceWorkload(wl)
