@@ -65,7 +65,8 @@ def parse():
                         "(one JSON line)")
     p.add_argument("--read-ceiling-sweep", action="store_true",
                    help="with --read-ceiling (implied): also the read probe at 0.5 to 8 waves "
-                        "per SIMD over the launch's bytes and four times them (a second JSON line)")
+                        "per SIMD over the launch's bytes, four and sixteen times them (a second "
+                        "JSON line)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one plain 256 MiB read + 256 MiB write elementwise kernel first "
                         "(scale reference for HBM byte counters)")
@@ -315,8 +316,8 @@ def read_ceiling(wl, n_att: int, repeats: int = 20) -> dict:
 
 
 def read_ceiling_sweep(wl, n_att: int, repeats: int = 10) -> dict:
-    """The read probe over the launch's bytes and four times them, with 0.5 to 8 waves per
-    SIMD: whether the one-wave-per-SIMD figure is the chip's streaming rate or an artefact of
+    """The read probe over the launch's bytes, four and sixteen times them, with 0.5 to 8
+    waves per SIMD: whether the one-wave-per-SIMD figure is the chip's streaming rate or an artefact of
     the geometry, and what a launch's fixed ramp and tail cost at this size."""
     import numpy as np
     import torch
@@ -327,7 +328,7 @@ def read_ceiling_sweep(wl, n_att: int, repeats: int = 10) -> dict:
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rows = []
-    for scale in (1, 4):
+    for scale in (1, 4, 16):
         nbytes = base * scale
         buf = torch.randint(0, 1 << 30, (nbytes // 4,), dtype=torch.int32, device="cuda")
         for per_simd in (0.5, 1, 2, 4, 8):
