@@ -272,15 +272,37 @@ __device__ __forceinline__ void flush_record(const AttnArgs& a, long worker, int
   }
 }
 
-// Write every staged unit: 2 heads x 32 tokens per wave store.
+// Write every staged unit: 2 heads x 32 tokens per wave store.  Units go in
+// batches of kFlushBatch whose LDS reads are all issued before the first store
+// needs one: a store per LDS round trip would leave every wave ~5 round trips
+// per unit at the end of the launch, when nothing else hides them.
+constexpr int kFlushBatch = 8;
+
 __device__ __forceinline__ void flush_stage(const AttnArgs& a, int lane, int G, Stage& sg) {
-  for (int u = 0; u < sg.n; ++u) {
-    const long dst = sg.dst[u];
-    const int n = sg.count[u];
-    const float* src = sg.buf + u * G * 32;
-    for (int hh = lane >> 5; hh < G; hh += 2) {
-      const int t = lane & 31;
-      if (t < n) a.alpha[dst + hh * a.alpha_stride + t] = src[hh * 32 + t];
+  const int t = lane & 31;
+  const int half = lane >> 5;
+  for (int u0 = 0; u0 < sg.n; u0 += kFlushBatch) {
+    long dst[kFlushBatch];
+    int cnt[kFlushBatch];
+#pragma unroll
+    for (int i = 0; i < kFlushBatch; ++i) {
+      const int u = min(u0 + i, sg.n - 1);  // reads stay inside the staged units
+      dst[i] = sg.dst[u];
+      cnt[i] = sg.count[u];
+    }
+#pragma unroll
+    for (int i = 0; i < kFlushBatch; ++i)
+      if (u0 + i >= sg.n) cnt[i] = 0;  // past the last staged unit: nothing to write
+    for (int h0 = 0; h0 < G; h0 += 2) {
+      const bool real = h0 + half < G;
+      const int hh = real ? h0 + half : G - 1;
+      float v[kFlushBatch];
+#pragma unroll
+      for (int i = 0; i < kFlushBatch; ++i)
+        v[i] = sg.buf[min(u0 + i, sg.n - 1) * G * 32 + hh * 32 + t];
+#pragma unroll
+      for (int i = 0; i < kFlushBatch; ++i)
+        if (real && t < cnt[i]) a.alpha[dst[i] + hh * a.alpha_stride + t] = v[i];
     }
   }
   sg.n = 0;
