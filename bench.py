@@ -20,6 +20,7 @@ Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -464,6 +465,14 @@ def main():
     flush_buf = None
     re_kernels = "assign_tiers,reloc_scan,quantize_t2,reloc_stage,reloc_to_t1,reloc_to_t0,t2_scan,t2_move"
 
+    def release():
+        """Hand what the last run left (its cache, which may sit in reference cycles) back
+        to torch's caching allocator, so that the next run's cache takes the same blocks.
+        Memory returned to the driver (torch.cuda.empty_cache) is cleared by it in the
+        background, and that clearing took HBM bandwidth from the next run's timed steps
+        (3-4% fewer steps/s)."""
+        gc.collect()
+
     def run(timed_kernels, every=1, flush=False, attend_t2=False, alpha_scratch=False):
         """Fresh cache, W warm-up steps (at least Delta: the first reassignment is behind
         them), then exactly K steps between two syncs with the kernel timers on for
@@ -572,14 +581,14 @@ def main():
         reps.append((amortised_elapsed(r), r["elapsed"], r["re_alone"], r["issued"]))
         last = r
         del r["cache"]
-        torch.cuda.empty_cache()
+        release()
     att_reps = []
     for _ in range(max(1, (args.repeats + 1) // 2)):
         r = run(["attn_partial"])
         att_reps.append(r["kernels"].get("attn_partial", {}).get("avg_us", float("nan")))
         last_att = r
         del r["cache"]
-        torch.cuda.empty_cache()
+        release()
     elapsed = float(np.median([x[0] for x in reps]))
     attn_med = float(np.median(att_reps))
     n_att_steps, n_steps, re_info = last["n_att"], last["n_all"], last["re"]
@@ -684,7 +693,7 @@ def main():
         # a real decode streams the model weights between two visits of a layer, which
         # evicts the memory-side cache: the same steps with 512 MB read before each one
         del cache, bd
-        torch.cuda.empty_cache()
+        release()
         print("[bench] cache-flushed run", file=sys.stderr, flush=True)
         flush_buf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
         fr = run(["attn_partial"], flush=True)
@@ -709,11 +718,11 @@ def main():
     for r in sr:
         del r["cache"]
     del sr
-    torch.cuda.empty_cache()
+    release()
     if not args.no_t2_leg:
         # the variant that attends the 8-bit T2 rows after T1: same inputs and policy
         del cache
-        torch.cuda.empty_cache()
+        release()
         print("[bench] attended-T2 run", file=sys.stderr, flush=True)
         tr = run(["attn_partial"], attend_t2=True)
         cache = tr["cache"]
@@ -734,7 +743,7 @@ def main():
         # layer l + 1): the whole step as the pages describe it, host-link bound
         from tiered_kv_cache_amd.driver import T1Stream
         del cache
-        torch.cuda.empty_cache()
+        release()
         print("[bench] streamed-T1 run", file=sys.stderr, flush=True)
         cache = dw.make_cache(contexts=contexts, t0_budget=True, per_sequence=True)
         stream = T1Stream(cache, chunk_layers=args.stream_chunk)
