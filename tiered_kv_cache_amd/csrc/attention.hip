@@ -36,7 +36,8 @@
 //       values are requested as soon as this unit has consumed its own.  The
 //       logits of a wave's units are staged in LDS and written in bursts once
 //       its key/value stream is done (stores interleaved with the stream slow
-//       its reads down).  The logits are kept in base 2 (q.k * softmax_scale *
+//       its reads down; a stage that fills before then is written with
+//       non-temporal stores).  The logits are kept in base 2 (q.k * softmax_scale *
 //       log2 e), so every weight is one v_exp_f32; they go to `alpha` and are
 //       normalised there by the merge kernels.  With a new token, the wave
 //       whose range holds the T0 unit of its slot also writes its key and
@@ -272,37 +273,51 @@ __device__ __forceinline__ void flush_record(const AttnArgs& a, long worker, int
   }
 }
 
-// Write every staged unit: 2 heads x 32 tokens per wave store.  Units go in
-// batches of kFlushBatch whose LDS reads are all issued before the first store
-// needs one: a store per LDS round trip would leave every wave ~5 round trips
-// per unit at the end of the launch, when nothing else hides them.
+// Write every staged unit.  Units go in batches of kFlushBatch whose LDS reads are
+// all issued before the first store needs one: a store per LDS round trip would leave
+// every wave ~5 round trips per unit at the end of the launch, when nothing else hides
+// them.  A store covers one head of two consecutive units (lanes 0-31 and 32-63): 256
+// contiguous bytes of a logit row when the units are consecutive.  NT: a flush made
+// while the wave still streams keys and values (its stage full) uses non-temporal
+// stores -- lines written with normal stores are held in the caches and written back in
+// the middle of the read stream, which on large launches cost more than the stores
+// themselves; the last flush of a wave uses normal stores, as the merge reads those
+// lines back next.  Whether the first kind goes out non-temporal is the launch's
+// `stage_nt`, set on the host (see launch_attn_partial).
 constexpr int kFlushBatch = 8;
 
+template <bool NT>
 __device__ __forceinline__ void flush_stage(const AttnArgs& a, int lane, int G, Stage& sg) {
+  constexpr int J = kFlushBatch / 2;  // unit pairs per batch
   const int t = lane & 31;
   const int half = lane >> 5;
   for (int u0 = 0; u0 < sg.n; u0 += kFlushBatch) {
-    long dst[kFlushBatch];
-    int cnt[kFlushBatch];
+    int src[J], cnt[J];
+    long dst[J];
 #pragma unroll
-    for (int i = 0; i < kFlushBatch; ++i) {
-      const int u = min(u0 + i, sg.n - 1);  // reads stay inside the staged units
-      dst[i] = sg.dst[u];
-      cnt[i] = sg.count[u];
+    for (int j = 0; j < J; ++j) {
+      src[j] = min(u0 + 2 * j + half, sg.n - 1);  // reads stay inside the staged units
+      dst[j] = sg.dst[src[j]];
+      cnt[j] = sg.count[src[j]];
     }
 #pragma unroll
-    for (int i = 0; i < kFlushBatch; ++i)
-      if (u0 + i >= sg.n) cnt[i] = 0;  // past the last staged unit: nothing to write
+    for (int j = 0; j < J; ++j)
+      if (u0 + 2 * j + half >= sg.n) cnt[j] = 0;  // past the last staged unit: nothing to write
     for (int h0 = 0; h0 < G; h0 += 2) {
-      const bool real = h0 + half < G;
-      const int hh = real ? h0 + half : G - 1;
-      float v[kFlushBatch];
+      float v[2][J];
 #pragma unroll
-      for (int i = 0; i < kFlushBatch; ++i)
-        v[i] = sg.buf[min(u0 + i, sg.n - 1) * G * 32 + hh * 32 + t];
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int i = 0; i < kFlushBatch; ++i)
-        if (real && t < cnt[i]) a.alpha[dst[i] + hh * a.alpha_stride + t] = v[i];
+        for (int j = 0; j < J; ++j) v[e][j] = sg.buf[(src[j] * G + min(h0 + e, G - 1)) * 32 + t];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (h0 + e < G && t < cnt[j]) {
+            float* p = a.alpha + dst[j] + (h0 + e) * a.alpha_stride + t;
+            if constexpr (NT) __builtin_nontemporal_store(v[e][j], p);
+            else *p = v[e][j];
+          }
     }
   }
   sg.n = 0;
@@ -642,7 +657,10 @@ __device__ __forceinline__ void process_unit(const AttnArgs& a, const Cursor& c,
     flush_record<D>(a, w, h, grp, G, st);
     begin_group<D, GEO>(a, c, h, grp, G, st);
   }
-  if (sg.n == sg.cap) flush_stage(a, lane, G, sg);
+  if (sg.n == sg.cap) {  // two instances: a store hint chosen at run time would be merged away
+    if (a.stage_nt) flush_stage<true>(a, lane, G, sg);
+    else flush_stage<false>(a, lane, G, sg);
+  }
   bf16x8_t phi, plo;
   const bool full = unit_full<Q8>(c);
   if constexpr (Q8) {  // 8-bit T2 rows (codes are finite: no tail clearing of values)
@@ -768,7 +786,7 @@ __global__ __launch_bounds__(256, 1) void attn_partial_mfma_kernel(AttnArgs a) {
     }
   }
   flush_record<D>(a, w, h, grp, G, st);
-  flush_stage(a, lane, G, sg);
+  flush_stage<false>(a, lane, G, sg);
 }
 
 // ---------------------------------------------------------------------------
@@ -1002,8 +1020,20 @@ int mfma_resident_waves(int head_dim) {
   return cached;
 }
 
-void launch_attn_partial(const AttnArgs& a, int kv_dtype, int head_dim, int group, hipStream_t s) {
+// Logit stages that fill before a wave's last load are written with non-temporal
+// stores when the launch's logits exceed the memory-side cache (256 MB on MI355X):
+// then their lines would only churn it, and written back in the middle of the
+// key/value stream they cost more than the stores (a 4 x 32K chain: 2.50 -> 2.22 ms).
+// Logits that fit stay cached until the merge reads them back (a 16-sequence batch
+// with 158 MB of logits: 0.54 ms, 0.57 ms with non-temporal stores).
+constexpr double kMemorySideCacheBytes = 256.0 * 1024 * 1024;
+
+void launch_attn_partial(const AttnArgs& args, int kv_dtype, int head_dim, int group,
+                         hipStream_t s) {
   KernelTimer timer("attn_partial", s);
+  AttnArgs a = args;
+  a.stage_nt = (double)a.total_units * a.unit * (a.hq / a.hkv) * sizeof(float) >
+               kMemorySideCacheBytes;
   if (kv_dtype == TKV_BF16) {
     dim3 grid((unsigned)((a.workers + 3) / 4));
     // variants: a T2 pool with rows in this launch; a T1 window of the call's layers

@@ -78,6 +78,7 @@ struct AttnArgs {
   long t1_rs;        // T1 window: elements between consecutive (sequence, layer, KV head) rows
   int io_L, io_l0;   // q / out / alpha rows: layers they hold per sequence, the call's first
   float scale;       // softmax_scale * log2(e): logits are kept in base 2
+  int stage_nt;      // logit stages that fill before a wave's last load go out non-temporal
   SeqTable seq;
   PoolTable pool;    // the T0 pool and (unless a window call) the T1 pool rows
   // append fused into the bf16 kernel (kn null: none).  The new row of sequence i
