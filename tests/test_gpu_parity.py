@@ -221,3 +221,14 @@ def test_chain32k_full_size_sampled():
     st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 64, 65, 128},
                      heads=heads, full_inc_steps={66}, byte_seqs={1})
     assert st["reassignments"] == 2 * 4
+
+
+def test_chain32k_per_sequence_pools_full_size_sampled():
+    # the bench's long-chain configuration: per-sequence pools, T0 at each sequence's
+    # budget; its 430 MB of logits per launch take the non-temporal stage flushes
+    wl = WORKLOADS["chain32k"]
+    heads = [(0, 0), (9, 12), (31, 31)]
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 65, 100, 128},
+                     heads=heads, full_inc_steps={70}, byte_seqs={0, 3},
+                     per_sequence=True, t0_budget=True)
+    assert st["reassignments"] == 2 * 4
