@@ -228,7 +228,7 @@ def test_chain32k_per_sequence_pools_full_size_sampled():
     # budget; its 430 MB of logits per launch take the non-temporal stage flushes
     wl = WORKLOADS["chain32k"]
     heads = [(0, 0), (9, 12), (31, 31)]
-    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={1, 65, 100, 128},
-                     heads=heads, full_inc_steps={70}, byte_seqs={0, 3},
+    st = run_sampled(wl, n_steps=wl.total_steps, sample_steps={65, 128},
+                     heads=heads, full_inc_steps={70}, byte_seqs={3},
                      per_sequence=True, t0_budget=True)
     assert st["reassignments"] == 2 * 4
